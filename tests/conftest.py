@@ -1,0 +1,23 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line(
+        "markers", "gpu: needs an MI355X (gfx950) GPU and the HIP library")
+
+
+@pytest.fixture(scope="session")
+def oracle_lib():
+    """The CPU oracle, built on first use if no build is present."""
+    import oracle
+    from oracle import _build
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    return oracle
