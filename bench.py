@@ -1,0 +1,372 @@
+#!/usr/bin/env python
+"""Benchmark of the fused-dequantize Q4_K GEMV on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5]
+
+Default workload: Q4_K GEMV, input_dim 4096 x output_dim 4096, batch 1,
+fp32 activations, 64 distinct weight copies (604 MB, more than twice the
+256 MB Infinity Cache) used in rotation so that every call streams its
+weights from HBM.  A step is one q4k_gemv call on the next copy.  Inputs
+are generated (seeded, synthetic) and copied to HBM before timing.  Calls
+are issued as replays of a captured HIP graph (one graph node per call),
+so the timed region holds kernel work, not Python launch overhead.
+
+Prints one JSON line: mean us/call (value), achieved GB/s of algorithmic
+bytes against the 8 TB/s HBM peak (roofline), and the CPU oracle timed on
+a bounded sample on this host (cpu_baseline).
+
+Other workloads (measurement of the sibling paths, same JSON shape):
+  c1  Q4_K GEMV 1024 x 1024, batch 1 (911 rotating copies)
+  c3  Q4_K FFN pair: up 4096->14336 then down 14336->4096, batch 1; a step
+      is the pair (9 rotating pairs)
+  c4  Q4_K prefill 64 tokens x 4096 -> 4096 (64 rotating weight copies)
+  c5  ternary GEMV 4096 x 4096, batch 1 (128 rotating copies)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+ROTATION_BYTES = 2 * 256 * 2 ** 20
+
+
+def kernel_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+GEMV_SRC = ["q4_packed_weight_amd/csrc/q4k_gemv.hip",
+            "q4_packed_weight_amd/csrc/device_common.h"]
+PREFILL_SRC = ["q4_packed_weight_amd/csrc/q4k_prefill.hip",
+               "q4_packed_weight_amd/csrc/device_common.h"]
+TERNARY_SRC = ["q4_packed_weight_amd/csrc/ternary_gemv.hip",
+               "q4_packed_weight_amd/csrc/device_common.h"]
+
+
+class Workload:
+    """Inputs resident on the GPU plus a `call(i)` that runs step i."""
+
+
+def make_workload(name, torch, binding, synth):
+    import numpy as np
+    dev = "cuda:0"
+    wl = Workload()
+    wl.name = name
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if name in ("c1", "c2"):
+        K = N = 1024 if name == "c1" else 4096
+        cfg = synth.C1_Q4K_1K if name == "c1" else synth.C2_Q4K_4K
+        wbytes = N * K // 256 * 144
+        copies = 64 if name == "c2" else -(-ROTATION_BYTES // wbytes)
+        wl.W = [to_dev(synth.q4k_weights(N, K, config=cfg, copy=c)) for c in range(copies)]
+        wl.x = to_dev(synth.activations(K, config=cfg))
+        wl.y = torch.empty(N, dtype=torch.float32, device=dev)
+        wl.call = lambda i: binding.q4k_gemv(wl.x, wl.W[i % copies], K, N, wl.y)
+        wl.copies = copies
+        wl.bytes = wbytes + 4 * K + 4 * N
+        wl.flops = 2 * K * N
+        wl.kernel = "q4k_gemv_kernel"
+        wl.src = GEMV_SRC
+        wl.config = {"workload": f"q4k_gemv {K}x{N} batch 1", "input_dim": K,
+                     "output_dim": N, "batch": 1, "rotating_copies": copies,
+                     "weight_bytes_per_copy": wbytes}
+        wl.metric = f"Q4_K GEMV us/call + achieved HBM GB/s (% peak) at {K}x{N}, batch 1"
+
+        def cpu(oracle):
+            w0 = wl.W[0].cpu().numpy()
+            x0 = wl.x.cpu().numpy()
+            return (lambda: oracle.q4k_gemv(x0, w0, K, N)), 1.0, f"oracle q4k_gemv {K}x{N}, full call"
+        wl.cpu = cpu
+    elif name == "c3":
+        K1, N1, K2, N2 = 4096, 14336, 14336, 4096
+        b1, b2 = N1 * K1 // 256 * 144, N2 * K2 // 256 * 144
+        copies = -(-ROTATION_BYTES // (b1 + b2))
+        wl.Wu = [to_dev(synth.q4k_weights(N1, K1, config=synth.C3_FFN, copy=c)) for c in range(copies)]
+        wl.Wd = [to_dev(synth.q4k_weights(N2, K2, config=synth.C3_FFN, copy=c, extra=1)) for c in range(copies)]
+        wl.xu = to_dev(synth.activations(K1, config=synth.C3_FFN))
+        wl.xd = to_dev(synth.activations(K2, config=synth.C3_FFN, extra=1))
+        wl.yu = torch.empty(N1, dtype=torch.float32, device=dev)
+        wl.yd = torch.empty(N2, dtype=torch.float32, device=dev)
+
+        def call(i):
+            binding.q4k_gemv(wl.xu, wl.Wu[i % copies], K1, N1, wl.yu)
+            binding.q4k_gemv(wl.xd, wl.Wd[i % copies], K2, N2, wl.yd)
+        wl.call = call
+        wl.copies = copies
+        wl.bytes = b1 + b2 + 4 * (K1 + N1 + K2 + N2)
+        wl.flops = 2 * (K1 * N1 + K2 * N2)
+        wl.kernel = "q4k_gemv_kernel"
+        wl.src = GEMV_SRC
+        wl.config = {"workload": "q4k_gemv FFN pair 4096->14336 + 14336->4096 batch 1",
+                     "rotating_pairs": copies}
+        wl.metric = "Q4_K FFN GEMV pair us/pair + achieved HBM GB/s (% peak), batch 1"
+
+        def cpu(oracle):
+            wu, wd = wl.Wu[0].cpu().numpy(), wl.Wd[0].cpu().numpy()
+            xu, xd = wl.xu.cpu().numpy(), wl.xd.cpu().numpy()
+            return (lambda: (oracle.q4k_gemv(xu, wu, K1, N1), oracle.q4k_gemv(xd, wd, K2, N2))), \
+                1.0, "oracle q4k_gemv up+down pair, full call"
+        wl.cpu = cpu
+    elif name == "c4":
+        M, K, N = 64, 4096, 4096
+        wbytes = N * K // 256 * 144
+        copies = 64
+        wl.W = [to_dev(synth.q4k_weights(N, K, config=synth.C4_PREFILL, copy=c)) for c in range(copies)]
+        wl.X = to_dev(synth.activations(K, n_tokens=M, config=synth.C4_PREFILL))
+        wl.Y = torch.empty(M, N, dtype=torch.float32, device=dev)
+        wl.call = lambda i: binding.q4k_matmul(wl.X, wl.W[i % copies], M, K, N, wl.Y)
+        wl.copies = copies
+        wl.bytes = wbytes + 4 * M * K + 4 * M * N
+        wl.flops = 2 * M * K * N
+        wl.kernel = "q4k_prefill"
+        wl.src = PREFILL_SRC
+        wl.config = {"workload": "q4k_matmul prefill 64 tokens x 4096 -> 4096",
+                     "tokens": M, "input_dim": K, "output_dim": N, "rotating_copies": copies}
+        wl.metric = "Q4_K prefill matmul us/call + achieved TFLOP/s (% fp16 MFMA peak), 64x4096x4096"
+
+        def cpu(oracle):
+            w0, X0 = wl.W[0].cpu().numpy(), wl.X.cpu().numpy()
+            return (lambda: oracle.q4k_matmul_part(X0, w0, M, K, N, (0, 2), (0, N))), M / 2, \
+                "oracle q4k_matmul on 2 of 64 token rows, scaled x32 to a call"
+        wl.cpu = cpu
+    elif name == "c5":
+        K = N = 4096
+        cbytes = N * K // 4
+        copies = -(-ROTATION_BYTES // cbytes)
+        wl.C = [to_dev(synth.ternary_codes(N, K, copy=c)[0]) for c in range(copies)]
+        wl.x = to_dev(synth.activations(K, config=synth.C5_TERNARY))
+        wl.scale = float(synth.ternary_scale())
+        wl.y = torch.empty(N, dtype=torch.float32, device=dev)
+        wl.call = lambda i: binding.ternary_gemv(wl.x, wl.C[i % copies], wl.scale, K, N, wl.y)
+        wl.copies = copies
+        wl.bytes = cbytes + 4 * K + 4 * N + 4
+        wl.flops = 2 * K * N
+        wl.kernel = "ternary_gemv_kernel"
+        wl.src = TERNARY_SRC
+        wl.config = {"workload": "ternary_gemv 4096x4096 batch 1", "input_dim": K,
+                     "output_dim": N, "rotating_copies": copies}
+        wl.metric = "Ternary GEMV us/call + achieved HBM GB/s (% peak) at 4096x4096, batch 1"
+
+        def cpu(oracle):
+            c0, x0 = wl.C[0].cpu().numpy(), wl.x.cpu().numpy()
+            return (lambda: oracle.ternary_gemv(x0, c0, wl.scale, K, N)), 1.0, \
+                "oracle ternary_gemv 4096x4096, full call"
+        wl.cpu = cpu
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    return wl
+
+
+def capture(torch, wl, start, count):
+    """A HIP graph of `count` consecutive steps starting at step `start`."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(start, start + count):
+                wl.call(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_steps(torch, wl, steps, launch, graphs):
+    """Mean ms per step over exactly `steps` steps, HIP events on the stream
+    the kernels run on."""
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    if launch == "eager":
+        for i in range(steps):
+            wl.call(i)
+    else:
+        full, rem = graphs
+        G = wl.copies
+        for _ in range(steps // G):
+            full.replay()
+        if rem is not None:
+            rem.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def context_measurements(torch, binding, wl, launch_graph_len):
+    """Launch floor (empty kernel) and a streaming read of the same rotating
+    weight copies, each as graph replays like the main measurement."""
+    out = {}
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s), torch.cuda.graph(g, stream=s):
+        for _ in range(launch_graph_len):
+            binding.bench_empty()
+    torch.cuda.current_stream().wait_stream(s)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    out["empty_kernel_us"] = round(e0.elapsed_time(e1) * 1000 / (reps * launch_graph_len), 3)
+
+    bufs = getattr(wl, "W", None) or getattr(wl, "C", None)
+    if bufs:
+        sink = torch.zeros(65536, dtype=torch.int32, device="cuda:0")
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s), torch.cuda.graph(g2, stream=s):
+            for b in bufs:
+                binding.bench_stream_read(b, sink)
+        torch.cuda.current_stream().wait_stream(s)
+        for _ in range(3):
+            g2.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g2.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000 / (reps * len(bufs))
+        nbytes = bufs[0].numel()
+        out["stream_read_same_bytes_us"] = round(us, 3)
+        out["stream_read_GBps"] = round(nbytes / us / 1e3, 1)
+    return out
+
+
+def cpu_baseline(wl, seconds):
+    import oracle
+    fn, scale, sample = wl.cpu(oracle)
+    fn()  # warm caches / page in
+    times = []
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end or len(times) < 3:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    med = times[len(times) // 2] * scale
+    return {"value": round(med * 1e6, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
+            "sample": f"{sample}; median of {len(times)} calls, single thread, "
+                      f"{os.cpu_count()} host cpus visible"}
+
+
+def traffic_for(wl):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_hash(wl.src):
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64000)
+    ap.add_argument("--warmup", type=int, default=6400)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the Q4_K GEMV path here has no multi-GPU form.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from q4_packed_weight_amd import binding, synth
+
+    binding.lib()  # fail loudly now if the HIP library is missing
+    wl = make_workload(args.workload, torch, binding, synth)
+    steps, warmup = args.steps, args.warmup
+    print(f"[bench] workload {wl.name}: {wl.config}", file=sys.stderr, flush=True)
+
+    graphs = None
+    if args.launch == "graph":
+        full = capture(torch, wl, 0, wl.copies)
+        rem = capture(torch, wl, 0, steps % wl.copies) if steps % wl.copies else None
+        graphs = (full, rem)
+        for _ in range(max(1, warmup // wl.copies)):
+            full.replay()
+    else:
+        for i in range(warmup):
+            wl.call(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done, timing {steps} steps", file=sys.stderr, flush=True)
+
+    ms = time_steps(torch, wl, steps, args.launch, graphs)
+    us = ms * 1000.0
+    torch.cuda.synchronize()
+    print(f"[bench] {us:.3f} us/step", file=sys.stderr, flush=True)
+
+    gbps = wl.bytes / us / 1e3
+    if wl.name == "c4":
+        tflops = wl.flops / us / 1e6
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": traffic_for(wl)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_for(wl)}
+
+    line = {
+        "metric": wl.metric,
+        "value": round(us, 3),
+        "unit": "us/call" if wl.name != "c3" else "us/pair",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy generators; random Q4_K blocks, N(0,1) activations)",
+        "config": dict(wl.config, launch="hipGraph replay, one node per call"
+                       if args.launch == "graph" else "eager, one ctypes call per step"),
+        "achieved_GBps": round(gbps, 1),
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "gflops": round(wl.flops / us / 1e3, 1),
+        "roofline": roof,
+        "algorithmic_bytes_per_step": wl.bytes,
+        "kernel_source_hash": kernel_hash(wl.src),
+    }
+    if not args.no_context:
+        line["context"] = context_measurements(torch, binding, wl, min(wl.copies, 256))
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * q4k.h -- C ABI of libq4k.so, the MI355X (gfx950) fused-dequantize Q4_K
+ * matrix-vector product, its batched (prefill) form and the ternary
+ * BitNet b1.58 sibling.
+ *
+ * Common contract for every compute entry point:
+ *   - x, w_blocks/codes and y are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees, synchronizes or keeps state; it
+ *     validates the arguments, enqueues its kernels on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream) and returns.
+ *   - Arguments are validated before anything is launched, in this order:
+ *     dimensions, then NULL pointers, then alignment.  On any error nothing
+ *     is launched and y is left untouched.
+ *   - y must not overlap x or the weights (not checked).
+ *   - Stateless and safe to call from any host thread on any stream.
+ *   - Results are deterministic: every output has exactly one writer and
+ *     the summation order depends only on the shapes.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef Q4K_H
+#define Q4K_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define Q4K_OK 0
+#define Q4K_EINVAL_DIM (-1) /* a dimension is <= 0 or not a multiple of the block size */
+#define Q4K_ENULL (-2)      /* a required pointer is NULL */
+#define Q4K_EALIGN (-3)     /* a pointer is not 16-byte aligned where required */
+#define Q4K_EHIP (-4)       /* the HIP runtime reported an error (see q4k_strerror) */
+
+/*
+ * Q4_K weight format (block_q4_K, 256 weights in 144 bytes), as the Q4_K
+ * page (SKaiNET PR #562, "feat(kernel): SIMD-fused Q4_K matmul kernel +
+ * Q4KMatmulKernel SPI", section "Pipeline") uses it:
+ *   bytes 0..1    d     binary16, little-endian
+ *   bytes 2..3    dmin  binary16, little-endian
+ *   bytes 4..15   eight 6-bit scales sc[s] and eight 6-bit mins m[s] in the
+ *                 ggml packing: s<4: sc=S[s]&63, m=S[s+4]&63; s>=4:
+ *                 sc=(S[s+4]&15)|(S[s-4]>>6)<<4, m=(S[s+4]>>4)|(S[s]>>6)<<4
+ *   bytes 16..143 qs; byte 32j+l holds position l of sub-block 2j in its low
+ *                 nibble and position l of sub-block 2j+1 in its high nibble
+ * Weight k of a block (sub-block s = k/32, code q) is d*sc[s]*q - dmin*m[s].
+ * The matrix is row-major [output_dim][input_dim/256] blocks: row o is the
+ * input_dim/256 consecutive blocks starting at byte o*(input_dim/256)*144.
+ */
+
+/*
+ * q4k_gemv -- y[o] = sum_k W[o,k] * x[k] for o < output_dim (batch 1).
+ * The fused Q4_K matrix-vector product of the Q4_K page, sections "Summary"
+ * and "Pipeline": every output is the per-sub-block lazy-dmin sum
+ * sum_s (d*sc[s]*sum_l q*x - dmin*m[s]*sum_l x), accumulated in fp32.
+ *   x          fp32 [input_dim], 16-byte aligned
+ *   w_blocks   uint8 [output_dim * input_dim/256 * 144], 16-byte aligned
+ *   input_dim  K; must be > 0 and a multiple of 256 (the page's test plan
+ *              rejects any other inputDim), else Q4K_EINVAL_DIM
+ *   output_dim N > 0
+ *   y          fp32 [output_dim]
+ * fp32 accumulation; agreement with the exact product is within about 1e-4
+ * relative (elementwise against 1e-4*|y| + 1e-4*rms(y)).  |x| should stay
+ * above ~1e-30 for full precision (codes enter the multiply scaled by 2^-24).
+ */
+int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+             int64_t output_dim, float *y, void *stream);
+
+/*
+ * q4k_matmul -- Y[r, o] = sum_k W[o,k] * X[r,k] for r < n_tokens: the
+ * batched (prefill) form.  Row r of X starts at X + r*input_dim and row r
+ * of Y at Y + r*output_dim, the row offsets of the ternary page's prefill
+ * row loop (SKaiNET issue #1138, section "Tasks"); the weights are read
+ * once per call for all tokens, the lesson of the tiling page (llama.cpp
+ * fork PR #37, "ggml-cpu: cache-aware tiling in ggml_compute_forward_mul_mat",
+ * section "Summary", fix 1).
+ *   X          fp32 [n_tokens, input_dim], 16-byte aligned
+ *   w_blocks   as for q4k_gemv
+ *   n_tokens   M > 0 (M == 1 runs q4k_gemv)
+ *   input_dim, output_dim as for q4k_gemv
+ *   Y          fp32 [n_tokens, output_dim]
+ * Same error behaviour and tolerance as q4k_gemv.  For M > 1 the
+ * activations pass through fp16 (split into a high and a low half) and must
+ * satisfy |x| < 65504.
+ */
+int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
+               int64_t input_dim, int64_t output_dim, float *Y, void *stream);
+
+/*
+ * Ternary BitNet b1.58 format (ternary page, SKaiNET issue #1138, section
+ * "Tasks"): four codes per byte in sequence; element i of a row is
+ * ((byte[i/4] >> 2*(i%4)) & 3) - 1, so field values 0, 1, 2 decode to
+ * -1, 0, +1 (field value 3 decodes to +2 by the same formula).  The matrix
+ * is row-major: row o is input_dim/4 bytes starting at o*input_dim/4.
+ */
+
+/*
+ * ternary_gemv_codes -- t[o] = sum_i code(o,i) * x[i]: the codes-dot with
+ * the scale NOT applied, the gemvPacked contract of the ternary page.
+ *   x          fp32 [input_dim] (any alignment; 16-byte alignment, together
+ *              with input_dim % 64 == 0 and 16-byte aligned codes, selects
+ *              the fast kernel)
+ *   codes      uint8 [output_dim * input_dim/4]
+ *   input_dim  K > 0 and a multiple of 4, else Q4K_EINVAL_DIM
+ *   output_dim N > 0
+ *   y          fp32 [output_dim]
+ * fp32 accumulation.  Exact (bit-equal to the exact result) whenever every
+ * x[i] is an integer and sum_i |x[i]| * 2 < 2^22.
+ */
+int ternary_gemv_codes(const float *x, const uint8_t *codes, int64_t input_dim,
+                       int64_t output_dim, float *y, void *stream);
+
+/*
+ * ternary_gemv -- y[o] = scale * t[o]: the per-tensor scale is multiplied
+ * after the codes-dot, as the ternary page's reference view kernel does
+ * (one fp32 rounding of scale * t).  Arguments as ternary_gemv_codes.
+ */
+int ternary_gemv(const float *x, const uint8_t *codes, float scale,
+                 int64_t input_dim, int64_t output_dim, float *y,
+                 void *stream);
+
+/*
+ * q4k_gemv_shaped -- q4k_gemv with an explicit launch shape, for sweeps and
+ * for the benchmark's launch configuration.  rows_per_lane in {1, 2, 4, 8}
+ * (rows whose partial sums one lane carries); k_waves in {1, 2, 4} (waves
+ * of one workgroup that split input_dim between them).  A value of 0 lets
+ * the library choose.  Any other value gives Q4K_EINVAL_DIM.  Results are
+ * within the q4k_gemv tolerance for every shape (the summation order
+ * depends on the shape).
+ */
+int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+                    int64_t output_dim, float *y, void *stream,
+                    int rows_per_lane, int k_waves);
+
+/* Static description of a return code; for Q4K_EHIP it includes the HIP
+ * error text of the failing call on this host thread. */
+const char *q4k_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4K_H */

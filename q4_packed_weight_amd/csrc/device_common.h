@@ -1,0 +1,57 @@
+// device_common.h -- small gfx950 device helpers shared by the GEMV kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4k {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The two binary16 halves of a dword as fp32.  When the result feeds an FMA
+// with an fp32 operand, the compiler folds the conversion into
+// v_fma_mix_f32 (op_sel picks the half), so a masked nibble or 2-bit field
+// sitting in a half's low bits acts as an exact fp16 subnormal
+// (value * 2^-24) at no conversion cost.
+__device__ __forceinline__ float half_lo(uint32_t v) {
+  return (float)__builtin_bit_cast(half2_t, v).x;
+}
+__device__ __forceinline__ float half_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(half2_t, v).y;
+}
+
+// Streaming (non-temporal) 16-byte load for data read exactly once.
+__device__ __forceinline__ uint4 load_stream16(const uint8_t *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float4 load_f4(const float *p) {
+  return *reinterpret_cast<const float4 *>(p);
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64);
+// every lane of the group receives the group sum.  Steps below 16 lanes use
+// DPP quad permutes and row mirrors; the 16- and 32-lane steps use
+// ds_swizzle-free bpermute via __shfl_xor (issued once per output).
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (width >= 2)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+        __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+  if constexpr (width >= 4)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+        __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+  if constexpr (width >= 8)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+        __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)); // row_half_mirror
+  if constexpr (width >= 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+        __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)); // row_mirror
+  if constexpr (width >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (width >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+}  // namespace q4k

@@ -1,0 +1,108 @@
+// q4k_capi.hip -- the C ABI of libq4k.so: argument validation, launch-shape
+// selection and dispatch to the kernels.  Declarations and the contract are
+// in include/q4k.h.
+#include <stdio.h>
+#include <string.h>
+
+#include "q4k.h"
+#include "q4k_internal.h"
+
+namespace {
+
+thread_local char g_hip_detail[256] = "";
+
+int hip_fail(hipError_t e, const char *what) {
+  snprintf(g_hip_detail, sizeof g_hip_detail, "%s: %s (%d)", what,
+           hipGetErrorString(e), (int)e);
+  return Q4K_EHIP;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest input_dim accepted: keeps every in-kernel index within 32 bits.
+constexpr int64_t kMaxInputDim = (int64_t)1 << 30;
+
+int check_q4k(const void *x, const uint8_t *w, const void *y, int64_t M,
+              int64_t K, int64_t N) {
+  if (M <= 0 || K <= 0 || N <= 0 || K % 256 != 0 || K > kMaxInputDim)
+    return Q4K_EINVAL_DIM;
+  if (!x || !w || !y) return Q4K_ENULL;
+  if (!aligned16(x) || !aligned16(w)) return Q4K_EALIGN;
+  return Q4K_OK;
+}
+
+int check_ternary(const void *x, const uint8_t *c, const void *y, int64_t K,
+                  int64_t N) {
+  if (K <= 0 || N <= 0 || K % 4 != 0 || K > kMaxInputDim) return Q4K_EINVAL_DIM;
+  if (!x || !c || !y) return Q4K_ENULL;
+  return Q4K_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+                    int64_t output_dim, float *y, void *stream,
+                    int rows_per_lane, int k_waves) {
+  int rc = check_q4k(x, w_blocks, y, 1, input_dim, output_dim);
+  if (rc) return rc;
+  if (!(rows_per_lane == 0 || rows_per_lane == 1 || rows_per_lane == 2 ||
+        rows_per_lane == 4 || rows_per_lane == 8) ||
+      !(k_waves == 0 || k_waves == 1 || k_waves == 2 || k_waves == 4))
+    return Q4K_EINVAL_DIM;
+  const int64_t nb = input_dim / 256;
+  const q4k::GemvShape s = q4k::choose_gemv_shape(nb, output_dim, rows_per_lane, k_waves);
+  hipError_t e = q4k::gemv_launch(x, w_blocks, y, nb, output_dim, s,
+                                  (hipStream_t)stream);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_gemv launch");
+}
+
+int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+             int64_t output_dim, float *y, void *stream) {
+  return q4k_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0);
+}
+
+int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
+               int64_t input_dim, int64_t output_dim, float *Y, void *stream) {
+  int rc = check_q4k(X, w_blocks, Y, n_tokens, input_dim, output_dim);
+  if (rc) return rc;
+  if (n_tokens == 1) return q4k_gemv(X, w_blocks, input_dim, output_dim, Y, stream);
+  hipError_t e = q4k::prefill_launch(X, w_blocks, n_tokens, input_dim,
+                                     output_dim, Y, (hipStream_t)stream);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_matmul launch");
+}
+
+int ternary_gemv_codes(const float *x, const uint8_t *codes, int64_t input_dim,
+                       int64_t output_dim, float *y, void *stream) {
+  int rc = check_ternary(x, codes, y, input_dim, output_dim);
+  if (rc) return rc;
+  hipError_t e = q4k::ternary_launch(x, codes, 1.0f, false, input_dim,
+                                     output_dim, y, (hipStream_t)stream);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "ternary_gemv_codes launch");
+}
+
+int ternary_gemv(const float *x, const uint8_t *codes, float scale,
+                 int64_t input_dim, int64_t output_dim, float *y,
+                 void *stream) {
+  int rc = check_ternary(x, codes, y, input_dim, output_dim);
+  if (rc) return rc;
+  hipError_t e = q4k::ternary_launch(x, codes, scale, true, input_dim,
+                                     output_dim, y, (hipStream_t)stream);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "ternary_gemv launch");
+}
+
+const char *q4k_strerror(int code) {
+  switch (code) {
+    case Q4K_OK: return "ok";
+    case Q4K_EINVAL_DIM:
+      return "invalid dimension: every dimension must be > 0, input_dim a "
+             "multiple of 256 for Q4_K (of 4 for ternary) and at most 2^30";
+    case Q4K_ENULL: return "a required pointer is NULL";
+    case Q4K_EALIGN: return "x and the Q4_K blocks must be 16-byte aligned";
+    case Q4K_EHIP: return g_hip_detail[0] ? g_hip_detail : "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

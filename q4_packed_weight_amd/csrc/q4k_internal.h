@@ -1,0 +1,27 @@
+// q4k_internal.h -- declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4k {
+
+// Launch shape of the Q4_K GEMV kernel.
+struct GemvShape {
+  int lanes = 64;         // lanes spanning the slabs of one row: 16, 32 or 64
+  int rows_per_lane = 4;  // rows whose partial sums one lane carries: 1, 2, 4, 8
+  int k_waves = 1;        // waves of a workgroup splitting input_dim: 1, 2, 4
+};
+
+GemvShape choose_gemv_shape(int64_t nb, int64_t N, int rows_per_lane, int k_waves);
+hipError_t gemv_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
+                       int64_t N, const GemvShape &s, hipStream_t stream);
+
+hipError_t ternary_launch(const float *x, const uint8_t *codes, float scale,
+                          bool apply_scale, int64_t K, int64_t N, float *y,
+                          hipStream_t stream);
+
+hipError_t prefill_launch(const float *X, const uint8_t *w, int64_t M,
+                          int64_t K, int64_t N, float *Y, hipStream_t stream);
+
+}  // namespace q4k

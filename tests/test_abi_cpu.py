@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/*.h declares, and rejects bad arguments before launching anything
+(the Q4_K page's test plan: inputDim not a multiple of 256 is rejected).
+
+The rejection calls pass fake, never-dereferenced pointers: validation runs
+before any HIP call, so these return without touching a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from q4_packed_weight_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from q4_packed_weight_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_headers_declare_the_boundary():
+    names = set(_declared_functions())
+    for n in ("q4k_gemv", "q4k_matmul", "ternary_gemv_codes", "ternary_gemv",
+              "q4k_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_every_export(lib):
+    from q4_packed_weight_amd import binding
+    assert set(_declared_functions()) == set(binding.EXPORTED)
+
+
+P = ctypes.c_void_p
+GOOD = P(0x10000)       # 16-byte aligned fake device addresses
+GOOD2 = P(0x20000)
+GOOD3 = P(0x30000)
+ODD = P(0x10004)
+
+
+@pytest.mark.parametrize("K", [255, 257, 4000, 0, -256, 1 << 31])
+def test_q4k_rejects_bad_input_dim(lib, K):
+    assert lib.q4k_gemv(GOOD, GOOD2, K, 16, GOOD3, None) == -1
+    assert lib.q4k_matmul(GOOD, GOOD2, 4, K, 16, GOOD3, None) == -1
+    assert lib.q4k_gemv_shaped(GOOD, GOOD2, K, 16, GOOD3, None, 0, 0) == -1
+
+
+@pytest.mark.parametrize("N", [0, -1])
+def test_q4k_rejects_bad_output_dim(lib, N):
+    assert lib.q4k_gemv(GOOD, GOOD2, 256, N, GOOD3, None) == -1
+    assert lib.q4k_matmul(GOOD, GOOD2, 2, 256, N, GOOD3, None) == -1
+
+
+@pytest.mark.parametrize("M", [0, -3])
+def test_q4k_matmul_rejects_bad_tokens(lib, M):
+    assert lib.q4k_matmul(GOOD, GOOD2, M, 256, 8, GOOD3, None) == -1
+
+
+def test_q4k_rejects_null_pointers(lib):
+    assert lib.q4k_gemv(None, GOOD2, 256, 8, GOOD3, None) == -2
+    assert lib.q4k_gemv(GOOD, None, 256, 8, GOOD3, None) == -2
+    assert lib.q4k_gemv(GOOD, GOOD2, 256, 8, None, None) == -2
+    assert lib.q4k_matmul(GOOD, None, 3, 256, 8, GOOD3, None) == -2
+
+
+def test_q4k_rejects_misaligned(lib):
+    assert lib.q4k_gemv(ODD, GOOD2, 256, 8, GOOD3, None) == -3
+    assert lib.q4k_gemv(GOOD, ODD, 256, 8, GOOD3, None) == -3
+    assert lib.q4k_matmul(GOOD, ODD, 3, 256, 8, GOOD3, None) == -3
+
+
+def test_dimension_error_takes_precedence(lib):
+    assert lib.q4k_gemv(None, ODD, 100, 8, None, None) == -1
+
+
+@pytest.mark.parametrize("rpl,kw", [(3, 0), (16, 1), (0, 3), (1, 8), (-1, 0)])
+def test_shaped_rejects_bad_launch_shape(lib, rpl, kw):
+    assert lib.q4k_gemv_shaped(GOOD, GOOD2, 256, 8, GOOD3, None, rpl, kw) == -1
+
+
+@pytest.mark.parametrize("K", [3, 5, 4098, 0, -4])
+def test_ternary_rejects_bad_input_dim(lib, K):
+    assert lib.ternary_gemv_codes(GOOD, GOOD2, K, 8, GOOD3, None) == -1
+    assert lib.ternary_gemv(GOOD, GOOD2, 1.0, K, 8, GOOD3, None) == -1
+
+
+def test_ternary_rejects_null(lib):
+    assert lib.ternary_gemv_codes(GOOD, None, 64, 8, GOOD3, None) == -2
+    assert lib.ternary_gemv(None, GOOD2, 2.0, 64, 8, GOOD3, None) == -2
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, 7):
+        s = lib.q4k_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert b"256" in lib.q4k_strerror(-1)
+
+
+def test_binding_raises_value_error_on_bad_dim(lib):
+    """The Python layer turns Q4K_EINVAL_DIM into ValueError, mirroring the
+    page's IllegalArgumentException."""
+    from q4_packed_weight_amd import binding
+    rc = lib.q4k_gemv(GOOD, GOOD2, 300, 1, GOOD3, None)
+    with pytest.raises(ValueError) as e:
+        binding._check(rc, "q4k_gemv")
+    assert e.value.code == binding.Q4K_EINVAL_DIM
+
+
+def test_bench_helpers_validate(lib):
+    assert lib.q4k_bench_stream_read(GOOD, 100, GOOD2, 4, None) == -1
+    assert lib.q4k_bench_stream_read(ODD, 160, GOOD2, 4, None) == -3
+    assert lib.q4k_bench_copy(GOOD, None, 160, None) == -2

@@ -1,0 +1,164 @@
+"""Q4_K GEMV on the GPU against the CPU oracle, through the C ABI.
+
+Parity bar: |y - ref| <= 1e-4*|ref| + 1e-4*rms(ref) elementwise (the Q4_K
+page's "within 1e-4 relative", read as in tests/tolerance.py); bit-exact
+where every product and partial sum is exact (one-hot and integer inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+from q4_packed_weight_amd import binding, synth
+from gpu_util import canary_intact, dev, host, out_with_canary
+from tolerance import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gemv(x, w, K, N, shape=None):
+    xd, wd = dev(x), dev(w)
+    buf, y = out_with_canary(N)
+    if shape is None:
+        binding.q4k_gemv(xd, wd, K, N, y)
+    else:
+        binding.q4k_gemv_shaped(xd, wd, K, N, y, *shape)
+    out = host(y)
+    assert canary_intact(buf, N), "write past the end of y"
+    return out
+
+
+# (K, N): single block, multi-block, multi-row, the page's 4096x64, ragged
+# slab counts (K/256 not a multiple of 16) and ragged row counts.
+SHAPES = [(256, 1), (512, 1), (256, 7), (4096, 64), (768, 37), (1280, 5),
+          (2304, 129), (3840, 333), (4352, 1000), (14336, 100), (1024, 1024),
+          (8192, 17), (256, 4097)]
+
+
+@pytest.mark.parametrize("K,N", SHAPES)
+def test_gemv_parity(oracle_lib, K, N):
+    w = synth.q4k_weights(N, K, config=10, copy=K + N)
+    x = synth.activations(K, config=10, copy=K + N)
+    y = run_gemv(x, w, K, N)
+    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=f"K={K} N={N}")
+
+
+@pytest.mark.parametrize("K,N,name", [(1024, 1024, "c1"), (4096, 4096, "c2"),
+                                      (4096, 14336, "c3-up"), (14336, 4096, "c3-down")])
+def test_gemv_parity_full_configs(oracle_lib, K, N, name):
+    cfg = {"c1": synth.C1_Q4K_1K, "c2": synth.C2_Q4K_4K}.get(name, synth.C3_FFN)
+    extra = 1 if name == "c3-down" else 0
+    w = synth.q4k_weights(N, K, config=cfg, extra=extra)
+    x = synth.activations(K, config=cfg, extra=extra)
+    y = run_gemv(x, w, K, N)
+    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=name)
+
+
+@pytest.mark.parametrize("rpl", [1, 2, 4, 8])
+@pytest.mark.parametrize("kw", [1, 2, 4])
+@pytest.mark.parametrize("K,N", [(4096, 333), (14336, 67), (1024, 129), (256, 50)])
+def test_every_launch_shape(oracle_lib, K, N, rpl, kw):
+    w = synth.q4k_weights(N, K, config=11, copy=K)
+    x = synth.activations(K, config=11, copy=K)
+    y = run_gemv(x, w, K, N, shape=(rpl, kw))
+    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=f"shape {rpl},{kw}")
+
+
+def test_one_hot_bit_exact_all_positions(oracle_lib):
+    """x = e_k: y[o] is the oracle's fp32 weight W[o,k] exactly (every other
+    term is an exact zero), for every k of a block -- pins the nibble and
+    sub-block mapping and the scale unpacking on the GPU."""
+    K, N = 256, 9
+    w = synth.q4k_weights(N, K, config=12)
+    wd = dev(w)
+    buf, y = out_with_canary(N)
+    X = np.eye(K, dtype=np.float32)
+    for k in range(K):
+        binding.q4k_gemv(dev(X[k]), wd, K, N, y)
+        got = host(y)
+        ref = oracle_lib.q4k_gemv(X[k], w, K, N).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), k
+    assert canary_intact(buf, N)
+
+
+def test_one_hot_bit_exact_sampled_large(oracle_lib):
+    K, N = 4096, 300
+    w = synth.q4k_weights(N, K, config=13)
+    wd = dev(w)
+    g = np.random.default_rng(3)
+    for k in g.choice(K, 48, replace=False):
+        x = np.zeros(K, np.float32)
+        x[k] = 1.0
+        buf, yd = out_with_canary(N)
+        binding.q4k_gemv(dev(x), wd, K, N, yd)
+        got = host(yd)
+        ref = oracle_lib.q4k_gemv(x, w, K, N).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), k
+
+
+@pytest.mark.parametrize("K,N", [(4096, 512), (14336, 64), (768, 100)])
+def test_integer_inputs_bit_exact(oracle_lib, K, N):
+    """d = dmin = 1, x in {-1, 0, 1}: all partial sums are integers below
+    2^24, so any summation order is exact and the GPU equals the oracle."""
+    w = synth.q4k_integer_weights(N, K, config=14)
+    x = synth.integer_activations(K, config=14)
+    y = run_gemv(x, w, K, N)
+    ref = oracle_lib.q4k_gemv(x, w, K, N)
+    assert np.all(ref == np.round(ref))
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+def test_zero_activation_exact_zero():
+    K, N = 4096, 256
+    w = synth.q4k_weights(N, K, config=15)
+    y = run_gemv(np.zeros(K, np.float32), w, K, N)
+    assert np.all(y == 0.0)
+
+
+def test_deterministic():
+    K, N = 4096, 1024
+    w = synth.q4k_weights(N, K, config=16)
+    x = synth.activations(K, config=16)
+    a = run_gemv(x, w, K, N)
+    b = run_gemv(x, w, K, N)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_many_rows_sampled(oracle_lib):
+    """2^20 rows of one block (151 MB of weights): sampled rows against the
+    oracle run on just those rows."""
+    K, N = 256, 1 << 20
+    w = synth.q4k_weights(N, K, config=17)
+    x = synth.activations(K, config=17)
+    y = run_gemv(x, w, K, N)
+    rows = np.random.default_rng(4).choice(N, 2000, replace=False)
+    rows = np.concatenate([rows, [0, N - 1]])
+    ref = oracle_lib.q4k_gemv(x, w[rows], K, len(rows))
+    assert_parity(y[rows], ref, what="sampled rows")
+
+
+def test_long_rows(oracle_lib):
+    """input_dim = 65536 (256 blocks per row)."""
+    K, N = 65536, 40
+    w = synth.q4k_weights(N, K, config=18)
+    x = synth.activations(K, config=18)
+    y = run_gemv(x, w, K, N)
+    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what="K=65536")
+
+
+def test_rejects_bad_input_dim_and_leaves_y_untouched():
+    x = torch.zeros(4000, dtype=torch.float32, device="cuda:0")
+    w = torch.zeros(144 * 16, dtype=torch.uint8, device="cuda:0")
+    buf, y = out_with_canary(8)
+    for K in (255, 257, 4000):
+        with pytest.raises(ValueError):
+            binding.q4k_gemv(x, w, K, 8, y)
+    torch.cuda.synchronize()
+    assert bool(torch.all(torch.isnan(buf)))
+
+
+def test_rejects_misaligned_weights():
+    x = torch.zeros(256, dtype=torch.float32, device="cuda:0")
+    w = torch.zeros(144 * 4 + 4, dtype=torch.uint8, device="cuda:0")
+    buf, y = out_with_canary(4)
+    with pytest.raises(ValueError):
+        binding.q4k_gemv(x, w[4:], 256, 4, y)
