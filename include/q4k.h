@@ -57,7 +57,8 @@ extern "C" {
  *   x          fp32 [input_dim], 16-byte aligned
  *   w_blocks   uint8 [output_dim * input_dim/256 * 144], 16-byte aligned
  *   input_dim  K; must be > 0 and a multiple of 256 (the page's test plan
- *              rejects any other inputDim), else Q4K_EINVAL_DIM
+ *              rejects any other inputDim) and at most 2^24, else
+ *              Q4K_EINVAL_DIM
  *   output_dim N > 0
  *   y          fp32 [output_dim]
  * fp32 accumulation; agreement with the exact product is within about 1e-4
@@ -102,7 +103,7 @@ int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
  *              with input_dim % 64 == 0 and 16-byte aligned codes, selects
  *              the fast kernel)
  *   codes      uint8 [output_dim * input_dim/4]
- *   input_dim  K > 0 and a multiple of 4, else Q4K_EINVAL_DIM
+ *   input_dim  K > 0, a multiple of 4 and at most 2^24, else Q4K_EINVAL_DIM
  *   output_dim N > 0
  *   y          fp32 [output_dim]
  * fp32 accumulation.  Exact (bit-equal to the exact result) whenever every
@@ -123,15 +124,16 @@ int ternary_gemv(const float *x, const uint8_t *codes, float scale,
 /*
  * q4k_gemv_shaped -- q4k_gemv with an explicit launch shape, for sweeps and
  * for the benchmark's launch configuration.  rows_per_lane in {1, 2, 4, 8}
- * (rows whose partial sums one lane carries); k_waves in {1, 2, 4} (waves
- * of one workgroup that split input_dim between them).  A value of 0 lets
- * the library choose.  Any other value gives Q4K_EINVAL_DIM.  Results are
- * within the q4k_gemv tolerance for every shape (the summation order
- * depends on the shape).
+ * (rows whose partial sums one lane carries), k_waves in {1, 2, 4} (waves
+ * of one workgroup that split input_dim between them), workgroup_waves in
+ * {1, 2, 4} (a multiple of k_waves).  A value of 0 lets the library choose
+ * (k_waves = 0 never exceeds the workgroup size).  Any other value gives
+ * Q4K_EINVAL_DIM.  Results are within the q4k_gemv tolerance for every
+ * shape (the summation order depends on the shape).
  */
 int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                     int64_t output_dim, float *y, void *stream,
-                    int rows_per_lane, int k_waves);
+                    int rows_per_lane, int k_waves, int workgroup_waves);
 
 /* Static description of a return code; for Q4K_EHIP it includes the HIP
  * error text of the failing call on this host thread. */

@@ -52,7 +52,7 @@ def lib():
         "q4k_matmul": [P, P, I64, I64, I64, P, P],
         "ternary_gemv_codes": [P, P, I64, I64, P, P],
         "ternary_gemv": [P, P, F, I64, I64, P, P],
-        "q4k_gemv_shaped": [P, P, I64, I64, P, P, I, I],
+        "q4k_gemv_shaped": [P, P, I64, I64, P, P, I, I, I],
         "q4k_bench_empty": [P],
         "q4k_bench_stream_read": [P, I64, P, I64, P],
         "q4k_bench_copy": [P, P, I64, P],
@@ -118,14 +118,15 @@ def q4k_gemv(x, w_blocks, input_dim, output_dim, y, stream=None):
 
 
 def q4k_gemv_shaped(x, w_blocks, input_dim, output_dim, y, rows_per_lane=0,
-                    k_waves=0, stream=None):
+                    k_waves=0, workgroup_waves=0, stream=None):
     K, N = int(input_dim), int(output_dim)
     _expect(x, torch.float32, "x", K if _pos(K, N) else 0)
     _expect(w_blocks, torch.uint8, "w_blocks", _q4k_need(K, N))
     _expect(y, torch.float32, "y", N if _pos(K, N) else 0)
     _check(lib().q4k_gemv_shaped(_ptr(x), _ptr(w_blocks), int(input_dim),
                                  int(output_dim), _ptr(y), _stream(stream),
-                                 int(rows_per_lane), int(k_waves)), "q4k_gemv_shaped")
+                                 int(rows_per_lane), int(k_waves), int(workgroup_waves)),
+           "q4k_gemv_shaped")
     return y
 
 

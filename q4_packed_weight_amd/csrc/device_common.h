@@ -8,6 +8,7 @@ namespace q4k {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // The two binary16 halves of a dword as fp32.  When the result feeds an FMA
 // with an fp32 operand, the compiler folds the conversion into
@@ -29,6 +30,26 @@ __device__ __forceinline__ uint4 load_stream16(const uint8_t *p) {
 
 __device__ __forceinline__ float4 load_f4(const float *p) {
   return *reinterpret_cast<const float4 *>(p);
+}
+
+// Raw buffer view of `bytes` bytes at `base` (gfx9 descriptor word 3):
+// loads at offsets past the end return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
+                                                          int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n,
+                                           0x00020000);
+}
+
+// 16-byte loads through a buffer view at a byte offset; the streaming form
+// sets the non-temporal hint (aux bit 1 on gfx94x/gfx950).
+__device__ __forceinline__ uint4 load_buf_stream16(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load_buf_f4(__amdgpu_buffer_rsrc_t r, int off) {
+  const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return make_float4(v.x, v.y, v.z, v.w);
 }
 
 // Sum over aligned groups of `width` lanes (width a power of two <= 64);

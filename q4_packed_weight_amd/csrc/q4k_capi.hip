@@ -19,8 +19,10 @@ int hip_fail(hipError_t e, const char *what) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Largest input_dim accepted: keeps every in-kernel index within 32 bits.
-constexpr int64_t kMaxInputDim = (int64_t)1 << 30;
+// Largest input_dim accepted (2^24): every buffer offset a kernel forms
+// (up to 128 rows of one workgroup, the whole activation vector) then stays
+// below 2^31.
+constexpr int64_t kMaxInputDim = (int64_t)1 << 24;
 
 int check_q4k(const void *x, const uint8_t *w, const void *y, int64_t M,
               int64_t K, int64_t N) {
@@ -44,15 +46,20 @@ extern "C" {
 
 int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                     int64_t output_dim, float *y, void *stream,
-                    int rows_per_lane, int k_waves) {
+                    int rows_per_lane, int k_waves, int workgroup_waves) {
   int rc = check_q4k(x, w_blocks, y, 1, input_dim, output_dim);
   if (rc) return rc;
-  if (!(rows_per_lane == 0 || rows_per_lane == 1 || rows_per_lane == 2 ||
-        rows_per_lane == 4 || rows_per_lane == 8) ||
-      !(k_waves == 0 || k_waves == 1 || k_waves == 2 || k_waves == 4))
+  const auto pow2_le = [](int v, int hi) {
+    return v == 0 || ((v & (v - 1)) == 0 && v > 0 && v <= hi);
+  };
+  if (!pow2_le(rows_per_lane, 8) || !pow2_le(k_waves, 4) ||
+      !pow2_le(workgroup_waves, 4))
     return Q4K_EINVAL_DIM;
+  const int wg = workgroup_waves ? workgroup_waves : 4;
+  if (k_waves > wg) return Q4K_EINVAL_DIM;
   const int64_t nb = input_dim / 256;
-  const q4k::GemvShape s = q4k::choose_gemv_shape(nb, output_dim, rows_per_lane, k_waves);
+  const q4k::GemvShape s = q4k::choose_gemv_shape(nb, output_dim, rows_per_lane,
+                                                  k_waves, workgroup_waves);
   hipError_t e = q4k::gemv_launch(x, w_blocks, y, nb, output_dim, s,
                                   (hipStream_t)stream);
   return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_gemv launch");
@@ -60,7 +67,7 @@ int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
 
 int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
              int64_t output_dim, float *y, void *stream) {
-  return q4k_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0);
+  return q4k_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0, 0);
 }
 
 int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
@@ -97,7 +104,7 @@ const char *q4k_strerror(int code) {
     case Q4K_OK: return "ok";
     case Q4K_EINVAL_DIM:
       return "invalid dimension: every dimension must be > 0, input_dim a "
-             "multiple of 256 for Q4_K (of 4 for ternary) and at most 2^30";
+             "multiple of 256 for Q4_K (of 4 for ternary) and at most 2^24";
     case Q4K_ENULL: return "a required pointer is NULL";
     case Q4K_EALIGN: return "x and the Q4_K blocks must be 16-byte aligned";
     case Q4K_EHIP: return g_hip_detail[0] ? g_hip_detail : "HIP runtime error";

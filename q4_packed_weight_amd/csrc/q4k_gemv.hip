@@ -37,7 +37,6 @@ namespace q4k {
 namespace {
 
 constexpr int kBlockBytes = 144;
-constexpr int kThreads = 256;
 
 // Per-lane decoded header values for the lane's two sub-blocks.
 struct SlabScales {
@@ -92,17 +91,38 @@ __device__ __forceinline__ void nibble_dots(uint32_t w, float4 xl, float4 xh,
 
 __device__ __forceinline__ float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
 
-template <int L, int R, int KW>
-__global__ __launch_bounds__(kThreads) void q4k_gemv_kernel(
-    const float *__restrict__ x, const uint8_t *__restrict__ w,
-    float *__restrict__ y, int nb, int64_t N) {
-  constexpr int G = 64 / L;         // rows side by side in one wave instruction
-  constexpr int RG = (kThreads / 64) / KW;  // row groups (of KW waves) per workgroup
-  constexpr int ROWS_W = G * R;     // rows per wave
-  __shared__ float partial[KW > 1 ? (kThreads / 64) * ROWS_W * 2 : 1];
+template <int L, int R, int KW, int W>
+__global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
+    const float *x, const uint8_t *w, float *__restrict__ y, int nb,
+    int64_t N) {
+  // x and w are deliberately not __restrict__: that keeps their loads
+  // ordered before the compiler fence that closes each load phase.
+  constexpr int kThreads = 64 * W;          // W waves per workgroup
+  constexpr int G = 64 / L;                 // rows side by side in one wave instruction
+  constexpr int RG = W / KW;                // row groups (of KW waves) per workgroup
+  constexpr int ROWS_W = G * R;             // rows per wave
+  constexpr int BPS = L / 4;                // blocks of one row covered by one step
+  constexpr int CH_ROW = BPS * 9;           // 16-byte chunks of one row per step
+  constexpr int TILE = ROWS_W * CH_ROW;     // chunks of a wave's weight tile
+  constexpr int NM = (TILE + 63) / 64;      // load instructions per tile
+  constexpr int S = KW * L;                 // slabs whose activations are staged together
+  constexpr int SP = S + 1;                 // padded row of the staged layout (float4)
+  constexpr int XQ = 16 * S / kThreads;     // staged float4 per thread
+  static_assert(16 * S % kThreads == 0, "staging must divide evenly");
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Staged activations: float4 k of slab ls at slot k*SP + ls.  A wave
+  // reading float4 k of consecutive slabs touches consecutive slots, and the
+  // one-slot pad per k-row spreads the staging writes (16 k of one slab per
+  // 16 lanes) over distinct banks.  Then the two sub-block sums of each
+  // staged slab, and one weight tile per wave.
+  __shared__ float4 xs4[16 * SP];
+  __shared__ float2 xsum[S];
+  __shared__ uint4 wt[W][TILE];
+  __shared__ float partial[KW > 1 ? W * ROWS_W : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int kw = wave % KW;
   const int rg = wave / KW;
   const int g = lane / L;
@@ -110,162 +130,209 @@ __global__ __launch_bounds__(kThreads) void q4k_gemv_kernel(
   const int64_t row0 = (int64_t)blockIdx.x * (RG * ROWS_W) + (int64_t)rg * ROWS_W;
   const int n_slabs = 4 * nb;
   const int steps = (n_slabs + L - 1) / L;
+  const int iters = (steps + KW - 1) / KW;
   const int64_t row_bytes = (int64_t)nb * kBlockBytes;
+  const int j = u & 3;
+  const uint32_t sh = (uint32_t)(j & 1) * 16u;
+  const bool jhi = j >= 2;
+  const int ls = kw * L + u;  // this lane's slab within the staged range
+  // Range-checked buffer views: activations, and this workgroup's rows of
+  // the weight matrix (rows past N read as zeros, so no clamping).
+  const int64_t wg_row0 = (int64_t)blockIdx.x * (RG * ROWS_W);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)nb * 1024);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(w + wg_row0 * row_bytes, (N - wg_row0) * row_bytes);
+  const int wave_off = (int)((row0 - wg_row0) * row_bytes);
 
-  float acc_c[R], acc_m[R];
+  float acc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc_c[r] = acc_m[r] = 0.0f;
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 
-  for (int t = kw; t < steps; t += KW) {
+  for (int it = 0; it < iters; ++it) {
+    // 1. Load phase.  Activations for staging first (coalesced, L2-resident,
+    //    they return first), then this wave's weight tile as a coalesced
+    //    stream: chunk q of the tile is row q / CH_ROW of the wave, chunk
+    //    q % CH_ROW of this step's piece of that row.  Slabs past the end of
+    //    x and rows past N read as zeros; blocks past the end of a row read
+    //    the next row's bytes and are never consumed.
+    const int slab_base = it * S;
+    float4 xv[XQ];
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+      const int f = tid + kThreads * q;
+      xv[q] = load_buf_f4(xr, 4 * (64 * (slab_base + (f >> 4)) + 4 * (f & 15)));
+    }
+    const int t = it * KW + kw;
+    const int b0 = t * BPS;
+    uint4 wv[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int q = 64 * m + lane;
+      const int rt = q / CH_ROW;
+      const int within = q - rt * CH_ROW;
+      wv[m] = load_buf_stream16(wr, wave_off + rt * (int)row_bytes + b0 * kBlockBytes + 16 * within);
+    }
+    // Keep the LDS stores below from being hoisted above the load phase.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. Stage the activations and their sub-block sums (the 8 float4 of a
+    //    sub-block sit in 8 aligned lanes); only the activation loads are
+    //    waited for, the weight stream keeps flowing.
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+      const int f = tid + kThreads * q;
+      const int sl = f >> 4, k = f & 15;
+      xs4[k * SP + sl] = xv[q];
+      const float part = group_sum<8>(sum4(xv[q]));
+      if (k == 0) xsum[sl].x = part;
+      if (k == 8) xsum[sl].y = part;
+    }
+    __syncthreads();
+
+    // 3. Compute.  Before row slot r, the tile chunks that carry its rows
+    //    are written to this wave's LDS tile (waiting only for those loads),
+    //    then each lane reads its slab's header and 32 qs bytes back.
     const int i = t * L + u;
-    // Lanes past the last slab of a row add nothing; the whole slab body is
-    // predicated on this (no zero fill needed).
-    if (i >= n_slabs) continue;
-    const int b = i >> 2;
-    const int j = i & 3;
-    const uint32_t sh = (uint32_t)(j & 1) * 16u;
-    const bool jhi = j >= 2;
-
-    // Weight loads for all R rows first (the HBM stream), then activations.
-    // Rows past N read row N-1 instead: their sums are never stored.
-    uint4 hdr[R], q0[R], q1[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      int64_t row = row0 + (int64_t)r * G + g;
-      row = row < N ? row : N - 1;
-      const uint8_t *blk = w + row * row_bytes + (int64_t)b * kBlockBytes;
-      hdr[r] = load_stream16(blk);
-      q0[r] = load_stream16(blk + 16 + 32 * j);
-      q1[r] = load_stream16(blk + 32 + 32 * j);
-    }
+    const bool active = t < steps && i < n_slabs;
     float4 xl[8], xh[8];
-    const float *xs = x + 256 * (int64_t)b + 64 * j;
+    float2 xsm = make_float2(0.f, 0.f);
+    if (active) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      xl[k] = load_f4(xs + 4 * k);
-      xh[k] = load_f4(xs + 32 + 4 * k);
+      for (int k = 0; k < 8; ++k) {
+        xl[k] = xs4[k * SP + ls];
+        xh[k] = xs4[(k + 8) * SP + ls];
+      }
+      xsm = xsum[ls];
     }
-    // Lazy-dmin input sums of the two sub-blocks, once per slab.
-    float xsum_lo = 0.f, xsum_hi = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      xsum_lo += sum4(xl[k]);
-      xsum_hi += sum4(xh[k]);
-    }
-
+    const int bl = u >> 2;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float s_lo = 0.f, s_hi = 0.f;
-      const uint32_t qw[8] = {q0[r].x, q0[r].y, q0[r].z, q0[r].w,
-                              q1[r].x, q1[r].y, q1[r].z, q1[r].w};
+      const int prev_last = r == 0 ? -1 : (r * G * CH_ROW - 1) / 64;
+      const int last_m = ((r + 1) * G * CH_ROW - 1) / 64;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) nibble_dots(qw[k], xl[k], xh[k], s_lo, s_hi);
-      const SlabScales sc = decode_header(hdr[r], sh, jhi);
-      // code part in units of 2^-20: 16*sc_lo*s_lo + sc_hi*s_hi
-      const float tc = __builtin_fmaf(sc.sc_lo16, s_lo, sc.sc_hi * s_hi);
-      const float tm = __builtin_fmaf(sc.m_lo, xsum_lo, sc.m_hi * xsum_hi);
-      acc_c[r] = __builtin_fmaf(sc.d, tc, acc_c[r]);
-      acc_m[r] = __builtin_fmaf(sc.dmin, tm, acc_m[r]);
+      for (int m = 0; m < NM; ++m)
+        if (m > prev_last && m <= last_m && 64 * m + lane < TILE) wt[wave][64 * m + lane] = wv[m];
+      if (active) {
+        const int base = ((r * G + g) * BPS + bl) * 9;
+        const uint4 hdr = wt[wave][base];
+        const uint4 q0 = wt[wave][base + 1 + 2 * j];
+        const uint4 q1 = wt[wave][base + 2 + 2 * j];
+        float s_lo = 0.f, s_hi = 0.f;
+        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) nibble_dots(qw[k], xl[k], xh[k], s_lo, s_hi);
+        const SlabScales sc = decode_header(hdr, sh, jhi);
+        // code part in units of 2^-20: 16*sc_lo*s_lo + sc_hi*s_hi
+        const float tc = __builtin_fmaf(sc.sc_lo16, s_lo, sc.sc_hi * s_hi);
+        const float tm = __builtin_fmaf(sc.m_lo, xsm.x, sc.m_hi * xsm.y);
+        // this slab's contribution: d * 2^20 * tc - dmin * tm
+        acc[r] = __builtin_fmaf(sc.d * 0x1p20f, tc, __builtin_fmaf(-sc.dmin, tm, acc[r]));
+      }
     }
+    // every wave must be done with the staged activations before the next
+    // iteration overwrites them (the weight tile is private to the wave)
+    if (it + 1 < iters) __syncthreads();
   }
 
   // Reduce each row over the L lanes of its group.
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    acc_c[r] = group_sum<L>(acc_c[r]);
-    acc_m[r] = group_sum<L>(acc_m[r]);
-  }
+  for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(acc[r]);
 
   if constexpr (KW == 1) {
     if (u == 0) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int64_t row = row0 + (int64_t)r * G + g;
-        if (row < N) y[row] = __builtin_fmaf(acc_c[r], 0x1p20f, -acc_m[r]);
+        if (row < N) y[row] = acc[r];
       }
     }
   } else {
-    // partial[wave][row_in_wave][c|m]
+    // partial[wave][row_in_wave], summed over the KW waves in wave order
     if (u == 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int idx = (wave * ROWS_W + r * G + g) * 2;
-        partial[idx] = acc_c[r];
-        partial[idx + 1] = acc_m[r];
-      }
+      for (int r = 0; r < R; ++r) partial[wave * ROWS_W + r * G + g] = acc[r];
     }
     __syncthreads();
     if (kw == 0 && lane < ROWS_W) {
-      float c = 0.f, m = 0.f;
+      float v = 0.f;
 #pragma unroll
-      for (int k = 0; k < KW; ++k) {
-        const int idx = ((wave + k) * ROWS_W + lane) * 2;
-        c += partial[idx];
-        m += partial[idx + 1];
-      }
+      for (int k = 0; k < KW; ++k) v += partial[(wave + k) * ROWS_W + lane];
       const int64_t row = row0 + lane;
-      if (row < N) y[row] = __builtin_fmaf(c, 0x1p20f, -m);
+      if (row < N) y[row] = v;
     }
   }
 }
 
-template <int L, int R, int KW>
+template <int L, int R, int KW, int W>
 hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, int nb,
                        int64_t N, hipStream_t stream) {
   constexpr int G = 64 / L;
-  constexpr int RG = (kThreads / 64) / KW;
-  constexpr int64_t rows_per_wg = (int64_t)RG * G * R;
+  constexpr int64_t rows_per_wg = (int64_t)(W / KW) * G * R;
   const int64_t grid = (N + rows_per_wg - 1) / rows_per_wg;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((q4k_gemv_kernel<L, R, KW>), dim3((unsigned)grid),
-                     dim3(kThreads), 0, stream, x, w, y, nb, N);
+  hipLaunchKernelGGL((q4k_gemv_kernel<L, R, KW, W>), dim3((unsigned)grid),
+                     dim3(64 * W), 0, stream, x, w, y, nb, N);
   return hipGetLastError();
 }
 
 template <int L, int R>
-hipError_t launch_kw(int kw, const float *x, const uint8_t *w, float *y,
-                     int nb, int64_t N, hipStream_t s) {
-  switch (kw) {
-    case 1: return launch_gemv<L, R, 1>(x, w, y, nb, N, s);
-    case 2: return launch_gemv<L, R, 2>(x, w, y, nb, N, s);
-    default: return launch_gemv<L, R, 4>(x, w, y, nb, N, s);
+hipError_t launch_w(int waves, int kw, const float *x, const uint8_t *w,
+                    float *y, int nb, int64_t N, hipStream_t s) {
+  if (waves == 1) return launch_gemv<L, R, 1, 1>(x, w, y, nb, N, s);
+  if (waves == 2) {
+    if (kw == 1) return launch_gemv<L, R, 1, 2>(x, w, y, nb, N, s);
+    return launch_gemv<L, R, 2, 2>(x, w, y, nb, N, s);
   }
+  if (kw == 1) return launch_gemv<L, R, 1, 4>(x, w, y, nb, N, s);
+  if (kw == 2) return launch_gemv<L, R, 2, 4>(x, w, y, nb, N, s);
+  return launch_gemv<L, R, 4, 4>(x, w, y, nb, N, s);
 }
 
 template <int L>
-hipError_t launch_r(int r, int kw, const float *x, const uint8_t *w, float *y,
-                    int nb, int64_t N, hipStream_t s) {
-  switch (r) {
-    case 1: return launch_kw<L, 1>(kw, x, w, y, nb, N, s);
-    case 2: return launch_kw<L, 2>(kw, x, w, y, nb, N, s);
-    case 4: return launch_kw<L, 4>(kw, x, w, y, nb, N, s);
-    default: return launch_kw<L, 8>(kw, x, w, y, nb, N, s);
+hipError_t launch_r(const GemvShape &sh, const float *x, const uint8_t *w,
+                    float *y, int nb, int64_t N, hipStream_t s) {
+  switch (sh.rows_per_lane) {
+    case 1: return launch_w<L, 1>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
+    case 2: return launch_w<L, 2>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
+    case 4: return launch_w<L, 4>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
+    default: return launch_w<L, 8>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
   }
 }
 
 }  // namespace
 
 GemvShape choose_gemv_shape(int64_t nb, int64_t N, int rows_per_lane,
-                            int k_waves) {
+                            int k_waves, int waves) {
+  // Defaults measured on MI355X (graph-replayed calls over rotating
+  // weights): 4-wave workgroups, 4 rows per lane while that still gives
+  // every SIMD a wave, and a 2-way split of input_dim across the waves of a
+  // workgroup once a row needs several steps; small problems fall back to
+  // smaller workgroups so that every CU gets one.
   GemvShape s;
   const int64_t slabs = 4 * nb;
   s.lanes = slabs <= 16 ? 16 : (slabs <= 32 ? 32 : 64);
   const int64_t steps = (slabs + s.lanes - 1) / s.lanes;
   const int64_t g = 64 / s.lanes;
-  if (k_waves > 0) {
-    s.k_waves = k_waves;
-  } else {
-    s.k_waves = steps >= 4 ? 4 : (steps >= 2 ? 2 : 1);
-  }
+  s.k_waves = k_waves > 0 ? k_waves : (steps >= 2 ? 2 : 1);
   if (rows_per_lane > 0) {
     s.rows_per_lane = rows_per_lane;
   } else {
-    // Enough waves to give every SIMD of the 256 CUs at least one.
     const int64_t target_waves = 1024;
     int r = 4;
     while (r > 1 && (N + g * r - 1) / (g * r) * s.k_waves < target_waves) r /= 2;
     s.rows_per_lane = r;
   }
+  if (waves > 0) {
+    s.waves = waves;
+  } else {
+    s.waves = 4;
+    while (s.waves > s.k_waves &&
+           (N + (s.waves / s.k_waves) * g * s.rows_per_lane - 1) /
+                   ((s.waves / s.k_waves) * g * s.rows_per_lane) < 256)
+      s.waves /= 2;
+  }
+  if (s.k_waves > s.waves) s.k_waves = s.waves;
   return s;
 }
 
@@ -273,9 +340,9 @@ hipError_t gemv_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
                        int64_t N, const GemvShape &s, hipStream_t stream) {
   const int nbi = (int)nb;
   switch (s.lanes) {
-    case 16: return launch_r<16>(s.rows_per_lane, s.k_waves, x, w, y, nbi, N, stream);
-    case 32: return launch_r<32>(s.rows_per_lane, s.k_waves, x, w, y, nbi, N, stream);
-    default: return launch_r<64>(s.rows_per_lane, s.k_waves, x, w, y, nbi, N, stream);
+    case 16: return launch_r<16>(s, x, w, y, nbi, N, stream);
+    case 32: return launch_r<32>(s, x, w, y, nbi, N, stream);
+    default: return launch_r<64>(s, x, w, y, nbi, N, stream);
   }
 }
 

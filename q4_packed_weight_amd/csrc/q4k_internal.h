@@ -11,9 +11,11 @@ struct GemvShape {
   int lanes = 64;         // lanes spanning the slabs of one row: 16, 32 or 64
   int rows_per_lane = 4;  // rows whose partial sums one lane carries: 1, 2, 4, 8
   int k_waves = 1;        // waves of a workgroup splitting input_dim: 1, 2, 4
+  int waves = 4;          // waves per workgroup: 1, 2, 4 (a multiple of k_waves)
 };
 
-GemvShape choose_gemv_shape(int64_t nb, int64_t N, int rows_per_lane, int k_waves);
+GemvShape choose_gemv_shape(int64_t nb, int64_t N, int rows_per_lane, int k_waves,
+                            int waves);
 hipError_t gemv_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
                        int64_t N, const GemvShape &s, hipStream_t stream);
 

@@ -9,7 +9,7 @@ namespace q4k {
 hipError_t prefill_launch(const float *X, const uint8_t *w, int64_t M,
                           int64_t K, int64_t N, float *Y, hipStream_t stream) {
   const int64_t nb = K / 256;
-  const GemvShape s = choose_gemv_shape(nb, N, 0, 0);
+  const GemvShape s = choose_gemv_shape(nb, N, 0, 0, 0);
   for (int64_t r = 0; r < M; ++r) {
     hipError_t e = gemv_launch(X + r * K, w, Y + r * N, nb, N, s, stream);
     if (e != hipSuccess) return e;

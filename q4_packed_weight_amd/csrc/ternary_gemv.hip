@@ -51,17 +51,20 @@ __global__ __launch_bounds__(kThreads) void ternary_gemv_kernel(
   float xsum = 0.f;
 
   for (int i = lane; i < n_items; i += 64) {
-    uint4 cw[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t row = row0 + r;
-      cw[r] = row < N ? load_stream16(codes + row * row_bytes + 16 * (int64_t)i)
-                      : make_uint4(0, 0, 0, 0);
-    }
+    // Load phase: activations first (L2-resident), then the codes of all R
+    // rows; nothing is consumed before every load is issued.  Rows past N
+    // read row N-1 instead: their sums are never stored.
     float4 xq[16];
     const float *xs = x + 64 * (int64_t)i;
 #pragma unroll
     for (int k = 0; k < 16; ++k) xq[k] = load_f4(xs + 4 * k);
+    uint4 cw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row0 + r < N ? row0 + r : N - 1;
+      cw[r] = load_stream16(codes + row * row_bytes + 16 * (int64_t)i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 16; ++k) xsum += (xq[k].x + xq[k].y) + (xq[k].z + xq[k].w);
 

@@ -59,11 +59,11 @@ GOOD3 = P(0x30000)
 ODD = P(0x10004)
 
 
-@pytest.mark.parametrize("K", [255, 257, 4000, 0, -256, 1 << 31])
+@pytest.mark.parametrize("K", [255, 257, 4000, 0, -256, 1 << 31, (1 << 24) + 256])
 def test_q4k_rejects_bad_input_dim(lib, K):
     assert lib.q4k_gemv(GOOD, GOOD2, K, 16, GOOD3, None) == -1
     assert lib.q4k_matmul(GOOD, GOOD2, 4, K, 16, GOOD3, None) == -1
-    assert lib.q4k_gemv_shaped(GOOD, GOOD2, K, 16, GOOD3, None, 0, 0) == -1
+    assert lib.q4k_gemv_shaped(GOOD, GOOD2, K, 16, GOOD3, None, 0, 0, 0) == -1
 
 
 @pytest.mark.parametrize("N", [0, -1])
@@ -94,9 +94,11 @@ def test_dimension_error_takes_precedence(lib):
     assert lib.q4k_gemv(None, ODD, 100, 8, None, None) == -1
 
 
-@pytest.mark.parametrize("rpl,kw", [(3, 0), (16, 1), (0, 3), (1, 8), (-1, 0)])
-def test_shaped_rejects_bad_launch_shape(lib, rpl, kw):
-    assert lib.q4k_gemv_shaped(GOOD, GOOD2, 256, 8, GOOD3, None, rpl, kw) == -1
+@pytest.mark.parametrize("rpl,kw,wg", [(3, 0, 0), (16, 1, 0), (0, 3, 0), (1, 8, 0),
+                                       (-1, 0, 0), (1, 1, 3), (1, 4, 2), (2, 2, 1),
+                                       (1, 1, 8)])
+def test_shaped_rejects_bad_launch_shape(lib, rpl, kw, wg):
+    assert lib.q4k_gemv_shaped(GOOD, GOOD2, 256, 8, GOOD3, None, rpl, kw, wg) == -1
 
 
 @pytest.mark.parametrize("K", [3, 5, 4098, 0, -4])

@@ -54,13 +54,13 @@ def test_gemv_parity_full_configs(oracle_lib, K, N, name):
 
 
 @pytest.mark.parametrize("rpl", [1, 2, 4, 8])
-@pytest.mark.parametrize("kw", [1, 2, 4])
+@pytest.mark.parametrize("kw,wg", [(1, 1), (1, 2), (2, 2), (1, 4), (2, 4), (4, 4)])
 @pytest.mark.parametrize("K,N", [(4096, 333), (14336, 67), (1024, 129), (256, 50)])
-def test_every_launch_shape(oracle_lib, K, N, rpl, kw):
+def test_every_launch_shape(oracle_lib, K, N, rpl, kw, wg):
     w = synth.q4k_weights(N, K, config=11, copy=K)
     x = synth.activations(K, config=11, copy=K)
-    y = run_gemv(x, w, K, N, shape=(rpl, kw))
-    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=f"shape {rpl},{kw}")
+    y = run_gemv(x, w, K, N, shape=(rpl, kw, wg))
+    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=f"shape {rpl},{kw},{wg}")
 
 
 def test_one_hot_bit_exact_all_positions(oracle_lib):
