@@ -21,6 +21,8 @@ Other workloads (measurement of the sibling paths, same JSON shape):
       is the pair (9 rotating pairs)
   c4  Q4_K prefill 64 tokens x 4096 -> 4096 (64 rotating weight copies)
   c5  ternary GEMV 4096 x 4096, batch 1 (128 rotating copies)
+  copy  plain 64 MiB device-to-device copy kernel (4 rotating buffer pairs):
+      the kernel of known traffic used to scale hardware byte counters
 """
 import argparse
 import hashlib
@@ -79,7 +81,7 @@ def make_workload(name, torch, binding, synth):
         wl.bytes = wbytes + 4 * K + 4 * N
         wl.flops = 2 * K * N
         wl.kernel = "q4k_gemv_kernel"
-        wl.src = GEMV_SRC
+        wl.src_files = GEMV_SRC
         wl.config = {"workload": f"q4k_gemv {K}x{N} batch 1", "input_dim": K,
                      "output_dim": N, "batch": 1, "rotating_copies": copies,
                      "weight_bytes_per_copy": wbytes}
@@ -109,7 +111,7 @@ def make_workload(name, torch, binding, synth):
         wl.bytes = b1 + b2 + 4 * (K1 + N1 + K2 + N2)
         wl.flops = 2 * (K1 * N1 + K2 * N2)
         wl.kernel = "q4k_gemv_kernel"
-        wl.src = GEMV_SRC
+        wl.src_files = GEMV_SRC
         wl.config = {"workload": "q4k_gemv FFN pair 4096->14336 + 14336->4096 batch 1",
                      "rotating_pairs": copies}
         wl.metric = "Q4_K FFN GEMV pair us/pair + achieved HBM GB/s (% peak), batch 1"
@@ -132,7 +134,7 @@ def make_workload(name, torch, binding, synth):
         wl.bytes = wbytes + 4 * M * K + 4 * M * N
         wl.flops = 2 * M * K * N
         wl.kernel = "q4k_prefill"
-        wl.src = PREFILL_SRC
+        wl.src_files = PREFILL_SRC
         wl.config = {"workload": "q4k_matmul prefill 64 tokens x 4096 -> 4096",
                      "tokens": M, "input_dim": K, "output_dim": N, "rotating_copies": copies}
         wl.metric = "Q4_K prefill matmul us/call + achieved TFLOP/s (% fp16 MFMA peak), 64x4096x4096"
@@ -155,7 +157,7 @@ def make_workload(name, torch, binding, synth):
         wl.bytes = cbytes + 4 * K + 4 * N + 4
         wl.flops = 2 * K * N
         wl.kernel = "ternary_gemv_kernel"
-        wl.src = TERNARY_SRC
+        wl.src_files = TERNARY_SRC
         wl.config = {"workload": "ternary_gemv 4096x4096 batch 1", "input_dim": K,
                      "output_dim": N, "rotating_copies": copies}
         wl.metric = "Ternary GEMV us/call + achieved HBM GB/s (% peak) at 4096x4096, batch 1"
@@ -165,6 +167,21 @@ def make_workload(name, torch, binding, synth):
             return (lambda: oracle.ternary_gemv(x0, c0, wl.scale, K, N)), 1.0, \
                 "oracle ternary_gemv 4096x4096, full call"
         wl.cpu = cpu
+    elif name == "copy":
+        nbytes = 64 * 2 ** 20
+        copies = 4
+        wl.src = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(c + 1) for c in range(copies)]
+        wl.dst = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for c in range(copies)]
+        wl.call = lambda i: binding.bench_copy(wl.src[i % copies], wl.dst[i % copies])
+        wl.copies = copies
+        wl.bytes = 2 * nbytes
+        wl.flops = 0
+        wl.kernel = "copy_kernel"
+        wl.src_files = ["q4_packed_weight_amd/csrc/bench_kernels.hip"]
+        wl.config = {"workload": "device copy 64 MiB (read 64 MiB + write 64 MiB)",
+                     "rotating_pairs": copies}
+        wl.metric = "copy kernel us/call + GB/s (read + write bytes)"
+        wl.cpu = None
     else:
         raise SystemExit(f"unknown workload {name}")
     return wl
@@ -230,6 +247,8 @@ def context_measurements(torch, binding, wl, launch_graph_len):
     out["empty_kernel_us"] = round(e0.elapsed_time(e1) * 1000 / (reps * launch_graph_len), 3)
 
     bufs = getattr(wl, "W", None) or getattr(wl, "C", None)
+    if wl.name == "copy":
+        bufs = None
     if bufs:
         sink = torch.zeros(65536, dtype=torch.int32, device="cuda:0")
         g2 = torch.cuda.CUDAGraph()
@@ -269,15 +288,20 @@ def cpu_baseline(wl, seconds):
                       f"{os.cpu_count()} host cpus visible"}
 
 
+TRAFFIC_FILES = {"c2": "q4k_gemv_4096x4096_b1.traffic.json"}
+
+
 def traffic_for(wl):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by the copy-kernel calibration), if
     it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
-    if not os.path.exists(path):
+    name = TRAFFIC_FILES.get(wl.name)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_hash") != kernel_hash(wl.src):
+    if t.get("kernel_hash") != kernel_hash(wl.src_files):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -287,7 +311,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64000)
     ap.add_argument("--warmup", type=int, default=6400)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "copy"])
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -355,14 +379,14 @@ def main():
                        if args.launch == "graph" else "eager, one ctypes call per step"),
         "achieved_GBps": round(gbps, 1),
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "gflops": round(wl.flops / us / 1e3, 1),
+        "gflops": round(wl.flops / us / 1e3, 1) if wl.flops else None,
         "roofline": roof,
         "algorithmic_bytes_per_step": wl.bytes,
-        "kernel_source_hash": kernel_hash(wl.src),
+        "kernel_source_hash": kernel_hash(wl.src_files),
     }
     if not args.no_context:
         line["context"] = context_measurements(torch, binding, wl, min(wl.copies, 256))
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl.cpu is not None:
         print(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

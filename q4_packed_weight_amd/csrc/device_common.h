@@ -52,6 +52,8 @@ __device__ __forceinline__ float4 load_buf_f4(__amdgpu_buffer_rsrc_t r, int off)
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
+__device__ __forceinline__ float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
+
 // Sum over aligned groups of `width` lanes (width a power of two <= 64);
 // every lane of the group receives the group sum.  Steps below 16 lanes use
 // DPP quad permutes and row mirrors; the 16- and 32-lane steps use

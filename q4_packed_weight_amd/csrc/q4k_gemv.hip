@@ -89,8 +89,6 @@ __device__ __forceinline__ void nibble_dots(uint32_t w, float4 xl, float4 xh,
   acc_hi = __builtin_fmaf(half_hi(hi13), xh.w, acc_hi);
 }
 
-__device__ __forceinline__ float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
-
 template <int L, int R, int KW, int W>
 __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
     const float *x, const uint8_t *w, float *__restrict__ y, int nb,

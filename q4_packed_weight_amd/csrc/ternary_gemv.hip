@@ -35,13 +35,30 @@ __device__ __forceinline__ float comp(float4 v, int f) {
 
 template <int R>
 __global__ __launch_bounds__(kThreads) void ternary_gemv_kernel(
-    const float *__restrict__ x, const uint8_t *__restrict__ codes,
-    float *__restrict__ y, float scale, int apply_scale, int n_items,
-    int64_t N) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t row0 = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * R;
-  const int64_t row_bytes = (int64_t)n_items * 16;
+    const float *x, const uint8_t *codes, float *__restrict__ y, float scale,
+    int apply_scale, int n_items, int64_t N) {
+  // x and codes are deliberately not __restrict__: that keeps their loads
+  // ordered before the compiler fence that closes each load phase.
+  constexpr int S = 64;                     // 16-byte items staged per iteration
+  constexpr int SP = S + 1;                 // padded row of the staged layout
+  constexpr int XQ = 16 * S / kThreads;     // staged float4 per thread
+  // Staged activations: float4 k of item it at slot k*SP + it (consecutive
+  // items in consecutive slots for the per-lane reads; the pad spreads the
+  // staging writes), and the activation sum of each staged item.
+  __shared__ float4 xs4[16 * SP];
+  __shared__ float xsum_item[S];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t wg_row0 = (int64_t)blockIdx.x * (kThreads / 64) * R;
+  const int64_t row0 = wg_row0 + (int64_t)wave * R;
+  const int row_bytes = n_items * 16;
+  // Range-checked views: rows past N and items past the end read as zeros.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)n_items * 256);
+  const __amdgpu_buffer_rsrc_t cr =
+      make_rsrc(codes + wg_row0 * row_bytes, (N - wg_row0) * (int64_t)row_bytes);
+  const int wave_off = wave * R * row_bytes;
 
   float acc[R][4];
 #pragma unroll
@@ -50,44 +67,63 @@ __global__ __launch_bounds__(kThreads) void ternary_gemv_kernel(
     for (int f = 0; f < 4; ++f) acc[r][f] = 0.f;
   float xsum = 0.f;
 
-  for (int i = lane; i < n_items; i += 64) {
-    // Load phase: activations first (L2-resident), then the codes of all R
-    // rows; nothing is consumed before every load is issued.  Rows past N
-    // read row N-1 instead: their sums are never stored.
-    float4 xq[16];
-    const float *xs = x + 64 * (int64_t)i;
+  const int iters = (n_items + S - 1) / S;
+  for (int it = 0; it < iters; ++it) {
+    // Load phase: activations for staging (coalesced), then the 16 code
+    // bytes of this lane's item in each of the R rows (coalesced rows).
+    const int item_base = it * S;
+    float4 xv[XQ];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) xq[k] = load_f4(xs + 4 * k);
+    for (int q = 0; q < XQ; ++q) {
+      const int f = tid + kThreads * q;
+      xv[q] = load_buf_f4(xr, 4 * (64 * (item_base + (f >> 4)) + 4 * (f & 15)));
+    }
+    const int i = item_base + lane;
     uint4 cw[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t row = row0 + r < N ? row0 + r : N - 1;
-      cw[r] = load_stream16(codes + row * row_bytes + 16 * (int64_t)i);
-    }
+    for (int r = 0; r < R; ++r) cw[r] = load_buf_stream16(cr, wave_off + r * row_bytes + 16 * i);
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) xsum += (xq[k].x + xq[k].y) + (xq[k].z + xq[k].w);
 
+    // Stage the activations and the per-item sums (the 16 float4 of an item
+    // sit in 16 aligned lanes).
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t dw[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+    for (int q = 0; q < XQ; ++q) {
+      const int f = tid + kThreads * q;
+      const int itm = f >> 4, k = f & 15;
+      xs4[k * SP + itm] = xv[q];
+      const float part = group_sum<16>(sum4(xv[q]));
+      if (k == 0) xsum_item[itm] = part;
+    }
+    __syncthreads();
+
+    if (i < n_items) {
+      float4 xq[16];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        // dword t holds positions 16t..16t+15: byte kb, field f -> 16t+4kb+f
-        const uint32_t w0 = dw[t];
-        const uint32_t w8 = w0 >> 8;
+      for (int k = 0; k < 16; ++k) xq[k] = xs4[k * SP + lane];
+      xsum += xsum_item[lane];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          const uint32_t mask = 0x00030003u << (2 * f);
-          const uint32_t a = w0 & mask;  // bytes 0 and 2
-          const uint32_t b = w8 & mask;  // bytes 1 and 3
-          acc[r][f] = __builtin_fmaf(half_lo(a), comp(xq[4 * t + 0], f), acc[r][f]);
-          acc[r][f] = __builtin_fmaf(half_lo(b), comp(xq[4 * t + 1], f), acc[r][f]);
-          acc[r][f] = __builtin_fmaf(half_hi(a), comp(xq[4 * t + 2], f), acc[r][f]);
-          acc[r][f] = __builtin_fmaf(half_hi(b), comp(xq[4 * t + 3], f), acc[r][f]);
+      for (int r = 0; r < R; ++r) {
+        const uint32_t dw[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          // dword t holds positions 16t..16t+15: byte kb, field f -> 16t+4kb+f
+          const uint32_t w0 = dw[t];
+          const uint32_t w8 = w0 >> 8;
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const uint32_t mask = 0x00030003u << (2 * f);
+            const uint32_t a = w0 & mask;  // bytes 0 and 2
+            const uint32_t b = w8 & mask;  // bytes 1 and 3
+            acc[r][f] = __builtin_fmaf(half_lo(a), comp(xq[4 * t + 0], f), acc[r][f]);
+            acc[r][f] = __builtin_fmaf(half_lo(b), comp(xq[4 * t + 1], f), acc[r][f]);
+            acc[r][f] = __builtin_fmaf(half_hi(a), comp(xq[4 * t + 2], f), acc[r][f]);
+            acc[r][f] = __builtin_fmaf(half_hi(b), comp(xq[4 * t + 3], f), acc[r][f]);
+          }
         }
       }
     }
+    if (it + 1 < iters) __syncthreads();
   }
 
   xsum = group_sum<64>(xsum);
@@ -136,6 +172,8 @@ hipError_t launch_fast(const float *x, const uint8_t *codes, float scale,
                        hipStream_t s) {
   const int64_t rows_per_wg = (kThreads / 64) * R;
   const int64_t grid = (N + rows_per_wg - 1) / rows_per_wg;
+  // per-workgroup code offsets must stay below 2^31
+  if (rows_per_wg * (K / 4) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((ternary_gemv_kernel<R>), dim3((unsigned)grid),
                      dim3(kThreads), 0, s, x, codes, y, scale, apply ? 1 : 0,
