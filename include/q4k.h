@@ -132,8 +132,9 @@ int ternary_gemv(const float *x, const uint8_t *codes, float scale,
  * for the benchmark's launch configuration.  rows_per_lane in {1, 2, 4, 8}
  * (rows whose partial sums one lane carries), k_waves in {1, 2, 4} (waves
  * of one workgroup that split input_dim between them), workgroup_waves in
- * {1, 2, 4} (a multiple of k_waves).  A value of 0 lets the library choose
- * (k_waves = 0 never exceeds the workgroup size).  Any other value gives
+ * {1, 2, 4, 8} (a multiple of k_waves; with 8 waves k_waves <= 2 and
+ * rows_per_lane <= 4).  A value of 0 lets the library choose (k_waves = 0
+ * never exceeds the workgroup size).  Any other value gives
  * Q4K_EINVAL_DIM.  Results are within the q4k_gemv tolerance for every
  * shape (the summation order depends on the shape).
  */

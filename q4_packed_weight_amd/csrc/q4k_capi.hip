@@ -53,10 +53,11 @@ int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
     return v == 0 || ((v & (v - 1)) == 0 && v > 0 && v <= hi);
   };
   if (!pow2_le(rows_per_lane, 8) || !pow2_le(k_waves, 4) ||
-      !pow2_le(workgroup_waves, 4))
+      !pow2_le(workgroup_waves, 8))
     return Q4K_EINVAL_DIM;
   const int wg = workgroup_waves ? workgroup_waves : 4;
-  if (k_waves > wg) return Q4K_EINVAL_DIM;
+  if (k_waves > wg || (wg == 8 && (k_waves == 4 || rows_per_lane == 8)))
+    return Q4K_EINVAL_DIM;
   const int64_t nb = input_dim / 256;
   const q4k::GemvShape s = q4k::choose_gemv_shape(nb, output_dim, rows_per_lane,
                                                   k_waves, workgroup_waves);

@@ -70,23 +70,25 @@ __device__ __forceinline__ SlabScales decode_header(uint4 h, uint32_t sh,
 }
 
 // Code dots of one qs dword (slab bytes 4t..4t+3): low nibbles against
-// xl[0..3], high nibbles against xh[0..3].  acc_lo is in units of 2^-24,
-// acc_hi in units of 2^-20 (the high nibble is used in place, times 16).
+// xl[0..3], high nibbles against xh[0..3].  The lo accumulators are in units
+// of 2^-24, the hi ones in units of 2^-20 (the high nibble is used in place,
+// times 16); bytes 0/2 and 1/3 feed separate accumulators so that four
+// independent chains hide the FMA latency.
 __device__ __forceinline__ void nibble_dots(uint32_t w, float4 xl, float4 xh,
-                                            float &acc_lo, float &acc_hi) {
+                                            float (&lo)[2], float (&hi)[2]) {
   const uint32_t lo02 = w & 0x000F000Fu;
   const uint32_t hi02 = w & 0x00F000F0u;
   const uint32_t w8 = w >> 8;
   const uint32_t lo13 = w8 & 0x000F000Fu;
   const uint32_t hi13 = w8 & 0x00F000F0u;
-  acc_lo = __builtin_fmaf(half_lo(lo02), xl.x, acc_lo);
-  acc_hi = __builtin_fmaf(half_lo(hi02), xh.x, acc_hi);
-  acc_lo = __builtin_fmaf(half_lo(lo13), xl.y, acc_lo);
-  acc_hi = __builtin_fmaf(half_lo(hi13), xh.y, acc_hi);
-  acc_lo = __builtin_fmaf(half_hi(lo02), xl.z, acc_lo);
-  acc_hi = __builtin_fmaf(half_hi(hi02), xh.z, acc_hi);
-  acc_lo = __builtin_fmaf(half_hi(lo13), xl.w, acc_lo);
-  acc_hi = __builtin_fmaf(half_hi(hi13), xh.w, acc_hi);
+  lo[0] = __builtin_fmaf(half_lo(lo02), xl.x, lo[0]);
+  hi[0] = __builtin_fmaf(half_lo(hi02), xh.x, hi[0]);
+  lo[1] = __builtin_fmaf(half_lo(lo13), xl.y, lo[1]);
+  hi[1] = __builtin_fmaf(half_lo(hi13), xh.y, hi[1]);
+  lo[0] = __builtin_fmaf(half_hi(lo02), xl.z, lo[0]);
+  hi[0] = __builtin_fmaf(half_hi(hi02), xh.z, hi[0]);
+  lo[1] = __builtin_fmaf(half_hi(lo13), xl.w, lo[1]);
+  hi[1] = __builtin_fmaf(half_hi(hi13), xh.w, hi[1]);
 }
 
 template <int L, int R, int KW, int W>
@@ -105,8 +107,9 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
   constexpr int NM = (TILE + 63) / 64;      // load instructions per tile
   constexpr int S = KW * L;                 // slabs whose activations are staged together
   constexpr int SP = S + 1;                 // padded row of the staged layout (float4)
-  constexpr int XQ = 16 * S / kThreads;     // staged float4 per thread
-  static_assert(16 * S % kThreads == 0, "staging must divide evenly");
+  constexpr int XF = 16 * S;                // staged float4 per iteration
+  constexpr int XQ = (XF + kThreads - 1) / kThreads;  // staged float4 per thread
+  static_assert(XF % 64 == 0, "staging guard must be wave-uniform");
 
   // Staged activations: float4 k of slab ls at slot k*SP + ls.  A wave
   // reading float4 k of consecutive slabs touches consecutive slots, and the
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
     float4 xv[XQ];
 #pragma unroll
     for (int q = 0; q < XQ; ++q) {
-      const int f = tid + kThreads * q;
+      const int f = min(tid + kThreads * q, XF - 1);
       xv[q] = load_buf_f4(xr, 4 * (64 * (slab_base + (f >> 4)) + 4 * (f & 15)));
     }
     const int t = it * KW + kw;
@@ -180,6 +183,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
 #pragma unroll
     for (int q = 0; q < XQ; ++q) {
       const int f = tid + kThreads * q;
+      if (XF % kThreads != 0 && f >= XF) break;  // wave-uniform
       const int sl = f >> 4, k = f & 15;
       xs4[k * SP + sl] = xv[q];
       const float part = group_sum<8>(sum4(xv[q]));
@@ -216,10 +220,11 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
         const uint4 hdr = wt[wave][base];
         const uint4 q0 = wt[wave][base + 1 + 2 * j];
         const uint4 q1 = wt[wave][base + 2 + 2 * j];
-        float s_lo = 0.f, s_hi = 0.f;
+        float lo[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f};
         const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) nibble_dots(qw[k], xl[k], xh[k], s_lo, s_hi);
+        for (int k = 0; k < 8; ++k) nibble_dots(qw[k], xl[k], xh[k], lo, hi);
+        const float s_lo = lo[0] + lo[1], s_hi = hi[0] + hi[1];
         const SlabScales sc = decode_header(hdr, sh, jhi);
         // code part in units of 2^-20: 16*sc_lo*s_lo + sc_hi*s_hi
         const float tc = __builtin_fmaf(sc.sc_lo16, s_lo, sc.sc_hi * s_hi);
@@ -277,6 +282,14 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, int nb,
 template <int L, int R>
 hipError_t launch_w(int waves, int kw, const float *x, const uint8_t *w,
                     float *y, int nb, int64_t N, hipStream_t s) {
+  if (waves == 8) {
+    if constexpr (R <= 4) {  // 8 waves x 8 rows would exceed the 160 KB of LDS
+      if (kw == 1) return launch_gemv<L, R, 1, 8>(x, w, y, nb, N, s);
+      return launch_gemv<L, R, 2, 8>(x, w, y, nb, N, s);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (waves == 1) return launch_gemv<L, R, 1, 1>(x, w, y, nb, N, s);
   if (waves == 2) {
     if (kw == 1) return launch_gemv<L, R, 1, 2>(x, w, y, nb, N, s);
