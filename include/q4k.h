@@ -13,12 +13,8 @@
  *     is launched and y is left untouched.
  *   - y must not overlap x or the weights (not checked).
  *   - Stateless and safe to call from any host thread on any stream.
- *   - q4k_gemv, q4k_gemv_shaped and the ternary calls are deterministic:
- *     every output has exactly one writer and the summation order depends
- *     only on the shapes.  q4k_matmul with n_tokens > 1 adds the partial
- *     sums of its input_dim splits into Y with fp32 atomics, so its low
- *     bits may differ between runs (exact arithmetic, e.g. integer inputs,
- *     stays exact).
+ *   - Every call is deterministic: each output has exactly one writer and
+ *     the summation order depends only on the shapes.
  *   - No C++ exception crosses this interface.
  */
 #ifndef Q4K_H
@@ -87,9 +83,8 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
  *   Y          fp32 [n_tokens, output_dim]
  * Same error behaviour and tolerance as q4k_gemv.  For M > 1 the
  * activations pass through fp16 (split into a high and a low half, both
- * exact MFMA operands) and must satisfy |x| < 65504; Y is zero-filled and
- * then accumulated (see the determinism note above), so Y must not alias X
- * or the weights.
+ * exact MFMA operands) and must satisfy |x| < 65504.  Y must not alias X or
+ * the weights.
  */
 int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
                int64_t input_dim, int64_t output_dim, float *Y, void *stream);

@@ -43,12 +43,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
 
 // 16-byte loads through a buffer view at a byte offset; the streaming form
 // sets the non-temporal hint (aux bit 1 on gfx94x/gfx950).
-__device__ __forceinline__ uint4 load_buf_stream16(__amdgpu_buffer_rsrc_t r, int off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+// `soff` is an optional wave-uniform part of the offset (the instruction's
+// scalar offset operand).
+__device__ __forceinline__ uint4 load_buf_stream16(__amdgpu_buffer_rsrc_t r, int off,
+                                                   int soff = 0) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 2);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ float4 load_buf_f4(__amdgpu_buffer_rsrc_t r, int off) {
-  const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+__device__ __forceinline__ float4 load_buf_f4(__amdgpu_buffer_rsrc_t r, int off, int soff = 0) {
+  const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
   return make_float4(v.x, v.y, v.z, v.w);
 }
 

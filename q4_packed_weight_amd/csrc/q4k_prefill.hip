@@ -5,28 +5,44 @@
 // kernel + Q4KMatmulKernel SPI", sections "Summary" and "Pipeline"),
 //     Y[r, o] = sum_b d[o,b] * sum_s sc[o,b,s] * sum_l q * X[r, k]
 //             - sum_b dmin[o,b] * sum_s m[o,b,s] * sum_l X[r, k]
-// with every weight tile read once for all tokens of the call (the tiling
-// page: llama.cpp fork PR #37, "ggml-cpu: cache-aware tiling in
+// with the weights of a tile read once for all tokens of the tile (the
+// tiling page: llama.cpp fork PR #37, "ggml-cpu: cache-aware tiling in
 // ggml_compute_forward_mul_mat", section "Summary", fix 1).
 //
-// Work decomposition (MI355X): a workgroup of 4 waves owns 128 weight rows
-// (8 MFMA row tiles of 16), PF_KB super-blocks of input_dim and up to 64
-// tokens (4 MFMA column tiles); input_dim is split across workgroups so that
-// no CU has to pull the whole activation matrix out of L2 (a CU reads L2 at
-// roughly 120 GB/s, so 1 MB of activations per CU would cost ~8 us).
-// Partial results are added into Y with fp32 atomics after a zero fill, so
-// the low bits of Y can depend on the order in which the splits land
-// (results are exact whenever the arithmetic is, e.g. integer inputs).
+// Work decomposition (MI355X): a workgroup owns 64 weight rows (4 MFMA row
+// tiles) and 16 tokens (one MFMA token tile) over the WHOLE of input_dim, so
+// every output has exactly one writer: plain stores, no zero fill, no
+// atomics, and the result does not depend on scheduling.  For 256
+// workgroups the 64x16 tile keeps the bytes a CU pulls from L2 near their
+// minimum (64 rows of weights and 16 rows of activations per unit of
+// input_dim).  The token groups of a row tile are gridDim.x workgroup ids
+// apart, which puts them on the same XCD (and its L2) whenever the number
+// of row tiles is a multiple of 8.
 //
-// Precision: the A operand is the exact integer sc*q (<= 945) in fp16.  The
-// activations are split into fp16 hi + lo (hi = fp16(x), lo = fp16(x - hi)),
-// two MFMAs per tile, so every product is exact and the MFMA's fp32
-// accumulation gives fp32-level results (|x| must stay below 65504).  A
-// k-step of 32 is exactly one sub-block; the 8 sub-blocks of a super-block
-// accumulate into one tile that is scaled by d once per super-block.  The
-// lazy-dmin term sum_s (dmin*m_s) * (sum of x over sub-block s) is itself a
-// small contraction and runs on the fp32 MFMA (16x16x4) with exact fp32
-// operands.
+// Pipeline: input_dim is walked in stages of 4 super-blocks.  All 256
+// threads load a stage with coalesced 16-byte loads (every wave instruction
+// reads 1 KB of one activation row, or consecutive 16-byte chunks of the
+// weight rows) into registers one stage ahead, then write it to LDS: the
+// activations already split into fp16 hi + lo in MFMA operand order, the
+// weight blocks raw.  Wave w then computes super-block w of the stage:
+// decodes the 64 block headers (one row per lane), dequantizes A operands
+// from LDS and runs the MFMAs, while the next stage's loads are in flight.
+//
+// MFMA layout (16x16x32 f16): lane (r = lane % 16, g = lane / 16) holds for
+// the A operand row 16a + r of row tile a, positions 8g .. 8g+7 of one
+// sub-block (the qs bytes 32j + 8g .. +7 give sub-block 2j in their low
+// nibbles and 2j+1 in their high nibbles); for the B operand token r at the
+// same positions.  The D tile has rows 16a + 4g + e and token r in lane
+// (r, g), element e.
+//
+// Precision: A = sc*q (<= 945) is exact in fp16.  The activations are split
+// into fp16 hi + lo (hi = fp16(x), lo = fp16(x - hi)), two MFMAs per tile,
+// so every product is exact and the MFMA's fp32 accumulation gives
+// fp32-level results (|x| must stay below 65504).  The per-block tile is
+// scaled by d once.  The sums of x over each sub-block come from an MFMA
+// with an all-ones A operand, and the lazy-dmin term sum_s (dmin*m_s) *
+// (sum of x over sub-block s) runs on the fp32 MFMA (16x16x4) with exact
+// fp32 operands.
 #include "device_common.h"
 #include "q4k_internal.h"
 
@@ -38,63 +54,87 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlockBytes = 144;
-constexpr int PF_ROWS = 128;   // weight rows per workgroup
-constexpr int PF_KB = 2;       // super-blocks of input_dim per workgroup
-constexpr int PF_TOK = 64;     // tokens per workgroup
-constexpr int PF_THREADS = 256;
-constexpr int CH_PER_ROW = PF_KB * 9;                 // 16-byte chunks per row piece
-constexpr int W_CHUNKS = PF_ROWS * CH_PER_ROW;        // 2304
-constexpr int W_PER_THREAD = W_CHUNKS / PF_THREADS;   // 9
-static_assert(W_CHUNKS % PF_THREADS == 0, "tile must divide evenly");
-
-// The 8 activations a lane feeds to one MFMA are positions 8g + perm[e] of a
-// sub-block, in the order the weight side produces its fp16 pairs:
-// (byte0, byte2), (byte1, byte3), (byte4, byte6), (byte5, byte7).
-__device__ constexpr int kPerm[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+constexpr int PF_ROWS = 64;           // weight rows per workgroup (4 row tiles)
+constexpr int PF_TOK = 16;            // tokens per workgroup (one token tile)
+constexpr int PF_WAVES = 4;           // super-blocks per stage, one per wave
+constexpr int PF_THREADS = 64 * PF_WAVES;
+constexpr int PF_RPAD = PF_ROWS + 4;  // padded row dimension of the header tables
+// LDS row pitches in dwords: an activation row (256 fp16 positions) + 16 B,
+// a staged weight block (144 B) + 8 B, and one super-block of all 64 rows
+// + 32 B; the pads spread consecutive rows over the banks.
+constexpr int XROW = 128 + 4;
+constexpr int WROW = 36 + 2;
+constexpr int WBLK = PF_ROWS * WROW + 8;
+constexpr int W_CHUNKS = PF_ROWS * PF_WAVES * 9;          // 16-byte chunks per stage
+constexpr int W_PER_THREAD = W_CHUNKS / PF_THREADS;       // 9
+static_assert(W_CHUNKS % PF_THREADS == 0, "weight chunks must divide evenly");
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 __device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
-// Eight codes of one sub-block as fp16 sc*q: `p` holds 1024 + q pairs built
-// with the 0x6400 exponent bias; fma(1024+q, sc, -1024*sc) = sc*q exactly.
-__device__ __forceinline__ half8_t dequant8(uint32_t p0, uint32_t p1, uint32_t p2,
-                                            uint32_t p3, half2_t sc, half2_t nsc) {
-  const half2_t a = __builtin_elementwise_fma(as_h2(p0), sc, nsc);
-  const half2_t b = __builtin_elementwise_fma(as_h2(p1), sc, nsc);
-  const half2_t c = __builtin_elementwise_fma(as_h2(p2), sc, nsc);
-  const half2_t d = __builtin_elementwise_fma(as_h2(p3), sc, nsc);
-  half8_t r;
-  r[0] = a.x; r[1] = a.y; r[2] = b.x; r[3] = b.y;
-  r[4] = c.x; r[5] = c.y; r[6] = d.x; r[7] = d.y;
-  return r;
+// Bytes (0, 2) or (1, 3) of `t` as the low bytes of two fp16 halves whose
+// high byte is 0x64: a byte value v becomes the fp16 number 1024 + v.
+__device__ __forceinline__ uint32_t spread02(uint32_t t) {
+  return __builtin_amdgcn_perm(0x64646464u, t, 0x04020400u);
+}
+__device__ __forceinline__ uint32_t spread13(uint32_t t) {
+  return __builtin_amdgcn_perm(0x64646464u, t, 0x04030401u);
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ y, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) y[i] = 0.f;
+// One MFMA A operand from two qs dwords: their low nibbles (hi_nib false)
+// or their high nibbles (true; kept in place, i.e. as 16 v).  mul/add are
+// the per-sub-block fp16 pairs that turn 1024 + v (or 1024 + 16 v) into
+// sc*v: (sc, -1024 sc) for low nibbles and (sc/16, -64 sc) for high ones.
+// The fused multiply-add rounds once, and sc*v is exact in fp16.
+__device__ __forceinline__ half8_t dequant8(uint32_t w0, uint32_t w1, bool hi_nib,
+                                            uint32_t mul, uint32_t add) {
+  const uint32_t mask = hi_nib ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+  const uint32_t t0 = w0 & mask, t1 = w1 & mask;
+  const half2_t m2 = as_h2(mul), a2 = as_h2(add);
+  const half2_t p0 = __builtin_elementwise_fma(as_h2(spread02(t0)), m2, a2);
+  const half2_t p1 = __builtin_elementwise_fma(as_h2(spread13(t0)), m2, a2);
+  const half2_t p2 = __builtin_elementwise_fma(as_h2(spread02(t1)), m2, a2);
+  const half2_t p3 = __builtin_elementwise_fma(as_h2(spread13(t1)), m2, a2);
+  half8_t v;
+  v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+  v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+  return v;
+}
+
+// lo = fp16(x - hi) for the two halves of `hi2` (fp16 hi parts of x0, x1):
+// v_fma_mix evaluates x - hi exactly in fp32 and rounds once to fp16.
+__device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi2), "v"(x0));
+  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(r) : "v"(hi2), "v"(x1));
+  return r;
 }
 
 __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     const float *X, const uint8_t *w, float *__restrict__ Y, int M, int nb,
     int N) {
-  // LDS: weight tile (row r, block kb at chunks (r*PF_KB + kb)*9 ..), the
-  // activation fragments of one super-block [s][token tile][hi|lo][lane],
-  // sub-block activation sums, and the decoded block headers.
-  __shared__ uint4 wt[W_CHUNKS];
-  __shared__ uint4 bfrag[8][4][2][64];
-  __shared__ float xs_tab[8][PF_TOK];
-  __shared__ float d_tab[PF_KB][PF_ROWS];
-  __shared__ float c_tab[PF_KB][8][PF_ROWS];
-  __shared__ uint32_t sc_tab[PF_KB][8][PF_ROWS];
+  // xh/xl: fp16 hi and lo activations [block of stage][token][position
+  // pairs in operand order]; wt: raw weight blocks [block of stage][row];
+  // per-wave header tables of the block the wave computes: fp16 scale pairs
+  // (mul, add) per sub-block and row, dmin*m, d.
+  __shared__ __align__(16) uint32_t xh[PF_WAVES][PF_TOK][XROW];
+  __shared__ __align__(16) uint32_t xl[PF_WAVES][PF_TOK][XROW];
+  __shared__ __align__(16) uint32_t wt[PF_WAVES * WBLK];
+  __shared__ uint2 sc_tab[PF_WAVES][8][PF_RPAD];
+  __shared__ float c_tab[PF_WAVES][8][PF_RPAD];
+  __shared__ __align__(16) float d_tab[PF_WAVES][PF_ROWS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int r = lane & 15;  // A: row within a row tile; B and D: token
+  const int g = lane >> 4;  // lane group
   const int row0 = blockIdx.x * PF_ROWS;
-  const int kb0 = blockIdx.y * PF_KB;
-  const int tok0 = blockIdx.z * PF_TOK;
+  const int tok0 = blockIdx.y * PF_TOK;
   const int K = nb * 256;
-  const int64_t row_bytes = (int64_t)nb * kBlockBytes;
+  const int row_bytes = nb * kBlockBytes;
+  const int n_stages = (nb + PF_WAVES - 1) / PF_WAVES;
 
   // Range-checked views: rows past N and tokens past M read as zeros.
   const __amdgpu_buffer_rsrc_t wr =
@@ -102,203 +142,180 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(X + (int64_t)tok0 * K, (int64_t)(M - tok0) * K * 4);
 
-  // 1. Weight tile: each row's PF_KB blocks are one contiguous 288-byte
-  //    piece; chunk q = row (q / CH_PER_ROW), piece chunk (q % CH_PER_ROW).
-  //    Blocks past nb read the next row's bytes and are never consumed.
+  // Load roles of a stage (1024 positions of input_dim, 4 super-blocks):
+  // activation load i is token i, positions 4*tid .. 4*tid+3 of the stage
+  // (so block `wave`, positions 4*lane ..); weight chunk q = tid + 256 m is
+  // 16-byte chunk q % 36 of row q / 36's 576-byte stage piece.  Chunks past
+  // a row's last block (ragged last stage) are never consumed.
+  // The per-thread part of every load offset is fixed; the stage and token
+  // parts are wave-uniform and go into the loads' scalar offset.
+  float4 xv[PF_TOK];
   uint4 wv[W_PER_THREAD];
+  int woff[W_PER_THREAD];
 #pragma unroll
   for (int m = 0; m < W_PER_THREAD; ++m) {
     const int q = tid + PF_THREADS * m;
-    const int r = q / CH_PER_ROW;
-    const int within = q - r * CH_PER_ROW;
-    wv[m] = load_buf_stream16(wr, (int)(r * row_bytes) + kb0 * kBlockBytes + 16 * within);
+    const int row = q / 36;
+    woff[m] = row * row_bytes + 16 * (q - 36 * row);
   }
-
-  // Activation staging roles: thread -> token tok = tid / 4, group g = tid % 4
-  // (positions 8g..8g+7 of every sub-block).
-  const int s_tok = tid >> 2;
-  const int s_g = tid & 3;
-
-  float4 xv[16];
-  auto load_x = [&](int kb) {
-    const int kbase = (kb0 + kb) * 256;
+  auto load_stage = [&](int st) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int off = 4 * (s_tok * K + kbase + 32 * s + 8 * s_g);
-      xv[2 * s] = load_buf_f4(xr, off);
-      xv[2 * s + 1] = load_buf_f4(xr, off + 16);
-    }
+    for (int i = 0; i < PF_TOK; ++i)
+      xv[i] = load_buf_f4(xr, 16 * tid, 4 * (i * K + st * 1024));
+#pragma unroll
+    for (int m = 0; m < W_PER_THREAD; ++m)
+      wv[m] = __builtin_bit_cast(uint4, load_buf_f4(wr, woff[m], st * (4 * kBlockBytes)));
   };
-  auto stage_x = [&]() {
+  auto stage_to_lds = [&]() {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const float v[8] = {xv[2 * s].x, xv[2 * s].y, xv[2 * s].z, xv[2 * s].w,
-                          xv[2 * s + 1].x, xv[2 * s + 1].y, xv[2 * s + 1].z, xv[2 * s + 1].w};
-      uint32_t hi[4], lo[4];
+    for (int i = 0; i < PF_TOK; ++i) {
+      // positions (0,2) and (1,3) of this lane's four: operand order
+      const float4 v = xv[i];
+      half2_t h02, h13;
+      h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
+      h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
+      const uint32_t hw02 = as_u32(h02), hw13 = as_u32(h13);
+      *reinterpret_cast<uint2 *>(&xh[wave][i][2 * lane]) = make_uint2(hw02, hw13);
+      *reinterpret_cast<uint2 *>(&xl[wave][i][2 * lane]) =
+          make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
+    }
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float a = v[kPerm[e]], b = v[kPerm[e + 1]];
-        const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-        const _Float16 la = (_Float16)(a - (float)ha), lb = (_Float16)(b - (float)hb);
-        half2_t h2, l2;
-        h2.x = ha; h2.y = hb;
-        l2.x = la; l2.y = lb;
-        hi[e / 2] = as_u32(h2);
-        lo[e / 2] = as_u32(l2);
-      }
-      const int flane = 16 * s_g + (s_tok & 15);
-      bfrag[s][s_tok >> 4][0][flane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      bfrag[s][s_tok >> 4][1][flane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      // sub-block activation sum over the 4 groups of this token
-      float part = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-      part = group_sum<4>(part);
-      if (s_g == 0) xs_tab[s][s_tok] = part;
+    for (int m = 0; m < W_PER_THREAD; ++m) {
+      const int q = tid + PF_THREADS * m;
+      const int row = q / 36;
+      const int cc = q - 36 * row;
+      const int bb = cc / 9;
+      uint32_t *dst = &wt[bb * WBLK + row * WROW + 4 * (cc - 9 * bb)];
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(wv[m].x, wv[m].y);
+      *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wv[m].z, wv[m].w);
     }
   };
 
-  load_x(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
+  floatx4 y_acc[4], m_acc[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) y_acc[a] = m_acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+  half8_t ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
+  const uint32_t *wblk = &wt[wave * WBLK];
 
-  // 2. Weight tile and activations of the first block into LDS.
-#pragma unroll
-  for (int m = 0; m < W_PER_THREAD; ++m) wt[tid + PF_THREADS * m] = wv[m];
-  stage_x();
-  __syncthreads();
+  // The token groups of a row tile start at different stages (and wrap
+  // around), so that together they read whole weight rows at any moment
+  // (contiguous DRAM pages) rather than the same quarter of every row.
+  const int st0 = blockIdx.y % n_stages;
+  load_stage(st0);
+  for (int it = 0; it < n_stages; ++it) {
+    const int st = st0 + it < n_stages ? st0 + it : st0 + it - n_stages;
+    stage_to_lds();
+    __syncthreads();
+    if (it + 1 < n_stages) load_stage(st + 1 < n_stages ? st + 1 : 0);  // in flight during the MFMAs
 
-  // 3. Decode the PF_ROWS * PF_KB block headers once: thread -> (row, kb).
-  {
-    const int r = tid >> 1, kb = tid & 1;
-    const uint4 h = wt[(r * PF_KB + kb) * 9];
-    const float d = half_lo(h.x), dmin = half_hi(h.x);
-    const uint32_t S[12] = {h.y & 255u, (h.y >> 8) & 255u, (h.y >> 16) & 255u, h.y >> 24,
-                            h.z & 255u, (h.z >> 8) & 255u, (h.z >> 16) & 255u, h.z >> 24,
-                            h.w & 255u, (h.w >> 8) & 255u, (h.w >> 16) & 255u, h.w >> 24};
-    d_tab[kb][r] = d;
+    if (st * PF_WAVES + wave < nb) {
+      // ---- headers of block `wave` of the stage: lane = row
+      {
+        const uint2 h01 = *reinterpret_cast<const uint2 *>(&wblk[lane * WROW]);
+        const uint2 h23 = *reinterpret_cast<const uint2 *>(&wblk[lane * WROW + 2]);
+        const float d = half_lo(h01.x), dmin = half_hi(h01.x);
+        // 6-bit scales and mins, four per dword (one per byte)
+        const uint32_t sc03 = h01.y & 0x3F3F3F3Fu;
+        const uint32_t mn03 = h23.x & 0x3F3F3F3Fu;
+        const uint32_t sc47 = (h23.y & 0x0F0F0F0Fu) | ((h01.y >> 2) & 0x30303030u);
+        const uint32_t mn47 = ((h23.y >> 4) & 0x0F0F0F0Fu) | ((h23.x >> 2) & 0x30303030u);
+        d_tab[wave][lane] = d;
+        const uint32_t scw[2] = {sc03, sc47}, mnw[2] = {mn03, mn47};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint32_t sc = s < 4 ? (S[s] & 63u) : ((S[s + 4] & 15u) | ((S[s - 4] >> 6) << 4));
-      const uint32_t mm = s < 4 ? (S[s + 4] & 63u) : ((S[s + 4] >> 4) | ((S[s] >> 6) << 4));
-      c_tab[kb][s][r] = dmin * (float)mm;
-      half2_t sc2;
-      sc2.x = (_Float16)(float)sc;
-      sc2.y = sc2.x;
-      sc_tab[kb][s][r] = as_u32(sc2);
-    }
-  }
-  __syncthreads();
-
-  // 4. MFMA main loop.  Wave w owns row tiles 2w and 2w+1; lane l works on
-  //    row l % 16 of a tile and activation group g = l / 16.
-  const int lr = lane & 15;
-  const int g = lane >> 4;
-  floatx4 y_acc[2][4], m_acc[2][4];
+        for (int hw = 0; hw < 2; ++hw) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) y_acc[a][t] = m_acc[a][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kb = 0; kb < PF_KB; ++kb) {
-    if (kb0 + kb >= nb) break;  // ragged last split (uniform)
-    if (kb > 0) {
-      __syncthreads();  // everyone is done with the previous block's fragments
-      load_x(kb);
-      stage_x();
-      __syncthreads();
-    }
-    floatx4 acc[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[a][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // qs bytes 32j + 8g .. +7 of each of the wave's two rows (this lane's)
-      uint2 qb[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int r = (2 * wave + a) * 16 + lr;
-        const uint8_t *blk = reinterpret_cast<const uint8_t *>(&wt[(r * PF_KB + kb) * 9]);
-        qb[a] = *reinterpret_cast<const uint2 *>(blk + 16 + 32 * j + 8 * g);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {  // h = 0: sub-block 2j (low nibbles), 1: 2j+1 (high)
-        const int s = 2 * j + h;
-        uint4 bh[4], bl[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          bh[t] = bfrag[s][t][0][lane];
-          bl[t] = bfrag[s][t][1][lane];
-        }
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int r = (2 * wave + a) * 16 + lr;
-          const uint32_t w0 = h ? (qb[a].x >> 4) : qb[a].x;
-          const uint32_t w1 = h ? (qb[a].y >> 4) : qb[a].y;
-          const uint32_t p0 = (w0 & 0x000F000Fu) | 0x64006400u;
-          const uint32_t p1 = ((w0 >> 8) & 0x000F000Fu) | 0x64006400u;
-          const uint32_t p2 = (w1 & 0x000F000Fu) | 0x64006400u;
-          const uint32_t p3 = ((w1 >> 8) & 0x000F000Fu) | 0x64006400u;
-          const half2_t sc = as_h2(sc_tab[kb][s][r]);
-          const half2_t nsc = sc * (_Float16)(-1024.0f);
-          const half8_t A = dequant8(p0, p1, p2, p3, sc, nsc);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(half8_t, bh[t]), acc[a][t], 0, 0, 0);
-            acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(half8_t, bl[t]), acc[a][t], 0, 0, 0);
+          for (int e = 0; e < 4; ++e) {
+            const int s = 4 * hw + e;
+            const float scf = (float)((scw[hw] >> (8 * e)) & 255u);
+            const float mnf = (float)((mnw[hw] >> (8 * e)) & 255u);
+            c_tab[wave][s][lane] = dmin * mnf;
+            // even sub-blocks are low nibbles, odd ones high nibbles (16 v)
+            const float mulf = (s & 1) ? scf * 0.0625f : scf;
+            const float addf = (s & 1) ? scf * -64.0f : scf * -1024.0f;
+            half2_t m2, a2;
+            m2.x = m2.y = (_Float16)mulf;
+            a2.x = a2.y = (_Float16)addf;
+            sc_tab[wave][s][lane] = make_uint2(as_u32(m2), as_u32(a2));
           }
         }
       }
-    }
 
-    // Epilogue of this super-block: scale by d (per row) into y_acc, and the
-    // lazy-dmin term on the fp32 MFMA: sum_s (dmin*m_s)[row] * xs[s][token].
+      // ---- MFMAs.  The four row tiles' accumulator chains are interleaved
+      //      so that consecutive MFMAs never depend on each other.
+      floatx4 acc[4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int rt0 = (2 * wave + a) * 16;
-      float dv[4];
+      for (int a = 0; a < 4; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+      // xsb[c]: the B operand of the fp32 MFMA, the sum of x over
+      // sub-block 4c + g for token r (lane group g picks its sub-block)
+      float xsb[2] = {0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dv[e] = d_tab[kb][rt0 + 4 * g + e];
+      for (int j = 0; j < 4; ++j) {
+        uint2 qb[4], tl[4], th[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+        for (int a = 0; a < 4; ++a) {
+          qb[a] = *reinterpret_cast<const uint2 *>(&wblk[(16 * a + r) * WROW + 4 + 8 * j + 2 * g]);
+          tl[a] = sc_tab[wave][2 * j][16 * a + r];
+          th[a] = sc_tab[wave][2 * j + 1][16 * a + r];
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y_acc[a][t][e] = __builtin_fmaf(dv[e], acc[a][t][e], y_acc[a][t][e]);
+        for (int h = 0; h < 2; ++h) {
+          const int s = 2 * j + h;
+          const half8_t Bh = *reinterpret_cast<const half8_t *>(&xh[wave][r][16 * s + 4 * g]);
+          const half8_t Bl = *reinterpret_cast<const half8_t *>(&xl[wave][r][16 * s + 4 * g]);
+          half8_t A[4];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          const float ca = c_tab[kb][4 * mi + g][rt0 + lr];
-          const float xb = xs_tab[4 * mi + g][16 * t + lr];
-          m_acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ca, xb, m_acc[a][t], 0, 0, 0);
+          for (int a = 0; a < 4; ++a)
+            A[a] = h ? dequant8(qb[a].x, qb[a].y, true, th[a].x, th[a].y)
+                     : dequant8(qb[a].x, qb[a].y, false, tl[a].x, tl[a].y);
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[a], Bh, acc[a], 0, 0, 0);
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[a], Bl, acc[a], 0, 0, 0);
+          // sum of x over sub-block s for token r (every row of the tile)
+          floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bl, sx, 0, 0, 0);
+          if ((s & 3) == g) xsb[s >> 2] = sx[0];
         }
       }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        // d of rows 16a + 4g + e (the rows of this lane's D elements)
+        const float4 dv = *reinterpret_cast<const float4 *>(&d_tab[wave][16 * a + 4 * g]);
+        y_acc[a][0] = __builtin_fmaf(dv.x, acc[a][0], y_acc[a][0]);
+        y_acc[a][1] = __builtin_fmaf(dv.y, acc[a][1], y_acc[a][1]);
+        y_acc[a][2] = __builtin_fmaf(dv.z, acc[a][2], y_acc[a][2]);
+        y_acc[a][3] = __builtin_fmaf(dv.w, acc[a][3], y_acc[a][3]);
+        // lazy-dmin term: A[row][kk] = dmin*m of sub-block 4c + kk, B = sums
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(c_tab[wave][4 * c + g][16 * a + r], xsb[c],
+                                                          m_acc[a], 0, 0, 0);
+      }
     }
+    __syncthreads();  // the next stage overwrites the LDS tiles
   }
 
-  // 5. Add this split's partial results into Y.  Each wave first transposes
-  //    its 32 rows x 64 tokens through LDS (row stride 33 floats against
-  //    bank conflicts) so that one atomic instruction covers 2 tokens x 32
-  //    consecutive rows (2 cache lines) instead of 16 scattered lines.  Rows
-  //    past N and tokens past M are dropped.
-  __syncthreads();  // every wave is done reading the activation fragments
-  float *T = reinterpret_cast<float *>(&bfrag[0][0][0][0]) + wave * (PF_TOK * 33);
+  // ---- add the waves' partial tiles (through the activation tiles, no
+  //      longer needed) and store.  Lane (token r, group g) holds rows
+  //      16a + 4g + e of its token.
+  float4 *red = reinterpret_cast<float4 *>(&xh[0][0][0]);  // [wave][token][17]
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
+    red[(wave * PF_TOK + r) * 17 + 4 * a + g] =
+        make_float4(y_acc[a][0] - m_acc[a][0], y_acc[a][1] - m_acc[a][1],
+                    y_acc[a][2] - m_acc[a][2], y_acc[a][3] - m_acc[a][3]);
+  __syncthreads();
+  const float *redf = reinterpret_cast<const float *>(red);
+  for (int o = tid; o < PF_TOK * PF_ROWS; o += PF_THREADS) {
+    const int tok = o / PF_ROWS, rr = o % PF_ROWS;
+    float v = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        T[(16 * t + lr) * 33 + 16 * a + 4 * g + e] = y_acc[a][t][e] - m_acc[a][t][e];
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
-  const int rr = lane & 31;
-  const int row = row0 + wave * 32 + rr;
-#pragma unroll 4
-  for (int i = 0; i < PF_TOK / 2; ++i) {
-    const int tl = 2 * i + (lane >> 5);
-    const int tok = tok0 + tl;
-    const float v = T[tl * 33 + rr];
-    if (tok < M && row < N) unsafeAtomicAdd(Y + (int64_t)tok * N + row, v);
+    for (int wv2 = 0; wv2 < PF_WAVES; ++wv2) v += redf[(wv2 * PF_TOK + tok) * 68 + rr];
+    if (tok0 + tok < M && row0 + rr < N) Y[(int64_t)(tok0 + tok) * N + row0 + rr] = v;
   }
 }
 
@@ -307,20 +324,14 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
 hipError_t prefill_launch(const float *X, const uint8_t *w, int64_t M,
                           int64_t K, int64_t N, float *Y, hipStream_t stream) {
   const int64_t nb = K / 256;
-  // Offsets formed in the kernel: row tile of 128 rows and a token group of
-  // 64 rows of X must stay below 2^31 bytes.
-  if ((int64_t)PF_ROWS * nb * kBlockBytes >= ((int64_t)1 << 31) ||
-      (int64_t)PF_TOK * K * 4 >= ((int64_t)1 << 31) || N > 0x7FFFFFFF || M > 0x7FFFFFFF)
+  // Offsets formed in the kernel (a row tile of 64 rows plus one stage past
+  // its end, 16 rows of X plus one stage) must stay below 2^31 bytes.
+  if ((int64_t)PF_ROWS * nb * kBlockBytes + 4096 >= ((int64_t)1 << 31) ||
+      ((int64_t)PF_TOK * K + 2048) * 4 >= ((int64_t)1 << 31) || N > 0x7FFFFFFF ||
+      M > 0x7FFFFFFF)
     return hipErrorInvalidValue;
-  const int64_t total = M * N;
-  int64_t fill_grid = (total + 255) / 256;
-  if (fill_grid > 4096) fill_grid = 4096;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)fill_grid), dim3(256), 0, stream, Y, total);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((N + PF_ROWS - 1) / PF_ROWS), (unsigned)((nb + PF_KB - 1) / PF_KB),
-                  (unsigned)((M + PF_TOK - 1) / PF_TOK));
-  if (grid.y > 65535 || grid.z > 65535) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)((N + PF_ROWS - 1) / PF_ROWS), (unsigned)((M + PF_TOK - 1) / PF_TOK));
+  if (grid.y > 65535) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(q4k_prefill_kernel, grid, dim3(PF_THREADS), 0, stream, X, w, Y, (int)M,
                      (int)nb, (int)N);
   return hipGetLastError();

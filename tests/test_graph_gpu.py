@@ -57,16 +57,15 @@ def test_ternary_graph_replays():
 
 
 def test_matmul_graph_replays():
-    """The batched path zero-fills Y with a kernel (no memset node) and adds
-    split partials atomically: replays match the eager result to the parity
-    bar, and bit for bit on integer inputs."""
+    """The batched path: replays match the eager result bit for bit, on
+    float and on integer inputs."""
     M, K, N = 64, 2048, 384
     w = dev(synth.q4k_weights(N, K, config=42))
     X = dev(synth.activations(K, n_tokens=M, config=42))
     Y = torch.empty(M, N, dtype=torch.float32, device=DEV)
     binding.q4k_matmul(X, w, M, K, N, Y)
     eager = host(Y).copy()
-    _replays_match(lambda: binding.q4k_matmul(X, w, M, K, N, Y), Y, eager, exact=False)
+    _replays_match(lambda: binding.q4k_matmul(X, w, M, K, N, Y), Y, eager, exact=True)
     wi = dev(synth.q4k_integer_weights(N, K, config=43))
     Xi = dev(synth.integer_activations(K, n_tokens=M, config=43))
     binding.q4k_matmul(Xi, wi, M, K, N, Y)

@@ -57,6 +57,29 @@ def test_matmul_rows_match_gemv_on_integer_inputs(oracle_lib):
     assert np.array_equal(Y.astype(np.float64), ref)
 
 
+def test_matmul_deterministic():
+    """Every output has one writer: repeated calls agree bit for bit."""
+    M, K, N = 64, 4096, 512
+    w = dev(synth.q4k_weights(N, K, config=34))
+    X = dev(synth.activations(K, n_tokens=M, config=34))
+    Y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    outs = []
+    for _ in range(3):
+        binding.q4k_matmul(X, w, M, K, N, Y)
+        outs.append(host(Y).copy())
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 256, 64), (17, 768, 65), (33, 1280, 130)])
+def test_matmul_ragged_stage_and_tile_edges(oracle_lib, M, K, N):
+    """input_dim not a multiple of the 4-block stage, and partial row and
+    token tiles."""
+    w = synth.q4k_weights(N, K, config=35, copy=K + N)
+    X = synth.activations(K, n_tokens=M, config=35, copy=K + N)
+    Y = run(X, w, M, K, N)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"{M}x{K}x{N}")
+
+
 def test_matmul_zero_activation():
     M, K, N = 64, 1024, 256
     w = synth.q4k_weights(N, K, config=33)
