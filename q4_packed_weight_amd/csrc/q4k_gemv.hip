@@ -121,6 +121,10 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
   __shared__ uint4 wt[W][TILE];
   __shared__ float partial[KW > 1 ? W * ROWS_W : 1];
 
+  // The host validates nb >= 1; saying so lets the compiler fetch every
+  // kernel argument in one round trip instead of two (the loop-entry test
+  // would otherwise sit between them).
+  __builtin_assume(nb >= 1);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
