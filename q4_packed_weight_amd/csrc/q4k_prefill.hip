@@ -56,7 +56,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kBlockBytes = 144;
 constexpr int PF_ROWS = 64;           // weight rows per workgroup (4 row tiles)
 constexpr int PF_TOK = 16;            // tokens per workgroup (one token tile)
-constexpr int PF_WAVES = 4;           // super-blocks per stage, one per wave
+constexpr int PF_BLKS = 4;            // super-blocks per stage
+constexpr int PF_WAVES = 8;           // two waves per block: row tiles {0,1} and {2,3}
 constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int PF_RPAD = PF_ROWS + 4;  // padded row dimension of the header tables
 // LDS row pitches in dwords: an activation row (256 fp16 positions) + 16 B,
@@ -65,9 +66,14 @@ constexpr int PF_RPAD = PF_ROWS + 4;  // padded row dimension of the header tabl
 constexpr int XROW = 128 + 4;
 constexpr int WROW = 36 + 2;
 constexpr int WBLK = PF_ROWS * WROW + 8;
-constexpr int W_CHUNKS = PF_ROWS * PF_WAVES * 9;          // 16-byte chunks per stage
-constexpr int W_PER_THREAD = W_CHUNKS / PF_THREADS;       // 9
-static_assert(W_CHUNKS % PF_THREADS == 0, "weight chunks must divide evenly");
+// Loads of a stage: waves 0-3 (256 threads) bring the weights, 16-byte
+// chunk q = t + 256 m of the 64 rows' 576-byte stage pieces; all 8 waves
+// bring the activations, float4 i of thread tid = token 2i + (tid >= 256),
+// positions 4t .. 4t+3 of the stage (t = tid % 256).
+constexpr int W_CHUNKS = PF_ROWS * PF_BLKS * 9;           // 2304
+constexpr int W_PER_THREAD = W_CHUNKS / 256;              // 9
+constexpr int X_PER_THREAD = PF_TOK / 2;                  // 8
+static_assert(W_CHUNKS % 256 == 0, "weight chunks must divide evenly");
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 __device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
@@ -116,14 +122,14 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     int N) {
   // xh/xl: fp16 hi and lo activations [block of stage][token][position
   // pairs in operand order]; wt: raw weight blocks [block of stage][row];
-  // per-wave header tables of the block the wave computes: fp16 scale pairs
-  // (mul, add) per sub-block and row, dmin*m, d.
-  __shared__ __align__(16) uint32_t xh[PF_WAVES][PF_TOK][XROW];
-  __shared__ __align__(16) uint32_t xl[PF_WAVES][PF_TOK][XROW];
-  __shared__ __align__(16) uint32_t wt[PF_WAVES * WBLK];
-  __shared__ uint2 sc_tab[PF_WAVES][8][PF_RPAD];
-  __shared__ float c_tab[PF_WAVES][8][PF_RPAD];
-  __shared__ __align__(16) float d_tab[PF_WAVES][PF_ROWS];
+  // header tables of the stage's blocks: fp16 scale pairs (mul, add) per
+  // sub-block and row, dmin*m, d.
+  __shared__ __align__(16) uint32_t xh[PF_BLKS][PF_TOK][XROW];
+  __shared__ __align__(16) uint32_t xl[PF_BLKS][PF_TOK][XROW];
+  __shared__ __align__(16) uint32_t wt[PF_BLKS * WBLK];
+  __shared__ uint2 sc_tab[PF_BLKS][8][PF_RPAD];
+  __shared__ float c_tab[PF_BLKS][8][PF_RPAD];
+  __shared__ __align__(16) float d_tab[PF_BLKS][PF_ROWS];
 
   // The host validates nb >= 1; saying so lets the compiler fetch every
   // kernel argument in one round trip.
@@ -131,13 +137,17 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const bool w_loader = wave < 4;
+  const int t = tid & 255;  // thread index within its loader half
+  const int bb = wave & 3;  // block of the stage this wave computes
+  const int half = wave >> 2;  // row tiles 2*half and 2*half + 1
   const int r = lane & 15;  // A: row within a row tile; B and D: token
   const int g = lane >> 4;  // lane group
   const int row0 = blockIdx.x * PF_ROWS;
   const int tok0 = blockIdx.y * PF_TOK;
   const int K = nb * 256;
   const int row_bytes = nb * kBlockBytes;
-  const int n_stages = (nb + PF_WAVES - 1) / PF_WAVES;
+  const int n_stages = (nb + PF_BLKS - 1) / PF_BLKS;
 
   // Range-checked views: rows past N and tokens past M read as zeros.
   const __amdgpu_buffer_rsrc_t wr =
@@ -145,62 +155,67 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(X + (int64_t)tok0 * K, (int64_t)(M - tok0) * K * 4);
 
-  // Load roles of a stage (1024 positions of input_dim, 4 super-blocks):
-  // activation load i is token i, positions 4*tid .. 4*tid+3 of the stage
-  // (so block `wave`, positions 4*lane ..); weight chunk q = tid + 256 m is
-  // 16-byte chunk q % 36 of row q / 36's 576-byte stage piece.  Chunks past
-  // a row's last block (ragged last stage) are never consumed.
-  // The per-thread part of every load offset is fixed; the stage and token
-  // parts are wave-uniform and go into the loads' scalar offset.
-  float4 xv[PF_TOK];
+  // Prefetch registers.  The per-thread part of every load offset is fixed;
+  // the stage part is wave-uniform and goes into the loads' scalar offset.
+  // Chunks past a row's last block (ragged last stage) are never consumed.
   uint4 wv[W_PER_THREAD];
+  float4 xv[X_PER_THREAD];
   int woff[W_PER_THREAD];
 #pragma unroll
   for (int m = 0; m < W_PER_THREAD; ++m) {
-    const int q = tid + PF_THREADS * m;
+    const int q = t + 256 * m;
     const int row = q / 36;
     woff[m] = row * row_bytes + 16 * (q - 36 * row);
   }
+  const int tok_lo = tid >> 8;  // tokens 2i + tok_lo
   auto load_stage = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < PF_TOK; ++i)
-      xv[i] = load_buf_f4(xr, 16 * tid, 4 * (i * K + st * 1024));
+    for (int i = 0; i < X_PER_THREAD; ++i)
+      xv[i] = load_buf_f4(xr, 16 * t + 4 * K * (2 * i + tok_lo), 4096 * st);
+    if (w_loader) {
 #pragma unroll
-    for (int m = 0; m < W_PER_THREAD; ++m)
-      wv[m] = __builtin_bit_cast(uint4, load_buf_f4(wr, woff[m], st * (4 * kBlockBytes)));
+      for (int m = 0; m < W_PER_THREAD; ++m)
+        wv[m] = __builtin_bit_cast(uint4, load_buf_f4(wr, woff[m], st * (4 * kBlockBytes)));
+    }
   };
   auto stage_to_lds = [&]() {
+    // float4 i: token 2i + tok_lo, block (t / 64), positions 4*lane ..
+    // 4*lane+3; stored as pairs (0,2) and (1,3): operand order
+    const int xb = t >> 6;
 #pragma unroll
-    for (int i = 0; i < PF_TOK; ++i) {
-      // positions (0,2) and (1,3) of this lane's four: operand order
+    for (int i = 0; i < X_PER_THREAD; ++i) {
       const float4 v = xv[i];
       half2_t h02, h13;
       h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
       h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
       const uint32_t hw02 = as_u32(h02), hw13 = as_u32(h13);
-      *reinterpret_cast<uint2 *>(&xh[wave][i][2 * lane]) = make_uint2(hw02, hw13);
-      *reinterpret_cast<uint2 *>(&xl[wave][i][2 * lane]) =
+      const int tok = 2 * i + tok_lo;
+      *reinterpret_cast<uint2 *>(&xh[xb][tok][2 * lane]) = make_uint2(hw02, hw13);
+      *reinterpret_cast<uint2 *>(&xl[xb][tok][2 * lane]) =
           make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
     }
+    if (w_loader) {
 #pragma unroll
-    for (int m = 0; m < W_PER_THREAD; ++m) {
-      const int q = tid + PF_THREADS * m;
-      const int row = q / 36;
-      const int cc = q - 36 * row;
-      const int bb = cc / 9;
-      uint32_t *dst = &wt[bb * WBLK + row * WROW + 4 * (cc - 9 * bb)];
-      *reinterpret_cast<uint2 *>(dst) = make_uint2(wv[m].x, wv[m].y);
-      *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wv[m].z, wv[m].w);
+      for (int m = 0; m < W_PER_THREAD; ++m) {
+        const int q = t + 256 * m;
+        const int row = q / 36;
+        const int cc = q - 36 * row;
+        const int b = cc / 9;
+        uint32_t *dst = &wt[b * WBLK + row * WROW + 4 * (cc - 9 * b)];
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(wv[m].x, wv[m].y);
+        *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wv[m].z, wv[m].w);
+      }
     }
   };
 
-  floatx4 y_acc[4], m_acc[4];
+  floatx4 y_acc[2], m_acc[2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) y_acc[a] = m_acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < 2; ++a) y_acc[a] = m_acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
   half8_t ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
-  const uint32_t *wblk = &wt[wave * WBLK];
+  const uint32_t *wblk = &wt[bb * WBLK];
+  const int hrow = 32 * half + (lane & 31);  // header row decoded by this lane
 
   // The token groups of a row tile start at different stages (and wrap
   // around), so that together they read whole weight rows at any moment
@@ -213,18 +228,19 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     __syncthreads();
     if (it + 1 < n_stages) load_stage(st + 1 < n_stages ? st + 1 : 0);  // in flight during the MFMAs
 
-    if (st * PF_WAVES + wave < nb) {
-      // ---- headers of block `wave` of the stage: lane = row
+    if (st * PF_BLKS + bb < nb) {
+      // ---- headers of this wave's 32 rows of block bb (lanes 32-63 repeat
+      //      lanes 0-31 and write the same values)
       {
-        const uint2 h01 = *reinterpret_cast<const uint2 *>(&wblk[lane * WROW]);
-        const uint2 h23 = *reinterpret_cast<const uint2 *>(&wblk[lane * WROW + 2]);
+        const uint2 h01 = *reinterpret_cast<const uint2 *>(&wblk[hrow * WROW]);
+        const uint2 h23 = *reinterpret_cast<const uint2 *>(&wblk[hrow * WROW + 2]);
         const float d = half_lo(h01.x), dmin = half_hi(h01.x);
         // 6-bit scales and mins, four per dword (one per byte)
         const uint32_t sc03 = h01.y & 0x3F3F3F3Fu;
         const uint32_t mn03 = h23.x & 0x3F3F3F3Fu;
         const uint32_t sc47 = (h23.y & 0x0F0F0F0Fu) | ((h01.y >> 2) & 0x30303030u);
         const uint32_t mn47 = ((h23.y >> 4) & 0x0F0F0F0Fu) | ((h23.x >> 2) & 0x30303030u);
-        d_tab[wave][lane] = d;
+        d_tab[bb][hrow] = d;
         const uint32_t scw[2] = {sc03, sc47}, mnw[2] = {mn03, mn47};
 #pragma unroll
         for (int hw = 0; hw < 2; ++hw) {
@@ -233,61 +249,63 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
             const int s = 4 * hw + e;
             const float scf = (float)((scw[hw] >> (8 * e)) & 255u);
             const float mnf = (float)((mnw[hw] >> (8 * e)) & 255u);
-            c_tab[wave][s][lane] = dmin * mnf;
+            c_tab[bb][s][hrow] = dmin * mnf;
             // even sub-blocks are low nibbles, odd ones high nibbles (16 v)
             const float mulf = (s & 1) ? scf * 0.0625f : scf;
             const float addf = (s & 1) ? scf * -64.0f : scf * -1024.0f;
             half2_t m2, a2;
             m2.x = m2.y = (_Float16)mulf;
             a2.x = a2.y = (_Float16)addf;
-            sc_tab[wave][s][lane] = make_uint2(as_u32(m2), as_u32(a2));
+            sc_tab[bb][s][hrow] = make_uint2(as_u32(m2), as_u32(a2));
           }
         }
       }
 
-      // ---- MFMAs.  The four row tiles' accumulator chains are interleaved
-      //      so that consecutive MFMAs never depend on each other.
-      floatx4 acc[4];
+      // ---- MFMAs for row tiles 2*half + a.  The two accumulator chains are
+      //      interleaved with the sub-block-sum chain.
+      floatx4 acc[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int a = 0; a < 2; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
       // xsb[c]: the B operand of the fp32 MFMA, the sum of x over
       // sub-block 4c + g for token r (lane group g picks its sub-block)
       float xsb[2] = {0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint2 qb[4], tl[4], th[4];
+        uint2 qb[2], tl[2], th[2];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          qb[a] = *reinterpret_cast<const uint2 *>(&wblk[(16 * a + r) * WROW + 4 + 8 * j + 2 * g]);
-          tl[a] = sc_tab[wave][2 * j][16 * a + r];
-          th[a] = sc_tab[wave][2 * j + 1][16 * a + r];
+        for (int a = 0; a < 2; ++a) {
+          const int row = 16 * (2 * half + a) + r;
+          qb[a] = *reinterpret_cast<const uint2 *>(&wblk[row * WROW + 4 + 8 * j + 2 * g]);
+          tl[a] = sc_tab[bb][2 * j][row];
+          th[a] = sc_tab[bb][2 * j + 1][row];
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int s = 2 * j + h;
-          const half8_t Bh = *reinterpret_cast<const half8_t *>(&xh[wave][r][16 * s + 4 * g]);
-          const half8_t Bl = *reinterpret_cast<const half8_t *>(&xl[wave][r][16 * s + 4 * g]);
-          half8_t A[4];
+          const half8_t Bh = *reinterpret_cast<const half8_t *>(&xh[bb][r][16 * s + 4 * g]);
+          const half8_t Bl = *reinterpret_cast<const half8_t *>(&xl[bb][r][16 * s + 4 * g]);
+          half8_t A[2];
 #pragma unroll
-          for (int a = 0; a < 4; ++a)
+          for (int a = 0; a < 2; ++a)
             A[a] = h ? dequant8(qb[a].x, qb[a].y, true, th[a].x, th[a].y)
                      : dequant8(qb[a].x, qb[a].y, false, tl[a].x, tl[a].y);
+          floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-          for (int a = 0; a < 4; ++a)
+          for (int a = 0; a < 2; ++a)
             acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[a], Bh, acc[a], 0, 0, 0);
+          sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bl, sx, 0, 0, 0);
 #pragma unroll
-          for (int a = 0; a < 4; ++a)
+          for (int a = 0; a < 2; ++a)
             acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[a], Bl, acc[a], 0, 0, 0);
           // sum of x over sub-block s for token r (every row of the tile)
-          floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bl, sx, 0, 0, 0);
           if ((s & 3) == g) xsb[s >> 2] = sx[0];
         }
       }
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        // d of rows 16a + 4g + e (the rows of this lane's D elements)
-        const float4 dv = *reinterpret_cast<const float4 *>(&d_tab[wave][16 * a + 4 * g]);
+      for (int a = 0; a < 2; ++a) {
+        const int rt = 2 * half + a;
+        // d of rows 16 rt + 4g + e (the rows of this lane's D elements)
+        const float4 dv = *reinterpret_cast<const float4 *>(&d_tab[bb][16 * rt + 4 * g]);
         y_acc[a][0] = __builtin_fmaf(dv.x, acc[a][0], y_acc[a][0]);
         y_acc[a][1] = __builtin_fmaf(dv.y, acc[a][1], y_acc[a][1]);
         y_acc[a][2] = __builtin_fmaf(dv.z, acc[a][2], y_acc[a][2]);
@@ -295,20 +313,20 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
         // lazy-dmin term: A[row][kk] = dmin*m of sub-block 4c + kk, B = sums
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(c_tab[wave][4 * c + g][16 * a + r], xsb[c],
+          m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(c_tab[bb][4 * c + g][16 * rt + r], xsb[c],
                                                           m_acc[a], 0, 0, 0);
       }
     }
     __syncthreads();  // the next stage overwrites the LDS tiles
   }
 
-  // ---- add the waves' partial tiles (through the activation tiles, no
-  //      longer needed) and store.  Lane (token r, group g) holds rows
-  //      16a + 4g + e of its token.
-  float4 *red = reinterpret_cast<float4 *>(&xh[0][0][0]);  // [wave][token][17]
+  // ---- add the four blocks' partial tiles (through the activation tiles,
+  //      no longer needed) and store.  Lane (token r, group g) holds rows
+  //      16 rt + 4g + e of its token.
+  float4 *red = reinterpret_cast<float4 *>(&xh[0][0][0]);  // [block][token][17]
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-    red[(wave * PF_TOK + r) * 17 + 4 * a + g] =
+  for (int a = 0; a < 2; ++a)
+    red[(bb * PF_TOK + r) * 17 + 4 * (2 * half + a) + g] =
         make_float4(y_acc[a][0] - m_acc[a][0], y_acc[a][1] - m_acc[a][1],
                     y_acc[a][2] - m_acc[a][2], y_acc[a][3] - m_acc[a][3]);
   __syncthreads();
@@ -317,7 +335,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     const int tok = o / PF_ROWS, rr = o % PF_ROWS;
     float v = 0.f;
 #pragma unroll
-    for (int wv2 = 0; wv2 < PF_WAVES; ++wv2) v += redf[(wv2 * PF_TOK + tok) * 68 + rr];
+    for (int b = 0; b < PF_BLKS; ++b) v += redf[(b * PF_TOK + tok) * 68 + rr];
     if (tok0 + tok < M && row0 + rr < N) Y[(int64_t)(tok0 + tok) * N + row0 + rr] = v;
   }
 }
