@@ -288,7 +288,10 @@ def cpu_baseline(wl, seconds):
                       f"{os.cpu_count()} host cpus visible"}
 
 
-TRAFFIC_FILES = {"c2": "q4k_gemv_4096x4096_b1.traffic.json"}
+TRAFFIC_FILES = {"c2": "q4k_gemv_4096x4096_b1.traffic.json",
+                 "c3": "q4k_gemv_ffn_4096x14336_pair.traffic.json",
+                 "c4": "q4k_prefill_64x4096x4096.traffic.json",
+                 "c5": "ternary_gemv_4096x4096_b1.traffic.json"}
 
 
 def traffic_for(wl):
