@@ -48,6 +48,7 @@ def kernel_hash(files):
 
 
 GEMV_SRC = ["q4_packed_weight_amd/csrc/q4k_gemv.hip",
+            "q4_packed_weight_amd/csrc/q4k_gemv_mfma.hip",
             "q4_packed_weight_amd/csrc/device_common.h"]
 PREFILL_SRC = ["q4_packed_weight_amd/csrc/q4k_prefill.hip",
                "q4_packed_weight_amd/csrc/device_common.h"]
@@ -80,7 +81,8 @@ def make_workload(name, torch, binding, synth):
         wl.copies = copies
         wl.bytes = wbytes + 4 * K + 4 * N
         wl.flops = 2 * K * N
-        wl.kernel = "q4k_gemv_kernel"
+        # 4096 x 4096 runs the matrix-core form (256 workgroups of 16 rows)
+        wl.kernel = "q4k_gemv_mfma_kernel" if name == "c2" else "q4k_gemv_kernel"
         wl.src_files = GEMV_SRC
         wl.config = {"workload": f"q4k_gemv {K}x{N} batch 1", "input_dim": K,
                      "output_dim": N, "batch": 1, "rotating_copies": copies,

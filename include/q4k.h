@@ -63,7 +63,16 @@ extern "C" {
  *   y          fp32 [output_dim]
  * fp32 accumulation; agreement with the exact product is within about 1e-4
  * relative (elementwise against 1e-4*|y| + 1e-4*rms(y)).  |x| should stay
- * above ~1e-30 for full precision (codes enter the multiply scaled by 2^-24).
+ * above ~1e-30 for full precision (the vector form's codes enter the
+ * multiply scaled by 2^-24).
+ * Two kernels compute it: a vector form (lanes own 32-byte slabs of a row
+ * and walk rows) and a matrix-core form (16x16x32 f16 MFMA over 16 rows x
+ * one sub-block; each 32-activation sub-block is scaled by a power of two
+ * and split into exact fp16 hi and lo halves, which holds for |x| < 2^96,
+ * about 7.9e28).  The
+ * call picks the matrix-core form when ceil(output_dim/16) is 240..256 and
+ * input_dim/256 is 8..24 (where it measured faster on MI355X), else the
+ * vector form; q4k_gemv_shaped selects either explicitly.
  */
 int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
              int64_t output_dim, float *y, void *stream);
@@ -129,9 +138,10 @@ int ternary_gemv(const float *x, const uint8_t *codes, float scale,
  * of one workgroup that split input_dim between them), workgroup_waves in
  * {1, 2, 4, 8} (a multiple of k_waves; with 8 waves k_waves <= 2 and
  * rows_per_lane <= 4).  A value of 0 lets the library choose (k_waves = 0
- * never exceeds the workgroup size).  Any other value gives
- * Q4K_EINVAL_DIM.  Results are within the q4k_gemv tolerance for every
- * shape (the summation order depends on the shape).
+ * never exceeds the workgroup size).  workgroup_waves = 16 selects the
+ * matrix-core form instead (rows_per_lane and k_waves must then be 0).  Any
+ * other value gives Q4K_EINVAL_DIM.  Results are within the q4k_gemv
+ * tolerance for every shape (the summation order depends on the shape).
  */
 int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                     int64_t output_dim, float *y, void *stream,

@@ -61,6 +61,22 @@ __device__ __forceinline__ float sum4(float4 v) { return (v.x + v.y) + (v.z + v.
 // every lane of the group receives the group sum.  Steps below 16 lanes use
 // DPP quad permutes and row mirrors; the 16- and 32-lane steps use
 // ds_swizzle-free bpermute via __shfl_xor (issued once per output).
+// Maximum over aligned groups of `width` lanes (width 2, 4 or 8): DPP quad
+// permutes and the half-row mirror; every lane of the group receives it.
+template <int width>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(width == 2 || width == 4 || width == 8, "group_max covers 2, 4 or 8 lanes");
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+      __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true)));  // quad_perm [1,0,3,2]
+  if constexpr (width >= 4)
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+        __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true)));  // quad_perm [2,3,0,1]
+  if constexpr (width >= 8)
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+        __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)));  // row_half_mirror
+  return v;
+}
+
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (width >= 2)

@@ -24,6 +24,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // below 2^31.
 constexpr int64_t kMaxInputDim = (int64_t)1 << 24;
 
+
 int check_q4k(const void *x, const uint8_t *w, const void *y, int64_t M,
               int64_t K, int64_t N) {
   if (M <= 0 || K <= 0 || N <= 0 || K % 256 != 0 || K > kMaxInputDim)
@@ -49,6 +50,12 @@ int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                     int rows_per_lane, int k_waves, int workgroup_waves) {
   int rc = check_q4k(x, w_blocks, y, 1, input_dim, output_dim);
   if (rc) return rc;
+  if (workgroup_waves == 16) {  // the matrix-core form
+    if (rows_per_lane != 0 || k_waves != 0) return Q4K_EINVAL_DIM;
+    hipError_t e = q4k::gemv_mfma_launch(x, w_blocks, y, input_dim / 256, output_dim,
+                                         (hipStream_t)stream);
+    return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_gemv launch");
+  }
   const auto pow2_le = [](int v, int hi) {
     return v == 0 || ((v & (v - 1)) == 0 && v > 0 && v <= hi);
   };
@@ -68,7 +75,8 @@ int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
 
 int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
              int64_t output_dim, float *y, void *stream) {
-  return q4k_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0, 0);
+  return q4k_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0,
+                         q4k::use_gemv_mfma(input_dim / 256, output_dim) ? 16 : 0);
 }
 
 int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,

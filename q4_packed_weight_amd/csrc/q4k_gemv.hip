@@ -271,6 +271,157 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
   }
 }
 
+// Persistent form for rows that fit in one step (4*nb <= L slabs) and
+// more row groups than stay resident: a workgroup stages the activations
+// once, then walks units u = blockIdx.x, blockIdx.x + gridDim.x, ... (a unit
+// is the W*R*G rows one launch of the kernel above would give a
+// workgroup), loading the weight tile of the next unit while it computes
+// the current one.  Arithmetic and summation order per row are those of
+// q4k_gemv_kernel with KW = 1, so results are identical.
+template <int L, int R, int W>
+__global__ __launch_bounds__(64 * W) void q4k_gemv_persist_kernel(
+    const float *x, const uint8_t *w, float *__restrict__ y, int nb,
+    int64_t N, int n_units) {
+  constexpr int kThreads = 64 * W;
+  constexpr int G = 64 / L;
+  constexpr int ROWS_W = G * R;
+  constexpr int BPS = L / 4;
+  constexpr int CH_ROW = BPS * 9;
+  constexpr int TILE = ROWS_W * CH_ROW;
+  constexpr int NM = (TILE + 63) / 64;
+  constexpr int S = L;
+  constexpr int SP = S + 1;
+  constexpr int XF = 16 * S;
+  constexpr int XQ = (XF + kThreads - 1) / kThreads;
+  static_assert(XF % 64 == 0, "staging guard must be wave-uniform");
+  __shared__ float4 xs4[16 * SP];
+  __shared__ float2 xsum[S];
+  __shared__ uint4 wt[W][TILE];
+
+  __builtin_assume(nb >= 1);
+  __builtin_assume(n_units >= 1);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane / L;
+  const int u = lane % L;
+  const int n_slabs = 4 * nb;
+  const int64_t row_bytes = (int64_t)nb * kBlockBytes;
+  const int j = u & 3;
+  const uint32_t sh = (uint32_t)(j & 1) * 16u;
+  const bool jhi = j >= 2;
+  const int64_t unit_rows = (int64_t)W * ROWS_W;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)nb * 1024);
+
+  // Weight tile of a unit: chunk q of this wave's tile is row q / CH_ROW of
+  // the wave, chunk q % CH_ROW of the row (the whole row: one step).
+  auto load_tile = [&](int unit, uint4 (&wv)[NM]) {
+    const int64_t r0 = (int64_t)unit * unit_rows;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + r0 * row_bytes, (N - r0) * row_bytes);
+    const int wave_off = (int)(wave * ROWS_W * row_bytes);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int q = 64 * m + lane;
+      const int rt = q / CH_ROW;
+      const int within = q - rt * CH_ROW;
+      wv[m] = load_buf_stream16(wr, wave_off + rt * (int)row_bytes + 16 * within);
+    }
+  };
+
+  // Activations (all slabs) and the first unit's tile.
+  float4 xv[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) {
+    const int f = min(tid + kThreads * q, XF - 1);
+    xv[q] = load_buf_f4(xr, 4 * (64 * (f >> 4) + 4 * (f & 15)));
+  }
+  uint4 wa[NM], wb[NM];
+  int unit = blockIdx.x;
+  load_tile(unit, wa);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) {
+    const int f = tid + kThreads * q;
+    if (XF % kThreads != 0 && f >= XF) break;  // wave-uniform
+    const int sl = f >> 4, k = f & 15;
+    xs4[k * SP + sl] = xv[q];
+    const float part = group_sum<8>(sum4(xv[q]));
+    if (k == 0) xsum[sl].x = part;
+    if (k == 8) xsum[sl].y = part;
+  }
+  __syncthreads();
+  const bool active = u < n_slabs;
+  float4 xl[8], xh[8];
+  float2 xsm = make_float2(0.f, 0.f);
+  if (active) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      xl[k] = xs4[k * SP + u];
+      xh[k] = xs4[(k + 8) * SP + u];
+    }
+    xsm = xsum[u];
+  }
+  const int bl = u >> 2;
+
+  auto compute = [&](int cur, const uint4 (&wv)[NM]) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int prev_last = r == 0 ? -1 : (r * G * CH_ROW - 1) / 64;
+      const int last_m = ((r + 1) * G * CH_ROW - 1) / 64;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        if (m > prev_last && m <= last_m && 64 * m + lane < TILE) wt[wave][64 * m + lane] = wv[m];
+      acc[r] = 0.0f;
+      if (active) {
+        const int base = ((r * G + g) * BPS + bl) * 9;
+        const uint4 hdr = wt[wave][base];
+        const uint4 q0 = wt[wave][base + 1 + 2 * j];
+        const uint4 q1 = wt[wave][base + 2 + 2 * j];
+        float lo[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f};
+        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) nibble_dots(qw[k], xl[k], xh[k], lo, hi);
+        const float s_lo = lo[0] + lo[1], s_hi = hi[0] + hi[1];
+        const SlabScales sc = decode_header(hdr, sh, jhi);
+        const float tc = __builtin_fmaf(sc.sc_lo16, s_lo, sc.sc_hi * s_hi);
+        const float tm = __builtin_fmaf(sc.m_lo, xsm.x, sc.m_hi * xsm.y);
+        acc[r] = __builtin_fmaf(sc.d * 0x1p20f, tc, __builtin_fmaf(-sc.dmin, tm, acc[r]));
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(acc[r]);
+    if (u == 0) {
+      const int64_t row0 = (int64_t)cur * unit_rows + (int64_t)wave * ROWS_W;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t row = row0 + (int64_t)r * G + g;
+        if (row < N) y[row] = acc[r];
+      }
+    }
+  };
+
+  // Ping-pong over the two tile registers: the next unit's loads are in
+  // flight while the current unit is computed.
+  for (;;) {
+    const int nxt = unit + (int)gridDim.x;
+    if (nxt < n_units) load_tile(nxt, wb);
+    compute(unit, wa);
+    if (nxt >= n_units) break;
+    unit = nxt;
+    const int nxt2 = unit + (int)gridDim.x;
+    if (nxt2 < n_units) load_tile(nxt2, wa);
+    compute(unit, wb);
+    if (nxt2 >= n_units) break;
+    unit = nxt2;
+  }
+}
+
+// Workgroups of the persistent form that stay resident on the 256 CUs (two
+// per CU, the LDS limit of the 4-wave form).
+constexpr int64_t kPersistSlots = 512;
+
 template <int L, int R, int KW, int W>
 hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, int nb,
                        int64_t N, hipStream_t stream) {
@@ -278,6 +429,17 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, int nb,
   constexpr int64_t rows_per_wg = (int64_t)(W / KW) * G * R;
   const int64_t grid = (N + rows_per_wg - 1) / rows_per_wg;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if constexpr (KW == 1 && W == 4) {
+    // One step per row and more units than resident slots: walk the units
+    // with as few workgroups as give every workgroup the same unit count.
+    if (4 * (int64_t)nb <= L && grid > kPersistSlots) {
+      const int64_t per = (grid + kPersistSlots - 1) / kPersistSlots;
+      const int64_t pgrid = (grid + per - 1) / per;
+      hipLaunchKernelGGL((q4k_gemv_persist_kernel<L, R, W>), dim3((unsigned)pgrid),
+                         dim3(64 * W), 0, stream, x, w, y, nb, N, (int)grid);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((q4k_gemv_kernel<L, R, KW, W>), dim3((unsigned)grid),
                      dim3(64 * W), 0, stream, x, w, y, nb, N);
   return hipGetLastError();

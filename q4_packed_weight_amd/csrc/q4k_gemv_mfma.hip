@@ -1,0 +1,282 @@
+// q4k_gemv_mfma.hip -- Q4_K matrix-vector product with the multiplies on the
+// gfx950 matrix cores.
+//
+// What it computes is q4k_gemv's product (Q4_K page: SKaiNET PR #562,
+// "feat(kernel): SIMD-fused Q4_K matmul kernel + Q4KMatmulKernel SPI",
+// sections "Summary" and "Pipeline"): y[o] = sum over super-blocks and
+// sub-blocks of d*sc*sum_l q*x - dmin*m*sum_l x, the lazy-dmin form.
+//
+// Why MFMA for a batch of one: on the vector path every weight costs a
+// mask and an fma_mix; here the nibbles are only masked into fp16
+// subnormals (q * 2^-24, exact) and one 16x16x32 f16 MFMA takes 512 of
+// them.  The MFMA's B operand is 16 weight rows x 32 positions of one
+// sub-block; its A operand carries the activations: rows 0, 2, 4, ... hold
+// the fp16 hi part of x and rows 1, 3, 5, ... the lo part (hi = fp16(x),
+// lo = fp16(x - hi), both exact as MFMA inputs), so D rows 4g and 4g + 1
+// of every lane hold the hi and lo halves of the same dot product and one
+// instruction does both.  Before the split each 32-activation sub-block is
+// scaled by a power of two that brings its largest |x| into [2^14, 2^15):
+// the halves can neither overflow fp16 nor, for any element within 2^-17 of
+// the sub-block's largest, lose bits of lo to fp16's subnormal range.  The
+// power of two is folded into the per-sub-block scale d*sc, which (like the
+// lazy-dmin term) is applied once per sub-block in fp32; that scale stays
+// finite for every |x| < 2^96 (d*sc < 2^22).
+//
+// Work decomposition: a workgroup owns 16 rows; its 16 waves (four per
+// SIMD, so that one wave's LDS and MFMA latencies hide under another's
+// work) split the super-blocks of input_dim (contiguous ranges).  A wave
+// walks its range one super-block at a time: it loads it (16 rows x 144
+// bytes of weights, 256 activations) with coalesced 16-byte loads one ahead,
+// stores it in a wave-private LDS area (activations already split and in
+// operand order, with their sub-block sums), then runs the MFMAs.  Lane
+// (n = lane % 16, g = lane / 16) applies the scales of sub-blocks 2g and
+// 2g+1 of row n; the four lane groups and the four waves are summed at the
+// end, so every output has one writer and a fixed summation order.
+#include "device_common.h"
+#include "q4k_internal.h"
+
+namespace q4k {
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlockBytes = 144;
+constexpr int MV_ROWS = 16;           // rows per workgroup (one MFMA column tile)
+constexpr int MV_WAVES = 16;
+constexpr int MV_CB = 1;              // super-blocks per chunk
+constexpr int MV_WCH = MV_ROWS * MV_CB * 9;             // 16-byte weight chunks per chunk
+constexpr int MV_WPL = (MV_WCH + 63) / 64;              // weight loads per lane
+constexpr int MV_XPL = MV_CB * 256 / 4 / 64;            // activation float4 per lane
+constexpr int MV_WROW = MV_CB * 36 + 2;                 // LDS dwords per staged row (+ 8 B)
+static_assert(MV_XPL * 64 * 4 == MV_CB * 256, "activation chunk must split evenly");
+
+__device__ __forceinline__ uint32_t as_u32h(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// lo = fp16(x - hi) for the two halves of `hi2` (fp16 hi parts of x0, x1):
+// v_fma_mix evaluates x - hi exactly in fp32 and rounds once to fp16.
+__device__ __forceinline__ uint32_t lo_pair_mv(uint32_t hi2, float x0, float x1) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi2), "v"(x0));
+  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(r) : "v"(hi2), "v"(x1));
+  return r;
+}
+
+__global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
+    const float *x, const uint8_t *w, float *__restrict__ y, int nb, int N) {
+  // Per wave: staged weight rows, fp16 hi and lo activations of the chunk
+  // (positions in operand order: pairs (0,2), (1,3), (4,6), (5,7) of every
+  // 8), the chunk's sub-block sums; then the cross-wave partials.
+  __shared__ __align__(16) uint32_t wt[MV_WAVES][MV_ROWS * MV_WROW];
+  __shared__ __align__(16) uint32_t xh[MV_WAVES][MV_CB * 128];
+  __shared__ __align__(16) uint32_t xl[MV_WAVES][MV_CB * 128];
+  // per sub-block pair p (sub-blocks 2p, 2p+1): their x sums, then their
+  // scaling exponents (int bits), read by one lane as one 16-byte word
+  __shared__ __align__(16) float xse[MV_WAVES][MV_CB * 16];
+  __shared__ float part[MV_WAVES][MV_ROWS];
+
+  __builtin_assume(nb >= 1);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;  // B column / D column: weight row; A row
+  const int g = lane >> 4;  // lane group: positions 8g .. 8g+7
+  const int row0 = blockIdx.x * MV_ROWS;
+  const int row_bytes = nb * kBlockBytes;
+  // this wave's super-blocks [b_lo, b_hi)
+  const int b_lo = (int)(((int64_t)nb * wave) / MV_WAVES);
+  const int b_hi = (int)(((int64_t)nb * (wave + 1)) / MV_WAVES);
+  const int n_chunks = (b_hi - b_lo + MV_CB - 1) / MV_CB;
+
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(w + (int64_t)row0 * row_bytes, (int64_t)(N - row0) * row_bytes);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)nb * 1024);
+
+  // Load roles: weight chunk q (clamped; the duplicates are never stored)
+  // is row q / (9 MV_CB), chunk q % (9 MV_CB) of the row's piece of the chunk;
+  // activation float4 i is positions 4*(lane + 64 i) of the chunk.
+  int woff[MV_WPL];
+#pragma unroll
+  for (int m = 0; m < MV_WPL; ++m) {
+    const int q = min(lane + 64 * m, MV_WCH - 1);
+    const int row = q / (9 * MV_CB);
+    woff[m] = row * row_bytes + 16 * (q - row * 9 * MV_CB);
+  }
+  uint4 wa[MV_WPL], wb[MV_WPL];
+  float4 xa[MV_XPL], xb[MV_XPL];
+  auto load_chunk = [&](int c, uint4 (&wv)[MV_WPL], float4 (&xv)[MV_XPL]) {
+    const int b0 = __builtin_amdgcn_readfirstlane(b_lo + c * MV_CB);  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < MV_XPL; ++i) xv[i] = load_buf_f4(xr, 16 * (lane + 64 * i), 1024 * b0);
+#pragma unroll
+    for (int m = 0; m < MV_WPL; ++m) wv[m] = load_buf_stream16(wr, woff[m], kBlockBytes * b0);
+  };
+
+  uint32_t *wtw = wt[wave];
+  auto stage_chunk = [&](const uint4 (&wv)[MV_WPL], const float4 (&xv)[MV_XPL]) {
+#pragma unroll
+    for (int m = 0; m < MV_WPL; ++m) {
+      const int q = lane + 64 * m;
+      if (MV_WCH % 64 != 0 && q >= MV_WCH) break;  // only the last load is partial
+      const int row = q / (9 * MV_CB);
+      uint32_t *dst = &wtw[row * MV_WROW + 4 * (q - row * 9 * MV_CB)];
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(wv[m].x, wv[m].y);
+      *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wv[m].z, wv[m].w);
+    }
+#pragma unroll
+    for (int i = 0; i < MV_XPL; ++i) {
+      const float4 v0 = xv[i];
+      // sub-block (f / 8, 8 aligned lanes) scaling: |x| * 2^-e < 2^15
+      float mx = fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w)));
+      mx = group_max<8>(mx);
+      const int e = __builtin_amdgcn_frexp_expf(mx) - 15;
+      const float4 v = make_float4(__builtin_ldexpf(v0.x, -e), __builtin_ldexpf(v0.y, -e),
+                                   __builtin_ldexpf(v0.z, -e), __builtin_ldexpf(v0.w, -e));
+      half2_t h02, h13;
+      h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
+      h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
+      const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
+      const int f = lane + 64 * i;  // float4 index: positions 4f .. 4f+3
+      *reinterpret_cast<uint2 *>(&xh[wave][2 * f]) = make_uint2(hw02, hw13);
+      *reinterpret_cast<uint2 *>(&xl[wave][2 * f]) =
+          make_uint2(lo_pair_mv(hw02, v.x, v.z), lo_pair_mv(hw13, v.y, v.w));
+      // sub-block f / 8: the 8 float4 of a sub-block sit in 8 aligned lanes
+      const float s = group_sum<8>(sum4(v0));
+      if ((lane & 7) == 0) {
+        const int sb = f >> 3;
+        xse[wave][4 * (sb >> 1) + (sb & 1)] = s;
+        xse[wave][4 * (sb >> 1) + 2 + (sb & 1)] = __builtin_bit_cast(float, e);
+      }
+    }
+  };
+
+  // A operand rows: even rows the hi part, odd rows the lo part.
+  const uint32_t *xa_src = (n & 1) ? xl[wave] : xh[wave];
+  const int j_mine = g;  // sub-blocks 2g, 2g+1 are scaled by this lane
+  const uint32_t sh = (uint32_t)(g & 1) * 16u;
+  const bool jhi = g >= 2;
+  float yacc = 0.f;
+
+  auto compute_chunk = [&](int c) {
+    const int nblk = min(MV_CB, b_hi - (b_lo + c * MV_CB));
+#pragma unroll
+    for (int bb = 0; bb < MV_CB; ++bb) {
+      if (bb >= nblk) break;  // wave-uniform
+      const uint32_t *rowp = &wtw[n * MV_WROW + 36 * bb];
+      // header of row n: d, dmin and the scale/min of sub-blocks 2g, 2g+1
+      const uint2 h01 = *reinterpret_cast<const uint2 *>(rowp);
+      const uint2 h23 = *reinterpret_cast<const uint2 *>(rowp + 2);
+      const uint32_t p1 = h01.y >> sh, p2 = h23.x >> sh, t3 = h23.y >> sh;
+      const uint32_t sc_src = jhi ? t3 : p1;
+      const uint32_t m_src = jhi ? (t3 >> 4) : p2;
+      const uint32_t mask_lo = jhi ? 0x0F0Fu : 0x3F3Fu;
+      const uint32_t mask_hi = jhi ? 0x3030u : 0u;
+      const uint32_t scp = (sc_src & mask_lo) | ((p1 >> 2) & mask_hi);
+      const uint32_t mp = (m_src & mask_lo) | ((p2 >> 2) & mask_hi);
+      const float d = half_lo(h01.x), dmin = half_hi(h01.x);
+      const float4 xsp = *reinterpret_cast<const float4 *>(&xse[wave][4 * (4 * bb + j_mine)]);
+      // codes enter as q * 2^-24 (low nibbles) and 16q * 2^-24 (high), the
+      // activations as x * 2^-e
+      const float s_lo = __builtin_ldexpf(d * (float)(scp & 0xFFu),
+                                          __builtin_bit_cast(int, xsp.z) + 24);
+      const float s_hi = __builtin_ldexpf(d * (float)((scp >> 8) & 0xFFu),
+                                          __builtin_bit_cast(int, xsp.w) + 20);
+      yacc = __builtin_fmaf(-dmin, __builtin_fmaf((float)(mp & 0xFFu), xsp.x,
+                                                  (float)((mp >> 8) & 0xFFu) * xsp.y), yacc);
+      // All operands of the block first, then eight independent MFMAs, then
+      // the combine: no read waits on a just-issued MFMA.
+      uint2 qb[4];
+      half8_t alo[4], ahi[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qb[j] = *reinterpret_cast<const uint2 *>(rowp + 4 + 8 * j + 2 * g);
+        const int pos = 256 * bb + 64 * j + 8 * g;  // sub-block 2j, positions 8g..
+        alo[j] = *reinterpret_cast<const half8_t *>(&xa_src[pos / 2]);
+        ahi[j] = *reinterpret_cast<const half8_t *>(&xa_src[(pos + 32) / 2]);
+      }
+      floatx4 dlo[4], dhi[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t s0 = qb[j].x >> 8, s1 = qb[j].y >> 8;
+        uint4 blo, bhi;
+        blo.x = qb[j].x & 0x000F000Fu; blo.y = s0 & 0x000F000Fu;
+        blo.z = qb[j].y & 0x000F000Fu; blo.w = s1 & 0x000F000Fu;
+        bhi.x = qb[j].x & 0x00F000F0u; bhi.y = s0 & 0x00F000F0u;
+        bhi.z = qb[j].y & 0x00F000F0u; bhi.w = s1 & 0x00F000F0u;
+        dlo[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            alo[j], __builtin_bit_cast(half8_t, blo), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        dhi[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            ahi[j], __builtin_bit_cast(half8_t, bhi), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
+      // D rows 4g (hi part) and 4g + 1 (lo part) of row n; this lane keeps
+      // sub-block pair j = g
+      float t_lo = dlo[0][0] + dlo[0][1], t_hi = dhi[0][0] + dhi[0][1];
+#pragma unroll
+      for (int j = 1; j < 4; ++j) {
+        if (j == j_mine) {
+          t_lo = dlo[j][0] + dlo[j][1];
+          t_hi = dhi[j][0] + dhi[j][1];
+        }
+      }
+      yacc = __builtin_fmaf(s_lo, t_lo, __builtin_fmaf(s_hi, t_hi, yacc));
+    }
+  };
+
+  if (n_chunks > 0) {  // wave-uniform
+    load_chunk(0, wa, xa);
+    for (int c = 0;;) {
+      const bool more = c + 1 < n_chunks;
+      if (more) load_chunk(c + 1, wb, xb);
+      stage_chunk(wa, xa);
+      compute_chunk(c);
+      if (!more) break;
+      ++c;
+      const bool more2 = c + 1 < n_chunks;
+      if (more2) load_chunk(c + 1, wa, xa);
+      stage_chunk(wb, xb);
+      compute_chunk(c);
+      if (!more2) break;
+      ++c;
+    }
+  }
+
+  // Sum the four lane groups (lanes n, n+16, n+32, n+48), then the waves.
+  yacc += __shfl_xor(yacc, 16, 64);
+  yacc += __shfl_xor(yacc, 32, 64);
+  if (lane < MV_ROWS) part[wave][lane] = yacc;
+  __syncthreads();
+  if (tid < MV_ROWS) {
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < MV_WAVES; ++k) v += part[k][tid];
+    if (row0 + tid < N) y[row0 + tid] = v;
+  }
+}
+
+}  // namespace
+
+bool use_gemv_mfma(int64_t nb, int64_t N) {
+  // Measured (graph-replayed calls over rotating weights, input_dim 2048 to
+  // 6144, output_dim 2048 to 12288): the matrix-core form wins when its
+  // grid fills the 256 CUs once, one 16-wave workgroup each; with more
+  // workgroups than CUs the vector kernel's several-per-CU occupancy wins.
+  const int64_t grid = (N + MV_ROWS - 1) / MV_ROWS;
+  return grid >= 240 && grid <= 256 && nb >= 8 && nb <= 24;
+}
+
+hipError_t gemv_mfma_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
+                            int64_t N, hipStream_t stream) {
+  const int64_t grid = (N + MV_ROWS - 1) / MV_ROWS;
+  // Offsets formed in the kernel: 16 rows of weights and the activation
+  // vector stay below 2^31 bytes.
+  if (grid > 0x7FFFFFFF || N > 0x7FFFFFFF ||
+      (int64_t)MV_ROWS * nb * kBlockBytes >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(q4k_gemv_mfma_kernel, dim3((unsigned)grid), dim3(64 * MV_WAVES), 0, stream,
+                     x, w, y, (int)nb, (int)N);
+  return hipGetLastError();
+}
+
+}  // namespace q4k

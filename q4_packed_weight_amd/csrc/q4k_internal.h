@@ -19,6 +19,14 @@ GemvShape choose_gemv_shape(int64_t nb, int64_t N, int rows_per_lane, int k_wave
 hipError_t gemv_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
                        int64_t N, const GemvShape &s, hipStream_t stream);
 
+// Q4_K GEMV with the multiplies on the matrix cores (16 rows per workgroup).
+hipError_t gemv_mfma_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
+                            int64_t N, hipStream_t stream);
+// Whether q4k_gemv's automatic choice is the matrix-core form (measured on
+// MI355X: it wins while every wave owns at most one super-block and all
+// workgroups are resident at once).
+bool use_gemv_mfma(int64_t nb, int64_t N);
+
 hipError_t ternary_launch(const float *x, const uint8_t *codes, float scale,
                           bool apply_scale, int64_t K, int64_t N, float *y,
                           hipStream_t stream);

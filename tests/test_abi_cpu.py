@@ -96,7 +96,8 @@ def test_dimension_error_takes_precedence(lib):
 
 @pytest.mark.parametrize("rpl,kw,wg", [(3, 0, 0), (16, 1, 0), (0, 3, 0), (1, 8, 0),
                                        (-1, 0, 0), (1, 1, 3), (1, 4, 2), (2, 2, 1),
-                                       (1, 1, 16), (8, 1, 8), (1, 4, 8)])
+                                       (1, 1, 16), (8, 1, 8), (1, 4, 8), (4, 0, 16),
+                                       (0, 2, 16), (0, 0, 32)])
 def test_shaped_rejects_bad_launch_shape(lib, rpl, kw, wg):
     assert lib.q4k_gemv_shaped(GOOD, GOOD2, 256, 8, GOOD3, None, rpl, kw, wg) == -1
 

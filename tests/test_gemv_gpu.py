@@ -53,6 +53,54 @@ def test_gemv_parity_full_configs(oracle_lib, K, N, name):
     assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=name)
 
 
+@pytest.mark.parametrize("K,N", SHAPES + [(4096, 4096), (14336, 300), (2560, 4090)])
+def test_matrix_core_form_parity(oracle_lib, K, N):
+    """workgroup_waves = 16: the MFMA form at every shape (single block,
+    ragged rows and super-block counts, waves without blocks, long rows)."""
+    w = synth.q4k_weights(N, K, config=20, copy=K + N)
+    x = synth.activations(K, config=20, copy=K + N)
+    y = run_gemv(x, w, K, N, shape=(0, 0, 16))
+    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=f"mfma K={K} N={N}")
+
+
+@pytest.mark.parametrize("K,N", [(4096, 4096), (14336, 64), (768, 100)])
+def test_matrix_core_form_integer_bit_exact(oracle_lib, K, N):
+    """Integer weights and activations: the MFMA form is exact too (the
+    codes and the hi/lo activation halves are exact fp16 operands)."""
+    w = synth.q4k_integer_weights(N, K, config=21)
+    x = synth.integer_activations(K, config=21)
+    y = run_gemv(x, w, K, N, shape=(0, 0, 16))
+    assert np.array_equal(y.astype(np.float64), oracle_lib.q4k_gemv(x, w, K, N))
+
+
+@pytest.mark.parametrize("form", [None, (0, 0, 16)], ids=["auto", "mfma"])
+@pytest.mark.parametrize("K,N,lo,hi", [(4096, 4096, -40, 40), (2560, 300, -40, 40),
+                                       (4096, 256, -60, 92)])
+def test_wide_range_activations(oracle_lib, K, N, lo, hi, form):
+    """Activations far outside fp16's range, with every 32-element sub-block
+    at its own scale 2^lo .. 2^hi (up to just below the documented 2^96
+    bound of the matrix-core form) and some sub-blocks all zero: both forms
+    stay within the bar (the matrix-core form rescales each sub-block by a
+    power of two before its fp16 split)."""
+    w = synth.q4k_weights(N, K, config=22, copy=K + N)
+    x = synth.activations(K, config=22, copy=K + N)
+    g = np.random.default_rng(22)
+    scale = np.exp2(g.integers(lo, hi + 1, K // 32)).astype(np.float32)
+    scale[g.choice(K // 32, 3, replace=False)] = 0.0
+    x = (x.reshape(-1, 32) * scale[:, None]).reshape(-1)
+    assert np.abs(x).max() > 1e9
+    y = run_gemv(x, w, K, N, shape=form)
+    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=f"wide K={K} N={N}")
+
+
+def test_matrix_core_form_rejects_shape_fields():
+    xd = dev(np.zeros(256, np.float32))
+    wd = dev(np.zeros(144, np.uint8))
+    buf, y = out_with_canary(1)
+    with pytest.raises(ValueError):
+        binding.q4k_gemv_shaped(xd, wd, 256, 1, y, 4, 0, 16)
+
+
 @pytest.mark.parametrize("rpl", [1, 2, 4, 8])
 @pytest.mark.parametrize("kw,wg", [(1, 1), (1, 2), (2, 2), (1, 4), (2, 4), (4, 4), (1, 8), (2, 8)])
 @pytest.mark.parametrize("K,N", [(4096, 333), (14336, 67), (1024, 129), (256, 50)])
@@ -97,7 +145,7 @@ def test_one_hot_bit_exact_sampled_large(oracle_lib):
         assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), k
 
 
-@pytest.mark.parametrize("K,N", [(4096, 512), (14336, 64), (768, 100)])
+@pytest.mark.parametrize("K,N", [(4096, 512), (14336, 64), (768, 100), (4096, 8200)])
 def test_integer_inputs_bit_exact(oracle_lib, K, N):
     """d = dmin = 1, x in {-1, 0, 1}: all partial sums are integers below
     2^24, so any summation order is exact and the GPU equals the oracle."""
@@ -107,6 +155,17 @@ def test_integer_inputs_bit_exact(oracle_lib, K, N):
     ref = oracle_lib.q4k_gemv(x, w, K, N)
     assert np.all(ref == np.round(ref))
     assert np.array_equal(y.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("K,N", [(4096, 8200), (4096, 14341), (512, 70001), (2048, 33000)])
+def test_persistent_walk(oracle_lib, K, N):
+    """More row groups than resident workgroups: each workgroup walks several
+    units with the next unit's tile prefetched (ragged last unit, one
+    workgroup with a shorter walk, exact and uneven unit counts)."""
+    w = synth.q4k_weights(N, K, config=19, copy=K + N)
+    x = synth.activations(K, config=19, copy=K + N)
+    y = run_gemv(x, w, K, N)
+    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=f"K={K} N={N}")
 
 
 def test_zero_activation_exact_zero():
