@@ -57,10 +57,6 @@ __device__ __forceinline__ float4 load_buf_f4(__amdgpu_buffer_rsrc_t r, int off,
 
 __device__ __forceinline__ float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64);
-// every lane of the group receives the group sum.  Steps below 16 lanes use
-// DPP quad permutes and row mirrors; the 16- and 32-lane steps use
-// ds_swizzle-free bpermute via __shfl_xor (issued once per output).
 // Maximum over aligned groups of `width` lanes (width 2, 4 or 8): DPP quad
 // permutes and the half-row mirror; every lane of the group receives it.
 template <int width>
@@ -77,6 +73,10 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Sum over aligned groups of `width` lanes (width a power of two <= 64);
+// every lane of the group receives the group sum.  Steps below 16 lanes use
+// DPP quad permutes and row mirrors; the 16- and 32-lane steps use
+// ds_swizzle-free bpermute via __shfl_xor (issued once per output).
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (width >= 2)
