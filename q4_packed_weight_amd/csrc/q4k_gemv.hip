@@ -498,6 +498,11 @@ GemvShape choose_gemv_shape(int64_t nb, int64_t N, int rows_per_lane,
     const int64_t target_waves = 1024;
     int r = 4;
     while (r > 1 && (N + g * r - 1) / (g * r) * s.k_waves < target_waves) r /= 2;
+    // Where the persistent walk runs (one step per row, more than 512
+    // workgroups of 4 waves x 4 rows), 2 rows per lane balances the walk
+    // better: measured 0.4-2.1 us faster at input_dim 3072-4096 and
+    // output_dim 11008-28672, slower at input_dim 2048.
+    if (r == 4 && s.k_waves == 1 && s.lanes == 64 && nb >= 12 && N > 512 * 16) r = 2;
     s.rows_per_lane = r;
   }
   if (waves > 0) {
