@@ -90,10 +90,15 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
  *   n_tokens   M > 0 (M == 1 runs q4k_gemv)
  *   input_dim, output_dim as for q4k_gemv
  *   Y          fp32 [n_tokens, output_dim]
- * Same error behaviour and tolerance as q4k_gemv.  For M > 1 the
- * activations pass through fp16 (split into a high and a low half, both
- * exact MFMA operands) and must satisfy |x| < 65504.  Y must not alias X or
- * the weights.
+ * Same error behaviour and tolerance as q4k_gemv.  Three kernels serve it:
+ * M == 1 is q4k_gemv; a few tokens (M <= 2 at any output_dim, M <= 4 with
+ * output_dim <= 8192, M <= 8 with output_dim <= 4096) run on a batched
+ * matrix-core GEMV that reads each weight once for all of them; larger
+ * batches run on the prefill tiles (64 rows x 16 tokens).  The batched and
+ * prefill kernels pass the activations through fp16 (split into a high and
+ * a low half, both exact MFMA operands); the batched one first scales each
+ * token's super-block by a power of two (any |x| < 2^96), the prefill one
+ * requires |x| < 65504.  Y must not alias X or the weights.
  */
 int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
                int64_t input_dim, int64_t output_dim, float *Y, void *stream);

@@ -34,4 +34,9 @@ hipError_t ternary_launch(const float *x, const uint8_t *codes, float scale,
 hipError_t prefill_launch(const float *X, const uint8_t *w, int64_t M,
                           int64_t K, int64_t N, float *Y, hipStream_t stream);
 
+// 1 <= M <= 8 tokens on the matrix cores (q4k_gemv_batch.hip); X is
+// [M][nb*256], Y is [M][N].
+hipError_t gemv_batch_launch(const float *X, const uint8_t *w, float *Y, int64_t M, int64_t nb,
+                             int64_t N, hipStream_t stream);
+
 }  // namespace q4k

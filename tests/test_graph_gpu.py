@@ -71,3 +71,16 @@ def test_matmul_graph_replays():
     binding.q4k_matmul(Xi, wi, M, K, N, Y)
     eager = host(Y).copy()
     _replays_match(lambda: binding.q4k_matmul(Xi, wi, M, K, N, Y), Y, eager, exact=True)
+
+
+@pytest.mark.parametrize("M", [2, 5, 8])
+def test_matmul_few_tokens_graph_replays(M):
+    """The few-token path (the batched matrix-core GEMV): replays match the
+    eager result bit for bit."""
+    K, N = 4096, 512
+    w = dev(synth.q4k_weights(N, K, config=44))
+    X = dev(synth.activations(K, n_tokens=M, config=44))
+    Y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    binding.q4k_matmul(X, w, M, K, N, Y)
+    eager = host(Y).copy()
+    _replays_match(lambda: binding.q4k_matmul(X, w, M, K, N, Y), Y, eager, exact=True)

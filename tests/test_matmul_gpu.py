@@ -95,3 +95,67 @@ def test_matmul_rejects_bad_input_dim():
         binding.q4k_matmul(X, w, 4, 300, 8, Y)
     torch.cuda.synchronize()
     assert bool(torch.all(torch.isnan(buf)))
+
+
+# ---- a few tokens: the batched matrix-core GEMV (M <= 8 at output_dim <=
+#      4096; 9 to 16 tokens check the hand-over to the prefill tiles)
+
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 7, 8, 9, 12, 15, 16])
+def test_batch_token_counts(oracle_lib, M):
+    """Every token count of the batched form (2, 4 and 8-token kernels with
+    tokens past M zero), and the counts just above it."""
+    K, N = 4096, 300
+    w = synth.q4k_weights(N, K, config=36, copy=M)
+    X = synth.activations(K, n_tokens=M, config=36, copy=M)
+    Y = run(X, w, M, K, N)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"M={M}")
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 256, 1), (4, 512, 17), (6, 1280, 129), (8, 14336, 64),
+                                   (3, 768, 4097), (8, 2304, 1000), (2, 65536, 40), (7, 1792, 16),
+                                   (2, 1024, 14341)])
+def test_batch_shapes(oracle_lib, M, K, N):
+    """One super-block (7 of 8 waves without work), ragged super-block counts
+    per wave, ragged row tiles, long rows."""
+    w = synth.q4k_weights(N, K, config=37, copy=K + N)
+    X = synth.activations(K, n_tokens=M, config=37, copy=K + N)
+    Y = run(X, w, M, K, N)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"{M}x{K}x{N}")
+
+
+def test_batch_full_size(oracle_lib):
+    """8 tokens x 4096 -> 4096, every output."""
+    M, K, N = 8, 4096, 4096
+    w = synth.q4k_weights(N, K, config=synth.C2_Q4K_4K)
+    X = synth.activations(K, n_tokens=M, config=synth.C2_Q4K_4K)
+    Y = run(X, w, M, K, N)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what="8x4096x4096")
+
+
+@pytest.mark.parametrize("M", [2, 8, 13])
+def test_batch_integer_bit_exact(oracle_lib, M):
+    """d = dmin = 1, x in {-1, 0, 1}: every partial sum is an exact integer,
+    so the batched form equals the oracle bit for bit."""
+    K, N = 4096, 256
+    w = synth.q4k_integer_weights(N, K, config=38)
+    X = synth.integer_activations(K, n_tokens=M, config=38)
+    Y = run(X, w, M, K, N)
+    assert np.array_equal(Y.astype(np.float64), oracle_lib.q4k_matmul(X, w, M, K, N))
+
+
+def test_batch_wide_range_tokens(oracle_lib):
+    """Tokens at very different scales (2^-30 .. 2^60, one all zero), and
+    sub-blocks within a token at scales 2^-20 .. 2^20: each token's
+    activations are rescaled per super-block before their fp16 split."""
+    M, K, N = 8, 2048, 200
+    w = synth.q4k_weights(N, K, config=39)
+    X = synth.activations(K, n_tokens=M, config=39)
+    g = np.random.default_rng(39)
+    sub = np.exp2(g.integers(-20, 21, (M, K // 32))).astype(np.float32)
+    tok = np.exp2(np.array([-30, 0, 10, 30, 50, 60, -10, 0], np.float64)).astype(np.float32)
+    X = (X.reshape(M, -1, 32) * sub[:, :, None] * tok[:, None, None]).reshape(M, K)
+    X[6] = 0.0
+    Y = run(X, w, M, K, N)
+    ref = oracle_lib.q4k_matmul(X, w, M, K, N)
+    assert np.all(Y[6] == 0.0)
+    assert_parity(Y, ref, rowwise=True, what="wide-range tokens")
