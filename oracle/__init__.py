@@ -1,4 +1,4 @@
-"""CPU oracle for the Q4_K and ternary matrix-vector products.
+"""CPU oracle for the Q4_K, Q4_0 and ternary matrix-vector products.
 
 TEST INFRASTRUCTURE ONLY: this package may be imported by tests/, by the
 package smoke check and by bench.py's CPU-baseline leg, nothing else.  It
@@ -51,6 +51,10 @@ def _load():
     lib.oracle_q4k_matmul_part.argtypes = [P, P, I64, I64, I64, I64, I64,
                                            I64, I64, P]
     lib.oracle_q4k_matmul_part.restype = ctypes.c_int
+    lib.oracle_q4_0_dequant_block.argtypes = [P, P]
+    lib.oracle_q4_0_dequant_block.restype = None
+    lib.oracle_q4_0_gemv.argtypes = [P, P, I64, I64, P]
+    lib.oracle_q4_0_gemv.restype = ctypes.c_int
     lib.oracle_ternary_decode_byte.argtypes = [ctypes.c_uint8, P]
     lib.oracle_ternary_decode_byte.restype = None
     lib.oracle_ternary_gemv_codes.argtypes = [P, P, I64, I64, P]
@@ -148,6 +152,24 @@ def q4k_matmul_part(X, w_blocks, n_tokens, input_dim, output_dim, tokens,
         _ptr(xx), _ptr(ww), n_tokens, input_dim, output_dim, tokens[0],
         tokens[1], rows[0], rows[1], _ptr(Y)))
     return Y
+
+
+def q4_0_dequant_block(block):
+    """One 18-byte Q4_0 block -> 32 fp32 weights."""
+    b = _u8(block)
+    assert b.size == 18
+    w = np.empty(32, np.float32)
+    _load().oracle_q4_0_dequant_block(_ptr(b), _ptr(w))
+    return w
+
+
+def q4_0_gemv(x, w_blocks, input_dim, output_dim):
+    """y = W x for a Q4_0 matrix, float64 (dequantize, then a double dot)."""
+    xx, ww = _f32(x), _u8(w_blocks)
+    y = np.empty(max(int(output_dim), 0), np.float64)
+    _check(_load().oracle_q4_0_gemv(_ptr(xx), _ptr(ww), input_dim, output_dim,
+                                    _ptr(y)))
+    return y
 
 
 def ternary_decode_byte(byte):

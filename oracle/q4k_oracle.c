@@ -12,6 +12,8 @@
  *          Q4KMatmulKernel SPI" -- sections "Pipeline" (the canonical
  *          strided qs layout, the lazy-dmin correction) and "Test plan"
  *          (1e-4 parity bar, rejection of inputDim % 256 != 0).
+ *          Section "Out of scope" names the Q4_0 follow-up: the same
+ *          algorithm on a simpler block of 32 weights in 18 bytes.
  *   [TRN]  SKaiNET issue #1138, "[ternary-f32] Phase 2: TernaryF32GemvNative
  *          SPI + reference ViewKernel + TernaryF32KernelPack" -- section
  *          "Tasks" (the gemvPacked contract, the decode formula, the
@@ -26,6 +28,10 @@
  *     position l of sub-block 2j+1 (high nibble).
  *   - W is row-major [output][input]: row o holds inputDim/256 blocks.
  *   - weight = d*sc*q - dmin*m ("offset" is subtracted).
+ *   - block_q4_0 is 18 bytes: fp16 d at byte 0 (little-endian) and 16
+ *     bytes of qs at 2..17; element i < 16 is the low nibble of qs[i],
+ *     element 16 + i its high nibble; weight = d * (q - 8) (ggml's
+ *     block_q4_0 convention; the page gives only "32 / 18 bytes").
  *   - ternary element i of a row is bits 2*(i%4)..2*(i%4)+1 of byte i/4;
  *     code 3 decodes to +2 by the formula (never generated).
  *
@@ -234,6 +240,46 @@ int oracle_q4k_matmul_part(const float *X, const uint8_t *w, int64_t M,
             }
             Y[r * N + o] = acc;
         }
+    }
+    return ORACLE_OK;
+}
+
+#define QK40 32          /* weights per Q4_0 block */
+#define BLOCK40_BYTES 18 /* bytes per Q4_0 block */
+
+/* Dequantize one 18-byte Q4_0 block into 32 fp32 weights.  d has 11
+ * significant bits and q - 8 lies in [-8, 7], so every product is exact in
+ * fp32. */
+void oracle_q4_0_dequant_block(const uint8_t *blk, float *w)
+{
+    float d = oracle_f16_to_f32((uint16_t)(blk[0] | (blk[1] << 8)));
+    const uint8_t *qs = blk + 2;
+    for (int i = 0; i < 16; ++i) {
+        w[i] = d * (float)((int)(qs[i] & 15) - 8);
+        w[16 + i] = d * (float)((int)(qs[i] >> 4) - 8);
+    }
+}
+
+/* y[o] = sum_k W[o,k] * x[k] for a Q4_0 matrix whose row o holds inputDim/32
+ * blocks: dequantize each block, then a double-precision dot. */
+int oracle_q4_0_gemv(const float *x, const uint8_t *w, int64_t K, int64_t N,
+                     double *y)
+{
+    if (K <= 0 || N <= 0 || K % QK40 != 0)
+        return ORACLE_EINVAL_DIM;
+    if (!x || !w || !y)
+        return ORACLE_ENULL;
+    int64_t nb = K / QK40;
+    float wt[QK40];
+    for (int64_t o = 0; o < N; ++o) {
+        double acc = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            oracle_q4_0_dequant_block(w + (o * nb + b) * BLOCK40_BYTES, wt);
+            const float *xb = x + b * QK40;
+            for (int p = 0; p < QK40; ++p)
+                acc += (double)wt[p] * (double)xb[p];
+        }
+        y[o] = acc;
     }
     return ORACLE_OK;
 }

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the Q4_K and ternary products.
+"""Seeded synthetic inputs for the Q4_K, Q4_0 and ternary products.
 
 This module only draws random numbers and lays them out in the input
 formats; it holds none of the products' arithmetic.  Both the GPU path's
@@ -17,6 +17,10 @@ Q4_K matrix with R = rows * (K / 256) super-blocks, drawn in this order:
 and each block is d | dmin | scales | qs (144 bytes), blocks row-major.
 Activations: standard_normal(K) as float32 (or (M, K) for a token batch).
 
+Q4_0 matrix with R = rows * (K / 32) blocks: d = float16(|standard_normal(R)|
+/ 64), then qs = integers(0, 256, (R, 16)); each block is d | qs (18 bytes),
+blocks row-major.
+
 Ternary matrix: codes u = integers(0, 3, (N, K)) (so u - 1 is uniform over
 {-1, 0, 1}), four per byte as u0 | u1<<2 | u2<<4 | u3<<6, rows of K/4 bytes;
 one float32 per-tensor scale uniform(0.5, 2).
@@ -31,8 +35,12 @@ SEED = 2026
 BLOCK_BYTES = 144
 QK = 256
 
+Q40_BLOCK_BYTES = 18
+Q40_QK = 32
+
 # Configuration ids used in seeds.
 C1_Q4K_1K, C2_Q4K_4K, C3_FFN, C4_PREFILL, C5_TERNARY = 1, 2, 3, 4, 5
+Q40_4K = 6
 ROLE_W, ROLE_X = 0, 1
 
 
@@ -63,6 +71,26 @@ def q4k_weights(n_rows, input_dim, config=C2_Q4K_4K, copy=0, extra=0):
     scales = g.integers(0, 256, (R, 12), dtype=np.uint8)
     qs = g.integers(0, 256, (R, 128), dtype=np.uint8)
     return q4k_blocks_from_fields(d, dmin, scales, qs).reshape(n_rows, nb * BLOCK_BYTES)
+
+
+def q4_0_blocks_from_fields(d_f16, qs16):
+    """Assemble [R, 18] Q4_0 block bytes from already-drawn fields."""
+    R = d_f16.shape[0]
+    out = np.empty((R, Q40_BLOCK_BYTES), np.uint8)
+    out[:, 0:2] = np.ascontiguousarray(d_f16, np.float16).view(np.uint8).reshape(R, 2)
+    out[:, 2:18] = qs16
+    return out
+
+
+def q4_0_weights(n_rows, input_dim, config=Q40_4K, copy=0, extra=0):
+    """Random Q4_0 matrix as uint8 [n_rows, (input_dim/32)*18]."""
+    assert input_dim % Q40_QK == 0
+    nb = input_dim // Q40_QK
+    R = n_rows * nb
+    g = rng(config, copy, ROLE_W, extra)
+    d = (np.abs(g.standard_normal(R)) / 64).astype(np.float16)
+    qs = g.integers(0, 256, (R, 16), dtype=np.uint8)
+    return q4_0_blocks_from_fields(d, qs).reshape(n_rows, nb * Q40_BLOCK_BYTES)
 
 
 def activations(input_dim, n_tokens=None, config=C2_Q4K_4K, copy=0, extra=0):
@@ -109,6 +137,17 @@ def q4k_integer_weights(n_rows, input_dim, config=C2_Q4K_4K, copy=0, extra=0):
     scales = g.integers(0, 256, (R, 12), dtype=np.uint8)
     qs = g.integers(0, 256, (R, 128), dtype=np.uint8)
     return q4k_blocks_from_fields(one, one, scales, qs).reshape(n_rows, nb * BLOCK_BYTES)
+
+
+def q4_0_integer_weights(n_rows, input_dim, config=Q40_4K, copy=0, extra=0):
+    """Q4_0 blocks with d = 1.0 and random codes: every weight is an integer
+    in [-8, 7]."""
+    nb = input_dim // Q40_QK
+    R = n_rows * nb
+    g = rng(config, copy, ROLE_W, 500 + extra)
+    qs = g.integers(0, 256, (R, 16), dtype=np.uint8)
+    return q4_0_blocks_from_fields(np.ones(R, np.float16), qs).reshape(
+        n_rows, nb * Q40_BLOCK_BYTES)
 
 
 def integer_activations(input_dim, lo=-1, hi=1, n_tokens=None, config=C2_Q4K_4K,

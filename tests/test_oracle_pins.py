@@ -408,3 +408,162 @@ def test_ternary_rejects_input_dim_not_multiple_of_4(oracle_lib, K):
         oracle_lib.ternary_gemv_codes(np.zeros(max(K, 1), np.float32),
                                       np.zeros(8, np.uint8), K, 1)
     assert e.value.code == oracle_lib.EINVAL_DIM
+
+
+# ---------------------------------------------------------------------------
+# Q4_0 (the Q4_K page's follow-up format: 32 weights in 18 bytes).  The test
+# side addresses element k of a block directly (byte 2 + k % 16, nibble
+# k // 16) rather than looping over bytes as the oracle does.
+
+def q40_exact_weight(block, k):
+    d = _f16_value(block, 0)
+    q = (int(block[2 + k % 16]) >> (4 * (k // 16))) & 15
+    return d * (q - 8)
+
+
+def _q40_golden_block(spec):
+    blk = np.zeros(18, np.uint8)
+    blk[0:2] = np.array([spec["d_f16_bits"]], np.uint16).view(np.uint8)
+    blk[2:] = spec["qs"]
+    return blk
+
+
+@pytest.mark.parametrize("spec", _golden("q4_0_block_worked.json")["blocks"],
+                         ids=lambda s: s["name"])
+def test_q4_0_worked_blocks_golden(oracle_lib, spec):
+    blk = _q40_golden_block(spec)
+    assert float(np.frombuffer(bytes(blk[0:2]), np.float16)[0]) == spec["d"]
+    for case in spec["cases"]:
+        x = np.zeros(32, np.float32)
+        lo, hi = case["support"]
+        x[lo:hi] = case["value"]
+        assert oracle_lib.q4_0_gemv(x, blk, 32, 1)[0] == case["y"], case
+
+
+def test_q4_0_worked_matrix_golden(oracle_lib):
+    gold = _golden("q4_0_block_worked.json")
+    blocks = {s["name"][0]: _q40_golden_block(s) for s in gold["blocks"]}
+    mt = gold["matrix"]
+    w = np.stack([np.concatenate([blocks[n] for n in row]) for row in mt["rows"]])
+    x = np.concatenate([np.full(32, 1.0, np.float32), np.full(32, 2.0, np.float32)])
+    y = oracle_lib.q4_0_gemv(x, w, mt["input_dim"], len(mt["rows"]))
+    assert y.tolist() == mt["y"]
+
+
+def test_q4_0_dequant_is_exact_weight(oracle_lib):
+    """d * (q - 8) is exact in fp32 for every binary16 d, subnormals and the
+    largest finite value included."""
+    g = np.random.default_rng(40)
+    blocks = synth.q4_0_weights(12, 32, config=89).reshape(12, 18).copy()
+    blocks[0:4, 0:2] = g.integers(1, 1024, 4).astype(np.uint16).view(np.uint8).reshape(4, 2)
+    blocks[4, 0:2] = np.array([np.float16(65504.0)]).view(np.uint8)
+    blocks[5, 0:2] = np.array([np.float16(-3.5)]).view(np.uint8)
+    for blk in blocks:
+        w = oracle_lib.q4_0_dequant_block(blk)
+        for k in range(32):
+            assert Fraction(float(w[k])) == q40_exact_weight(blk, k), k
+
+
+@pytest.mark.parametrize("K,N", [(64, 3), (256, 2)])
+def test_q4_0_gemv_against_exact_rational(oracle_lib, K, N):
+    w = synth.q4_0_weights(N, K, config=88, copy=K)
+    x = synth.activations(K, config=88, copy=K)
+    y = oracle_lib.q4_0_gemv(x, w, K, N)
+    nb = K // 32
+    for o in range(N):
+        exact = Fraction(0)
+        terms = []
+        for b in range(nb):
+            blk = w[o, b * 18:(b + 1) * 18]
+            for k in range(32):
+                t = q40_exact_weight(blk, k) * Fraction(float(x[b * 32 + k]))
+                exact += t
+                terms.append(abs(float(t)))
+        # the weights are exact; only the double accumulation rounds
+        bound = K * 2.0 ** -53 * sum(terms)
+        assert abs(Fraction(float(y[o])) - exact) <= Fraction(bound) * (1 + 1e-9), o
+
+
+def _q40_to_q4k(w40, K, N):
+    """Re-pack a Q4_0 matrix whose eight blocks per 256 weights share d as the
+    Q4_K matrix with that d, dmin = d, every sc = 1 and every m = 8: the Q4_K
+    weight d*1*q - d*8 is then the Q4_0 weight d*(q - 8) at every position."""
+    nb40 = K // 32
+    out = np.zeros((N, (K // 256) * 144), np.uint8)
+    sc_m = pack_scales([1] * 8, [8] * 8)
+    for o in range(N):
+        for g in range(K // 256):
+            blocks = [w40[o, (8 * g + b) * 18:(8 * g + b + 1) * 18] for b in range(8)]
+            codes = [(int(blocks[e // 32][2 + (e % 32) % 16]) >> (4 * ((e % 32) // 16))) & 15
+                     for e in range(256)]
+            blk = np.zeros(144, np.uint8)
+            blk[0:2] = blocks[0][0:2]
+            blk[2:4] = blocks[0][0:2]
+            blk[4:16] = sc_m
+            for j in range(4):
+                for l in range(32):
+                    blk[16 + 32 * j + l] = codes[64 * j + l] | (codes[64 * j + 32 + l] << 4)
+            out[o, g * 144:(g + 1) * 144] = blk
+    assert nb40 == 8 * (K // 256)
+    return out
+
+
+def test_q4_0_equals_q4k_with_uniform_scales(oracle_lib):
+    """Special case that reduces to the (separately pinned) Q4_K oracle: the
+    same weights in both formats give bit-identical double results."""
+    K, N = 512, 6
+    w40 = synth.q4_0_weights(N, K, config=87).copy()
+    for o in range(N):  # share d within each group of eight blocks
+        for g in range(K // 256):
+            d = w40[o, g * 8 * 18:g * 8 * 18 + 2].copy()
+            for b in range(8):
+                w40[o, (8 * g + b) * 18:(8 * g + b) * 18 + 2] = d
+    w4k = _q40_to_q4k(w40, K, N)
+    x = synth.activations(K, config=87)
+    assert np.array_equal(oracle_lib.q4_0_gemv(x, w40, K, N),
+                          oracle_lib.q4k_gemv(x, w4k, K, N))
+
+
+def test_q4_0_integer_inputs_exact(oracle_lib):
+    """d = 1 and x in {-1, 0, 1}: the result is the integer sum of (q-8)*x."""
+    K, N = 4096, 16
+    w = synth.q4_0_integer_weights(N, K, config=86)
+    x = synth.integer_activations(K, config=86)
+    y = oracle_lib.q4_0_gemv(x, w, K, N)
+    blocks = w.reshape(N, K // 32, 18)
+    qs = blocks[:, :, 2:].astype(np.int64)
+    q = np.concatenate([qs & 15, qs >> 4], axis=2).reshape(N, K)
+    assert np.array_equal(y, ((q - 8) @ x.astype(np.int64)).astype(np.float64))
+
+
+def test_q4_0_constant_codes_closed_form(oracle_lib):
+    K, N = 512, 4
+    g = np.random.default_rng(7)
+    for c in (0, 5, 8, 15):
+        blk = np.zeros(18, np.uint8)
+        d = np.float16(0.0419)
+        blk[0:2] = np.array([d]).view(np.uint8)
+        blk[2:] = c | (c << 4)
+        w = np.tile(blk, (N, K // 32))
+        x = g.standard_normal(K).astype(np.float32)
+        y = oracle_lib.q4_0_gemv(x, w, K, N)
+        closed = float(d) * (c - 8) * float(np.sum(x.astype(np.float64)))
+        assert np.allclose(y, closed, rtol=1e-12, atol=1e-12), c
+
+
+def test_q4_0_zero_activation_and_linearity(oracle_lib):
+    K, N = 1024, 12
+    w = synth.q4_0_weights(N, K, config=85)
+    assert np.all(oracle_lib.q4_0_gemv(np.zeros(K, np.float32), w, K, N) == 0.0)
+    x1 = synth.activations(K, config=85, copy=1)
+    x2 = synth.activations(K, config=85, copy=2)
+    y = oracle_lib.q4_0_gemv(np.float32(0.5) * x1 - np.float32(3.0) * x2, w, K, N)
+    y12 = 0.5 * oracle_lib.q4_0_gemv(x1, w, K, N) - 3.0 * oracle_lib.q4_0_gemv(x2, w, K, N)
+    assert_parity(y, y12, rel=1e-6)
+
+
+@pytest.mark.parametrize("K", [31, 33, 100, 0, -32])
+def test_q4_0_rejects_input_dim_not_multiple_of_32(oracle_lib, K):
+    with pytest.raises(oracle_lib.OracleError) as e:
+        oracle_lib.q4_0_gemv(np.zeros(max(K, 1), np.float32), np.zeros(18 * 4, np.uint8), K, 1)
+    assert e.value.code == oracle_lib.EINVAL_DIM
