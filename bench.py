@@ -21,6 +21,8 @@ Other workloads (measurement of the sibling paths, same JSON shape):
       is the pair (9 rotating pairs)
   c4  Q4_K prefill 64 tokens x 4096 -> 4096 (64 rotating weight copies)
   c5  ternary GEMV 4096 x 4096, batch 1 (128 rotating copies)
+  q40 Q4_0 GEMV 4096 x 4096, batch 1 (64 rotating copies; the Q4_K page's
+      follow-up format, the same 9.4 MB of weights per call as c2)
   copy  plain 64 MiB device-to-device copy kernel (4 rotating buffer pairs):
       the kernel of known traffic used to scale hardware byte counters
 """
@@ -159,6 +161,7 @@ def make_workload(name, torch, binding, synth):
         wl.bytes = cbytes + 4 * K + 4 * N + 4
         wl.flops = 2 * K * N
         wl.kernel = "ternary_gemv_kernel"
+        wl.data = "synthetic (seeded numpy generators; random ternary codes, N(0,1) activations)"
         wl.src_files = TERNARY_SRC
         wl.config = {"workload": "ternary_gemv 4096x4096 batch 1", "input_dim": K,
                      "output_dim": N, "rotating_copies": copies}
@@ -168,6 +171,30 @@ def make_workload(name, torch, binding, synth):
             c0, x0 = wl.C[0].cpu().numpy(), wl.x.cpu().numpy()
             return (lambda: oracle.ternary_gemv(x0, c0, wl.scale, K, N)), 1.0, \
                 "oracle ternary_gemv 4096x4096, full call"
+        wl.cpu = cpu
+    elif name == "q40":
+        K = N = 4096
+        wbytes = N * K // 32 * 18
+        copies = 64
+        wl.W = [to_dev(synth.q4_0_weights(N, K, copy=c)) for c in range(copies)]
+        wl.x = to_dev(synth.activations(K, config=synth.Q40_4K))
+        wl.y = torch.empty(N, dtype=torch.float32, device=dev)
+        wl.call = lambda i: binding.q4_0_gemv(wl.x, wl.W[i % copies], K, N, wl.y)
+        wl.copies = copies
+        wl.bytes = wbytes + 4 * K + 4 * N
+        wl.flops = 2 * K * N
+        wl.kernel = "q4k_gemv_kernel<Q40, 64, 4, 1, 4>"
+        wl.src_files = GEMV_SRC
+        wl.data = "synthetic (seeded numpy generators; random Q4_0 blocks, N(0,1) activations)"
+        wl.config = {"workload": f"q4_0_gemv {K}x{N} batch 1", "input_dim": K,
+                     "output_dim": N, "batch": 1, "rotating_copies": copies,
+                     "weight_bytes_per_copy": wbytes}
+        wl.metric = f"Q4_0 GEMV us/call + achieved HBM GB/s (% peak) at {K}x{N}, batch 1"
+
+        def cpu(oracle):
+            w0 = wl.W[0].cpu().numpy()
+            x0 = wl.x.cpu().numpy()
+            return (lambda: oracle.q4_0_gemv(x0, w0, K, N)), 1.0, f"oracle q4_0_gemv {K}x{N}, full call"
         wl.cpu = cpu
     elif name == "copy":
         nbytes = 64 * 2 ** 20
@@ -179,6 +206,7 @@ def make_workload(name, torch, binding, synth):
         wl.bytes = 2 * nbytes
         wl.flops = 0
         wl.kernel = "copy_kernel"
+        wl.data = "synthetic (constant-filled device buffers)"
         wl.src_files = ["q4_packed_weight_amd/csrc/bench_kernels.hip"]
         wl.config = {"workload": "device copy 64 MiB (read 64 MiB + write 64 MiB)",
                      "rotating_pairs": copies}
@@ -293,7 +321,8 @@ def cpu_baseline(wl, seconds):
 TRAFFIC_FILES = {"c2": "q4k_gemv_4096x4096_b1.traffic.json",
                  "c3": "q4k_gemv_ffn_4096x14336_pair.traffic.json",
                  "c4": "q4k_prefill_64x4096x4096.traffic.json",
-                 "c5": "ternary_gemv_4096x4096_b1.traffic.json"}
+                 "c5": "ternary_gemv_4096x4096_b1.traffic.json",
+                 "q40": "q4_0_gemv_4096x4096_b1.traffic.json"}
 
 
 def traffic_for(wl):
@@ -316,7 +345,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64000)
     ap.add_argument("--warmup", type=int, default=6400)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "copy"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "q40", "copy"])
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -379,7 +408,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded numpy generators; random Q4_K blocks, N(0,1) activations)",
+        "data": getattr(wl, "data", "synthetic (seeded numpy generators; random Q4_K blocks, "
+                                       "N(0,1) activations)"),
         "config": dict(wl.config, launch="hipGraph replay, one node per call"
                        if args.launch == "graph" else "eager, one ctypes call per step"),
         "achieved_GBps": round(gbps, 1),

@@ -1,7 +1,7 @@
 /*
  * q4k.h -- C ABI of libq4k.so, the MI355X (gfx950) fused-dequantize Q4_K
- * matrix-vector product, its batched (prefill) form and the ternary
- * BitNet b1.58 sibling.
+ * matrix-vector product, its batched (prefill) form, the Q4_0 matrix-vector
+ * product and the ternary BitNet b1.58 sibling.
  *
  * Common contract for every compute entry point:
  *   - x, w_blocks/codes and y are DEVICE pointers owned by the caller.  The
@@ -102,6 +102,47 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
  */
 int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
                int64_t input_dim, int64_t output_dim, float *Y, void *stream);
+
+/*
+ * Q4_0 weight format (block_q4_0, 32 weights in 18 bytes): the simpler
+ * block the Q4_K page names as its follow-up (section "Out of scope": same
+ * algorithm, 32 / 18 bytes).  The page prints no more; this library reads
+ * it as ggml's block_q4_0:
+ *   bytes 0..1    d   binary16, little-endian
+ *   bytes 2..17   qs; byte i holds element i in its low nibble and element
+ *                 16+i in its high nibble
+ * Weight k of a block (code q) is d*(q - 8).  The matrix is row-major
+ * [output_dim][input_dim/32] blocks, row o starting at byte
+ * o*(input_dim/32)*18.
+ */
+
+/*
+ * q4_0_gemv -- y[o] = sum_k W[o,k] * x[k] for a Q4_0 matrix (batch 1), the
+ * same fused product as q4k_gemv: every block adds d*(sum q*x - 8*sum x),
+ * accumulated in fp32.
+ *   x          fp32 [input_dim], 16-byte aligned
+ *   w_blocks   uint8 [output_dim * input_dim/32 * 18], 16-byte aligned
+ *   input_dim  K > 0, a multiple of 256 and at most 2^24, else
+ *              Q4K_EINVAL_DIM.  The format itself only needs multiples of
+ *              32; this kernel walks rows in 144-byte groups of eight
+ *              blocks, which keeps every row 16-byte aligned.
+ *   output_dim N > 0
+ *   y          fp32 [output_dim]
+ * Same error behaviour, determinism and tolerance as q4k_gemv (vector
+ * form; |x| should stay above ~1e-30 for full precision).
+ */
+int q4_0_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+              int64_t output_dim, float *y, void *stream);
+
+/*
+ * q4_0_gemv_shaped -- q4_0_gemv with an explicit launch shape; the values
+ * of rows_per_lane, k_waves and workgroup_waves are those of
+ * q4k_gemv_shaped except that there is no matrix-core form (16 is
+ * Q4K_EINVAL_DIM).
+ */
+int q4_0_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+                     int64_t output_dim, float *y, void *stream,
+                     int rows_per_lane, int k_waves, int workgroup_waves);
 
 /*
  * Ternary BitNet b1.58 format (ternary page, SKaiNET issue #1138, section

@@ -45,6 +45,26 @@ int check_ternary(const void *x, const uint8_t *c, const void *y, int64_t K,
 
 extern "C" {
 
+}  // extern "C"
+
+namespace {
+
+// Validates an explicit vector-kernel launch shape (see q4k_gemv_shaped).
+bool valid_vector_shape(int rows_per_lane, int k_waves, int workgroup_waves) {
+  const auto pow2_le = [](int v, int hi) {
+    return v == 0 || ((v & (v - 1)) == 0 && v > 0 && v <= hi);
+  };
+  if (!pow2_le(rows_per_lane, 8) || !pow2_le(k_waves, 4) ||
+      !pow2_le(workgroup_waves, 8))
+    return false;
+  const int wg = workgroup_waves ? workgroup_waves : 4;
+  return !(k_waves > wg || (wg == 8 && (k_waves == 4 || rows_per_lane == 8)));
+}
+
+}  // namespace
+
+extern "C" {
+
 int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                     int64_t output_dim, float *y, void *stream,
                     int rows_per_lane, int k_waves, int workgroup_waves) {
@@ -56,21 +76,34 @@ int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                                          (hipStream_t)stream);
     return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_gemv launch");
   }
-  const auto pow2_le = [](int v, int hi) {
-    return v == 0 || ((v & (v - 1)) == 0 && v > 0 && v <= hi);
-  };
-  if (!pow2_le(rows_per_lane, 8) || !pow2_le(k_waves, 4) ||
-      !pow2_le(workgroup_waves, 8))
-    return Q4K_EINVAL_DIM;
-  const int wg = workgroup_waves ? workgroup_waves : 4;
-  if (k_waves > wg || (wg == 8 && (k_waves == 4 || rows_per_lane == 8)))
-    return Q4K_EINVAL_DIM;
+  if (!valid_vector_shape(rows_per_lane, k_waves, workgroup_waves)) return Q4K_EINVAL_DIM;
   const int64_t nb = input_dim / 256;
   const q4k::GemvShape s = q4k::choose_gemv_shape(nb, output_dim, rows_per_lane,
                                                   k_waves, workgroup_waves);
   hipError_t e = q4k::gemv_launch(x, w_blocks, y, nb, output_dim, s,
                                   (hipStream_t)stream);
   return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_gemv launch");
+}
+
+// Q4_0 rows of input_dim/32 18-byte blocks; a multiple of 256 keeps them
+// whole 144-byte groups (validation as for Q4_K).
+int q4_0_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+                     int64_t output_dim, float *y, void *stream,
+                     int rows_per_lane, int k_waves, int workgroup_waves) {
+  int rc = check_q4k(x, w_blocks, y, 1, input_dim, output_dim);
+  if (rc) return rc;
+  if (!valid_vector_shape(rows_per_lane, k_waves, workgroup_waves)) return Q4K_EINVAL_DIM;
+  const int64_t ng = input_dim / 256;
+  const q4k::GemvShape s = q4k::choose_gemv_shape(ng, output_dim, rows_per_lane,
+                                                  k_waves, workgroup_waves);
+  hipError_t e = q4k::gemv_q4_0_launch(x, w_blocks, y, ng, output_dim, s,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4_0_gemv launch");
+}
+
+int q4_0_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+              int64_t output_dim, float *y, void *stream) {
+  return q4_0_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0, 0);
 }
 
 int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
@@ -126,9 +159,9 @@ const char *q4k_strerror(int code) {
     case Q4K_OK: return "ok";
     case Q4K_EINVAL_DIM:
       return "invalid dimension: every dimension must be > 0, input_dim a "
-             "multiple of 256 for Q4_K (of 4 for ternary) and at most 2^24";
+             "multiple of 256 for Q4_K and Q4_0 (of 4 for ternary) and at most 2^24";
     case Q4K_ENULL: return "a required pointer is NULL";
-    case Q4K_EALIGN: return "x and the Q4_K blocks must be 16-byte aligned";
+    case Q4K_EALIGN: return "x and the Q4_K or Q4_0 blocks must be 16-byte aligned";
     case Q4K_EHIP: return g_hip_detail[0] ? g_hip_detail : "HIP runtime error";
     default: return "unknown error code";
   }

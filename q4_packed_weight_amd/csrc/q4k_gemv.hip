@@ -91,7 +91,69 @@ __device__ __forceinline__ void nibble_dots(uint32_t w, float4 xl, float4 xh,
   hi[1] = __builtin_fmaf(half_hi(hi13), xh.w, hi[1]);
 }
 
-template <int L, int R, int KW, int W>
+// Per-lane work of one (row, slab) pair, by weight format.  `grp` is the
+// 144-byte group (9 uint4 of the staged tile) holding this lane's slab; j
+// (0..3) is the slab within the group; xl/xh are the slab's 64 activations
+// (float4 k of xl is positions 4k..4k+3, of xh positions 32+4k..) and xsm
+// their sums over positions 0..31 and 32..63.  Returns acc plus the slab's
+// contribution to the row.
+//
+// Q4_K: the group is one super-block; the lane reads the header and the 32
+// qs bytes 32j..32j+31 (positions l of sub-blocks 2j and 2j+1).
+struct Q4K {
+  __device__ __forceinline__ static float slab(const uint4 *grp, int j, uint32_t sh, bool jhi,
+                                               const float4 (&xl)[8], const float4 (&xh)[8],
+                                               float2 xsm, float acc) {
+    const uint4 hdr = grp[0];
+    const uint4 q0 = grp[1 + 2 * j];
+    const uint4 q1 = grp[2 + 2 * j];
+    float lo[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f};
+    const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) nibble_dots(qw[k], xl[k], xh[k], lo, hi);
+    const float s_lo = lo[0] + lo[1], s_hi = hi[0] + hi[1];
+    const SlabScales sc = decode_header(hdr, sh, jhi);
+    // code part in units of 2^-20: 16*sc_lo*s_lo + sc_hi*s_hi
+    const float tc = __builtin_fmaf(sc.sc_lo16, s_lo, sc.sc_hi * s_hi);
+    const float tm = __builtin_fmaf(sc.m_lo, xsm.x, sc.m_hi * xsm.y);
+    // this slab's contribution: d * 2^20 * tc - dmin * tm
+    return __builtin_fmaf(sc.d * 0x1p20f, tc, __builtin_fmaf(-sc.dmin, tm, acc));
+  }
+};
+
+// Q4_0 (the Q4_K page's follow-up format, section "Out of scope": 32
+// weights in 18 bytes; fp16 d, then 16 qs bytes whose low nibbles are
+// elements 0..15 and high nibbles elements 16..31, weight d*(q - 8)).
+// Eight blocks make one 144-byte group, so a slab of 64 positions is the
+// two blocks 2j, 2j+1 at bytes 36j..36j+35: nine dwords.  The first block's
+// qs start 2 bytes into its first dword and are realigned; the second's
+// are dword-aligned.  Each block contributes d*(sum q*x - 8*sum x).
+struct Q40 {
+  __device__ __forceinline__ static float slab(const uint4 *grp, int j, uint32_t, bool,
+                                               const float4 (&xl)[8], const float4 (&xh)[8],
+                                               float2 xsm, float acc) {
+    const uint32_t *g32 = reinterpret_cast<const uint32_t *>(grp) + 9 * j;
+    uint32_t dw[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) dw[i] = g32[i];
+    float lo0[2] = {0.f, 0.f}, hi0[2] = {0.f, 0.f}, lo1[2] = {0.f, 0.f}, hi1[2] = {0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // block 2j: qs bytes 4t..4t+3 sit at bytes 2+4t.. of the slab
+      nibble_dots(__builtin_amdgcn_alignbyte(dw[t + 1], dw[t], 2), xl[t], xl[4 + t], lo0, hi0);
+      // block 2j+1: qs bytes 4t.. are dword 5+t
+      nibble_dots(dw[5 + t], xh[t], xh[4 + t], lo1, hi1);
+    }
+    const float d0 = half_lo(dw[0]), d1 = half_hi(dw[4]);
+    // sum q*x in units of 2^-20: 16*(low-nibble sums) + (high-nibble sums)
+    const float t0 = __builtin_fmaf(16.0f, lo0[0] + lo0[1], hi0[0] + hi0[1]);
+    const float t1 = __builtin_fmaf(16.0f, lo1[0] + lo1[1], hi1[0] + hi1[1]);
+    acc = __builtin_fmaf(d0 * 0x1p20f, t0, __builtin_fmaf(-8.0f * d0, xsm.x, acc));
+    return __builtin_fmaf(d1 * 0x1p20f, t1, __builtin_fmaf(-8.0f * d1, xsm.y, acc));
+  }
+};
+
+template <class F, int L, int R, int KW, int W>
 __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
     const float *x, const uint8_t *w, float *__restrict__ y, int nb,
     int64_t N) {
@@ -219,23 +281,8 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
 #pragma unroll
       for (int m = 0; m < NM; ++m)
         if (m > prev_last && m <= last_m && 64 * m + lane < TILE) wt[wave][64 * m + lane] = wv[m];
-      if (active) {
-        const int base = ((r * G + g) * BPS + bl) * 9;
-        const uint4 hdr = wt[wave][base];
-        const uint4 q0 = wt[wave][base + 1 + 2 * j];
-        const uint4 q1 = wt[wave][base + 2 + 2 * j];
-        float lo[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f};
-        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) nibble_dots(qw[k], xl[k], xh[k], lo, hi);
-        const float s_lo = lo[0] + lo[1], s_hi = hi[0] + hi[1];
-        const SlabScales sc = decode_header(hdr, sh, jhi);
-        // code part in units of 2^-20: 16*sc_lo*s_lo + sc_hi*s_hi
-        const float tc = __builtin_fmaf(sc.sc_lo16, s_lo, sc.sc_hi * s_hi);
-        const float tm = __builtin_fmaf(sc.m_lo, xsm.x, sc.m_hi * xsm.y);
-        // this slab's contribution: d * 2^20 * tc - dmin * tm
-        acc[r] = __builtin_fmaf(sc.d * 0x1p20f, tc, __builtin_fmaf(-sc.dmin, tm, acc[r]));
-      }
+      if (active)
+        acc[r] = F::slab(&wt[wave][((r * G + g) * BPS + bl) * 9], j, sh, jhi, xl, xh, xsm, acc[r]);
     }
     // every wave must be done with the staged activations before the next
     // iteration overwrites them (the weight tile is private to the wave)
@@ -278,7 +325,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
 // workgroup), loading the weight tile of the next unit while it computes
 // the current one.  Arithmetic and summation order per row are those of
 // q4k_gemv_kernel with KW = 1, so results are identical.
-template <int L, int R, int W>
+template <class F, int L, int R, int W>
 __global__ __launch_bounds__(64 * W) void q4k_gemv_persist_kernel(
     const float *x, const uint8_t *w, float *__restrict__ y, int nb,
     int64_t N, int n_units) {
@@ -374,21 +421,8 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_persist_kernel(
       for (int m = 0; m < NM; ++m)
         if (m > prev_last && m <= last_m && 64 * m + lane < TILE) wt[wave][64 * m + lane] = wv[m];
       acc[r] = 0.0f;
-      if (active) {
-        const int base = ((r * G + g) * BPS + bl) * 9;
-        const uint4 hdr = wt[wave][base];
-        const uint4 q0 = wt[wave][base + 1 + 2 * j];
-        const uint4 q1 = wt[wave][base + 2 + 2 * j];
-        float lo[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f};
-        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) nibble_dots(qw[k], xl[k], xh[k], lo, hi);
-        const float s_lo = lo[0] + lo[1], s_hi = hi[0] + hi[1];
-        const SlabScales sc = decode_header(hdr, sh, jhi);
-        const float tc = __builtin_fmaf(sc.sc_lo16, s_lo, sc.sc_hi * s_hi);
-        const float tm = __builtin_fmaf(sc.m_lo, xsm.x, sc.m_hi * xsm.y);
-        acc[r] = __builtin_fmaf(sc.d * 0x1p20f, tc, __builtin_fmaf(-sc.dmin, tm, acc[r]));
-      }
+      if (active)
+        acc[r] = F::slab(&wt[wave][((r * G + g) * BPS + bl) * 9], j, sh, jhi, xl, xh, xsm, acc[r]);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(acc[r]);
@@ -422,7 +456,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_persist_kernel(
 // per CU, the LDS limit of the 4-wave form).
 constexpr int64_t kPersistSlots = 512;
 
-template <int L, int R, int KW, int W>
+template <class F, int L, int R, int KW, int W>
 hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, int nb,
                        int64_t N, hipStream_t stream) {
   constexpr int G = 64 / L;
@@ -435,45 +469,45 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, int nb,
     if (4 * (int64_t)nb <= L && grid > kPersistSlots) {
       const int64_t per = (grid + kPersistSlots - 1) / kPersistSlots;
       const int64_t pgrid = (grid + per - 1) / per;
-      hipLaunchKernelGGL((q4k_gemv_persist_kernel<L, R, W>), dim3((unsigned)pgrid),
+      hipLaunchKernelGGL((q4k_gemv_persist_kernel<F, L, R, W>), dim3((unsigned)pgrid),
                          dim3(64 * W), 0, stream, x, w, y, nb, N, (int)grid);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((q4k_gemv_kernel<L, R, KW, W>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((q4k_gemv_kernel<F, L, R, KW, W>), dim3((unsigned)grid),
                      dim3(64 * W), 0, stream, x, w, y, nb, N);
   return hipGetLastError();
 }
 
-template <int L, int R>
+template <class F, int L, int R>
 hipError_t launch_w(int waves, int kw, const float *x, const uint8_t *w,
                     float *y, int nb, int64_t N, hipStream_t s) {
   if (waves == 8) {
     if constexpr (R <= 4) {  // 8 waves x 8 rows would exceed the 160 KB of LDS
-      if (kw == 1) return launch_gemv<L, R, 1, 8>(x, w, y, nb, N, s);
-      return launch_gemv<L, R, 2, 8>(x, w, y, nb, N, s);
+      if (kw == 1) return launch_gemv<F, L, R, 1, 8>(x, w, y, nb, N, s);
+      return launch_gemv<F, L, R, 2, 8>(x, w, y, nb, N, s);
     } else {
       return hipErrorInvalidValue;
     }
   }
-  if (waves == 1) return launch_gemv<L, R, 1, 1>(x, w, y, nb, N, s);
+  if (waves == 1) return launch_gemv<F, L, R, 1, 1>(x, w, y, nb, N, s);
   if (waves == 2) {
-    if (kw == 1) return launch_gemv<L, R, 1, 2>(x, w, y, nb, N, s);
-    return launch_gemv<L, R, 2, 2>(x, w, y, nb, N, s);
+    if (kw == 1) return launch_gemv<F, L, R, 1, 2>(x, w, y, nb, N, s);
+    return launch_gemv<F, L, R, 2, 2>(x, w, y, nb, N, s);
   }
-  if (kw == 1) return launch_gemv<L, R, 1, 4>(x, w, y, nb, N, s);
-  if (kw == 2) return launch_gemv<L, R, 2, 4>(x, w, y, nb, N, s);
-  return launch_gemv<L, R, 4, 4>(x, w, y, nb, N, s);
+  if (kw == 1) return launch_gemv<F, L, R, 1, 4>(x, w, y, nb, N, s);
+  if (kw == 2) return launch_gemv<F, L, R, 2, 4>(x, w, y, nb, N, s);
+  return launch_gemv<F, L, R, 4, 4>(x, w, y, nb, N, s);
 }
 
-template <int L>
+template <class F, int L>
 hipError_t launch_r(const GemvShape &sh, const float *x, const uint8_t *w,
                     float *y, int nb, int64_t N, hipStream_t s) {
   switch (sh.rows_per_lane) {
-    case 1: return launch_w<L, 1>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
-    case 2: return launch_w<L, 2>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
-    case 4: return launch_w<L, 4>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
-    default: return launch_w<L, 8>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
+    case 1: return launch_w<F, L, 1>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
+    case 2: return launch_w<F, L, 2>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
+    case 4: return launch_w<F, L, 4>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
+    default: return launch_w<F, L, 8>(sh.waves, sh.k_waves, x, w, y, nb, N, s);
   }
 }
 
@@ -518,14 +552,25 @@ GemvShape choose_gemv_shape(int64_t nb, int64_t N, int rows_per_lane,
   return s;
 }
 
-hipError_t gemv_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
-                       int64_t N, const GemvShape &s, hipStream_t stream) {
+template <class F>
+hipError_t gemv_launch_fmt(const float *x, const uint8_t *w, float *y, int64_t nb,
+                           int64_t N, const GemvShape &s, hipStream_t stream) {
   const int nbi = (int)nb;
   switch (s.lanes) {
-    case 16: return launch_r<16>(s, x, w, y, nbi, N, stream);
-    case 32: return launch_r<32>(s, x, w, y, nbi, N, stream);
-    default: return launch_r<64>(s, x, w, y, nbi, N, stream);
+    case 16: return launch_r<F, 16>(s, x, w, y, nbi, N, stream);
+    case 32: return launch_r<F, 32>(s, x, w, y, nbi, N, stream);
+    default: return launch_r<F, 64>(s, x, w, y, nbi, N, stream);
   }
+}
+
+hipError_t gemv_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
+                       int64_t N, const GemvShape &s, hipStream_t stream) {
+  return gemv_launch_fmt<Q4K>(x, w, y, nb, N, s, stream);
+}
+
+hipError_t gemv_q4_0_launch(const float *x, const uint8_t *w, float *y, int64_t ngroups,
+                            int64_t N, const GemvShape &s, hipStream_t stream) {
+  return gemv_launch_fmt<Q40>(x, w, y, ngroups, N, s, stream);
 }
 
 }  // namespace q4k
