@@ -1,4 +1,4 @@
-"""CPU oracle for the Q4_K, Q4_0 and ternary matrix-vector products.
+"""CPU oracle for the Q4_K, Q4_0, Q6_K and ternary matrix-vector products.
 
 TEST INFRASTRUCTURE ONLY: this package may be imported by tests/, by the
 package smoke check and by bench.py's CPU-baseline leg, nothing else.  It
@@ -55,6 +55,10 @@ def _load():
     lib.oracle_q4_0_dequant_block.restype = None
     lib.oracle_q4_0_gemv.argtypes = [P, P, I64, I64, P]
     lib.oracle_q4_0_gemv.restype = ctypes.c_int
+    lib.oracle_q6k_dequant_block.argtypes = [P, P]
+    lib.oracle_q6k_dequant_block.restype = None
+    lib.oracle_q6k_gemv.argtypes = [P, P, I64, I64, P]
+    lib.oracle_q6k_gemv.restype = ctypes.c_int
     lib.oracle_ternary_decode_byte.argtypes = [ctypes.c_uint8, P]
     lib.oracle_ternary_decode_byte.restype = None
     lib.oracle_ternary_gemv_codes.argtypes = [P, P, I64, I64, P]
@@ -169,6 +173,24 @@ def q4_0_gemv(x, w_blocks, input_dim, output_dim):
     y = np.empty(max(int(output_dim), 0), np.float64)
     _check(_load().oracle_q4_0_gemv(_ptr(xx), _ptr(ww), input_dim, output_dim,
                                     _ptr(y)))
+    return y
+
+
+def q6k_dequant_block(block):
+    """One 210-byte Q6_K block -> 256 fp32 weights."""
+    b = _u8(block)
+    assert b.size == 210
+    w = np.empty(256, np.float32)
+    _load().oracle_q6k_dequant_block(_ptr(b), _ptr(w))
+    return w
+
+
+def q6k_gemv(x, w_blocks, input_dim, output_dim):
+    """y = W x for a Q6_K matrix, float64 (dequantize, then a double dot)."""
+    xx, ww = _f32(x), _u8(w_blocks)
+    y = np.empty(max(int(output_dim), 0), np.float64)
+    _check(_load().oracle_q6k_gemv(_ptr(xx), _ptr(ww), input_dim, output_dim,
+                                   _ptr(y)))
     return y
 
 

@@ -12,8 +12,10 @@
  *          Q4KMatmulKernel SPI" -- sections "Pipeline" (the canonical
  *          strided qs layout, the lazy-dmin correction) and "Test plan"
  *          (1e-4 parity bar, rejection of inputDim % 256 != 0).
- *          Section "Out of scope" names the Q4_0 follow-up: the same
- *          algorithm on a simpler block of 32 weights in 18 bytes.
+ *          Section "Out of scope" names the follow-ups: Q4_0, the same
+ *          algorithm on a simpler block of 32 weights in 18 bytes, and Q6_K,
+ *          whose ql + qh layout packs four codes' high bits per qh byte in
+ *          two interleaved halves.
  *   [TRN]  SKaiNET issue #1138, "[ternary-f32] Phase 2: TernaryF32GemvNative
  *          SPI + reference ViewKernel + TernaryF32KernelPack" -- section
  *          "Tasks" (the gemvPacked contract, the decode formula, the
@@ -32,6 +34,13 @@
  *     bytes of qs at 2..17; element i < 16 is the low nibble of qs[i],
  *     element 16 + i its high nibble; weight = d * (q - 8) (ggml's
  *     block_q4_0 convention; the page gives only "32 / 18 bytes").
+ *   - block_q6_K is 210 bytes: ql[128] at 0, qh[64] at 128, 16 int8
+ *     scales at 192, fp16 d at 208 (ggml's block_q6_K; the page names only
+ *     ql, qh and the half-interleaved qh packing).  Element e = 128n + 32c
+ *     + l (half n, quadrant c, l < 32) has code q = lo | hi << 4 with lo the
+ *     low (c < 2) or high (c >= 2) nibble of ql[64n + 32(c & 1) + l] and hi
+ *     bits 2c..2c+1 of qh[32n + l]; its sub-block of 16 is 8n + 2c + l/16
+ *     and weight = d * scale[sub-block] * (q - 32).
  *   - ternary element i of a row is bits 2*(i%4)..2*(i%4)+1 of byte i/4;
  *     code 3 decodes to +2 by the formula (never generated).
  *
@@ -277,6 +286,56 @@ int oracle_q4_0_gemv(const float *x, const uint8_t *w, int64_t K, int64_t N,
             oracle_q4_0_dequant_block(w + (o * nb + b) * BLOCK40_BYTES, wt);
             const float *xb = x + b * QK40;
             for (int p = 0; p < QK40; ++p)
+                acc += (double)wt[p] * (double)xb[p];
+        }
+        y[o] = acc;
+    }
+    return ORACLE_OK;
+}
+
+#define QK6 256           /* weights per Q6_K block */
+#define BLOCK6_BYTES 210  /* bytes per Q6_K block */
+
+/* Dequantize one 210-byte Q6_K block into 256 fp32 weights.  d has 11
+ * significant bits, the scale 7 and q - 32 6, so d * scale * (q - 32) is
+ * exact in fp32 (evaluated as (d * scale) * (q - 32), both steps exact). */
+void oracle_q6k_dequant_block(const uint8_t *blk, float *w)
+{
+    const uint8_t *ql = blk;
+    const uint8_t *qh = blk + 128;
+    const int8_t *sc = (const int8_t *)(blk + 192);
+    float d = oracle_f16_to_f32((uint16_t)(blk[208] | (blk[209] << 8)));
+    for (int n = 0; n < 2; ++n) {
+        for (int c = 0; c < 4; ++c) {
+            for (int l = 0; l < 32; ++l) {
+                uint8_t lbyte = ql[64 * n + 32 * (c & 1) + l];
+                int lo = (c < 2) ? (lbyte & 15) : (lbyte >> 4);
+                int hi = (qh[32 * n + l] >> (2 * c)) & 3;
+                int q = lo | (hi << 4);
+                float s = d * (float)sc[8 * n + 2 * c + l / 16];
+                w[128 * n + 32 * c + l] = s * (float)(q - 32);
+            }
+        }
+    }
+}
+
+/* y[o] = sum_k W[o,k] * x[k] for a Q6_K matrix whose row o holds
+ * inputDim/256 blocks: dequantize each block, then a double-precision dot. */
+int oracle_q6k_gemv(const float *x, const uint8_t *w, int64_t K, int64_t N,
+                    double *y)
+{
+    if (K <= 0 || N <= 0 || K % QK6 != 0)
+        return ORACLE_EINVAL_DIM;
+    if (!x || !w || !y)
+        return ORACLE_ENULL;
+    int64_t nb = K / QK6;
+    float wt[QK6];
+    for (int64_t o = 0; o < N; ++o) {
+        double acc = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            oracle_q6k_dequant_block(w + (o * nb + b) * BLOCK6_BYTES, wt);
+            const float *xb = x + b * QK6;
+            for (int p = 0; p < QK6; ++p)
                 acc += (double)wt[p] * (double)xb[p];
         }
         y[o] = acc;

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the Q4_K, Q4_0 and ternary products.
+"""Seeded synthetic inputs for the Q4_K, Q4_0, Q6_K and ternary products.
 
 This module only draws random numbers and lays them out in the input
 formats; it holds none of the products' arithmetic.  Both the GPU path's
@@ -21,6 +21,11 @@ Q4_0 matrix with R = rows * (K / 32) blocks: d = float16(|standard_normal(R)|
 / 64), then qs = integers(0, 256, (R, 16)); each block is d | qs (18 bytes),
 blocks row-major.
 
+Q6_K matrix with R = rows * (K / 256) blocks: d = float16(|standard_normal(R)|
+/ 64), then ql = integers(0, 256, (R, 128)), qh = integers(0, 256, (R, 64))
+(uniform 6-bit codes), scales = integers(-128, 128, (R, 16)) as int8; each
+block is ql | qh | scales | d (210 bytes), blocks row-major.
+
 Ternary matrix: codes u = integers(0, 3, (N, K)) (so u - 1 is uniform over
 {-1, 0, 1}), four per byte as u0 | u1<<2 | u2<<4 | u3<<6, rows of K/4 bytes;
 one float32 per-tensor scale uniform(0.5, 2).
@@ -37,10 +42,12 @@ QK = 256
 
 Q40_BLOCK_BYTES = 18
 Q40_QK = 32
+Q6K_BLOCK_BYTES = 210
 
 # Configuration ids used in seeds.
 C1_Q4K_1K, C2_Q4K_4K, C3_FFN, C4_PREFILL, C5_TERNARY = 1, 2, 3, 4, 5
 Q40_4K = 6
+Q6K_4K = 7
 ROLE_W, ROLE_X = 0, 1
 
 
@@ -91,6 +98,30 @@ def q4_0_weights(n_rows, input_dim, config=Q40_4K, copy=0, extra=0):
     d = (np.abs(g.standard_normal(R)) / 64).astype(np.float16)
     qs = g.integers(0, 256, (R, 16), dtype=np.uint8)
     return q4_0_blocks_from_fields(d, qs).reshape(n_rows, nb * Q40_BLOCK_BYTES)
+
+
+def q6k_blocks_from_fields(ql128, qh64, scales16, d_f16):
+    """Assemble [R, 210] Q6_K block bytes from already-drawn fields."""
+    R = ql128.shape[0]
+    out = np.empty((R, Q6K_BLOCK_BYTES), np.uint8)
+    out[:, 0:128] = ql128
+    out[:, 128:192] = qh64
+    out[:, 192:208] = np.ascontiguousarray(scales16, np.int8).view(np.uint8)
+    out[:, 208:210] = np.ascontiguousarray(d_f16, np.float16).view(np.uint8).reshape(R, 2)
+    return out
+
+
+def q6k_weights(n_rows, input_dim, config=Q6K_4K, copy=0, extra=0):
+    """Random Q6_K matrix as uint8 [n_rows, (input_dim/256)*210]."""
+    assert input_dim % QK == 0
+    nb = input_dim // QK
+    R = n_rows * nb
+    g = rng(config, copy, ROLE_W, extra)
+    d = (np.abs(g.standard_normal(R)) / 64).astype(np.float16)
+    ql = g.integers(0, 256, (R, 128), dtype=np.uint8)
+    qh = g.integers(0, 256, (R, 64), dtype=np.uint8)
+    sc = g.integers(-128, 128, (R, 16)).astype(np.int8)
+    return q6k_blocks_from_fields(ql, qh, sc, d).reshape(n_rows, nb * Q6K_BLOCK_BYTES)
 
 
 def activations(input_dim, n_tokens=None, config=C2_Q4K_4K, copy=0, extra=0):
@@ -148,6 +179,19 @@ def q4_0_integer_weights(n_rows, input_dim, config=Q40_4K, copy=0, extra=0):
     qs = g.integers(0, 256, (R, 16), dtype=np.uint8)
     return q4_0_blocks_from_fields(np.ones(R, np.float16), qs).reshape(
         n_rows, nb * Q40_BLOCK_BYTES)
+
+
+def q6k_integer_weights(n_rows, input_dim, config=Q6K_4K, copy=0, extra=0):
+    """Q6_K blocks with d = 1.0, scales in {-1, 1} and random codes: every
+    weight is an integer in [-32, 32]."""
+    nb = input_dim // QK
+    R = n_rows * nb
+    g = rng(config, copy, ROLE_W, 500 + extra)
+    ql = g.integers(0, 256, (R, 128), dtype=np.uint8)
+    qh = g.integers(0, 256, (R, 64), dtype=np.uint8)
+    sc = (2 * g.integers(0, 2, (R, 16)) - 1).astype(np.int8)
+    return q6k_blocks_from_fields(ql, qh, sc, np.ones(R, np.float16)).reshape(
+        n_rows, nb * Q6K_BLOCK_BYTES)
 
 
 def integer_activations(input_dim, lo=-1, hi=1, n_tokens=None, config=C2_Q4K_4K,

@@ -567,3 +567,155 @@ def test_q4_0_rejects_input_dim_not_multiple_of_32(oracle_lib, K):
     with pytest.raises(oracle_lib.OracleError) as e:
         oracle_lib.q4_0_gemv(np.zeros(max(K, 1), np.float32), np.zeros(18 * 4, np.uint8), K, 1)
     assert e.value.code == oracle_lib.EINVAL_DIM
+
+
+# ---------------------------------------------------------------------------
+# Q6_K (the Q4_K page's other follow-up format: ql + qh).  The test side
+# decodes element e with divmod and a bit extraction per element, not the
+# oracle's loops over halves and quadrants.
+
+def q6k_exact_weight(block, e):
+    n, r = divmod(e, 128)
+    c, l = divmod(r, 32)
+    lbyte = int(block[64 * n + 32 * (c % 2) + l])
+    lo = (lbyte >> (4 * (c // 2))) & 15
+    hi = (int(block[128 + 32 * n + l]) >> (2 * c)) & 3
+    scale = int(np.int8(block[192 + 8 * n + 2 * c + l // 16]))
+    d = _f16_value(block, 208)
+    return d * scale * ((lo | (hi << 4)) - 32)
+
+
+def _q6k_golden_block(spec):
+    blk = np.zeros(210, np.uint8)
+    blk[0:128] = spec["ql"]
+    blk[128:192] = spec["qh"]
+    blk[192:208] = np.array(spec["scales"], np.int8).view(np.uint8)
+    blk[208:210] = np.array([spec["d_f16_bits"]], np.uint16).view(np.uint8)
+    return blk
+
+
+@pytest.mark.parametrize("spec", _golden("q6k_block_worked.json")["blocks"],
+                         ids=lambda s: s["name"][0])
+def test_q6k_worked_blocks_golden(oracle_lib, spec):
+    blk = _q6k_golden_block(spec)
+    assert float(np.frombuffer(bytes(blk[208:210]), np.float16)[0]) == spec["d"]
+    for case in spec["cases"]:
+        x = np.zeros(256, np.float32)
+        lo, hi = case["support"]
+        x[lo:hi] = 1.0
+        assert oracle_lib.q6k_gemv(x, blk, 256, 1)[0] == case["y"], case
+
+
+def test_q6k_dequant_is_exact_weight(oracle_lib):
+    g = np.random.default_rng(60)
+    blocks = synth.q6k_weights(8, 256, config=84).reshape(8, 210).copy()
+    blocks[0:3, 208:210] = g.integers(1, 1024, 3).astype(np.uint16).view(np.uint8).reshape(3, 2)
+    blocks[3, 208:210] = np.array([np.float16(65504.0)]).view(np.uint8)
+    blocks[4, 192:208] = np.array([-128, 127] * 8, np.int8).view(np.uint8)
+    for blk in blocks:
+        w = oracle_lib.q6k_dequant_block(blk)
+        for e in range(256):
+            assert Fraction(float(w[e])) == q6k_exact_weight(blk, e), e
+
+
+@pytest.mark.parametrize("K,N", [(256, 3), (512, 2)])
+def test_q6k_gemv_against_exact_rational(oracle_lib, K, N):
+    w = synth.q6k_weights(N, K, config=83, copy=K)
+    x = synth.activations(K, config=83, copy=K)
+    y = oracle_lib.q6k_gemv(x, w, K, N)
+    for o in range(N):
+        exact, terms = Fraction(0), []
+        for b in range(K // 256):
+            blk = w[o, b * 210:(b + 1) * 210]
+            for e in range(256):
+                t = q6k_exact_weight(blk, e) * Fraction(float(x[b * 256 + e]))
+                exact += t
+                terms.append(abs(float(t)))
+        bound = K * 2.0 ** -53 * sum(terms)
+        assert abs(Fraction(float(y[o])) - exact) <= Fraction(bound) * (1 + 1e-9), o
+
+
+def _q4k_to_q6k(w4k, K, N):
+    """Re-pack a Q4_K matrix whose mins are all 0 as Q6_K: code q + 32 (high
+    bits 2), both 16-halves of Q4_K sub-block s scaled by sc[s], the same d.
+    The Q6_K weight d*sc*((q + 32) - 32) is then the Q4_K weight d*sc*q."""
+    out = np.zeros((N, (K // 256) * 210), np.uint8)
+    for o in range(N):
+        for b in range(K // 256):
+            blk = w4k[o, b * 144:(b + 1) * 144]
+            sc, _ = unpack_scales_table(blk[4:16])
+            q = [(int(blk[16 + 32 * ((e // 32) // 2) + e % 32]) >> (4 * ((e // 32) % 2))) & 15
+                 for e in range(256)]
+            b6 = np.zeros(210, np.uint8)
+            for e in range(256):
+                n, r = divmod(e, 128)
+                c, l = divmod(r, 32)
+                b6[64 * n + 32 * (c % 2) + l] |= q[e] << (4 * (c // 2))
+                b6[128 + 32 * n + l] |= 2 << (2 * c)
+            for n in range(2):
+                for c in range(4):
+                    for h in range(2):
+                        b6[192 + 8 * n + 2 * c + h] = sc[4 * n + c]
+            b6[208:210] = blk[0:2]
+            out[o, b * 210:(b + 1) * 210] = b6
+    return out
+
+
+def test_q6k_equals_q4k_without_mins(oracle_lib):
+    """Special case that reduces to the separately pinned Q4_K oracle: the
+    same weights in both formats give bit-identical double results."""
+    K, N = 512, 5
+    w4k = synth.q4k_weights(N, K, config=82).copy()
+    blocks = w4k.reshape(-1, 144)
+    sc = np.random.default_rng(82).integers(0, 64, (blocks.shape[0], 8))
+    for i, blk in enumerate(blocks):
+        blk[4:16] = pack_scales(sc[i].tolist(), [0] * 8)
+    w4k = blocks.reshape(N, -1)
+    w6 = _q4k_to_q6k(w4k, K, N)
+    x = synth.activations(K, config=82)
+    assert np.array_equal(oracle_lib.q6k_gemv(x, w6, K, N), oracle_lib.q4k_gemv(x, w4k, K, N))
+
+
+def test_q6k_integer_inputs_exact(oracle_lib):
+    K, N = 4096, 12
+    w = synth.q6k_integer_weights(N, K, config=81)
+    x = synth.integer_activations(K, config=81)
+    y = oracle_lib.q6k_gemv(x, w, K, N)
+    W = np.array([[float(q6k_exact_weight(w[o, (e // 256) * 210:(e // 256 + 1) * 210], e % 256))
+                   for e in range(K)] for o in range(2)], np.float64)
+    assert np.array_equal(y[:2], W @ x.astype(np.float64))
+    assert np.all(y == np.round(y))
+
+
+def test_q6k_constant_codes_closed_form(oracle_lib):
+    K, N = 512, 3
+    g = np.random.default_rng(8)
+    for lo, hi, S in [(0, 0, 5), (15, 3, -7), (9, 2, 127), (4, 1, -128)]:
+        blk = np.zeros(210, np.uint8)
+        blk[0:128] = lo | (lo << 4)
+        blk[128:192] = hi | (hi << 2) | (hi << 4) | (hi << 6)
+        blk[192:208] = np.array([S] * 16, np.int8).view(np.uint8)
+        d = np.float16(0.0217)
+        blk[208:210] = np.array([d]).view(np.uint8)
+        w = np.tile(blk, (N, K // 256))
+        x = g.standard_normal(K).astype(np.float32)
+        closed = float(d) * S * ((lo | (hi << 4)) - 32) * float(np.sum(x.astype(np.float64)))
+        assert np.allclose(oracle_lib.q6k_gemv(x, w, K, N), closed, rtol=1e-12, atol=1e-12)
+
+
+def test_q6k_zero_activation_and_linearity(oracle_lib):
+    K, N = 1024, 8
+    w = synth.q6k_weights(N, K, config=80)
+    assert np.all(oracle_lib.q6k_gemv(np.zeros(K, np.float32), w, K, N) == 0.0)
+    x1 = synth.activations(K, config=80, copy=1)
+    x2 = synth.activations(K, config=80, copy=2)
+    y = oracle_lib.q6k_gemv(np.float32(2.0) * x1 + np.float32(0.25) * x2, w, K, N)
+    y12 = 2.0 * oracle_lib.q6k_gemv(x1, w, K, N) + 0.25 * oracle_lib.q6k_gemv(x2, w, K, N)
+    assert_parity(y, y12, rel=1e-6)
+
+
+@pytest.mark.parametrize("K", [255, 257, 32, 0, -256])
+def test_q6k_rejects_input_dim_not_multiple_of_256(oracle_lib, K):
+    with pytest.raises(oracle_lib.OracleError) as e:
+        oracle_lib.q6k_gemv(np.zeros(max(K, 1), np.float32), np.zeros(210 * 2, np.uint8), K, 1)
+    assert e.value.code == oracle_lib.EINVAL_DIM
