@@ -23,6 +23,8 @@ Other workloads (measurement of the sibling paths, same JSON shape):
   c5  ternary GEMV 4096 x 4096, batch 1 (128 rotating copies)
   q40 Q4_0 GEMV 4096 x 4096, batch 1 (64 rotating copies; the Q4_K page's
       follow-up format, the same 9.4 MB of weights per call as c2)
+  q6k Q6_K GEMV 4096 x 4096, batch 1 (43 rotating copies of 13.8 MB; the
+      page's other follow-up format)
   copy  plain 64 MiB device-to-device copy kernel (4 rotating buffer pairs):
       the kernel of known traffic used to scale hardware byte counters
 """
@@ -196,6 +198,30 @@ def make_workload(name, torch, binding, synth):
             x0 = wl.x.cpu().numpy()
             return (lambda: oracle.q4_0_gemv(x0, w0, K, N)), 1.0, f"oracle q4_0_gemv {K}x{N}, full call"
         wl.cpu = cpu
+    elif name == "q6k":
+        K = N = 4096
+        wbytes = N * K // 256 * 210
+        copies = -(-ROTATION_BYTES // wbytes)
+        wl.W = [to_dev(synth.q6k_weights(N, K, copy=c)) for c in range(copies)]
+        wl.x = to_dev(synth.activations(K, config=synth.Q6K_4K))
+        wl.y = torch.empty(N, dtype=torch.float32, device=dev)
+        wl.call = lambda i: binding.q6k_gemv(wl.x, wl.W[i % copies], K, N, wl.y)
+        wl.copies = copies
+        wl.bytes = wbytes + 4 * K + 4 * N
+        wl.flops = 2 * K * N
+        wl.kernel = "q4k_gemv_kernel<Q6K, 64, 2, 1, 4>"
+        wl.src_files = GEMV_SRC
+        wl.data = "synthetic (seeded numpy generators; random Q6_K blocks, N(0,1) activations)"
+        wl.config = {"workload": f"q6k_gemv {K}x{N} batch 1", "input_dim": K,
+                     "output_dim": N, "batch": 1, "rotating_copies": copies,
+                     "weight_bytes_per_copy": wbytes}
+        wl.metric = f"Q6_K GEMV us/call + achieved HBM GB/s (% peak) at {K}x{N}, batch 1"
+
+        def cpu(oracle):
+            w0 = wl.W[0].cpu().numpy()
+            x0 = wl.x.cpu().numpy()
+            return (lambda: oracle.q6k_gemv(x0, w0, K, N)), 1.0, f"oracle q6k_gemv {K}x{N}, full call"
+        wl.cpu = cpu
     elif name == "copy":
         nbytes = 64 * 2 ** 20
         copies = 4
@@ -322,7 +348,8 @@ TRAFFIC_FILES = {"c2": "q4k_gemv_4096x4096_b1.traffic.json",
                  "c3": "q4k_gemv_ffn_4096x14336_pair.traffic.json",
                  "c4": "q4k_prefill_64x4096x4096.traffic.json",
                  "c5": "ternary_gemv_4096x4096_b1.traffic.json",
-                 "q40": "q4_0_gemv_4096x4096_b1.traffic.json"}
+                 "q40": "q4_0_gemv_4096x4096_b1.traffic.json",
+                 "q6k": "q6k_gemv_4096x4096_b1.traffic.json"}
 
 
 def traffic_for(wl):
@@ -345,7 +372,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64000)
     ap.add_argument("--warmup", type=int, default=6400)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "q40", "copy"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "q40", "q6k", "copy"])
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

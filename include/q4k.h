@@ -1,7 +1,7 @@
 /*
  * q4k.h -- C ABI of libq4k.so, the MI355X (gfx950) fused-dequantize Q4_K
- * matrix-vector product, its batched (prefill) form, the Q4_0 matrix-vector
- * product and the ternary BitNet b1.58 sibling.
+ * matrix-vector product, its batched (prefill) form, the Q4_0 and Q6_K
+ * matrix-vector products and the ternary BitNet b1.58 sibling.
  *
  * Common contract for every compute entry point:
  *   - x, w_blocks/codes and y are DEVICE pointers owned by the caller.  The
@@ -143,6 +143,47 @@ int q4_0_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
 int q4_0_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                      int64_t output_dim, float *y, void *stream,
                      int rows_per_lane, int k_waves, int workgroup_waves);
+
+/*
+ * Q6_K weight format (block_q6_K, 256 weights in 210 bytes): the Q4_K page's
+ * other follow-up (section "Out of scope": ql holds the codes' low bits, qh
+ * their high bits, four codes per qh byte, in two interleaved halves).  Read
+ * as ggml's block_q6_K:
+ *   bytes 0..127    ql
+ *   bytes 128..191  qh
+ *   bytes 192..207  sixteen int8 scales
+ *   bytes 208..209  d   binary16, little-endian
+ * Element 128n + 32c + l (n < 2, c < 4, l < 32) has code q = lo | hi<<4: lo
+ * the low (c < 2) or high (c >= 2) nibble of ql[64n + 32*(c%2) + l], hi bits
+ * 2c..2c+1 of qh[32n + l]; its weight is d*scale[8n + 2c + l/16]*(q - 32).
+ * The matrix is row-major [output_dim][input_dim/256] blocks, row o
+ * starting at byte o*(input_dim/256)*210 (rows need not be 16-byte
+ * aligned; the matrix must).
+ */
+
+/*
+ * q6k_gemv -- y[o] = sum_k W[o,k] * x[k] for a Q6_K matrix (batch 1): every
+ * 16-weight group adds d*scale*(sum q*x - 32*sum x), accumulated in fp32.
+ *   x          fp32 [input_dim], 16-byte aligned
+ *   w_blocks   uint8 [output_dim * input_dim/256 * 210], 16-byte aligned
+ *   input_dim  K > 0, a multiple of 256 and at most 2^24, else Q4K_EINVAL_DIM
+ *   output_dim N > 0
+ *   y          fp32 [output_dim]
+ * Same error behaviour, determinism and tolerance as q4k_gemv (vector
+ * form; |x| should stay above ~1e-30 for full precision).
+ */
+int q6k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+             int64_t output_dim, float *y, void *stream);
+
+/*
+ * q6k_gemv_shaped -- q6k_gemv with an explicit launch shape; the values are
+ * those of q4k_gemv_shaped without the matrix-core form, except that
+ * rows_per_lane 8 with k_waves 4 and 4-wave workgroups is rejected for long
+ * rows (Q4K_EINVAL_DIM: the tiles would not fit in LDS).
+ */
+int q6k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+                    int64_t output_dim, float *y, void *stream,
+                    int rows_per_lane, int k_waves, int workgroup_waves);
 
 /*
  * Ternary BitNet b1.58 format (ternary page, SKaiNET issue #1138, section

@@ -21,7 +21,8 @@ Q4K_EHIP = -4
 
 EXPORTED = (
     "q4k_gemv", "q4k_matmul", "ternary_gemv_codes", "ternary_gemv",
-    "q4k_gemv_shaped", "q4_0_gemv", "q4_0_gemv_shaped", "q4k_strerror",
+    "q4k_gemv_shaped", "q4_0_gemv", "q4_0_gemv_shaped", "q6k_gemv", "q6k_gemv_shaped",
+    "q4k_strerror",
     "q4k_bench_empty", "q4k_bench_stream_read", "q4k_bench_copy",
 )
 
@@ -55,6 +56,8 @@ def lib():
         "q4k_gemv_shaped": [P, P, I64, I64, P, P, I, I, I],
         "q4_0_gemv": [P, P, I64, I64, P, P],
         "q4_0_gemv_shaped": [P, P, I64, I64, P, P, I, I, I],
+        "q6k_gemv": [P, P, I64, I64, P, P],
+        "q6k_gemv_shaped": [P, P, I64, I64, P, P, I, I, I],
         "q4k_bench_empty": [P],
         "q4k_bench_stream_read": [P, I64, P, I64, P],
         "q4k_bench_copy": [P, P, I64, P],
@@ -166,6 +169,32 @@ def q4_0_gemv_shaped(x, w_blocks, input_dim, output_dim, y, rows_per_lane=0,
     _check(lib().q4_0_gemv_shaped(_ptr(x), _ptr(w_blocks), K, N, _ptr(y), _stream(stream),
                                   int(rows_per_lane), int(k_waves), int(workgroup_waves)),
            "q4_0_gemv_shaped")
+    return y
+
+
+def _q6k_need(K, N):
+    return N * (K // 256) * 210 if (K > 0 and N > 0 and K % 256 == 0) else 0
+
+
+def q6k_gemv(x, w_blocks, input_dim, output_dim, y, stream=None):
+    K, N = int(input_dim), int(output_dim)
+    _expect(x, torch.float32, "x", K if _pos(K, N) else 0)
+    _expect(w_blocks, torch.uint8, "w_blocks", _q6k_need(K, N))
+    _expect(y, torch.float32, "y", N if _pos(K, N) else 0)
+    _check(lib().q6k_gemv(_ptr(x), _ptr(w_blocks), K, N, _ptr(y), _stream(stream)),
+           "q6k_gemv")
+    return y
+
+
+def q6k_gemv_shaped(x, w_blocks, input_dim, output_dim, y, rows_per_lane=0,
+                    k_waves=0, workgroup_waves=0, stream=None):
+    K, N = int(input_dim), int(output_dim)
+    _expect(x, torch.float32, "x", K if _pos(K, N) else 0)
+    _expect(w_blocks, torch.uint8, "w_blocks", _q6k_need(K, N))
+    _expect(y, torch.float32, "y", N if _pos(K, N) else 0)
+    _check(lib().q6k_gemv_shaped(_ptr(x), _ptr(w_blocks), K, N, _ptr(y), _stream(stream),
+                                 int(rows_per_lane), int(k_waves), int(workgroup_waves)),
+           "q6k_gemv_shaped")
     return y
 
 

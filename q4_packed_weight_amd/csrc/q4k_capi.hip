@@ -106,6 +106,38 @@ int q4_0_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
   return q4_0_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0, 0);
 }
 
+// Q6_K rows of input_dim/256 210-byte blocks (validation as for Q4_K).  The
+// kernel runs 32 or 64 lanes per row; 64 lanes with 8 rows per lane and a
+// 4-way split of input_dim would need more LDS than a CU has.
+int q6k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+                    int64_t output_dim, float *y, void *stream,
+                    int rows_per_lane, int k_waves, int workgroup_waves) {
+  int rc = check_q4k(x, w_blocks, y, 1, input_dim, output_dim);
+  if (rc) return rc;
+  if (!valid_vector_shape(rows_per_lane, k_waves, workgroup_waves)) return Q4K_EINVAL_DIM;
+  const int64_t nb = input_dim / 256;
+  const q4k::GemvShape s = q4k::choose_gemv_shape(nb, output_dim, rows_per_lane,
+                                                  k_waves, workgroup_waves, 32);
+  if (s.lanes == 64 && s.rows_per_lane == 8 && s.k_waves == 4) return Q4K_EINVAL_DIM;
+  hipError_t e = q4k::gemv_q6k_launch(x, w_blocks, y, nb, output_dim, s,
+                                      (hipStream_t)stream);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q6k_gemv launch");
+}
+
+// Measured on MI355X (graph-replayed calls over rotating weights, 13.8 to
+// 48 MB per matrix): no split of input_dim across waves (the Q6_K tiles
+// leave room for one workgroup per CU only when split) and at most 2 rows
+// per lane: 4096x4096 5.6 us, 4096->14336 14.0, 14336->4096 15.4,
+// 11008->4096 12.3, against 6.4 / 15.3 / 20.5 / 19.6 with the Q4_K rule.
+int q6k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+             int64_t output_dim, float *y, void *stream) {
+  int rc = check_q4k(x, w_blocks, y, 1, input_dim, output_dim);
+  if (rc) return rc;
+  const q4k::GemvShape s = q4k::choose_gemv_shape(input_dim / 256, output_dim, 0, 1, 0, 32);
+  return q6k_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream,
+                         s.rows_per_lane < 2 ? s.rows_per_lane : 2, 1, 0);
+}
+
 int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
              int64_t output_dim, float *y, void *stream) {
   return q4k_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0,
@@ -159,9 +191,10 @@ const char *q4k_strerror(int code) {
     case Q4K_OK: return "ok";
     case Q4K_EINVAL_DIM:
       return "invalid dimension: every dimension must be > 0, input_dim a "
-             "multiple of 256 for Q4_K and Q4_0 (of 4 for ternary) and at most 2^24";
+             "multiple of 256 for Q4_K, Q4_0 and Q6_K (of 4 for ternary) and at "
+             "most 2^24";
     case Q4K_ENULL: return "a required pointer is NULL";
-    case Q4K_EALIGN: return "x and the Q4_K or Q4_0 blocks must be 16-byte aligned";
+    case Q4K_EALIGN: return "x and the Q4_K, Q4_0 or Q6_K blocks must be 16-byte aligned";
     case Q4K_EHIP: return g_hip_detail[0] ? g_hip_detail : "HIP runtime error";
     default: return "unknown error code";
   }

@@ -91,19 +91,50 @@ __device__ __forceinline__ void nibble_dots(uint32_t w, float4 xl, float4 xh,
   hi[1] = __builtin_fmaf(half_hi(hi13), xh.w, hi[1]);
 }
 
-// Per-lane work of one (row, slab) pair, by weight format.  `grp` is the
-// 144-byte group (9 uint4 of the staged tile) holding this lane's slab; j
-// (0..3) is the slab within the group; xl/xh are the slab's 64 activations
-// (float4 k of xl is positions 4k..4k+3, of xh positions 32+4k..) and xsm
-// their sums over positions 0..31 and 32..63.  Returns acc plus the slab's
-// contribution to the row.
-//
-// Q4_K: the group is one super-block; the lane reads the header and the 32
+// Per-format parts of the GEMV kernels.  Each format defines
+//   kBlockBytes  bytes of one block (a Q4_K super-block, eight Q4_0 blocks,
+//                one Q6_K block); four lanes share a block, one 64-position
+//                slab each;
+//   kUnaligned   whether a row can start off a 16-byte boundary (then the
+//                tile holds each row piece from its aligned-down start, with
+//                one more chunk, and the lane adds the row's offset);
+//   load_x       the lane's 64 activations from the staged slabs, as two
+//                float4[8] (xl, xh), and the sums the format's offset term
+//                needs (xs);
+//   slab         acc plus the lane's slab contribution to a row, reading the
+//                block that starts `boff` bytes into the wave's LDS tile.
+// Staged layout: float4 k (positions 4k..4k+3) of staged slab ls is
+// xs4[k*SP + ls]; xsum[ls] holds the sums over positions 0..31 and 32..63.
+
+// The lane's staged slab as positions 0..31 (xl) and 32..63 (xh) with their
+// two 32-position sums (Q4_K sub-blocks 2j and 2j+1, Q4_0 blocks 2j and
+// 2j+1).
+__device__ __forceinline__ void load_x_slab(const float4 *xs4, int SP, int ls,
+                                            const float2 *xsum, float4 (&xl)[8],
+                                            float4 (&xh)[8], float4 &xs) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    xl[k] = xs4[k * SP + ls];
+    xh[k] = xs4[(k + 8) * SP + ls];
+  }
+  const float2 t = xsum[ls];
+  xs = make_float4(t.x, t.y, 0.f, 0.f);
+}
+
+// Q4_K: the block is one super-block; the lane reads the header and the 32
 // qs bytes 32j..32j+31 (positions l of sub-blocks 2j and 2j+1).
 struct Q4K {
-  __device__ __forceinline__ static float slab(const uint4 *grp, int j, uint32_t sh, bool jhi,
-                                               const float4 (&xl)[8], const float4 (&xh)[8],
-                                               float2 xsm, float acc) {
+  static constexpr int kBlockBytes = 144;
+  static constexpr bool kUnaligned = false;
+  __device__ __forceinline__ static void load_x(const float4 *xs4, int SP, int ls, int,
+                                                const float2 *xsum, float4 (&xl)[8],
+                                                float4 (&xh)[8], float4 &xs) {
+    load_x_slab(xs4, SP, ls, xsum, xl, xh, xs);
+  }
+  __device__ __forceinline__ static float slab(const uint4 *tile, int boff, int j, uint32_t sh,
+                                               bool jhi, const float4 (&xl)[8],
+                                               const float4 (&xh)[8], float4 xs, float acc) {
+    const uint4 *grp = tile + (boff >> 4);
     const uint4 hdr = grp[0];
     const uint4 q0 = grp[1 + 2 * j];
     const uint4 q1 = grp[2 + 2 * j];
@@ -115,7 +146,7 @@ struct Q4K {
     const SlabScales sc = decode_header(hdr, sh, jhi);
     // code part in units of 2^-20: 16*sc_lo*s_lo + sc_hi*s_hi
     const float tc = __builtin_fmaf(sc.sc_lo16, s_lo, sc.sc_hi * s_hi);
-    const float tm = __builtin_fmaf(sc.m_lo, xsm.x, sc.m_hi * xsm.y);
+    const float tm = __builtin_fmaf(sc.m_lo, xs.x, sc.m_hi * xs.y);
     // this slab's contribution: d * 2^20 * tc - dmin * tm
     return __builtin_fmaf(sc.d * 0x1p20f, tc, __builtin_fmaf(-sc.dmin, tm, acc));
   }
@@ -129,10 +160,17 @@ struct Q4K {
 // qs start 2 bytes into its first dword and are realigned; the second's
 // are dword-aligned.  Each block contributes d*(sum q*x - 8*sum x).
 struct Q40 {
-  __device__ __forceinline__ static float slab(const uint4 *grp, int j, uint32_t, bool,
+  static constexpr int kBlockBytes = 144;
+  static constexpr bool kUnaligned = false;
+  __device__ __forceinline__ static void load_x(const float4 *xs4, int SP, int ls, int,
+                                                const float2 *xsum, float4 (&xl)[8],
+                                                float4 (&xh)[8], float4 &xs) {
+    load_x_slab(xs4, SP, ls, xsum, xl, xh, xs);
+  }
+  __device__ __forceinline__ static float slab(const uint4 *tile, int boff, int j, uint32_t, bool,
                                                const float4 (&xl)[8], const float4 (&xh)[8],
-                                               float2 xsm, float acc) {
-    const uint32_t *g32 = reinterpret_cast<const uint32_t *>(grp) + 9 * j;
+                                               float4 xs, float acc) {
+    const uint32_t *g32 = reinterpret_cast<const uint32_t *>(tile + (boff >> 4)) + 9 * j;
     uint32_t dw[9];
 #pragma unroll
     for (int i = 0; i < 9; ++i) dw[i] = g32[i];
@@ -148,8 +186,99 @@ struct Q40 {
     // sum q*x in units of 2^-20: 16*(low-nibble sums) + (high-nibble sums)
     const float t0 = __builtin_fmaf(16.0f, lo0[0] + lo0[1], hi0[0] + hi0[1]);
     const float t1 = __builtin_fmaf(16.0f, lo1[0] + lo1[1], hi1[0] + hi1[1]);
-    acc = __builtin_fmaf(d0 * 0x1p20f, t0, __builtin_fmaf(-8.0f * d0, xsm.x, acc));
-    return __builtin_fmaf(d1 * 0x1p20f, t1, __builtin_fmaf(-8.0f * d1, xsm.y, acc));
+    acc = __builtin_fmaf(d0 * 0x1p20f, t0, __builtin_fmaf(-8.0f * d0, xs.x, acc));
+    return __builtin_fmaf(d1 * 0x1p20f, t1, __builtin_fmaf(-8.0f * d1, xs.y, acc));
+  }
+};
+
+// Q6_K (the Q4_K page's other follow-up format, section "Out of scope": ql
+// holds each code's low 4 bits, qh its high 2 bits, four codes per qh byte,
+// in two interleaved halves).  Read as ggml's block_q6_K, 210 bytes: ql[128],
+// qh[64], 16 int8 scales, fp16 d.  Element 128n + 32c + l (half n, quadrant
+// c) has the low (c < 2) or high (c >= 2) nibble of ql[64n + 32(c&1) + l],
+// bits 2c..2c+1 of qh[32n + l] on top, and scale 8n + 2c + l/16; weight
+// d*scale*(q - 32).  Lane j of a block takes half n = j/2 and quadrants
+// p = j%2 and p + 2: the same 32 ql bytes (low and high nibbles) and the
+// same 32 qh bytes, four 16-position scale groups.  Blocks start on even
+// bytes only, so every field is read as dwords from its aligned-down start
+// and shifted back by the block's offset (0 or 2 bytes).
+struct Q6K {
+  static constexpr int kBlockBytes = 210;
+  static constexpr bool kUnaligned = true;
+  // positions 32p..32p+31 of staged slabs 4b + 2n (xl: quadrant p) and
+  // 4b + 2n + 1 (xh: quadrant p + 2), and their four 16-position sums
+  __device__ __forceinline__ static void load_x(const float4 *xs4, int SP, int ls, int j,
+                                                const float2 *, float4 (&xl)[8],
+                                                float4 (&xh)[8], float4 &xs) {
+    const int p = j & 1;
+    const int a = ls - p;  // slab 4b + 2n of this lane's block
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xl[i] = xs4[(8 * p + i) * SP + a];
+      xh[i] = xs4[(8 * p + i) * SP + a + 1];
+    }
+    xs.x = (sum4(xl[0]) + sum4(xl[1])) + (sum4(xl[2]) + sum4(xl[3]));
+    xs.y = (sum4(xl[4]) + sum4(xl[5])) + (sum4(xl[6]) + sum4(xl[7]));
+    xs.z = (sum4(xh[0]) + sum4(xh[1])) + (sum4(xh[2]) + sum4(xh[3]));
+    xs.w = (sum4(xh[4]) + sum4(xh[5])) + (sum4(xh[6]) + sum4(xh[7]));
+  }
+  __device__ __forceinline__ static float slab(const uint4 *tile, int boff, int j, uint32_t, bool,
+                                               const float4 (&xl)[8], const float4 (&xh)[8],
+                                               float4 xs, float acc) {
+    const uint32_t *t32 = reinterpret_cast<const uint32_t *>(tile);
+    const int n = j >> 1, p = j & 1;
+    const uint32_t sb = (uint32_t)boff & 3u;  // 0 or 2: the block's byte offset in a dword
+    const int oq = (boff + 64 * n + 32 * p) >> 2;
+    const int oh = (boff + 128 + 32 * n) >> 2;
+    const int os = (boff + 192 + 8 * n) >> 2;
+    const int od = (boff + 208) >> 2;
+    uint32_t q[9], h[9], sd[3];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      q[i] = t32[oq + i];
+      h[i] = t32[oh + i];
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) sd[i] = t32[os + i];
+    const float d = half_lo(t32[od] >> (8u * sb));
+    // the four scales: bytes 2p, 2p+1 (quadrant p) and 2p+4, 2p+5 (p + 2)
+    const uint32_t s0 = __builtin_amdgcn_alignbyte(sd[1], sd[0], sb);
+    const uint32_t s1 = __builtin_amdgcn_alignbyte(sd[2], sd[1], sb);
+    // sign-extended bytes (the builtin's result type is unsigned: convert
+    // through int32_t)
+    const uint32_t sp = 16u * (uint32_t)p;
+    const float ds0 = d * (float)(int32_t)__builtin_amdgcn_sbfe(s0, sp, 8);
+    const float ds1 = d * (float)(int32_t)__builtin_amdgcn_sbfe(s0, sp + 8, 8);
+    const float ds2 = d * (float)(int32_t)__builtin_amdgcn_sbfe(s1, sp, 8);
+    const float ds3 = d * (float)(int32_t)__builtin_amdgcn_sbfe(s1, sp + 8, 8);
+    // code sums in units of 2^-24 (6-bit codes enter as fp16 subnormals):
+    // [quadrant p | p + 2][positions 0..15 | 16..31][two chains]
+    float c[2][2][2] = {};
+    const uint32_t hs = 2u * (uint32_t)p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ql = __builtin_amdgcn_alignbyte(q[i + 1], q[i], sb);
+      const uint32_t hq = __builtin_amdgcn_alignbyte(h[i + 1], h[i], sb) >> hs;
+      // four 6-bit codes per dword, one per byte
+      const uint32_t clo = (ql & 0x0F0F0F0Fu) | ((hq << 4) & 0x30303030u);
+      const uint32_t chi = ((ql >> 4) & 0x0F0F0F0Fu) | (hq & 0x30303030u);
+      const int hf = i >> 2;
+#pragma unroll
+      for (int qd = 0; qd < 2; ++qd) {
+        const uint32_t cw = qd ? chi : clo;
+        const float4 xv = qd ? xh[i] : xl[i];
+        const uint32_t a02 = cw & 0x003F003Fu, a13 = (cw >> 8) & 0x003F003Fu;
+        c[qd][hf][0] = __builtin_fmaf(half_lo(a02), xv.x, c[qd][hf][0]);
+        c[qd][hf][1] = __builtin_fmaf(half_lo(a13), xv.y, c[qd][hf][1]);
+        c[qd][hf][0] = __builtin_fmaf(half_hi(a02), xv.z, c[qd][hf][0]);
+        c[qd][hf][1] = __builtin_fmaf(half_hi(a13), xv.w, c[qd][hf][1]);
+      }
+    }
+    // each 16-position group adds d*scale*(2^24 * codes.x - 32 * sum x)
+    acc = __builtin_fmaf(ds0 * 0x1p24f, c[0][0][0] + c[0][0][1], __builtin_fmaf(-32.0f * ds0, xs.x, acc));
+    acc = __builtin_fmaf(ds1 * 0x1p24f, c[0][1][0] + c[0][1][1], __builtin_fmaf(-32.0f * ds1, xs.y, acc));
+    acc = __builtin_fmaf(ds2 * 0x1p24f, c[1][0][0] + c[1][0][1], __builtin_fmaf(-32.0f * ds2, xs.z, acc));
+    return __builtin_fmaf(ds3 * 0x1p24f, c[1][1][0] + c[1][1][1], __builtin_fmaf(-32.0f * ds3, xs.w, acc));
   }
 };
 
@@ -164,8 +293,10 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
   constexpr int RG = W / KW;                // row groups (of KW waves) per workgroup
   constexpr int ROWS_W = G * R;             // rows per wave
   constexpr int BPS = L / 4;                // blocks of one row covered by one step
-  constexpr int CH_ROW = BPS * 9;           // 16-byte chunks of one row per step
-  constexpr int TILE = ROWS_W * CH_ROW;     // chunks of a wave's weight tile
+  static_assert(BPS * F::kBlockBytes % 16 == 0, "a row piece must be whole 16-byte chunks");
+  constexpr int CH_ROW = BPS * F::kBlockBytes / 16;   // 16-byte chunks of one row per step
+  constexpr int CH_ROWP = CH_ROW + (F::kUnaligned ? 1 : 0);  // tile chunks per row piece
+  constexpr int TILE = ROWS_W * CH_ROWP;    // chunks of a wave's weight tile
   constexpr int NM = (TILE + 63) / 64;      // load instructions per tile
   constexpr int S = KW * L;                 // slabs whose activations are staged together
   constexpr int SP = S + 1;                 // padded row of the staged layout (float4)
@@ -198,18 +329,26 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
   const int n_slabs = 4 * nb;
   const int steps = (n_slabs + L - 1) / L;
   const int iters = (steps + KW - 1) / KW;
-  const int64_t row_bytes = (int64_t)nb * kBlockBytes;
+  const int64_t row_bytes = (int64_t)nb * F::kBlockBytes;
   const int j = u & 3;
   const uint32_t sh = (uint32_t)(j & 1) * 16u;
   const bool jhi = j >= 2;
   const int ls = kw * L + u;  // this lane's slab within the staged range
   // Range-checked buffer views: activations, and this workgroup's rows of
   // the weight matrix (rows past N read as zeros, so no clamping).
+  // Rows of an unaligned format are read from the workgroup's first byte
+  // rounded down to 16 (w itself is 16-byte aligned); wave_off is the
+  // wave's first row relative to that base.  The view ends at the matrix's
+  // end rounded up to a dword: the range check zeroes every dword that
+  // crosses the view's end, and the last bytes of a Q6_K matrix can share
+  // a dword with up to two bytes past it (never a page of their own).
   const int64_t wg_row0 = (int64_t)blockIdx.x * (RG * ROWS_W);
+  const int64_t wg_byte0 = wg_row0 * row_bytes;
+  const int64_t wg_base = F::kUnaligned ? (wg_byte0 & ~(int64_t)15) : wg_byte0;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)nb * 1024);
   const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(w + wg_row0 * row_bytes, (N - wg_row0) * row_bytes);
-  const int wave_off = (int)((row0 - wg_row0) * row_bytes);
+      make_rsrc(w + wg_base, ((N * row_bytes + 3) & ~(int64_t)3) - wg_base);
+  const int wave_off = (int)(wg_byte0 - wg_base + (row0 - wg_row0) * row_bytes);
 
   float acc[R];
 #pragma unroll
@@ -218,10 +357,11 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
   for (int it = 0; it < iters; ++it) {
     // 1. Load phase.  Activations for staging first (coalesced, L2-resident,
     //    they return first), then this wave's weight tile as a coalesced
-    //    stream: chunk q of the tile is row q / CH_ROW of the wave, chunk
-    //    q % CH_ROW of this step's piece of that row.  Slabs past the end of
-    //    x and rows past N read as zeros; blocks past the end of a row read
-    //    the next row's bytes and are never consumed.
+    //    stream: chunk q of the tile is row q / CH_ROWP of the wave, chunk
+    //    q % CH_ROWP of this step's piece of that row (from the piece's
+    //    first byte rounded down to 16).  Slabs past the end of x and rows
+    //    past N read as zeros; blocks past the end of a row read the next
+    //    row's bytes and are never consumed.
     const int slab_base = it * S;
     float4 xv[XQ];
 #pragma unroll
@@ -235,9 +375,10 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int q = 64 * m + lane;
-      const int rt = q / CH_ROW;
-      const int within = q - rt * CH_ROW;
-      wv[m] = load_buf_stream16(wr, wave_off + rt * (int)row_bytes + b0 * kBlockBytes + 16 * within);
+      const int rt = q / CH_ROWP;
+      const int within = q - rt * CH_ROWP;
+      const int start = wave_off + rt * (int)row_bytes + b0 * F::kBlockBytes;
+      wv[m] = load_buf_stream16(wr, (start & ~15) + 16 * within);
     }
     // Keep the LDS stores below from being hoisted above the load phase.
     asm volatile("" ::: "memory");
@@ -252,9 +393,11 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
       if (XF % kThreads != 0 && f >= XF) break;  // wave-uniform
       const int sl = f >> 4, k = f & 15;
       xs4[k * SP + sl] = xv[q];
-      const float part = group_sum<8>(sum4(xv[q]));
-      if (k == 0) xsum[sl].x = part;
-      if (k == 8) xsum[sl].y = part;
+      if constexpr (!F::kUnaligned) {  // Q6_K sums its own 16-position groups
+        const float part = group_sum<8>(sum4(xv[q]));
+        if (k == 0) xsum[sl].x = part;
+        if (k == 8) xsum[sl].y = part;
+      }
     }
     __syncthreads();
 
@@ -264,25 +407,23 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
     const int i = t * L + u;
     const bool active = t < steps && i < n_slabs;
     float4 xl[8], xh[8];
-    float2 xsm = make_float2(0.f, 0.f);
-    if (active) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        xl[k] = xs4[k * SP + ls];
-        xh[k] = xs4[(k + 8) * SP + ls];
-      }
-      xsm = xsum[ls];
-    }
+    float4 xs = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (active) F::load_x(xs4, SP, ls, j, xsum, xl, xh, xs);
     const int bl = u >> 2;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int prev_last = r == 0 ? -1 : (r * G * CH_ROW - 1) / 64;
-      const int last_m = ((r + 1) * G * CH_ROW - 1) / 64;
+      const int prev_last = r == 0 ? -1 : (r * G * CH_ROWP - 1) / 64;
+      const int last_m = ((r + 1) * G * CH_ROWP - 1) / 64;
 #pragma unroll
       for (int m = 0; m < NM; ++m)
         if (m > prev_last && m <= last_m && 64 * m + lane < TILE) wt[wave][64 * m + lane] = wv[m];
-      if (active)
-        acc[r] = F::slab(&wt[wave][((r * G + g) * BPS + bl) * 9], j, sh, jhi, xl, xh, xsm, acc[r]);
+      if (active) {
+        const int rr = r * G + g;  // row of the wave
+        int boff = rr * CH_ROWP * 16 + bl * F::kBlockBytes;
+        if constexpr (F::kUnaligned)
+          boff += (wave_off + rr * (int)row_bytes + b0 * F::kBlockBytes) & 15;
+        acc[r] = F::slab(wt[wave], boff, j, sh, jhi, xl, xh, xs, acc[r]);
+      }
     }
     // every wave must be done with the staged activations before the next
     // iteration overwrites them (the weight tile is private to the wave)
@@ -333,8 +474,10 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_persist_kernel(
   constexpr int G = 64 / L;
   constexpr int ROWS_W = G * R;
   constexpr int BPS = L / 4;
-  constexpr int CH_ROW = BPS * 9;
-  constexpr int TILE = ROWS_W * CH_ROW;
+  static_assert(BPS * F::kBlockBytes % 16 == 0, "a row piece must be whole 16-byte chunks");
+  constexpr int CH_ROW = BPS * F::kBlockBytes / 16;
+  constexpr int CH_ROWP = CH_ROW + (F::kUnaligned ? 1 : 0);
+  constexpr int TILE = ROWS_W * CH_ROWP;
   constexpr int NM = (TILE + 63) / 64;
   constexpr int S = L;
   constexpr int SP = S + 1;
@@ -353,25 +496,37 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_persist_kernel(
   const int g = lane / L;
   const int u = lane % L;
   const int n_slabs = 4 * nb;
-  const int64_t row_bytes = (int64_t)nb * kBlockBytes;
+  const int64_t row_bytes = (int64_t)nb * F::kBlockBytes;
   const int j = u & 3;
   const uint32_t sh = (uint32_t)(j & 1) * 16u;
   const bool jhi = j >= 2;
   const int64_t unit_rows = (int64_t)W * ROWS_W;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)nb * 1024);
 
-  // Weight tile of a unit: chunk q of this wave's tile is row q / CH_ROW of
-  // the wave, chunk q % CH_ROW of the row (the whole row: one step).
+  // Weight tile of a unit: chunk q of this wave's tile is row q / CH_ROWP
+  // of the wave, chunk q % CH_ROWP of the row (the whole row: one step),
+  // counted from the row's first byte rounded down to 16.  wave_off(unit)
+  // is the wave's first row relative to the unit's base.
+  auto unit_base = [&](int unit) {
+    const int64_t b = (int64_t)unit * unit_rows * row_bytes;
+    return F::kUnaligned ? (b & ~(int64_t)15) : b;
+  };
+  auto wave_off = [&](int unit) {
+    const int64_t b = (int64_t)unit * unit_rows * row_bytes;
+    return (int)(b - unit_base(unit) + wave * ROWS_W * row_bytes);
+  };
   auto load_tile = [&](int unit, uint4 (&wv)[NM]) {
-    const int64_t r0 = (int64_t)unit * unit_rows;
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + r0 * row_bytes, (N - r0) * row_bytes);
-    const int wave_off = (int)(wave * ROWS_W * row_bytes);
+    const int64_t base = unit_base(unit);
+    // ends at the matrix's end rounded up to a dword (see q4k_gemv_kernel)
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + base, ((N * row_bytes + 3) & ~(int64_t)3) - base);
+    const int woff = wave_off(unit);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int q = 64 * m + lane;
-      const int rt = q / CH_ROW;
-      const int within = q - rt * CH_ROW;
-      wv[m] = load_buf_stream16(wr, wave_off + rt * (int)row_bytes + 16 * within);
+      const int rt = q / CH_ROWP;
+      const int within = q - rt * CH_ROWP;
+      const int start = woff + rt * (int)row_bytes;
+      wv[m] = load_buf_stream16(wr, (start & ~15) + 16 * within);
     }
   };
 
@@ -393,36 +548,35 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_persist_kernel(
     if (XF % kThreads != 0 && f >= XF) break;  // wave-uniform
     const int sl = f >> 4, k = f & 15;
     xs4[k * SP + sl] = xv[q];
-    const float part = group_sum<8>(sum4(xv[q]));
-    if (k == 0) xsum[sl].x = part;
-    if (k == 8) xsum[sl].y = part;
+    if constexpr (!F::kUnaligned) {
+      const float part = group_sum<8>(sum4(xv[q]));
+      if (k == 0) xsum[sl].x = part;
+      if (k == 8) xsum[sl].y = part;
+    }
   }
   __syncthreads();
   const bool active = u < n_slabs;
   float4 xl[8], xh[8];
-  float2 xsm = make_float2(0.f, 0.f);
-  if (active) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      xl[k] = xs4[k * SP + u];
-      xh[k] = xs4[(k + 8) * SP + u];
-    }
-    xsm = xsum[u];
-  }
+  float4 xs = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (active) F::load_x(xs4, SP, u, j, xsum, xl, xh, xs);
   const int bl = u >> 2;
 
   auto compute = [&](int cur, const uint4 (&wv)[NM]) {
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int prev_last = r == 0 ? -1 : (r * G * CH_ROW - 1) / 64;
-      const int last_m = ((r + 1) * G * CH_ROW - 1) / 64;
+      const int prev_last = r == 0 ? -1 : (r * G * CH_ROWP - 1) / 64;
+      const int last_m = ((r + 1) * G * CH_ROWP - 1) / 64;
 #pragma unroll
       for (int m = 0; m < NM; ++m)
         if (m > prev_last && m <= last_m && 64 * m + lane < TILE) wt[wave][64 * m + lane] = wv[m];
       acc[r] = 0.0f;
-      if (active)
-        acc[r] = F::slab(&wt[wave][((r * G + g) * BPS + bl) * 9], j, sh, jhi, xl, xh, xsm, acc[r]);
+      if (active) {
+        const int rr = r * G + g;
+        int boff = rr * CH_ROWP * 16 + bl * F::kBlockBytes;
+        if constexpr (F::kUnaligned) boff += (wave_off(cur) + rr * (int)row_bytes) & 15;
+        acc[r] = F::slab(wt[wave], boff, j, sh, jhi, xl, xh, xs, acc[r]);
+      }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = group_sum<L>(acc[r]);
@@ -456,9 +610,23 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_persist_kernel(
 // per CU, the LDS limit of the 4-wave form).
 constexpr int64_t kPersistSlots = 512;
 
+// Static LDS of q4k_gemv_kernel<F, L, R, KW, W> (staged activations and
+// sums, the waves' tiles, the cross-wave partials).
+template <class F, int L, int R, int KW, int W>
+constexpr int gemv_lds_bytes() {
+  constexpr int rows_w = (64 / L) * R;
+  constexpr int ch_rowp = L / 4 * F::kBlockBytes / 16 + (F::kUnaligned ? 1 : 0);
+  return 16 * 16 * (KW * L + 1) + 8 * KW * L + 16 * W * rows_w * ch_rowp +
+         4 * (KW > 1 ? W * rows_w : 1);
+}
+constexpr int kMaxLds = 160 * 1024;
+
 template <class F, int L, int R, int KW, int W>
 hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, int nb,
                        int64_t N, hipStream_t stream) {
+  if constexpr (gemv_lds_bytes<F, L, R, KW, W>() > kMaxLds) {
+    return hipErrorInvalidConfiguration;  // the callers reject these shapes first
+  } else {
   constexpr int G = 64 / L;
   constexpr int64_t rows_per_wg = (int64_t)(W / KW) * G * R;
   const int64_t grid = (N + rows_per_wg - 1) / rows_per_wg;
@@ -477,6 +645,7 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, int nb,
   hipLaunchKernelGGL((q4k_gemv_kernel<F, L, R, KW, W>), dim3((unsigned)grid),
                      dim3(64 * W), 0, stream, x, w, y, nb, N);
   return hipGetLastError();
+  }
 }
 
 template <class F, int L, int R>
@@ -514,7 +683,7 @@ hipError_t launch_r(const GemvShape &sh, const float *x, const uint8_t *w,
 }  // namespace
 
 GemvShape choose_gemv_shape(int64_t nb, int64_t N, int rows_per_lane,
-                            int k_waves, int waves) {
+                            int k_waves, int waves, int min_lanes) {
   // Defaults measured on MI355X (graph-replayed calls over rotating
   // weights): 4-wave workgroups, 4 rows per lane while that still gives
   // every SIMD a wave, and a 2-way split of input_dim across the waves of a
@@ -523,6 +692,7 @@ GemvShape choose_gemv_shape(int64_t nb, int64_t N, int rows_per_lane,
   GemvShape s;
   const int64_t slabs = 4 * nb;
   s.lanes = slabs <= 16 ? 16 : (slabs <= 32 ? 32 : 64);
+  if (s.lanes < min_lanes) s.lanes = min_lanes;
   const int64_t steps = (slabs + s.lanes - 1) / s.lanes;
   const int64_t g = 64 / s.lanes;
   s.k_waves = k_waves > 0 ? k_waves : (steps >= 2 ? 2 : 1);
@@ -557,7 +727,11 @@ hipError_t gemv_launch_fmt(const float *x, const uint8_t *w, float *y, int64_t n
                            int64_t N, const GemvShape &s, hipStream_t stream) {
   const int nbi = (int)nb;
   switch (s.lanes) {
-    case 16: return launch_r<F, 16>(s, x, w, y, nbi, N, stream);
+    case 16:
+      // 16 lanes cover 4 blocks per step: whole 16-byte chunks for 144-byte
+      // blocks only
+      if constexpr (4 * F::kBlockBytes % 16 == 0) return launch_r<F, 16>(s, x, w, y, nbi, N, stream);
+      else return hipErrorInvalidValue;
     case 32: return launch_r<F, 32>(s, x, w, y, nbi, N, stream);
     default: return launch_r<F, 64>(s, x, w, y, nbi, N, stream);
   }
@@ -571,6 +745,11 @@ hipError_t gemv_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
 hipError_t gemv_q4_0_launch(const float *x, const uint8_t *w, float *y, int64_t ngroups,
                             int64_t N, const GemvShape &s, hipStream_t stream) {
   return gemv_launch_fmt<Q40>(x, w, y, ngroups, N, s, stream);
+}
+
+hipError_t gemv_q6k_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
+                           int64_t N, const GemvShape &s, hipStream_t stream) {
+  return gemv_launch_fmt<Q6K>(x, w, y, nb, N, s, stream);
 }
 
 }  // namespace q4k

@@ -6,7 +6,7 @@
 
 namespace q4k {
 
-// Launch shape of the vector GEMV kernel (Q4_K and Q4_0).
+// Launch shape of the vector GEMV kernel (Q4_K, Q4_0, Q6_K).
 struct GemvShape {
   int lanes = 64;         // lanes spanning the slabs of one row: 16, 32 or 64
   int rows_per_lane = 4;  // rows whose partial sums one lane carries: 1, 2, 4, 8
@@ -14,14 +14,20 @@ struct GemvShape {
   int waves = 4;          // waves per workgroup: 1, 2, 4 (a multiple of k_waves)
 };
 
+// min_lanes: 32 for Q6_K, whose 210-byte blocks make whole 16-byte chunks
+// only in groups of eight (a step of 32 lanes).
 GemvShape choose_gemv_shape(int64_t nb, int64_t N, int rows_per_lane, int k_waves,
-                            int waves);
+                            int waves, int min_lanes = 16);
 hipError_t gemv_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
                        int64_t N, const GemvShape &s, hipStream_t stream);
 // The same kernels on Q4_0 rows: ngroups = input_dim/256 groups of eight
 // 18-byte blocks per row.
 hipError_t gemv_q4_0_launch(const float *x, const uint8_t *w, float *y, int64_t ngroups,
                             int64_t N, const GemvShape &s, hipStream_t stream);
+// The same kernels on Q6_K rows of nb 210-byte blocks (rows need not start
+// 16-byte aligned; w must).
+hipError_t gemv_q6k_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
+                           int64_t N, const GemvShape &s, hipStream_t stream);
 
 // Q4_K GEMV with the multiplies on the matrix cores (16 rows per workgroup).
 hipError_t gemv_mfma_launch(const float *x, const uint8_t *w, float *y, int64_t nb,

@@ -120,6 +120,25 @@ def test_q4_0_rejects_null_misaligned_and_bad_shape(lib):
         assert lib.q4_0_gemv_shaped(GOOD, GOOD2, 256, 8, GOOD3, None, rpl, kw, wg) == -1
 
 
+@pytest.mark.parametrize("K", [32, 255, 257, 4000, 0, -256, 1 << 31, (1 << 24) + 256])
+def test_q6k_rejects_bad_input_dim(lib, K):
+    assert lib.q6k_gemv(GOOD, GOOD2, K, 16, GOOD3, None) == -1
+    assert lib.q6k_gemv_shaped(GOOD, GOOD2, K, 16, GOOD3, None, 0, 0, 0) == -1
+
+
+def test_q6k_rejects_null_misaligned_and_bad_shape(lib):
+    assert lib.q6k_gemv(GOOD, GOOD2, 256, 0, GOOD3, None) == -1
+    assert lib.q6k_gemv(None, GOOD2, 256, 8, GOOD3, None) == -2
+    assert lib.q6k_gemv(GOOD, None, 256, 8, GOOD3, None) == -2
+    assert lib.q6k_gemv(GOOD, GOOD2, 256, 8, None, None) == -2
+    assert lib.q6k_gemv(ODD, GOOD2, 256, 8, GOOD3, None) == -3
+    assert lib.q6k_gemv(GOOD, ODD, 256, 8, GOOD3, None) == -3
+    for rpl, kw, wg in [(3, 0, 0), (1, 8, 0), (8, 1, 8), (0, 0, 16)]:
+        assert lib.q6k_gemv_shaped(GOOD, GOOD2, 256, 8, GOOD3, None, rpl, kw, wg) == -1
+    # 64 lanes (input_dim > 2048), 8 rows per lane, a 4-way split: LDS too small
+    assert lib.q6k_gemv_shaped(GOOD, GOOD2, 4096, 8, GOOD3, None, 8, 4, 4) == -1
+
+
 @pytest.mark.parametrize("K", [3, 5, 4098, 0, -4])
 def test_ternary_rejects_bad_input_dim(lib, K):
     assert lib.ternary_gemv_codes(GOOD, GOOD2, K, 8, GOOD3, None) == -1
