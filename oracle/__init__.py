@@ -65,6 +65,8 @@ def _load():
     lib.oracle_ternary_gemv_codes.restype = ctypes.c_int
     lib.oracle_ternary_gemv.argtypes = [P, P, ctypes.c_float, I64, I64, P]
     lib.oracle_ternary_gemv.restype = ctypes.c_int
+    lib.oracle_ternary_matmul.argtypes = [P, P, ctypes.c_float, I64, I64, I64, P]
+    lib.oracle_ternary_matmul.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -216,3 +218,12 @@ def ternary_gemv(x, codes, scale, input_dim, output_dim):
     _check(_load().oracle_ternary_gemv(_ptr(xx), _ptr(cc), float(scale),
                                        input_dim, output_dim, _ptr(y)))
     return y
+
+
+def ternary_matmul(X, codes, scale, n_tokens, input_dim, output_dim):
+    """Y[r] = scale * codes-dot(X[r]) for each token row, float64 [M, N]."""
+    XX, cc = _f32(X), _u8(codes)
+    Y = np.empty((max(int(n_tokens), 0), max(int(output_dim), 0)), np.float64)
+    _check(_load().oracle_ternary_matmul(_ptr(XX), _ptr(cc), np.float32(scale), n_tokens,
+                                         input_dim, output_dim, _ptr(Y)))
+    return Y

@@ -383,6 +383,12 @@ int oracle_ternary_gemv_codes(const float *x, const uint8_t *codes, int64_t K,
     return ORACLE_OK;
 }
 
+/* Batched ternary product, the row loop of the ternary page's prefill path
+ * (section "Tasks"): Y[r, :] = scale * t(X[r, :]) for each token row r, row
+ * r of X at r*K and of Y at r*N. */
+int oracle_ternary_matmul(const float *X, const uint8_t *codes, float scale,
+                          int64_t M, int64_t K, int64_t N, double *Y);
+
 /* y[o] = scale * t[o]: the per-tensor scale is multiplied after the dot. */
 int oracle_ternary_gemv(const float *x, const uint8_t *codes, float scale,
                         int64_t K, int64_t N, double *y)
@@ -392,5 +398,21 @@ int oracle_ternary_gemv(const float *x, const uint8_t *codes, float scale,
         return rc;
     for (int64_t o = 0; o < N; ++o)
         y[o] = (double)scale * y[o];
+    return ORACLE_OK;
+}
+
+int oracle_ternary_matmul(const float *X, const uint8_t *codes, float scale,
+                          int64_t M, int64_t K, int64_t N, double *Y)
+{
+    if (M <= 0)
+        return ORACLE_EINVAL_DIM;
+    int rc = check_ternary(X, codes, Y, K, N);
+    if (rc)
+        return rc;
+    for (int64_t r = 0; r < M; ++r) {
+        rc = oracle_ternary_gemv(X + r * K, codes, scale, K, N, Y + r * N);
+        if (rc)
+            return rc;
+    }
     return ORACLE_OK;
 }

@@ -719,3 +719,32 @@ def test_q6k_rejects_input_dim_not_multiple_of_256(oracle_lib, K):
     with pytest.raises(oracle_lib.OracleError) as e:
         oracle_lib.q6k_gemv(np.zeros(max(K, 1), np.float32), np.zeros(210 * 2, np.uint8), K, 1)
     assert e.value.code == oracle_lib.EINVAL_DIM
+
+
+def test_ternary_matmul_integer_exact_against_int64(oracle_lib):
+    """Integer activations: every token row's codes-dot is exact, so the
+    batched product equals an int64 matrix product (field value 3 included),
+    and the scale is applied after the dot."""
+    M, K, N = 7, 1024, 24
+    codes, u = synth.ternary_codes(N, K, config=79, allow_code3=True)
+    X = synth.integer_activations(K, lo=-8, hi=8, n_tokens=M, config=79)
+    T = oracle_lib.ternary_matmul(X, codes, 1.0, M, K, N)
+    assert np.array_equal(T, (X.astype(np.int64) @ (u.astype(np.int64) - 1).T).astype(np.float64))
+    scale = synth.ternary_scale(config=79)
+    Y = oracle_lib.ternary_matmul(X, codes, scale, M, K, N)
+    assert np.array_equal(Y, np.float64(scale) * T)
+
+
+def test_ternary_matmul_random_close_to_float64_product(oracle_lib):
+    M, K, N = 5, 512, 16
+    codes, u = synth.ternary_codes(N, K, config=78)
+    X = synth.activations(K, n_tokens=M, config=78)
+    T = oracle_lib.ternary_matmul(X, codes, 1.0, M, K, N)
+    assert_parity(T, X.astype(np.float64) @ (u.astype(np.float64) - 1.0).T, rel=1e-12, rowwise=True)
+
+
+@pytest.mark.parametrize("M", [0, -2])
+def test_ternary_matmul_rejects_bad_tokens(oracle_lib, M):
+    with pytest.raises(oracle_lib.OracleError) as e:
+        oracle_lib.ternary_matmul(np.zeros((1, 64), np.float32), np.zeros(16, np.uint8), 1.0, M, 64, 1)
+    assert e.value.code == oracle_lib.EINVAL_DIM
