@@ -25,6 +25,7 @@ Other workloads (measurement of the sibling paths, same JSON shape):
       follow-up format, the same 9.4 MB of weights per call as c2)
   q6k Q6_K GEMV 4096 x 4096, batch 1 (43 rotating copies of 13.8 MB; the
       page's other follow-up format)
+  t64 ternary prefill 64 tokens x 4096 -> 4096 (128 rotating code copies)
   copy  plain 64 MiB device-to-device copy kernel (4 rotating buffer pairs):
       the kernel of known traffic used to scale hardware byte counters
 """
@@ -58,6 +59,8 @@ PREFILL_SRC = ["q4_packed_weight_amd/csrc/q4k_prefill.hip",
                "q4_packed_weight_amd/csrc/device_common.h"]
 TERNARY_SRC = ["q4_packed_weight_amd/csrc/ternary_gemv.hip",
                "q4_packed_weight_amd/csrc/device_common.h"]
+TERNARY_MM_SRC = ["q4_packed_weight_amd/csrc/ternary_matmul.hip",
+                  "q4_packed_weight_amd/csrc/device_common.h"]
 
 
 class Workload:
@@ -222,6 +225,30 @@ def make_workload(name, torch, binding, synth):
             x0 = wl.x.cpu().numpy()
             return (lambda: oracle.q6k_gemv(x0, w0, K, N)), 1.0, f"oracle q6k_gemv {K}x{N}, full call"
         wl.cpu = cpu
+    elif name == "t64":
+        M, K, N = 64, 4096, 4096
+        cbytes = N * K // 4
+        copies = -(-ROTATION_BYTES // cbytes)
+        wl.C = [to_dev(synth.ternary_codes(N, K, copy=c)[0]) for c in range(copies)]
+        wl.X = to_dev(synth.activations(K, n_tokens=M, config=synth.C5_TERNARY))
+        wl.scale = float(synth.ternary_scale())
+        wl.Y = torch.empty(M, N, dtype=torch.float32, device=dev)
+        wl.call = lambda i: binding.ternary_matmul(wl.X, wl.C[i % copies], wl.scale, M, K, N, wl.Y)
+        wl.copies = copies
+        wl.bytes = cbytes + 4 * M * K + 4 * M * N
+        wl.flops = 2 * M * K * N
+        wl.kernel = "ternary_matmul_kernel"
+        wl.src_files = TERNARY_MM_SRC
+        wl.data = "synthetic (seeded numpy generators; random ternary codes, N(0,1) activations)"
+        wl.config = {"workload": "ternary_matmul prefill 64 tokens x 4096 -> 4096",
+                     "tokens": M, "input_dim": K, "output_dim": N, "rotating_copies": copies}
+        wl.metric = "Ternary prefill matmul us/call + achieved TFLOP/s (% fp16 MFMA peak), 64x4096x4096"
+
+        def cpu(oracle):
+            c0, X0 = wl.C[0].cpu().numpy(), wl.X.cpu().numpy()
+            return (lambda: oracle.ternary_matmul(X0[:2], c0, wl.scale, 2, K, N)), M / 2, \
+                "oracle ternary_matmul on 2 of 64 token rows, scaled x32 to a call"
+        wl.cpu = cpu
     elif name == "copy":
         nbytes = 64 * 2 ** 20
         copies = 4
@@ -349,7 +376,8 @@ TRAFFIC_FILES = {"c2": "q4k_gemv_4096x4096_b1.traffic.json",
                  "c4": "q4k_prefill_64x4096x4096.traffic.json",
                  "c5": "ternary_gemv_4096x4096_b1.traffic.json",
                  "q40": "q4_0_gemv_4096x4096_b1.traffic.json",
-                 "q6k": "q6k_gemv_4096x4096_b1.traffic.json"}
+                 "q6k": "q6k_gemv_4096x4096_b1.traffic.json",
+                 "t64": "ternary_matmul_64x4096x4096.traffic.json"}
 
 
 def traffic_for(wl):
@@ -372,7 +400,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64000)
     ap.add_argument("--warmup", type=int, default=6400)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "q40", "q6k", "copy"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "q40", "q6k", "t64", "copy"])
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -413,7 +441,7 @@ def main():
     print(f"[bench] {us:.3f} us/step", file=sys.stderr, flush=True)
 
     gbps = wl.bytes / us / 1e3
-    if wl.name == "c4":
+    if wl.name in ("c4", "t64"):
         tflops = wl.flops / us / 1e6
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),

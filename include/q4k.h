@@ -219,6 +219,28 @@ int ternary_gemv(const float *x, const uint8_t *codes, float scale,
                  void *stream);
 
 /*
+ * ternary_matmul -- Y[r, o] = scale * sum_i code(o,i) * X[r,i] for r <
+ * n_tokens: the batched (prefill) ternary product, the row loop of the
+ * ternary page's prefill path (SKaiNET issue #1138, section "Tasks"), with
+ * each code read once for a tile of 16 tokens.
+ *   X          fp32 [n_tokens, input_dim] (row r at X + r*input_dim)
+ *   codes      as for ternary_gemv_codes
+ *   scale      per-tensor scale, multiplied after each dot
+ *   n_tokens   M > 0 (M == 1 runs ternary_gemv), else Q4K_EINVAL_DIM
+ *   input_dim, output_dim as for ternary_gemv_codes
+ *   Y          fp32 [n_tokens, output_dim] (row r at Y + r*output_dim)
+ * With input_dim % 64 == 0, 16-byte aligned X and codes, and more than 2
+ * tokens (more than 4 when input_dim > 8192) the products run
+ * on 16x16x32 f16 MFMA tiles: the codes enter exactly, and X, after each
+ * token's 256-position block is scaled by a power of two, as exact fp16 hi
+ * and lo halves (any |X| < 2^96); the sum is fp32 (tolerance as q4k_gemv;
+ * exact for integer X with sum_i |X[r,i]| * 3 < 2^22).  Otherwise it runs
+ * one ternary_gemv launch per token row.  Y must not alias X or the codes.
+ */
+int ternary_matmul(const float *X, const uint8_t *codes, float scale, int64_t n_tokens,
+                   int64_t input_dim, int64_t output_dim, float *Y, void *stream);
+
+/*
  * q4k_gemv_shaped -- q4k_gemv with an explicit launch shape, for sweeps and
  * for the benchmark's launch configuration.  rows_per_lane in {1, 2, 4, 8}
  * (rows whose partial sums one lane carries), k_waves in {1, 2, 4} (waves

@@ -20,7 +20,7 @@ Q4K_EALIGN = -3
 Q4K_EHIP = -4
 
 EXPORTED = (
-    "q4k_gemv", "q4k_matmul", "ternary_gemv_codes", "ternary_gemv",
+    "q4k_gemv", "q4k_matmul", "ternary_gemv_codes", "ternary_gemv", "ternary_matmul",
     "q4k_gemv_shaped", "q4_0_gemv", "q4_0_gemv_shaped", "q6k_gemv", "q6k_gemv_shaped",
     "q4k_strerror",
     "q4k_bench_empty", "q4k_bench_stream_read", "q4k_bench_copy",
@@ -53,6 +53,7 @@ def lib():
         "q4k_matmul": [P, P, I64, I64, I64, P, P],
         "ternary_gemv_codes": [P, P, I64, I64, P, P],
         "ternary_gemv": [P, P, F, I64, I64, P, P],
+        "ternary_matmul": [P, P, F, I64, I64, I64, P, P],
         "q4k_gemv_shaped": [P, P, I64, I64, P, P, I, I, I],
         "q4_0_gemv": [P, P, I64, I64, P, P],
         "q4_0_gemv_shaped": [P, P, I64, I64, P, P, I, I, I],
@@ -221,6 +222,17 @@ def ternary_gemv(x, codes, scale, input_dim, output_dim, y, stream=None):
     _check(lib().ternary_gemv(_ptr(x), _ptr(codes), float(scale), int(input_dim),
                               int(output_dim), _ptr(y), _stream(stream)), "ternary_gemv")
     return y
+
+
+def ternary_matmul(X, codes, scale, n_tokens, input_dim, output_dim, Y, stream=None):
+    M, K, N = int(n_tokens), int(input_dim), int(output_dim)
+    ok = M > 0 and _ternary_need(K, N) > 0
+    _expect(X, torch.float32, "X", M * K if ok else 0)
+    _expect(codes, torch.uint8, "codes", _ternary_need(K, N))
+    _expect(Y, torch.float32, "Y", M * N if ok else 0)
+    _check(lib().ternary_matmul(_ptr(X), _ptr(codes), float(scale), M, K, N, _ptr(Y),
+                                _stream(stream)), "ternary_matmul")
+    return Y
 
 
 def bench_empty(stream=None):

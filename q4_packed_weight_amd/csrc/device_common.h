@@ -73,6 +73,34 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Maximum over the 64 lanes of a wave (every lane receives it).
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max<8>(v);
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+      __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)));  // row_mirror
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// Maximum of a non-negative value over the 64 lanes of a wave, as a
+// wave-uniform value: DPP within each row of 16 lanes, then the four row
+// results through scalar registers (for non-negative floats, NaN included,
+// the integer order of the bit patterns is the float order).  No LDS
+// round trip, unlike wave_max.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  v = group_max<8>(v);
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+      __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)));  // row_mirror
+  const int b = __builtin_bit_cast(int, v);
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readlane(b, 0);
+  const uint32_t m1 = (uint32_t)__builtin_amdgcn_readlane(b, 16);
+  const uint32_t m2 = (uint32_t)__builtin_amdgcn_readlane(b, 32);
+  const uint32_t m3 = (uint32_t)__builtin_amdgcn_readlane(b, 48);
+  const uint32_t m01 = m0 > m1 ? m0 : m1, m23 = m2 > m3 ? m2 : m3;
+  return __builtin_bit_cast(float, m01 > m23 ? m01 : m23);
+}
+
 // Sum over aligned groups of `width` lanes (width a power of two <= 64);
 // every lane of the group receives the group sum.  Steps below 16 lanes use
 // DPP quad permutes and row mirrors; the 16- and 32-lane steps use

@@ -53,16 +53,6 @@ __device__ __forceinline__ uint32_t lo_pair_b(uint32_t hi2, float x0, float x1) 
   return r;
 }
 
-// Maximum over the 64 lanes of a wave (every lane receives it).
-__device__ __forceinline__ float wave_max(float v) {
-  v = group_max<8>(v);
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-      __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)));  // row_mirror
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
-}
-
 template <int T>  // tokens of the launch: 2, 4 or 8 (rows of X past M read as zeros)
 __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
     const float *X, const uint8_t *w, float *__restrict__ Y, int M, int nb, int N) {

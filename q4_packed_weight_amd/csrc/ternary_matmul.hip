@@ -1,0 +1,247 @@
+// ternary_matmul.hip -- batched (prefill) ternary product on gfx950 MFMA.
+//
+// What it computes: the ternary page's prefill path (SKaiNET issue #1138,
+// "[ternary-f32] Phase 2: TernaryF32GemvNative SPI + reference ViewKernel +
+// TernaryF32KernelPack", section "Tasks") is a loop over token rows of the
+// codes-dot; here every weight is read once for all tokens of a tile:
+//     Y[r, o] = scale * sum_i (u(o, i) - 1) * X[r, i]
+// with u the 2-bit field of element i (byte i/4, bits 2*(i%4)).
+//
+// Work decomposition and pipeline follow the Q4_K prefill kernel: a
+// workgroup owns 64 rows (4 MFMA row tiles) and 16 tokens (one token tile)
+// over the whole of input_dim and walks it in stages of 1024 positions.
+// Every thread loads two 16-byte code chunks and eight activation float4
+// of the next stage while the current one is computed; the activations go
+// to LDS already split into exact fp16 hi + lo halves in MFMA operand order
+// (positions paired (0,2), (1,3) within each group of four), each token's
+// 256-position block first scaled by the power of two that brings its
+// largest |x| into [2^14, 2^15) (so the halves neither overflow fp16 nor
+// lose bits of lo to its subnormal range, for any |x| below 2^96).  Wave w takes
+// positions 256*(w%4) .. +255 of the stage for row tiles 2*(w/4) and
+// 2*(w/4)+1.
+//
+// Operands (16x16x32 f16 MFMA; lane (r, g) = (lane % 16, lane / 16)): the A
+// operand is 8 codes of row 16a + r, positions 8g .. 8g+7 of one 32-position
+// step: two code bytes, each spread as b | b << 12 so that masking with
+// 0x00030003 leaves fields (0,2) and, after a shift by 2, (1,3) in the two
+// halves, in the activations' operand order.  Each field u becomes the fp16
+// 1024 + u (bits 0x6400 | u), and a packed subtraction of 1025 leaves the
+// code u - 1 in {-1, 0, 1, 2}, exactly.  (Feeding the raw fields as fp16
+// subnormals u*2^-24 loses products of the lo halves on the matrix cores.)
+// The MFMA products are exact and the accumulation is fp32: one tile per
+// block, scaled back by the token's power of two into the running sum; the
+// epilogue is Y = scale * D, one writer per output.
+#include "device_common.h"
+#include "q4k_internal.h"
+
+namespace q4k {
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int TR_ROWS = 64;            // rows per workgroup (4 row tiles)
+constexpr int TR_TOK = 16;             // tokens per workgroup
+constexpr int TR_WAVES = 8;
+constexpr int TR_THREADS = 64 * TR_WAVES;
+constexpr int TR_STAGE = 1024;         // positions per stage
+constexpr int TR_CB = TR_STAGE / 4;    // code bytes of one row per stage
+// LDS pitches in dwords: a token's activation row of one 256-position block
+// (128 fp16 pairs) + 16 B; a row's codes of one stage (256 B) + 8 B.
+constexpr int XROW = 128 + 4;
+constexpr int CROW = TR_CB / 4 + 2;
+constexpr int C_PER_THREAD = TR_ROWS * TR_CB / 16 / TR_THREADS;  // 2
+constexpr int X_PER_THREAD = TR_TOK / 2;                          // 8
+static_assert(C_PER_THREAD * 16 * TR_THREADS == TR_ROWS * TR_CB, "code chunks must divide evenly");
+
+__device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// lo = fp16(x - hi) for the two halves of `hi2` (fp16 hi parts of x0, x1):
+// v_fma_mix evaluates x - hi exactly in fp32 and rounds once to fp16.
+__device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi2), "v"(x0));
+  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(r) : "v"(hi2), "v"(x1));
+  return r;
+}
+
+// The A operand from 16 bits of codes (8 fields): fields (0,2), (1,3) of the
+// low byte, then (4,6), (5,7) of the high byte, as the fp16 codes u - 1.
+__device__ __forceinline__ half8_t code_operand(uint32_t w16) {
+  const uint32_t t0 = (w16 & 0xFFu) * 0x1001u;         // b0 | b0 << 12
+  const uint32_t t1 = ((w16 >> 8) & 0xFFu) * 0x1001u;  // b1 | b1 << 12
+  uint4 v;
+  v.x = (t0 & 0x00030003u) | 0x64006400u;  // fp16 1024 + u in each half
+  v.y = ((t0 >> 2) & 0x00030003u) | 0x64006400u;
+  v.z = (t1 & 0x00030003u) | 0x64006400u;
+  v.w = ((t1 >> 2) & 0x00030003u) | 0x64006400u;
+  half8_t a = __builtin_bit_cast(half8_t, v);
+  const _Float16 off = (_Float16)1025.0f;
+  return a - half8_t{off, off, off, off, off, off, off, off};
+}
+
+__global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
+    const float *X, const uint8_t *codes, float *__restrict__ Y, float scale, int M, int K,
+    int N) {
+  // xh/xl: fp16 hi and lo activations [block of stage][token][pairs in
+  // operand order]; ct: the stage's codes [row][dword].
+  __shared__ __align__(16) uint32_t xh[4][TR_TOK][XROW];
+  __shared__ __align__(16) uint32_t xl[4][TR_TOK][XROW];
+  __shared__ __align__(16) uint32_t ct[TR_ROWS * CROW];
+  __shared__ int xe[4][TR_TOK];  // scaling exponent per (block, token) of the stage
+
+  // The host validates K >= 64; saying so lets the compiler fetch every
+  // kernel argument in one round trip.
+  __builtin_assume(K >= 64);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = tid & 255;     // thread index within its half of the workgroup
+  const int bb = wave & 3;     // 256-position block of the stage this wave computes
+  const int half = wave >> 2;  // row tiles 2*half and 2*half + 1
+  const int r = lane & 15;     // A: row within a row tile; B and D: token
+  const int g = lane >> 4;
+  const int row0 = blockIdx.x * TR_ROWS;
+  const int tok0 = blockIdx.y * TR_TOK;
+  const int row_bytes = K / 4;
+  const int n_stages = (K + TR_STAGE - 1) / TR_STAGE;
+
+  // Range-checked views: rows past N and tokens past M read as zeros;
+  // positions past K are zeroed in the load offsets below (a zero
+  // activation makes any code byte harmless).
+  const __amdgpu_buffer_rsrc_t cr =
+      make_rsrc(codes + (int64_t)row0 * row_bytes, (int64_t)(N - row0) * row_bytes);
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(X + (int64_t)tok0 * K, (int64_t)(M - tok0) * K * 4);
+
+  // code chunk q = t + 256*m + ...: row q / 16, chunk q % 16 of the row's
+  // 256 stage bytes; activations: float4 i of thread tid is token
+  // 2i + (tid >= 256), positions 4t .. 4t+3 of the stage.
+  uint4 cv[C_PER_THREAD];
+  float4 xv[X_PER_THREAD];
+  int coff[C_PER_THREAD];
+#pragma unroll
+  for (int m = 0; m < C_PER_THREAD; ++m) {
+    const int q = tid + TR_THREADS * m;
+    coff[m] = (q >> 4) * row_bytes + 16 * (q & 15);
+  }
+  const int tok_lo = tid >> 8;
+  auto load_stage = [&](int st) {
+    // positions past K (a ragged last stage) read as zeros: their offsets
+    // are moved past the end of the view, since the bytes there would be
+    // the next token's activations
+    const bool in_k = st * TR_STAGE + 4 * t < K;
+#pragma unroll
+    for (int i = 0; i < X_PER_THREAD; ++i)
+      xv[i] = load_buf_f4(xr, in_k ? 16 * t + 4 * K * (2 * i + tok_lo) : 0x7FFFFFF0, 4096 * st);
+#pragma unroll
+    for (int m = 0; m < C_PER_THREAD; ++m)
+      cv[m] = __builtin_bit_cast(uint4, load_buf_f4(cr, coff[m], TR_CB * st));
+  };
+  auto stage_to_lds = [&]() {
+    // this wave stages block xb of the tokens of parity tok_lo: the block's
+    // largest |x| is a maximum over the wave
+    const int xb = t >> 6;
+#pragma unroll
+    for (int i = 0; i < X_PER_THREAD; ++i) {
+      const float4 v0 = xv[i];
+      const float mx = wave_max_nonneg(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
+      const int e = __builtin_amdgcn_frexp_expf(mx) - 15;  // |x| * 2^-e < 2^15
+      const float4 v = make_float4(__builtin_ldexpf(v0.x, -e), __builtin_ldexpf(v0.y, -e),
+                                   __builtin_ldexpf(v0.z, -e), __builtin_ldexpf(v0.w, -e));
+      half2_t h02, h13;
+      h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
+      h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
+      const uint32_t hw02 = as_u32(h02), hw13 = as_u32(h13);
+      const int tok = 2 * i + tok_lo;
+      if (lane == 0) xe[xb][tok] = e;
+      *reinterpret_cast<uint2 *>(&xh[xb][tok][2 * lane]) = make_uint2(hw02, hw13);
+      *reinterpret_cast<uint2 *>(&xl[xb][tok][2 * lane]) =
+          make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
+    }
+#pragma unroll
+    for (int m = 0; m < C_PER_THREAD; ++m) {
+      const int q = tid + TR_THREADS * m;
+      uint32_t *dst = &ct[(q >> 4) * CROW + 4 * (q & 15)];
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(cv[m].x, cv[m].y);
+      *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(cv[m].z, cv[m].w);
+    }
+  };
+
+  floatx4 acc[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // this lane's code bytes for step s of block bb: byte 64*bb + 8*s + 2*g
+  // of its row, i.e. half (g & 1) of dword 16*bb + 2*s + g/2
+  const uint32_t hsh = 16u * (uint32_t)(g & 1);
+
+  load_stage(0);
+  for (int st = 0; st < n_stages; ++st) {
+    stage_to_lds();
+    __syncthreads();
+    if (st + 1 < n_stages) load_stage(st + 1);  // in flight during the MFMAs
+    // per row tile: the block's hi and lo products in separate accumulators
+    // (four independent MFMA chains)
+    floatx4 bh[2], bl[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) bh[a] = bl[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const half8_t Bh = *reinterpret_cast<const half8_t *>(&xh[bb][r][16 * s + 4 * g]);
+      const half8_t Bl = *reinterpret_cast<const half8_t *>(&xl[bb][r][16 * s + 4 * g]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int row = 16 * (2 * half + a) + r;
+        const uint32_t w = ct[row * CROW + 16 * bb + 2 * s + (g >> 1)] >> hsh;
+        const half8_t A = code_operand(w);
+        bh[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, bh[a], 0, 0, 0);
+        bl[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, bl[a], 0, 0, 0);
+      }
+    }
+    // undo the scaling of token r's block (the D column of this lane)
+    const int e = xe[bb][r];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[a][k] += __builtin_ldexpf(bh[a][k] + bl[a][k], e);
+    __syncthreads();  // the next stage overwrites the LDS tiles
+  }
+
+  // Add the four blocks' partial tiles (through the activation tiles, no
+  // longer needed); lane (token r, group g) holds rows 16 rt + 4g + e.
+  float4 *red = reinterpret_cast<float4 *>(&xh[0][0][0]);  // [block][token][17]
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+    red[(bb * TR_TOK + r) * 17 + 4 * (2 * half + a) + g] =
+        make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
+  __syncthreads();
+  const float *redf = reinterpret_cast<const float *>(red);
+  for (int o = tid; o < TR_TOK * TR_ROWS; o += TR_THREADS) {
+    const int tok = o / TR_ROWS, rr = o % TR_ROWS;
+    float v = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v += redf[(b * TR_TOK + tok) * 68 + rr];
+    if (tok0 + tok < M && row0 + rr < N) Y[(int64_t)(tok0 + tok) * N + row0 + rr] = scale * v;
+  }
+}
+
+}  // namespace
+
+hipError_t ternary_matmul_launch(const float *X, const uint8_t *codes, float scale, int64_t M,
+                                 int64_t K, int64_t N, float *Y, hipStream_t stream) {
+  // Offsets formed in the kernel (64 rows of codes, 16 rows of X, plus one
+  // stage) must stay below 2^31 bytes; K must be whole 16-byte code chunks.
+  if (K % 64 != 0 || (int64_t)TR_ROWS * (K / 4) + 4096 >= ((int64_t)1 << 31) ||
+      ((int64_t)TR_TOK * K + 4096) * 4 >= ((int64_t)1 << 31) || N > 0x7FFFFFFF ||
+      M > 0x7FFFFFFF)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((N + TR_ROWS - 1) / TR_ROWS), (unsigned)((M + TR_TOK - 1) / TR_TOK));
+  if (grid.y > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(ternary_matmul_kernel, grid, dim3(TR_THREADS), 0, stream, X, codes, Y,
+                     scale, (int)M, (int)K, (int)N);
+  return hipGetLastError();
+}
+
+}  // namespace q4k

@@ -139,6 +139,17 @@ def test_q6k_rejects_null_misaligned_and_bad_shape(lib):
     assert lib.q6k_gemv_shaped(GOOD, GOOD2, 4096, 8, GOOD3, None, 8, 4, 4) == -1
 
 
+def test_ternary_matmul_rejects_bad_args(lib):
+    F = ctypes.c_float
+    assert lib.ternary_matmul(GOOD, GOOD2, F(1.0), 0, 64, 8, GOOD3, None) == -1
+    assert lib.ternary_matmul(GOOD, GOOD2, F(1.0), -2, 64, 8, GOOD3, None) == -1
+    assert lib.ternary_matmul(GOOD, GOOD2, F(1.0), 3, 66, 8, GOOD3, None) == -1
+    assert lib.ternary_matmul(GOOD, GOOD2, F(1.0), 3, 64, 0, GOOD3, None) == -1
+    assert lib.ternary_matmul(None, GOOD2, F(1.0), 3, 64, 8, GOOD3, None) == -2
+    assert lib.ternary_matmul(GOOD, None, F(1.0), 3, 64, 8, GOOD3, None) == -2
+    assert lib.ternary_matmul(GOOD, GOOD2, F(1.0), 3, 64, 8, None, None) == -2
+
+
 @pytest.mark.parametrize("K", [3, 5, 4098, 0, -4])
 def test_ternary_rejects_bad_input_dim(lib, K):
     assert lib.ternary_gemv_codes(GOOD, GOOD2, K, 8, GOOD3, None) == -1
