@@ -59,6 +59,8 @@ def _load():
     lib.oracle_q6k_dequant_block.restype = None
     lib.oracle_q6k_gemv.argtypes = [P, P, I64, I64, P]
     lib.oracle_q6k_gemv.restype = ctypes.c_int
+    lib.oracle_q4k_relayout_tiled.argtypes = [P, I64, I64, P]
+    lib.oracle_q4k_relayout_tiled.restype = ctypes.c_int
     lib.oracle_ternary_decode_byte.argtypes = [ctypes.c_uint8, P]
     lib.oracle_ternary_decode_byte.restype = None
     lib.oracle_ternary_gemv_codes.argtypes = [P, P, I64, I64, P]
@@ -158,6 +160,21 @@ def q4k_matmul_part(X, w_blocks, n_tokens, input_dim, output_dim, tokens,
         _ptr(xx), _ptr(ww), n_tokens, input_dim, output_dim, tokens[0],
         tokens[1], rows[0], rows[1], _ptr(Y)))
     return Y
+
+
+def q4k_tiled_size(input_dim, output_dim):
+    """Bytes of a Q4_K matrix in the tiled block order (row groups of 16)."""
+    return ((int(output_dim) + 15) // 16) * (int(input_dim) // 256) * 2304
+
+
+def q4k_relayout_tiled(w_blocks, input_dim, output_dim):
+    """The canonical Q4_K matrix moved into the tiled block order (uint8)."""
+    ww = _u8(w_blocks)
+    size = max(q4k_tiled_size(input_dim, output_dim), 0) if output_dim > 0 else 0
+    out = np.zeros(max(size, 1), np.uint8)
+    _check(_load().oracle_q4k_relayout_tiled(_ptr(ww), input_dim, output_dim,
+                                             _ptr(out)))
+    return out[:size]
 
 
 def q4_0_dequant_block(block):

@@ -16,6 +16,10 @@
  *          algorithm on a simpler block of 32 weights in 18 bytes, and Q6_K,
  *          whose ql + qh layout packs four codes' high bits per qh byte in
  *          two interleaved halves.
+ *   [EAG]  SKaiNET docs, "Eager execution: backends and kernels" -- packed
+ *          weights reach a kernel by declaring their block order, and a
+ *          canonical weight is relayouted into that order once, not per
+ *          call.
  *   [TRN]  SKaiNET issue #1138, "[ternary-f32] Phase 2: TernaryF32GemvNative
  *          SPI + reference ViewKernel + TernaryF32KernelPack" -- section
  *          "Tasks" (the gemvPacked contract, the decode formula, the
@@ -41,6 +45,10 @@
  *     low (c < 2) or high (c >= 2) nibble of ql[64n + 32(c & 1) + l] and hi
  *     bits 2c..2c+1 of qh[32n + l]; its sub-block of 16 is 8n + 2c + l/16
  *     and weight = d * scale[sub-block] * (q - 32).
+ *   - the tiled block order (see oracle_q4k_relayout_tiled) is this
+ *     library's own GPU block order: the docs page fixes only that a
+ *     packed weight declares its block order and that a canonical weight is
+ *     relayouted into it once.
  *   - ternary element i of a row is bits 2*(i%4)..2*(i%4)+1 of byte i/4;
  *     code 3 decodes to +2 by the formula (never generated).
  *
@@ -248,6 +256,50 @@ int oracle_q4k_matmul_part(const float *X, const uint8_t *w, int64_t M,
                     acc += (double)wt[p] * (double)xb[p];
             }
             Y[r * N + o] = acc;
+        }
+    }
+    return ORACLE_OK;
+}
+
+#define TILE_ROWS 16     /* rows per row group of the tiled order */
+#define TILE_BYTES 2304  /* 16 rows x 144 bytes */
+
+/* [EAG]: the one-time relayout of a canonical Q4_K matrix into the tiled
+ * block order.  The same bytes are moved, none is changed:
+ *   - rows are taken in groups of 16 (group G holds rows 16G .. 16G+15;
+ *     rows at or past N are zero bytes), and super-block b of group G is one
+ *     2304-byte tile at byte (G*nb + b)*2304, nb = K/256;
+ *   - tile bytes 0..2047 hold the qs bytes of the 16 rows in two halves of
+ *     1024: qs byte 32j + 8g + t (sub-block pair j < 4, g < 4, t < 8) of row
+ *     16G + n goes to byte 1024*(j/2) + 16*(n + 16g) + 8*(j%2) + t;
+ *   - tile bytes 2048..2303 hold the 16 block headers (bytes 0..15: d,
+ *     dmin, the 12 scale bytes) of rows 16G .. 16G+15, in row order.
+ * The walk below is the plain one: every tile, every row, every byte. */
+int oracle_q4k_relayout_tiled(const uint8_t *w, int64_t K, int64_t N,
+                              uint8_t *out)
+{
+    if (K <= 0 || N <= 0 || K % QK != 0)
+        return ORACLE_EINVAL_DIM;
+    if (!w || !out)
+        return ORACLE_ENULL;
+    int64_t nb = K / QK;
+    int64_t ng = (N + TILE_ROWS - 1) / TILE_ROWS;
+    for (int64_t G = 0; G < ng; ++G) {
+        for (int64_t b = 0; b < nb; ++b) {
+            uint8_t *tile = out + (G * nb + b) * TILE_BYTES;
+            for (int n = 0; n < TILE_ROWS; ++n) {
+                int64_t row = TILE_ROWS * G + n;
+                const uint8_t *blk =
+                    row < N ? w + (row * nb + b) * BLOCK_BYTES : NULL;
+                for (int c = 0; c < 16; ++c)
+                    tile[2048 + 16 * n + c] = blk ? blk[c] : 0;
+                for (int j = 0; j < 4; ++j)
+                    for (int g = 0; g < 4; ++g)
+                        for (int t = 0; t < 8; ++t)
+                            tile[1024 * (j / 2) + 16 * (n + 16 * g) +
+                                 8 * (j % 2) + t] =
+                                blk ? blk[16 + 32 * j + 8 * g + t] : 0;
+            }
         }
     }
     return ORACLE_OK;

@@ -748,3 +748,94 @@ def test_ternary_matmul_rejects_bad_tokens(oracle_lib, M):
     with pytest.raises(oracle_lib.OracleError) as e:
         oracle_lib.ternary_matmul(np.zeros((1, 64), np.float32), np.zeros(16, np.uint8), 1.0, M, 64, 1)
     assert e.value.code == oracle_lib.EINVAL_DIM
+
+
+# ---------------------------------------------------------------------------
+# The tiled block order (SKaiNET docs, "Eager execution: backends and
+# kernels": a packed weight declares its block order and a canonical weight
+# is relayouted into it once).  The order is this library's own; these pins
+# fix that the oracle's relayout is lossless and puts each weight where the
+# order's definition says, using test-side addressing that runs the other
+# way (from a weight's canonical position to its tiled byte).
+
+def _tiled_offset_of_qs(o, b, q, nb):
+    """Tiled byte of qs byte q (0..127) of block b of row o."""
+    G, n = divmod(o, 16)
+    j, l = divmod(q, 32)
+    g, t = divmod(l, 8)
+    return (G * nb + b) * 2304 + 1024 * (j // 2) + 16 * (n + 16 * g) + 8 * (j % 2) + t
+
+
+def _tiled_offset_of_header(o, b, c, nb):
+    G, n = divmod(o, 16)
+    return (G * nb + b) * 2304 + 2048 + 16 * n + c
+
+
+@pytest.mark.parametrize("K,N", [(256, 1), (512, 17), (768, 33), (1024, 16), (256, 47)])
+def test_tiled_relayout_moves_every_byte_exactly_once(oracle_lib, K, N):
+    """Tag each canonical byte with its index + 1 (three byte planes): every
+    index lands exactly once, and the only other bytes are the zero rows
+    that pad the last group of 16."""
+    nb = K // 256
+    n_bytes = N * nb * 144
+    tag = np.arange(1, n_bytes + 1, dtype=np.int64)
+    src = np.zeros(oracle_lib.q4k_tiled_size(K, N), np.int64)
+    for plane in range(3):
+        wb = ((tag >> (8 * plane)) & 0xFF).astype(np.uint8)
+        src |= oracle_lib.q4k_relayout_tiled(wb, K, N).astype(np.int64) << (8 * plane)
+    placed = src[src > 0] - 1
+    assert np.array_equal(np.sort(placed), np.arange(n_bytes))
+    n_pad = ((N + 15) // 16 * 16 - N) * nb * 144
+    assert np.count_nonzero(src == 0) == n_pad
+
+
+@pytest.mark.parametrize("K,N", [(256, 16), (1024, 37), (2304, 5)])
+def test_tiled_relayout_inverse_addressing_round_trip(oracle_lib, K, N):
+    nb = K // 256
+    w = synth.q4k_weights(N, K, copy=91 + N)
+    t = oracle_lib.q4k_relayout_tiled(w, K, N)
+    back = np.empty_like(w).reshape(N, nb, 144)
+    for o in range(N):
+        for b in range(nb):
+            for c in range(16):
+                back[o, b, c] = t[_tiled_offset_of_header(o, b, c, nb)]
+            for q in range(128):
+                back[o, b, 16 + q] = t[_tiled_offset_of_qs(o, b, q, nb)]
+    assert np.array_equal(back.reshape(N, -1), w)
+    # the padding rows of the last group are zero bytes
+    for o in range(N, (N + 15) // 16 * 16):
+        for b in range(nb):
+            assert all(t[_tiled_offset_of_header(o, b, c, nb)] == 0 for c in range(16))
+            assert all(t[_tiled_offset_of_qs(o, b, q, nb)] == 0 for q in range(128))
+
+
+def test_tiled_weights_read_back_per_position(oracle_lib):
+    """Weight k of row o read straight from the tiled bytes (its nibble from
+    the qs half/lane/pair position, its d, dmin and scales from the row's
+    header slot) equals the oracle's dequantization of the canonical block,
+    at every position."""
+    K, N = 512, 19
+    nb = K // 256
+    w = synth.q4k_weights(N, K, copy=93)
+    t = oracle_lib.q4k_relayout_tiled(w, K, N)
+    for o in range(N):
+        for b in range(nb):
+            hdr = np.array([t[_tiled_offset_of_header(o, b, c, nb)] for c in range(16)], np.uint8)
+            d = np.frombuffer(hdr[0:2].tobytes(), np.float16)[0].astype(np.float32)
+            dmin = np.frombuffer(hdr[2:4].tobytes(), np.float16)[0].astype(np.float32)
+            sc, m = unpack_scales_table(hdr[4:16])
+            ref = oracle_lib.q4k_dequant_block(w[o, b * 144:(b + 1) * 144])
+            for k in range(256):
+                s, l = divmod(k, 32)
+                byte = int(t[_tiled_offset_of_qs(o, b, 32 * (s // 2) + l, nb)])
+                q = byte >> 4 if s % 2 else byte & 15
+                got = np.float32(np.float32(d * np.float32(sc[s])) * np.float32(q)) - \
+                    np.float32(dmin * np.float32(m[s]))
+                assert got == ref[k], (o, b, k)
+
+
+@pytest.mark.parametrize("K,N", [(255, 1), (0, 1), (256, 0), (256, -3)])
+def test_tiled_relayout_rejects_bad_dims(oracle_lib, K, N):
+    with pytest.raises(oracle_lib.OracleError) as e:
+        oracle_lib.q4k_relayout_tiled(np.zeros(144, np.uint8), K, N)
+    assert e.value.code == oracle_lib.EINVAL_DIM
