@@ -26,6 +26,9 @@ Other workloads (measurement of the sibling paths, same JSON shape):
   q6k Q6_K GEMV 4096 x 4096, batch 1 (43 rotating copies of 13.8 MB; the
       page's other follow-up format)
   t64 ternary prefill 64 tokens x 4096 -> 4096 (128 rotating code copies)
+  c2t c2 with the weights relayouted once (before timing) into the tiled
+      block order and multiplied by q4k_gemv_tiled
+  c3t c3 with both matrices in the tiled block order
   copy  plain 64 MiB device-to-device copy kernel (4 rotating buffer pairs):
       the kernel of known traffic used to scale hardware byte counters
 """
@@ -59,6 +62,8 @@ PREFILL_SRC = ["q4_packed_weight_amd/csrc/q4k_prefill.hip",
                "q4_packed_weight_amd/csrc/device_common.h"]
 TERNARY_SRC = ["q4_packed_weight_amd/csrc/ternary_gemv.hip",
                "q4_packed_weight_amd/csrc/device_common.h"]
+TILED_SRC = ["q4_packed_weight_amd/csrc/q4k_tiled.hip",
+             "q4_packed_weight_amd/csrc/device_common.h"]
 TERNARY_MM_SRC = ["q4_packed_weight_amd/csrc/ternary_matmul.hip",
                   "q4_packed_weight_amd/csrc/device_common.h"]
 
@@ -249,6 +254,64 @@ def make_workload(name, torch, binding, synth):
             return (lambda: oracle.ternary_matmul(X0[:2], c0, wl.scale, 2, K, N)), M / 2, \
                 "oracle ternary_matmul on 2 of 64 token rows, scaled x32 to a call"
         wl.cpu = cpu
+    elif name in ("c2t", "c3t"):
+        # the canonical matrices of c2 / c3, each relayouted once into the
+        # tiled block order (outside the timed region: a load-time step)
+        mats = ([(4096, 4096, synth.C2_Q4K_4K, 0)] if name == "c2t" else
+                [(4096, 14336, synth.C3_FFN, 0), (14336, 4096, synth.C3_FFN, 1)])
+        per = sum(N * K // 256 * 144 for K, N, _, _ in mats)
+        copies = 64 if name == "c2t" else -(-ROTATION_BYTES // per)
+        wl.T = [[] for _ in mats]
+        relayout_ms = []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for m, (K, N, cfg, extra) in enumerate(mats):
+            for c in range(copies):
+                w = to_dev(synth.q4k_weights(N, K, config=cfg, copy=c, extra=extra))
+                t = torch.empty(binding.q4k_tiled_size(K, N), dtype=torch.uint8, device=dev)
+                e0.record()
+                binding.q4k_relayout_tiled(w, K, N, t)
+                e1.record()
+                torch.cuda.synchronize()
+                relayout_ms.append((m, e0.elapsed_time(e1)))
+                wl.T[m].append(t)
+                del w
+        wl.xs = [to_dev(synth.activations(K, config=cfg, extra=extra)) for K, _, cfg, extra in mats]
+        wl.ys = [torch.empty(N, dtype=torch.float32, device=dev) for _, N, _, _ in mats]
+
+        def call(i):
+            for m, (K, N, _, _) in enumerate(mats):
+                binding.q4k_gemv_tiled(wl.xs[m], wl.T[m][i % copies], K, N, wl.ys[m])
+        wl.call = call
+        wl.copies = copies
+        wl.W = wl.T[0] if name == "c2t" else None
+        wl.bytes = sum(N * K // 256 * 144 + 4 * (K + N) for K, N, _, _ in mats)
+        wl.flops = sum(2 * K * N for K, N, _, _ in mats)
+        wl.kernel = "q4k_gemv_tiled_kernel"
+        wl.src_files = TILED_SRC
+        relayout_us = []
+        for m in range(len(mats)):
+            ts = sorted(t for mm, t in relayout_ms if mm == m)
+            relayout_us.append(round(1000 * ts[len(ts) // 2], 1))  # median, one call each
+        if name == "c2t":
+            wl.config = {"workload": "q4k_gemv_tiled 4096x4096 batch 1 (tiled block order)",
+                         "input_dim": 4096, "output_dim": 4096, "batch": 1,
+                         "rotating_copies": copies, "weight_bytes_per_copy": per,
+                         "relayout_us_once_per_matrix": relayout_us[0]}
+            wl.metric = "Q4_K GEMV (tiled block order) us/call + achieved HBM GB/s (% peak) at 4096x4096, batch 1"
+        else:
+            wl.config = {"workload": "q4k_gemv_tiled FFN pair 4096->14336 + 14336->4096 batch 1 "
+                                     "(tiled block order)", "rotating_pairs": copies,
+                         "relayout_us_once_per_matrix": relayout_us}
+            wl.metric = "Q4_K FFN GEMV pair (tiled block order) us/pair + achieved HBM GB/s (% peak), batch 1"
+        wl.data = "synthetic (seeded numpy generators; random Q4_K blocks relayouted into the tiled order, N(0,1) activations)"
+
+        def cpu(oracle):
+            # the oracle multiplies the canonical matrices (the same weights)
+            ws = [synth.q4k_weights(N, K, config=cfg, copy=0, extra=extra) for K, N, cfg, extra in mats]
+            xs = [x.cpu().numpy() for x in wl.xs]
+            return (lambda: [oracle.q4k_gemv(xs[m], ws[m], K, N) for m, (K, N, _, _) in enumerate(mats)]), \
+                1.0, "oracle q4k_gemv on the canonical matrices, full call"
+        wl.cpu = cpu
     elif name == "copy":
         nbytes = 64 * 2 ** 20
         copies = 4
@@ -377,7 +440,9 @@ TRAFFIC_FILES = {"c2": "q4k_gemv_4096x4096_b1.traffic.json",
                  "c5": "ternary_gemv_4096x4096_b1.traffic.json",
                  "q40": "q4_0_gemv_4096x4096_b1.traffic.json",
                  "q6k": "q6k_gemv_4096x4096_b1.traffic.json",
-                 "t64": "ternary_matmul_64x4096x4096.traffic.json"}
+                 "t64": "ternary_matmul_64x4096x4096.traffic.json",
+                 "c2t": "q4k_gemv_tiled_4096x4096_b1.traffic.json",
+                 "c3t": "q4k_gemv_tiled_ffn_4096x14336_pair.traffic.json"}
 
 
 def traffic_for(wl):
@@ -400,7 +465,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64000)
     ap.add_argument("--warmup", type=int, default=6400)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "q40", "q6k", "t64", "copy"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "q40", "q6k", "t64", "c2t", "c3t", "copy"])
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -454,7 +519,7 @@ def main():
     line = {
         "metric": wl.metric,
         "value": round(us, 3),
-        "unit": "us/call" if wl.name != "c3" else "us/pair",
+        "unit": "us/pair" if wl.name in ("c3", "c3t") else "us/call",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,

@@ -256,6 +256,76 @@ int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                     int64_t output_dim, float *y, void *stream,
                     int rows_per_lane, int k_waves, int workgroup_waves);
 
+/*
+ * Q4_K tiled block order.  SKaiNET docs, "Eager execution: backends and
+ * kernels": a packed weight reaches a kernel by declaring its block order,
+ * and a canonical weight is relayouted into that order once, not per call.
+ * The tiled order is this library's GPU block order; it holds the canonical
+ * bytes, moved and never changed:
+ *   - rows in groups of 16: group G is rows 16G .. 16G+15, ceil(output_dim/16)
+ *     groups; rows at or past output_dim are zero bytes;
+ *   - super-block b of group G is one 2304-byte tile at byte (G*nb + b)*2304,
+ *     nb = input_dim/256;
+ *   - tile bytes 0..2047: the 16 rows' qs in two halves of 1024 bytes; qs
+ *     byte 32j + 8g + t (j, g < 4, t < 8) of row 16G + n is at tile byte
+ *     1024*(j/2) + 16*(n + 16g) + 8*(j%2) + t (so the 16 bytes at 16*lane of
+ *     a half are one lane's MFMA operand bytes for two sub-block pairs);
+ *   - tile bytes 2048..2303: the 16 rows' block headers (bytes 0..15 of the
+ *     block: d, dmin, the 12 scale bytes), row n at 2048 + 16n.
+ */
+
+/*
+ * q4k_tiled_size -- bytes of a matrix in the tiled order:
+ * ceil(output_dim/16) * (input_dim/256) * 2304, or Q4K_EINVAL_DIM (negative)
+ * when a dimension is invalid as for q4k_gemv.  Host-only; touches no GPU.
+ */
+int64_t q4k_tiled_size(int64_t input_dim, int64_t output_dim);
+
+/*
+ * q4k_relayout_tiled -- the one-time move of a canonical Q4_K matrix into
+ * the tiled order (meant for load time, not per call).
+ *   w_blocks   canonical uint8 [output_dim * input_dim/256 * 144], 16-byte
+ *              aligned (as for q4k_gemv)
+ *   input_dim, output_dim as for q4k_gemv
+ *   w_tiled    uint8 [q4k_tiled_size(input_dim, output_dim)], 16-byte
+ *              aligned, every byte written (padding rows as zeros); must not
+ *              overlap w_blocks (not checked)
+ * Errors as for q4k_gemv (dimensions, then NULL, then alignment); on error
+ * nothing is launched and w_tiled is untouched.  Pure byte moves: the
+ * result is bit-exact.
+ */
+int q4k_relayout_tiled(const uint8_t *w_blocks, int64_t input_dim, int64_t output_dim,
+                       uint8_t *w_tiled, void *stream);
+
+/*
+ * q4k_gemv_tiled -- q4k_gemv's product, y[o] = sum_k W[o,k] * x[k], with W
+ * given in the tiled order (the product of the Q4_K page, sections
+ * "Summary" and "Pipeline", in the lazy-dmin form).
+ *   x          fp32 [input_dim], 16-byte aligned
+ *   w_tiled    uint8 [q4k_tiled_size(input_dim, output_dim)], 16-byte
+ *              aligned, written by q4k_relayout_tiled (or laid out so)
+ *   input_dim, output_dim, y as for q4k_gemv
+ * Computed on 16x16x32 f16 MFMA tiles: each tile is three coalesced
+ * 16-byte loads per lane straight into registers; each 32-activation
+ * sub-block is scaled by a power of two and split into exact fp16 hi and lo
+ * halves (any |x| < 2^96); fp32 accumulation.  Errors and tolerance as for
+ * q4k_gemv.  Deterministic; the summation order depends only on the shape.
+ */
+int q4k_gemv_tiled(const float *x, const uint8_t *w_tiled, int64_t input_dim,
+                   int64_t output_dim, float *y, void *stream);
+
+/*
+ * q4k_gemv_tiled_shaped -- q4k_gemv_tiled with an explicit launch shape:
+ * waves per workgroup in {4, 8, 16}, row_groups (consecutive groups of 16
+ * rows per workgroup) in 1..4, depth (tiles each wave loads ahead) in
+ * {2, 4} ({2} with 16 waves); 0 lets the library choose that value.  Any
+ * other value gives Q4K_EINVAL_DIM.  Results are within the q4k_gemv
+ * tolerance for every shape.
+ */
+int q4k_gemv_tiled_shaped(const float *x, const uint8_t *w_tiled, int64_t input_dim,
+                          int64_t output_dim, float *y, void *stream, int waves,
+                          int row_groups, int depth);
+
 /* Static description of a return code; for Q4K_EHIP it includes the HIP
  * error text of the failing call on this host thread. */
 const char *q4k_strerror(int code);

@@ -22,6 +22,7 @@ Q4K_EHIP = -4
 EXPORTED = (
     "q4k_gemv", "q4k_matmul", "ternary_gemv_codes", "ternary_gemv", "ternary_matmul",
     "q4k_gemv_shaped", "q4_0_gemv", "q4_0_gemv_shaped", "q6k_gemv", "q6k_gemv_shaped",
+    "q4k_tiled_size", "q4k_relayout_tiled", "q4k_gemv_tiled", "q4k_gemv_tiled_shaped",
     "q4k_strerror",
     "q4k_bench_empty", "q4k_bench_stream_read", "q4k_bench_copy",
 )
@@ -59,6 +60,9 @@ def lib():
         "q4_0_gemv_shaped": [P, P, I64, I64, P, P, I, I, I],
         "q6k_gemv": [P, P, I64, I64, P, P],
         "q6k_gemv_shaped": [P, P, I64, I64, P, P, I, I, I],
+        "q4k_relayout_tiled": [P, I64, I64, P, P],
+        "q4k_gemv_tiled": [P, P, I64, I64, P, P],
+        "q4k_gemv_tiled_shaped": [P, P, I64, I64, P, P, I, I, I],
         "q4k_bench_empty": [P],
         "q4k_bench_stream_read": [P, I64, P, I64, P],
         "q4k_bench_copy": [P, P, I64, P],
@@ -67,6 +71,8 @@ def lib():
         f = getattr(L, name)
         f.argtypes = args
         f.restype = I
+    L.q4k_tiled_size.argtypes = [I64, I64]
+    L.q4k_tiled_size.restype = I64
     L.q4k_strerror.argtypes = [I]
     L.q4k_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -170,6 +176,48 @@ def q4_0_gemv_shaped(x, w_blocks, input_dim, output_dim, y, rows_per_lane=0,
     _check(lib().q4_0_gemv_shaped(_ptr(x), _ptr(w_blocks), K, N, _ptr(y), _stream(stream),
                                   int(rows_per_lane), int(k_waves), int(workgroup_waves)),
            "q4_0_gemv_shaped")
+    return y
+
+
+def q4k_tiled_size(input_dim, output_dim):
+    """Bytes of the tiled order (raises on invalid dimensions)."""
+    n = lib().q4k_tiled_size(int(input_dim), int(output_dim))
+    _check(n if n < 0 else Q4K_OK, "q4k_tiled_size")
+    return n
+
+
+def _tiled_need(K, N):
+    return ((N + 15) // 16) * (K // 256) * 2304 if (K > 0 and N > 0 and K % 256 == 0) else 0
+
+
+def q4k_relayout_tiled(w_blocks, input_dim, output_dim, w_tiled, stream=None):
+    K, N = int(input_dim), int(output_dim)
+    _expect(w_blocks, torch.uint8, "w_blocks", _q4k_need(K, N))
+    _expect(w_tiled, torch.uint8, "w_tiled", _tiled_need(K, N))
+    _check(lib().q4k_relayout_tiled(_ptr(w_blocks), K, N, _ptr(w_tiled), _stream(stream)),
+           "q4k_relayout_tiled")
+    return w_tiled
+
+
+def q4k_gemv_tiled(x, w_tiled, input_dim, output_dim, y, stream=None):
+    K, N = int(input_dim), int(output_dim)
+    _expect(x, torch.float32, "x", K if _pos(K, N) else 0)
+    _expect(w_tiled, torch.uint8, "w_tiled", _tiled_need(K, N))
+    _expect(y, torch.float32, "y", N if _pos(K, N) else 0)
+    _check(lib().q4k_gemv_tiled(_ptr(x), _ptr(w_tiled), K, N, _ptr(y), _stream(stream)),
+           "q4k_gemv_tiled")
+    return y
+
+
+def q4k_gemv_tiled_shaped(x, w_tiled, input_dim, output_dim, y, waves=0, row_groups=0,
+                          depth=0, stream=None):
+    K, N = int(input_dim), int(output_dim)
+    _expect(x, torch.float32, "x", K if _pos(K, N) else 0)
+    _expect(w_tiled, torch.uint8, "w_tiled", _tiled_need(K, N))
+    _expect(y, torch.float32, "y", N if _pos(K, N) else 0)
+    _check(lib().q4k_gemv_tiled_shaped(_ptr(x), _ptr(w_tiled), K, N, _ptr(y), _stream(stream),
+                                       int(waves), int(row_groups), int(depth)),
+           "q4k_gemv_tiled_shaped")
     return y
 
 

@@ -217,6 +217,43 @@ int ternary_matmul(const float *X, const uint8_t *codes, float scale, int64_t n_
   return Q4K_OK;
 }
 
+int64_t q4k_tiled_size(int64_t input_dim, int64_t output_dim) {
+  if (input_dim <= 0 || output_dim <= 0 || input_dim % 256 != 0 || input_dim > kMaxInputDim)
+    return Q4K_EINVAL_DIM;
+  return q4k::tiled_bytes(input_dim / 256, output_dim);
+}
+
+int q4k_relayout_tiled(const uint8_t *w_blocks, int64_t input_dim, int64_t output_dim,
+                       uint8_t *w_tiled, void *stream) {
+  int rc = check_q4k(w_blocks, w_blocks, w_tiled, 1, input_dim, output_dim);
+  if (rc) return rc;
+  if (!aligned16(w_tiled)) return Q4K_EALIGN;
+  hipError_t e = q4k::relayout_tiled_launch(w_blocks, w_tiled, input_dim / 256, output_dim,
+                                            (hipStream_t)stream);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_relayout_tiled launch");
+}
+
+int q4k_gemv_tiled_shaped(const float *x, const uint8_t *w_tiled, int64_t input_dim,
+                          int64_t output_dim, float *y, void *stream, int waves,
+                          int row_groups, int depth) {
+  int rc = check_q4k(x, w_tiled, y, 1, input_dim, output_dim);
+  if (rc) return rc;
+  if (!(waves == 0 || waves == 4 || waves == 8 || waves == 16) || row_groups < 0 ||
+      row_groups > 4 || !(depth == 0 || depth == 2 || depth == 4) ||
+      (waves == 16 && depth == 4))
+    return Q4K_EINVAL_DIM;
+  const q4k::TiledShape s = q4k::choose_tiled_shape(input_dim / 256, output_dim, waves,
+                                                    row_groups, depth);
+  hipError_t e = q4k::gemv_tiled_launch(x, w_tiled, y, input_dim / 256, output_dim, s,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_gemv_tiled launch");
+}
+
+int q4k_gemv_tiled(const float *x, const uint8_t *w_tiled, int64_t input_dim,
+                   int64_t output_dim, float *y, void *stream) {
+  return q4k_gemv_tiled_shaped(x, w_tiled, input_dim, output_dim, y, stream, 0, 0, 0);
+}
+
 const char *q4k_strerror(int code) {
   switch (code) {
     case Q4K_OK: return "ok";

@@ -37,6 +37,22 @@ hipError_t gemv_mfma_launch(const float *x, const uint8_t *w, float *y, int64_t 
 // workgroups are resident at once).
 bool use_gemv_mfma(int64_t nb, int64_t N);
 
+// The tiled block order (q4k_tiled.hip): bytes of an N-row matrix of nb
+// super-blocks per row, the one-time relayout, and the matrix-core GEMV
+// that streams it.
+struct TiledShape {
+  int waves = 8;       // waves per workgroup: 4, 8 or 16
+  int row_groups = 1;  // consecutive groups of 16 rows per workgroup: 1 .. 4
+  int depth = 4;       // tiles each wave loads ahead: 2 or 4 (16 waves: 2)
+};
+int64_t tiled_bytes(int64_t nb, int64_t N);
+hipError_t relayout_tiled_launch(const uint8_t *w, uint8_t *out, int64_t nb, int64_t N,
+                                 hipStream_t stream);
+// Zero fields of the request are chosen by the library.
+TiledShape choose_tiled_shape(int64_t nb, int64_t N, int waves, int row_groups, int depth);
+hipError_t gemv_tiled_launch(const float *x, const uint8_t *wt, float *y, int64_t nb, int64_t N,
+                             const TiledShape &s, hipStream_t stream);
+
 hipError_t ternary_launch(const float *x, const uint8_t *codes, float scale,
                           bool apply_scale, int64_t K, int64_t N, float *y,
                           hipStream_t stream);

@@ -150,6 +150,38 @@ def test_ternary_matmul_rejects_bad_args(lib):
     assert lib.ternary_matmul(GOOD, GOOD2, F(1.0), 3, 64, 8, None, None) == -2
 
 
+def test_tiled_size_is_host_only_arithmetic(lib):
+    assert lib.q4k_tiled_size(4096, 4096) == 256 * 16 * 2304
+    assert lib.q4k_tiled_size(256, 1) == 2304
+    assert lib.q4k_tiled_size(512, 17) == 2 * 2 * 2304
+    for K, N in ((255, 1), (0, 1), (256, 0), (-256, 4), ((1 << 24) + 256, 1)):
+        assert lib.q4k_tiled_size(K, N) == -1
+
+
+@pytest.mark.parametrize("K", [255, 257, 0, -256, (1 << 24) + 256])
+def test_tiled_entry_points_reject_bad_input_dim(lib, K):
+    assert lib.q4k_relayout_tiled(GOOD, K, 16, GOOD2, None) == -1
+    assert lib.q4k_gemv_tiled(GOOD, GOOD2, K, 16, GOOD3, None) == -1
+    assert lib.q4k_gemv_tiled_shaped(GOOD, GOOD2, K, 16, GOOD3, None, 0, 0, 0) == -1
+
+
+def test_tiled_entry_points_reject_null_misaligned_and_bad_shape(lib):
+    assert lib.q4k_relayout_tiled(GOOD, 256, 0, GOOD2, None) == -1
+    assert lib.q4k_relayout_tiled(None, 256, 16, GOOD2, None) == -2
+    assert lib.q4k_relayout_tiled(GOOD, 256, 16, None, None) == -2
+    assert lib.q4k_relayout_tiled(ODD, 256, 16, GOOD2, None) == -3
+    assert lib.q4k_relayout_tiled(GOOD, 256, 16, ODD, None) == -3
+    assert lib.q4k_gemv_tiled(None, GOOD2, 256, 16, GOOD3, None) == -2
+    assert lib.q4k_gemv_tiled(GOOD, None, 256, 16, GOOD3, None) == -2
+    assert lib.q4k_gemv_tiled(GOOD, GOOD2, 256, 16, None, None) == -2
+    assert lib.q4k_gemv_tiled(ODD, GOOD2, 256, 16, GOOD3, None) == -3
+    assert lib.q4k_gemv_tiled(GOOD, ODD, 256, 16, GOOD3, None) == -3
+    for waves, rg, depth in ((2, 0, 0), (32, 0, 0), (8, 5, 0), (8, -1, 0), (8, 0, 3),
+                             (16, 0, 4), (8, 0, 1)):
+        assert lib.q4k_gemv_tiled_shaped(GOOD, GOOD2, 4096, 16, GOOD3, None,
+                                         waves, rg, depth) == -1, (waves, rg, depth)
+
+
 @pytest.mark.parametrize("K", [3, 5, 4098, 0, -4])
 def test_ternary_rejects_bad_input_dim(lib, K):
     assert lib.ternary_gemv_codes(GOOD, GOOD2, K, 8, GOOD3, None) == -1
