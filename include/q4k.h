@@ -315,6 +315,24 @@ int q4k_gemv_tiled(const float *x, const uint8_t *w_tiled, int64_t input_dim,
                    int64_t output_dim, float *y, void *stream);
 
 /*
+ * q4k_matmul_tiled -- q4k_matmul's batched product, Y[r, o] = sum_k W[o,k] *
+ * X[r,k] for r < n_tokens, with W in the tiled order: a weight relayouted
+ * once serves both the single-token and the batched (prefill) calls.
+ *   X          fp32 [n_tokens, input_dim], 16-byte aligned (row r at
+ *              X + r*input_dim)
+ *   w_tiled    as for q4k_gemv_tiled
+ *   n_tokens   M > 0 (M == 1 runs q4k_gemv_tiled)
+ *   input_dim, output_dim, Y as for q4k_matmul
+ * The kernels mirror q4k_matmul's: a few tokens (M <= 4, or M <= 8 with
+ * output_dim <= 8192 and input_dim >= 4096) on the batched matrix-core GEMV
+ * (any |X| < 2^96), more on the 64-row x 16-token prefill tiles
+ * (|X| < 65504); every tile is loaded straight into registers.  Errors and
+ * tolerance as for q4k_matmul.
+ */
+int q4k_matmul_tiled(const float *X, const uint8_t *w_tiled, int64_t n_tokens,
+                     int64_t input_dim, int64_t output_dim, float *Y, void *stream);
+
+/*
  * q4k_gemv_tiled_shaped -- q4k_gemv_tiled with an explicit launch shape:
  * waves per workgroup in {4, 8, 16}, row_groups (consecutive groups of 16
  * rows per workgroup) in 1..4, depth (tiles each wave loads ahead) in

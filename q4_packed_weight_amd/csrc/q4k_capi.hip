@@ -254,6 +254,33 @@ int q4k_gemv_tiled(const float *x, const uint8_t *w_tiled, int64_t input_dim,
   return q4k_gemv_tiled_shaped(x, w_tiled, input_dim, output_dim, y, stream, 0, 0, 0);
 }
 
+// On tiled weights the batched kernel streams its tiles without LDS staging
+// and wins over the prefill tiles further out than on canonical weights:
+// measured (graph-replayed calls over rotating tiled copies, batched /
+// prefill us/call) 4096->14336 with 3 tokens 15.2 / 16.1, 4 tokens 15.8 /
+// 16.0, 5 tokens 21.4 / 16.1; 4096->8192 with 5 to 8 tokens 12.8-13.2 /
+// 15.3-15.4; 2048->8192 with 5 tokens 9.1 / 8.3; 14336->4096 equal up to 8.
+static bool use_tiled_batch(int64_t M, int64_t K, int64_t N) {
+  return M <= 4 || (M <= 8 && N <= 8192 && K >= 4096);
+}
+
+// One token is q4k_gemv_tiled, a few tokens the batched kernel, more the
+// prefill tiles.
+int q4k_matmul_tiled(const float *X, const uint8_t *w_tiled, int64_t n_tokens, int64_t input_dim,
+                     int64_t output_dim, float *Y, void *stream) {
+  int rc = check_q4k(X, w_tiled, Y, n_tokens, input_dim, output_dim);
+  if (rc) return rc;
+  if (n_tokens == 1) return q4k_gemv_tiled(X, w_tiled, input_dim, output_dim, Y, stream);
+  if (use_tiled_batch(n_tokens, input_dim, output_dim)) {
+    hipError_t e = q4k::gemv_tiled_batch_launch(X, w_tiled, Y, n_tokens, input_dim / 256,
+                                                output_dim, (hipStream_t)stream);
+    return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_matmul_tiled launch");
+  }
+  hipError_t e = q4k::prefill_tiled_launch(X, w_tiled, n_tokens, input_dim / 256, output_dim, Y,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_matmul_tiled launch");
+}
+
 const char *q4k_strerror(int code) {
   switch (code) {
     case Q4K_OK: return "ok";

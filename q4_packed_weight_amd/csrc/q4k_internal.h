@@ -52,6 +52,12 @@ hipError_t relayout_tiled_launch(const uint8_t *w, uint8_t *out, int64_t nb, int
 TiledShape choose_tiled_shape(int64_t nb, int64_t N, int waves, int row_groups, int depth);
 hipError_t gemv_tiled_launch(const float *x, const uint8_t *wt, float *y, int64_t nb, int64_t N,
                              const TiledShape &s, hipStream_t stream);
+// Batched products on tiled weights: 1 <= M <= 8 tokens (one row group per
+// workgroup), and the 64-row x 16-token prefill tiles.
+hipError_t gemv_tiled_batch_launch(const float *X, const uint8_t *wt, float *Y, int64_t M,
+                                   int64_t nb, int64_t N, hipStream_t stream);
+hipError_t prefill_tiled_launch(const float *X, const uint8_t *wt, int64_t M, int64_t nb,
+                                int64_t N, float *Y, hipStream_t stream);
 
 hipError_t ternary_launch(const float *x, const uint8_t *codes, float scale,
                           bool apply_scale, int64_t K, int64_t N, float *y,

@@ -27,6 +27,7 @@
 // by a power of two first, scales applied per sub-block in fp32 after the
 // MFMAs.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "q4k_internal.h"
@@ -307,6 +308,416 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_kernel(
   }
 }
 
+// A few tokens (2 to 8) on tiled weights: the batched product of
+// q4k_gemv_batch.hip (A rows 2t and 2t + 1 carry token t's fp16 hi and lo
+// parts, each token's super-block scaled by a power of two first; lane (n,
+// g) applies all eight sub-block scales of row n to tokens 2g and 2g + 1),
+// with each tile streamed straight into registers.  A workgroup owns one
+// row group; wave w takes its super-blocks w, w + W, ..., D ahead, with the
+// T tokens' activations of each super-block riding in the same ring and
+// staged in a wave-private LDS slot just before use (every super-block's
+// activations are staged once per workgroup, as in the canonical form).
+template <int T, int W, int D>
+__global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
+    const float *X, const uint8_t *wt, float *__restrict__ Y, int M, int nb, int N) {
+  __shared__ __align__(16) uint32_t xh[W][T][128];
+  __shared__ __align__(16) uint32_t xl[W][T][128];
+  __shared__ __align__(16) float xs[W][T][8];
+  __shared__ int xe[W][T];
+  __shared__ float part[W][T][kTileRows];
+
+  __builtin_assume(nb >= 1);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;  // weight row of the group; A row
+  const int g = lane >> 4;  // lane group: positions 8g .. 8g+7; tokens 2g, 2g+1
+  const int K = nb * 256;
+  const int rg = blockIdx.x;
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(wt + (int64_t)rg * nb * kTileBytes, (int64_t)nb * kTileBytes);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (int64_t)M * K * 4);
+  constexpr int kPastEnd = 0x7FFFF000;
+  const int nt = wave < nb ? (nb - wave + W - 1) / W : 0;  // this wave's super-blocks
+
+  const int vq0 = 16 * lane, vq1 = 1024 + 16 * lane, vhd = 2048 + 16 * n;
+  uint4 wq0[D], wq1[D], whd[D];
+  float4 xq[D][T];
+  // slot s <- super-block b (its tile and the tokens' activations); idle
+  // slots read zeros from past the end
+  auto load_unit = [&](int s, int b, bool valid) {
+    const int off = valid ? b * kTileBytes : kPastEnd;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      xq[s][t] = load_buf_f4(xr, t * K * 4 + 16 * lane, valid ? 1024 * b : kPastEnd);
+    wq0[s] = load_buf_stream16(wr, vq0, off);
+    wq1[s] = load_buf_stream16(wr, vq1, off);
+    whd[s] = load_buf_stream16(wr, vhd, off);
+  };
+
+  // A operand: row n is token n / 2 (rows past 2T repeat token T - 1 and are
+  // never read back), hi part in even rows, lo part in odd rows.
+  const int ta = min(n >> 1, T - 1);
+  const uint32_t *xa_src = (n & 1) ? xl[wave][ta] : xh[wave][ta];
+  const int t0 = min(2 * g, T - 1), t1 = min(2 * g + 1, T - 1);
+  float y0 = 0.f, y1 = 0.f;
+
+  auto compute = [&](int s) {
+    // stage the tokens' activations of this super-block (positions 4 lane ..)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float4 v0 = xq[s][t];
+      const float mx = wave_max_nonneg(
+          fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
+      const int e = __builtin_amdgcn_frexp_expf(mx) - 15;  // |x| * 2^-e < 2^15
+      const float4 v = make_float4(__builtin_ldexpf(v0.x, -e), __builtin_ldexpf(v0.y, -e),
+                                   __builtin_ldexpf(v0.z, -e), __builtin_ldexpf(v0.w, -e));
+      half2_t h02, h13;
+      h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
+      h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
+      const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
+      *reinterpret_cast<uint2 *>(&xh[wave][t][2 * lane]) = make_uint2(hw02, hw13);
+      *reinterpret_cast<uint2 *>(&xl[wave][t][2 * lane]) =
+          make_uint2(lo_pair_t(hw02, v.x, v.z), lo_pair_t(hw13, v.y, v.w));
+      xs[wave][t][lane >> 3] = group_sum<8>(sum4(v0));  // 8 lanes write one value
+      xe[wave][t] = e;                                  // every lane, one value
+    }
+    // the wave reads what its own lanes wrote: LDS executes one wave's
+    // instructions in order; keep the compiler from moving them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const uint4 hd = whd[s];
+    // header of row n: d, dmin and all eight 6-bit scales and mins
+    const uint32_t sc03 = hd.y & 0x3F3F3F3Fu;
+    const uint32_t mn03 = hd.z & 0x3F3F3F3Fu;
+    const uint32_t sc47 = (hd.w & 0x0F0F0F0Fu) | ((hd.y >> 2) & 0x30303030u);
+    const uint32_t mn47 = ((hd.w >> 4) & 0x0F0F0F0Fu) | ((hd.z >> 2) & 0x30303030u);
+    const float d = half_lo(hd.x), dmin = half_hi(hd.x);
+    uint2 qb[4];
+    qb[0] = make_uint2(wq0[s].x, wq0[s].y);
+    qb[1] = make_uint2(wq0[s].z, wq0[s].w);
+    qb[2] = make_uint2(wq1[s].x, wq1[s].y);
+    qb[3] = make_uint2(wq1[s].z, wq1[s].w);
+    half8_t alo[4], ahi[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      alo[j] = *reinterpret_cast<const half8_t *>(&xa_src[32 * j + 4 * g]);
+      ahi[j] = *reinterpret_cast<const half8_t *>(&xa_src[32 * j + 16 + 4 * g]);
+    }
+    floatx4 dlo[4], dhi[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t s0 = qb[j].x >> 8, s1 = qb[j].y >> 8;
+      uint4 blo, bhi;
+      blo.x = qb[j].x & 0x000F000Fu; blo.y = s0 & 0x000F000Fu;
+      blo.z = qb[j].y & 0x000F000Fu; blo.w = s1 & 0x000F000Fu;
+      bhi.x = qb[j].x & 0x00F000F0u; bhi.y = s0 & 0x00F000F0u;
+      bhi.z = qb[j].y & 0x00F000F0u; bhi.w = s1 & 0x00F000F0u;
+      dlo[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          alo[j], __builtin_bit_cast(half8_t, blo), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      dhi[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          ahi[j], __builtin_bit_cast(half8_t, bhi), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
+    // sub-block 2j (low nibbles, q * 2^-24) weighs sc, 2j+1 (16q * 2^-24) sc/16
+    float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t scw = j < 2 ? sc03 : sc47;
+      const float sl = (float)((scw >> (16 * (j & 1))) & 0xFFu);
+      const float shh = (float)((scw >> (16 * (j & 1) + 8)) & 0xFFu) * 0.0625f;
+      c0 = __builtin_fmaf(sl, dlo[j][0] + dlo[j][1], __builtin_fmaf(shh, dhi[j][0] + dhi[j][1], c0));
+      c1 = __builtin_fmaf(sl, dlo[j][2] + dlo[j][3], __builtin_fmaf(shh, dhi[j][2] + dhi[j][3], c1));
+    }
+    // lazy-dmin term: dmin * sum_s m_s * (sum of x over sub-block s)
+    const float4 sa0 = *reinterpret_cast<const float4 *>(&xs[wave][t0][0]);
+    const float4 sa1 = *reinterpret_cast<const float4 *>(&xs[wave][t0][4]);
+    const float4 sb0 = *reinterpret_cast<const float4 *>(&xs[wave][t1][0]);
+    const float4 sb1 = *reinterpret_cast<const float4 *>(&xs[wave][t1][4]);
+    const float m0 = (float)(mn03 & 0xFFu), m1 = (float)((mn03 >> 8) & 0xFFu);
+    const float m2 = (float)((mn03 >> 16) & 0xFFu), m3 = (float)(mn03 >> 24);
+    const float m4 = (float)(mn47 & 0xFFu), m5 = (float)((mn47 >> 8) & 0xFFu);
+    const float m6 = (float)((mn47 >> 16) & 0xFFu), m7 = (float)(mn47 >> 24);
+    const float z0 = m0 * sa0.x + m1 * sa0.y + m2 * sa0.z + m3 * sa0.w +
+                     m4 * sa1.x + m5 * sa1.y + m6 * sa1.z + m7 * sa1.w;
+    const float z1 = m0 * sb0.x + m1 * sb0.y + m2 * sb0.z + m3 * sb0.w +
+                     m4 * sb1.x + m5 * sb1.y + m6 * sb1.z + m7 * sb1.w;
+    // the activations entered as x * 2^-e, the codes as q * 2^-24
+    y0 += __builtin_ldexpf(d * c0, xe[wave][t0] + 24) - dmin * z0;
+    y1 += __builtin_ldexpf(d * c1, xe[wave][t1] + 24) - dmin * z1;
+    // the next staging overwrites this slot's activations only after these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  int lb = wave;
+#pragma unroll
+  for (int s = 0; s < D; ++s, lb += W) load_unit(s, lb, s < nt);
+  for (int u0 = 0; u0 < nt; u0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      if (u0 + s < nt) compute(s);  // wave-uniform
+      load_unit(s, lb, u0 + s + D < nt);  // always issued: equal loads in flight on every path
+      lb += W;
+    }
+  }
+
+  // Lane (n, g) holds tokens 2g and 2g+1 of row n (lane groups past the
+  // launch's tokens hold repeats and write nothing); sum the waves.
+  if (2 * g < T) part[wave][2 * g][n] = y0;
+  if (2 * g + 1 < T) part[wave][2 * g + 1][n] = y1;
+  __syncthreads();
+  if (tid < T * kTileRows) {
+    const int t = tid >> 4, r = tid & 15;
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < W; ++k) v += part[k][t][r];
+    const int row = rg * kTileRows + r;
+    if (t < M && row < N) Y[(int64_t)t * N + row] = v;
+  }
+}
+
+// Prefill on tiled weights: the 64-row x 16-token tiles of q4k_prefill.hip
+// (same arithmetic: A = sc*q exact in fp16, activations split into fp16 hi
+// + lo, d applied per block, the lazy-dmin term on the fp32 MFMA), with the
+// weights no longer staged through LDS.  Wave (bb, half) computes
+// super-block bb of each 4-super-block stage for row groups 2 half and
+// 2 half + 1: it loads those two tiles straight into registers one stage
+// ahead (its A operand bytes are its own 16-byte slots) and decodes its
+// rows' headers in registers; only the activations go through LDS.
+
+__device__ __forceinline__ half2_t as_h2t(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+// Bytes (0, 2) or (1, 3) of `t` as the low bytes of two fp16 halves whose
+// high byte is 0x64: a byte value v becomes the fp16 number 1024 + v.
+__device__ __forceinline__ uint32_t spread02_t(uint32_t t) {
+  return __builtin_amdgcn_perm(0x64646464u, t, 0x04020400u);
+}
+__device__ __forceinline__ uint32_t spread13_t(uint32_t t) {
+  return __builtin_amdgcn_perm(0x64646464u, t, 0x04030401u);
+}
+
+// One MFMA A operand (8 codes of one sub-block) from two qs dwords: their
+// low nibbles, or their high nibbles kept in place (16 v); (mul, add) turn
+// 1024 + v (or 1024 + 16 v) into sc * v, exact in fp16.
+__device__ __forceinline__ half8_t dequant8_t(uint32_t w0, uint32_t w1, bool hi_nib,
+                                              uint32_t mul, uint32_t add) {
+  const uint32_t mask = hi_nib ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+  const uint32_t t0 = w0 & mask, t1 = w1 & mask;
+  const half2_t m2 = as_h2t(mul), a2 = as_h2t(add);
+  const half2_t p0 = __builtin_elementwise_fma(as_h2t(spread02_t(t0)), m2, a2);
+  const half2_t p1 = __builtin_elementwise_fma(as_h2t(spread13_t(t0)), m2, a2);
+  const half2_t p2 = __builtin_elementwise_fma(as_h2t(spread02_t(t1)), m2, a2);
+  const half2_t p3 = __builtin_elementwise_fma(as_h2t(spread13_t(t1)), m2, a2);
+  half8_t v;
+  v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+  v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+  return v;
+}
+
+constexpr int TP_TOK = 16;    // tokens per workgroup (one MFMA token tile)
+constexpr int TP_BLKS = 4;    // super-blocks per stage
+constexpr int TP_WAVES = 8;
+constexpr int TP_XROW = 128 + 4;  // LDS dwords per staged activation row (+ 16 B)
+
+__global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
+    const float *X, const uint8_t *wt, float *__restrict__ Y, int M, int nb, int N) {
+  __shared__ __align__(16) uint32_t xh[TP_BLKS][TP_TOK][TP_XROW];
+  __shared__ __align__(16) uint32_t xl[TP_BLKS][TP_TOK][TP_XROW];
+  __shared__ __align__(16) float dtab[TP_WAVES][2][16];
+
+  __builtin_assume(nb >= 1);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bb = wave & 3;     // super-block of the stage this wave computes
+  const int half = wave >> 2;  // row groups 2 half and 2 half + 1 of the workgroup
+  const int r = lane & 15;     // A: row within a row group; B and D: token
+  const int g = lane >> 4;
+  const int t = tid & 255;
+  const int NG = (N + kTileRows - 1) / kTileRows;
+  const int rg0 = blockIdx.x * 4;
+  const int tok0 = blockIdx.y * TP_TOK;
+  const int K = nb * 256;
+  const int n_stages = (nb + TP_BLKS - 1) / TP_BLKS;
+
+  // the workgroup's (up to) four row groups, one contiguous tile stream
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(
+      wt + (int64_t)rg0 * nb * kTileBytes, (int64_t)min(4, NG - rg0) * nb * kTileBytes);
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(X + (int64_t)tok0 * K, (int64_t)(M - tok0) * K * 4);
+  constexpr int kPastEnd = 0x7FFFF000;
+
+  const int vq0 = 16 * lane, vq1 = 1024 + 16 * lane, vhd = 2048 + 16 * r;
+  uint4 q0[2][2], q1[2][2], hd[2][2];  // [buffer][row group a]
+  float4 xv[8];
+  const int tok_lo = tid >> 8;  // float4 i of this thread: token 2i + tok_lo
+  auto load_stage = [&](int st, int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      xv[i] = load_buf_f4(xr, 16 * t + 4 * K * (2 * i + tok_lo), 4096 * st);
+    const int b = st * TP_BLKS + bb;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int off = b < nb ? ((2 * half + a) * nb + b) * kTileBytes : kPastEnd;
+      q0[buf][a] = load_buf_stream16(wr, vq0, off);
+      q1[buf][a] = load_buf_stream16(wr, vq1, off);
+      hd[buf][a] = load_buf_stream16(wr, vhd, off);
+    }
+  };
+  auto stage_x = [&]() {
+    // float4 i: token 2i + tok_lo, block t / 64, positions 4 (t % 64) ..;
+    // stored as pairs (0,2) and (1,3): operand order
+    const int xb = t >> 6, l = t & 63;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = xv[i];
+      half2_t h02, h13;
+      h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
+      h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
+      const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
+      const int tok = 2 * i + tok_lo;
+      *reinterpret_cast<uint2 *>(&xh[xb][tok][2 * l]) = make_uint2(hw02, hw13);
+      *reinterpret_cast<uint2 *>(&xl[xb][tok][2 * l]) =
+          make_uint2(lo_pair_t(hw02, v.x, v.z), lo_pair_t(hw13, v.y, v.w));
+    }
+  };
+
+  floatx4 y_acc[2], m_acc[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) y_acc[a] = m_acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+  half8_t ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
+
+  auto compute = [&](int buf) {
+    // headers of row r of this wave's two row groups: the fp16 (mul, add)
+    // pairs per sub-block, dmin*m of sub-blocks g and 4 + g (the lazy-dmin
+    // MFMA's A operand), and d into the wave's table for the D rows
+    uint32_t mul[2][8], add[2][8];
+    float cm[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const uint4 h = hd[buf][a];
+      const float d = half_lo(h.x), dmin = half_hi(h.x);
+      const uint32_t sc03 = h.y & 0x3F3F3F3Fu;
+      const uint32_t mn03 = h.z & 0x3F3F3F3Fu;
+      const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+      const uint32_t mn47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+#pragma unroll
+      for (int sb = 0; sb < 8; ++sb) {
+        const float scf = (float)(((sb < 4 ? sc03 : sc47) >> (8 * (sb & 3))) & 255u);
+        // even sub-blocks are low nibbles, odd ones high nibbles (16 v)
+        const float mulf = (sb & 1) ? scf * 0.0625f : scf;
+        const float addf = (sb & 1) ? scf * -64.0f : scf * -1024.0f;
+        half2_t m2, a2;
+        m2.x = m2.y = (_Float16)mulf;
+        a2.x = a2.y = (_Float16)addf;
+        mul[a][sb] = as_u32h(m2);
+        add[a][sb] = as_u32h(a2);
+      }
+      cm[a][0] = dmin * (float)((mn03 >> (8 * g)) & 255u);  // sub-block g
+      cm[a][1] = dmin * (float)((mn47 >> (8 * g)) & 255u);  // sub-block 4 + g
+      dtab[wave][a][r] = d;  // the four lane groups write the same value
+    }
+    floatx4 acc[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float xsb[2] = {0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint2 qb[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const uint4 v = j < 2 ? q0[buf][a] : q1[buf][a];
+        qb[a] = (j & 1) ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int sb = 2 * j + hh;
+        const half8_t Bh = *reinterpret_cast<const half8_t *>(&xh[bb][r][16 * sb + 4 * g]);
+        const half8_t Bl = *reinterpret_cast<const half8_t *>(&xl[bb][r][16 * sb + 4 * g]);
+        half8_t A[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          A[a] = dequant8_t(qb[a].x, qb[a].y, hh != 0, mul[a][sb], add[a][sb]);
+        floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[a], Bh, acc[a], 0, 0, 0);
+        sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bl, sx, 0, 0, 0);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[a], Bl, acc[a], 0, 0, 0);
+        // sum of x over sub-block sb for token r (every row of the tile)
+        if ((sb & 3) == g) xsb[sb >> 2] = sx[0];
+      }
+    }
+    // d of the D rows 4g + e, written above by this wave's lanes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const float4 dv = *reinterpret_cast<const float4 *>(&dtab[wave][a][4 * g]);
+      y_acc[a][0] = __builtin_fmaf(dv.x, acc[a][0], y_acc[a][0]);
+      y_acc[a][1] = __builtin_fmaf(dv.y, acc[a][1], y_acc[a][1]);
+      y_acc[a][2] = __builtin_fmaf(dv.z, acc[a][2], y_acc[a][2]);
+      y_acc[a][3] = __builtin_fmaf(dv.w, acc[a][3], y_acc[a][3]);
+      // lazy-dmin term: A[row][kk] = dmin*m of sub-block 4c + kk, B = sums
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(cm[a][c], xsb[c], m_acc[a], 0, 0, 0);
+    }
+    // the next block's d values overwrite the table only after these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // The token groups of a row tile start at different stages (and wrap).
+  // Two stages per trip, so that each tile buffer is a fixed set of
+  // registers.
+  const int st0 = blockIdx.y % n_stages;
+  auto step = [&](int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int st = st0 + it < n_stages ? st0 + it : st0 + it - n_stages;
+    stage_x();
+    __syncthreads();
+    if (it + 1 < n_stages) load_stage(st + 1 < n_stages ? st + 1 : 0, buf ^ 1);
+    if (st * TP_BLKS + bb < nb) compute(buf);  // wave-uniform
+    __syncthreads();  // the next stage overwrites the activation tiles
+  };
+  load_stage(st0, 0);
+  for (int it = 0; it < n_stages; it += 2) {
+    step(it, std::integral_constant<int, 0>());
+    if (it + 1 >= n_stages) break;
+    step(it + 1, std::integral_constant<int, 1>());
+  }
+
+  // Add the four blocks' partial tiles (through the activation tiles, no
+  // longer needed) and store.  Lane (token r, group g) holds rows
+  // 16 (2 half + a) + 4g + e of its token.
+  float4 *red = reinterpret_cast<float4 *>(&xh[0][0][0]);  // [block][token][17]
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+    red[(bb * TP_TOK + r) * 17 + 4 * (2 * half + a) + g] =
+        make_float4(y_acc[a][0] - m_acc[a][0], y_acc[a][1] - m_acc[a][1],
+                    y_acc[a][2] - m_acc[a][2], y_acc[a][3] - m_acc[a][3]);
+  __syncthreads();
+  const float *redf = reinterpret_cast<const float *>(red);
+  for (int o = tid; o < TP_TOK * 64; o += 64 * TP_WAVES) {
+    const int tok = o / 64, rr = o % 64;
+    float v = 0.f;
+#pragma unroll
+    for (int b = 0; b < TP_BLKS; ++b) v += redf[(b * TP_TOK + tok) * 68 + rr];
+    const int row = rg0 * kTileRows + rr;
+    if (tok0 + tok < M && row < N) Y[(int64_t)(tok0 + tok) * N + row] = v;
+  }
+}
+
 template <int W, int D, int CAP>
 hipError_t launch_tiled(const float *x, const uint8_t *wt, float *y, int64_t nb, int64_t N,
                         int rg, hipStream_t stream) {
@@ -379,6 +790,42 @@ hipError_t gemv_tiled_launch(const float *x, const uint8_t *wt, float *y, int64_
   Q4K_TILED_CASE(16, 2)
 #undef Q4K_TILED_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t gemv_tiled_batch_launch(const float *X, const uint8_t *wt, float *Y, int64_t M,
+                                   int64_t nb, int64_t N, hipStream_t stream) {
+  // Offsets formed in the kernel: a row group's tiles and 8 token rows of X
+  // stay below the past-the-end offset.
+  if (M < 1 || M > 8 || N > 0x7FFFFFFF || nb * kTileBytes > 0x7FFF0000 ||
+      (int64_t)8 * nb * 1024 + 1024 * nb > 0x7FFF0000)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((N + kTileRows - 1) / kTileRows));
+  constexpr int W = 8, D = 2;
+  if (M <= 2)
+    hipLaunchKernelGGL((q4k_gemv_tiled_batch_kernel<2, W, D>), grid, dim3(64 * W), 0, stream, X,
+                       wt, Y, (int)M, (int)nb, (int)N);
+  else if (M <= 4)
+    hipLaunchKernelGGL((q4k_gemv_tiled_batch_kernel<4, W, D>), grid, dim3(64 * W), 0, stream, X,
+                       wt, Y, (int)M, (int)nb, (int)N);
+  else
+    hipLaunchKernelGGL((q4k_gemv_tiled_batch_kernel<8, W, D>), grid, dim3(64 * W), 0, stream, X,
+                       wt, Y, (int)M, (int)nb, (int)N);
+  return hipGetLastError();
+}
+
+hipError_t prefill_tiled_launch(const float *X, const uint8_t *wt, int64_t M, int64_t nb,
+                               int64_t N, float *Y, hipStream_t stream) {
+  // Offsets formed in the kernel: four row groups' tiles, and 16 rows of X
+  // plus one stage, stay below the past-the-end offset.
+  if (4 * nb * kTileBytes > 0x7FFF0000 || ((int64_t)TP_TOK * nb * 256 + 2048) * 4 > 0x7FFF0000 ||
+      N > 0x7FFFFFFF || M > 0x7FFFFFFF)
+    return hipErrorInvalidValue;
+  const int64_t NG = (N + kTileRows - 1) / kTileRows;
+  const dim3 grid((unsigned)((NG + 3) / 4), (unsigned)((M + TP_TOK - 1) / TP_TOK));
+  if (grid.y > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(q4k_prefill_tiled_kernel, grid, dim3(64 * TP_WAVES), 0, stream, X, wt, Y,
+                     (int)M, (int)nb, (int)N);
+  return hipGetLastError();
 }
 
 }  // namespace q4k

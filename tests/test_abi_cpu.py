@@ -176,6 +176,13 @@ def test_tiled_entry_points_reject_null_misaligned_and_bad_shape(lib):
     assert lib.q4k_gemv_tiled(GOOD, GOOD2, 256, 16, None, None) == -2
     assert lib.q4k_gemv_tiled(ODD, GOOD2, 256, 16, GOOD3, None) == -3
     assert lib.q4k_gemv_tiled(GOOD, ODD, 256, 16, GOOD3, None) == -3
+    for M in (0, -1):
+        assert lib.q4k_matmul_tiled(GOOD, GOOD2, M, 256, 16, GOOD3, None) == -1
+    assert lib.q4k_matmul_tiled(GOOD, GOOD2, 4, 255, 16, GOOD3, None) == -1
+    assert lib.q4k_matmul_tiled(None, GOOD2, 4, 256, 16, GOOD3, None) == -2
+    assert lib.q4k_matmul_tiled(GOOD, GOOD2, 4, 256, 16, None, None) == -2
+    assert lib.q4k_matmul_tiled(ODD, GOOD2, 4, 256, 16, GOOD3, None) == -3
+    assert lib.q4k_matmul_tiled(GOOD, ODD, 4, 256, 16, GOOD3, None) == -3
     for waves, rg, depth in ((2, 0, 0), (32, 0, 0), (8, 5, 0), (8, -1, 0), (8, 0, 3),
                              (16, 0, 4), (8, 0, 1)):
         assert lib.q4k_gemv_tiled_shaped(GOOD, GOOD2, 4096, 16, GOOD3, None,

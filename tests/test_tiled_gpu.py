@@ -222,3 +222,136 @@ def test_tiled_rejects_bad_args_and_leaves_outputs_untouched():
     with pytest.raises(ValueError):
         binding.q4k_relayout_tiled(w[8:], 256, 8, out)
     assert np.all(host(out) == 0xA5)
+
+
+# --- batched and prefill products on tiled weights (q4k_matmul_tiled) ------
+
+def matmul_tiled(X, wt, M, K, N):
+    buf, Y = out_with_canary(N, rows=M)
+    binding.q4k_matmul_tiled(dev(X), wt, M, K, N, Y)
+    out = host(Y)
+    assert canary_intact(buf, M * N), "write past the end of Y"
+    return out
+
+
+def matmul_canonical(X, w, M, K, N):
+    buf, Y = out_with_canary(N, rows=M)
+    binding.q4k_matmul(dev(X), dev(w), M, K, N, Y)
+    return host(Y)
+
+
+# few tokens take the batched kernel (2 .. 4 at input_dim 1024), more the
+# prefill tiles (5 .. 130: ragged token tiles)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 16, 17, 63, 64, 65, 130])
+def test_matmul_tiled_token_counts(oracle_lib, M):
+    K, N = 1024, 200
+    w = synth.q4k_weights(N, K, config=41, copy=M)
+    X = synth.activations(K, n_tokens=M, config=41, copy=M)
+    wt, _ = relayout(w, K, N)
+    Y = matmul_tiled(X, wt, M, K, N)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"M={M}")
+
+
+# ragged stages (input_dim/256 not a multiple of 4), ragged row groups and
+# row-group quartets, long rows, the batched kernel at several N regimes
+# (5 to 8 tokens with input_dim >= 4096 and up to 4 at any shape)
+@pytest.mark.parametrize("M,K,N", [(64, 256, 16), (64, 4096, 64), (5, 14336, 33), (64, 768, 1000),
+                                   (48, 2304, 129), (64, 512, 4097), (16, 256, 64), (17, 768, 65),
+                                   (33, 1280, 130), (8, 256, 1), (4, 512, 17), (6, 1280, 129),
+                                   (8, 14336, 64), (2, 4096, 12000), (3, 20480, 40), (7, 4096, 8000),
+                                   (4, 4096, 14336)])
+def test_matmul_tiled_shapes(oracle_lib, M, K, N):
+    w = synth.q4k_weights(N, K, config=42, copy=K + N)
+    X = synth.activations(K, n_tokens=M, config=42, copy=K + N)
+    wt, _ = relayout(w, K, N)
+    Y = matmul_tiled(X, wt, M, K, N)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"{M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 4096, 512), (17, 768, 65), (33, 1280, 130), (16, 14336, 64)])
+def test_prefill_tiled_equals_canonical_prefill(M, K, N):
+    """The tiled prefill does the canonical prefill's arithmetic in the same
+    order (only where the weight bytes come from differs): bit for bit."""
+    w = synth.q4k_weights(N, K, config=43, copy=M)
+    X = synth.activations(K, n_tokens=M, config=43, copy=M)
+    wt, _ = relayout(w, K, N)
+    a = matmul_tiled(X, wt, M, K, N)
+    b = matmul_canonical(X, w, M, K, N)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_batch_tiled_equals_canonical_batch_one_block_per_wave(M):
+    """With 8 super-blocks per row each of the 8 waves owns one super-block
+    in both batched forms: the tiled one equals the canonical one bit for
+    bit."""
+    K, N = 2048, 300
+    w = synth.q4k_weights(N, K, config=44, copy=M)
+    X = synth.activations(K, n_tokens=M, config=44, copy=M)
+    wt, _ = relayout(w, K, N)
+    a = matmul_tiled(X, wt, M, K, N)
+    b = matmul_canonical(X, w, M, K, N)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_matmul_tiled_full_config_sampled_tokens(oracle_lib):
+    """64 x 4096 x 4096: every output of 8 sampled token rows."""
+    M, K, N = 64, 4096, 4096
+    w = synth.q4k_weights(N, K, config=synth.C4_PREFILL)
+    X = synth.activations(K, n_tokens=M, config=synth.C4_PREFILL)
+    wt, _ = relayout(w, K, N)
+    Y = matmul_tiled(X, wt, M, K, N)
+    for t in (0, 7, 21, 33, 40, 52, 62, 63):
+        ref = oracle_lib.q4k_matmul_part(X, w, M, K, N, (t, t + 1), (0, N))[t]
+        assert_parity(Y[t], ref, what=f"token {t}")
+
+
+def test_batch_tiled_full_size(oracle_lib):
+    M, K, N = 8, 4096, 4096
+    w = synth.q4k_weights(N, K, config=synth.C2_Q4K_4K)
+    X = synth.activations(K, n_tokens=M, config=synth.C2_Q4K_4K)
+    wt, _ = relayout(w, K, N)
+    assert_parity(matmul_tiled(X, wt, M, K, N), oracle_lib.q4k_matmul(X, w, M, K, N),
+                  rowwise=True, what="8x4096x4096")
+
+
+@pytest.mark.parametrize("M", [2, 8, 13, 64])
+def test_matmul_tiled_integer_bit_exact(oracle_lib, M):
+    K, N = 4096, 256
+    w = synth.q4k_integer_weights(N, K, config=45)
+    X = synth.integer_activations(K, n_tokens=M, config=45)
+    wt, _ = relayout(w, K, N)
+    Y = matmul_tiled(X, wt, M, K, N)
+    assert np.array_equal(Y.astype(np.float64), oracle_lib.q4k_matmul(X, w, M, K, N))
+
+
+def test_batch_tiled_wide_range_tokens(oracle_lib):
+    """Tokens at 2^-30 .. 2^60 (one all zero), sub-blocks at 2^-20 .. 2^20:
+    each token's super-block is rescaled before its fp16 split (8 tokens
+    with input_dim 4096 take the batched kernel)."""
+    M, K, N = 8, 4096, 200
+    w = synth.q4k_weights(N, K, config=46)
+    X = synth.activations(K, n_tokens=M, config=46)
+    g = np.random.default_rng(46)
+    sub = np.exp2(g.integers(-20, 21, (M, K // 32))).astype(np.float32)
+    tok = np.exp2(np.array([-30, 0, 10, 30, 50, 60, -10, 0], np.float64)).astype(np.float32)
+    X = (X.reshape(M, -1, 32) * sub[:, :, None] * tok[:, None, None]).reshape(M, K)
+    X[6] = 0.0
+    wt, _ = relayout(w, K, N)
+    Y = matmul_tiled(X, wt, M, K, N)
+    assert np.all(Y[6] == 0.0)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what="wide-range tokens")
+
+
+def test_matmul_tiled_deterministic_and_rejects():
+    M, K, N = 64, 1024, 256
+    w = synth.q4k_weights(N, K, config=47)
+    X = synth.activations(K, n_tokens=M, config=47)
+    wt, _ = relayout(w, K, N)
+    a, b = matmul_tiled(X, wt, M, K, N), matmul_tiled(X, wt, M, K, N)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    buf, Y = out_with_canary(N, rows=M)
+    for bad_k in (255, 1000):
+        with pytest.raises(ValueError):
+            binding.q4k_matmul_tiled(dev(X), wt, M, bad_k, N, Y)
+    assert bool(torch.all(torch.isnan(buf)))
