@@ -7,8 +7,55 @@
 namespace q4k {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));  // one MFMA f16 operand
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));  // one 16x16 MFMA D tile per lane
+
+__device__ __forceinline__ uint32_t as_u32h(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+// lo = fp16(x - hi) for the two halves of `hi2` (fp16 hi parts of x0, x1):
+// v_fma_mix evaluates x - hi exactly in fp32 and rounds once to fp16, so
+// hi + lo carries x to 22 significant bits and both are exact MFMA inputs.
+__device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi2), "v"(x0));
+  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(r) : "v"(hi2), "v"(x1));
+  return r;
+}
+
+// Bytes (0, 2) or (1, 3) of `t` as the low bytes of two fp16 halves whose
+// high byte is 0x64: a byte value v becomes the fp16 number 1024 + v.
+__device__ __forceinline__ uint32_t spread02(uint32_t t) {
+  return __builtin_amdgcn_perm(0x64646464u, t, 0x04020400u);
+}
+__device__ __forceinline__ uint32_t spread13(uint32_t t) {
+  return __builtin_amdgcn_perm(0x64646464u, t, 0x04030401u);
+}
+
+// One MFMA A operand (8 codes of one sub-block) from two qs dwords: their
+// low nibbles (hi_nib false) or their high nibbles kept in place, i.e. as
+// 16 v (true).  mul/add are per-sub-block fp16 pairs that turn 1024 + v (or
+// 1024 + 16 v) into sc*v: (sc, -1024 sc) for low nibbles and (sc/16, -64 sc)
+// for high ones.  The fused multiply-add rounds once, and sc*v is exact in
+// fp16.  Codes come out in operand order: positions (0,2), (1,3), (4,6),
+// (5,7) of the 8.
+__device__ __forceinline__ half8_t dequant8(uint32_t w0, uint32_t w1, bool hi_nib,
+                                            uint32_t mul, uint32_t add) {
+  const uint32_t mask = hi_nib ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
+  const uint32_t t0 = w0 & mask, t1 = w1 & mask;
+  const half2_t m2 = as_h2(mul), a2 = as_h2(add);
+  const half2_t p0 = __builtin_elementwise_fma(as_h2(spread02(t0)), m2, a2);
+  const half2_t p1 = __builtin_elementwise_fma(as_h2(spread13(t0)), m2, a2);
+  const half2_t p2 = __builtin_elementwise_fma(as_h2(spread02(t1)), m2, a2);
+  const half2_t p3 = __builtin_elementwise_fma(as_h2(spread13(t1)), m2, a2);
+  half8_t v;
+  v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+  v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+  return v;
+}
 
 // The two binary16 halves of a dword as fp32.  When the result feeds an FMA
 // with an fp32 operand, the compiler folds the conversion into

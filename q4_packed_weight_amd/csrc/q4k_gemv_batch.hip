@@ -32,26 +32,12 @@ namespace q4k {
 
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
 constexpr int kBlockBytes = 144;
 constexpr int MB_ROWS = 16;                      // rows per workgroup
 constexpr int MB_WAVES = 8;
 constexpr int MB_WCH = MB_ROWS * 9;              // 16-byte weight pieces per super-block
 constexpr int MB_WPL = (MB_WCH + 63) / 64;       // weight loads per lane
 constexpr int MB_WROW = 36 + 2;                  // LDS dwords per staged row (+ 8 B)
-
-__device__ __forceinline__ uint32_t as_u32h(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
-
-// lo = fp16(x - hi) for the two halves of `hi2` (fp16 hi parts of x0, x1).
-__device__ __forceinline__ uint32_t lo_pair_b(uint32_t hi2, float x0, float x1) {
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi2), "v"(x0));
-  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-      : "+v"(r) : "v"(hi2), "v"(x1));
-  return r;
-}
 
 template <int T>  // tokens of the launch: 2, 4 or 8 (rows of X past M read as zeros)
 __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
@@ -125,7 +111,7 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
       const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
       *reinterpret_cast<uint2 *>(&xh[wave][t][2 * lane]) = make_uint2(hw02, hw13);
       *reinterpret_cast<uint2 *>(&xl[wave][t][2 * lane]) =
-          make_uint2(lo_pair_b(hw02, v.x, v.z), lo_pair_b(hw13, v.y, v.w));
+          make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
       // sub-block lane / 8: 8 aligned lanes, which all hold the same sum
       xs[wave][t][lane >> 3] = group_sum<8>(sum4(v0));
       xe[wave][t] = e;  // every lane, one value

@@ -39,9 +39,6 @@ namespace q4k {
 
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
 constexpr int kBlockBytes = 144;
 constexpr int MV_ROWS = 16;           // rows per workgroup (one MFMA column tile)
 constexpr int MV_WAVES = 16;
@@ -51,18 +48,6 @@ constexpr int MV_WPL = (MV_WCH + 63) / 64;              // weight loads per lane
 constexpr int MV_XPL = MV_CB * 256 / 4 / 64;            // activation float4 per lane
 constexpr int MV_WROW = MV_CB * 36 + 2;                 // LDS dwords per staged row (+ 8 B)
 static_assert(MV_XPL * 64 * 4 == MV_CB * 256, "activation chunk must split evenly");
-
-__device__ __forceinline__ uint32_t as_u32h(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
-
-// lo = fp16(x - hi) for the two halves of `hi2` (fp16 hi parts of x0, x1):
-// v_fma_mix evaluates x - hi exactly in fp32 and rounds once to fp16.
-__device__ __forceinline__ uint32_t lo_pair_mv(uint32_t hi2, float x0, float x1) {
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi2), "v"(x0));
-  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-      : "+v"(r) : "v"(hi2), "v"(x1));
-  return r;
-}
 
 __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
     const float *x, const uint8_t *w, float *__restrict__ y, int nb, int N) {
@@ -141,7 +126,7 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
       const int f = lane + 64 * i;  // float4 index: positions 4f .. 4f+3
       *reinterpret_cast<uint2 *>(&xh[wave][2 * f]) = make_uint2(hw02, hw13);
       *reinterpret_cast<uint2 *>(&xl[wave][2 * f]) =
-          make_uint2(lo_pair_mv(hw02, v.x, v.z), lo_pair_mv(hw13, v.y, v.w));
+          make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
       // sub-block f / 8: the 8 float4 of a sub-block sit in 8 aligned lanes
       const float s = group_sum<8>(sum4(v0));
       if ((lane & 7) == 0) {

@@ -50,9 +50,6 @@ namespace q4k {
 
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
 constexpr int kBlockBytes = 144;
 constexpr int PF_ROWS = 64;           // weight rows per workgroup (4 row tiles)
 constexpr int PF_TOK = 16;            // tokens per workgroup (one token tile)
@@ -74,48 +71,6 @@ constexpr int W_CHUNKS = PF_ROWS * PF_BLKS * 9;           // 2304
 constexpr int W_PER_THREAD = W_CHUNKS / 256;              // 9
 constexpr int X_PER_THREAD = PF_TOK / 2;                  // 8
 static_assert(W_CHUNKS % 256 == 0, "weight chunks must divide evenly");
-
-__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
-__device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
-
-// Bytes (0, 2) or (1, 3) of `t` as the low bytes of two fp16 halves whose
-// high byte is 0x64: a byte value v becomes the fp16 number 1024 + v.
-__device__ __forceinline__ uint32_t spread02(uint32_t t) {
-  return __builtin_amdgcn_perm(0x64646464u, t, 0x04020400u);
-}
-__device__ __forceinline__ uint32_t spread13(uint32_t t) {
-  return __builtin_amdgcn_perm(0x64646464u, t, 0x04030401u);
-}
-
-// One MFMA A operand from two qs dwords: their low nibbles (hi_nib false)
-// or their high nibbles (true; kept in place, i.e. as 16 v).  mul/add are
-// the per-sub-block fp16 pairs that turn 1024 + v (or 1024 + 16 v) into
-// sc*v: (sc, -1024 sc) for low nibbles and (sc/16, -64 sc) for high ones.
-// The fused multiply-add rounds once, and sc*v is exact in fp16.
-__device__ __forceinline__ half8_t dequant8(uint32_t w0, uint32_t w1, bool hi_nib,
-                                            uint32_t mul, uint32_t add) {
-  const uint32_t mask = hi_nib ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
-  const uint32_t t0 = w0 & mask, t1 = w1 & mask;
-  const half2_t m2 = as_h2(mul), a2 = as_h2(add);
-  const half2_t p0 = __builtin_elementwise_fma(as_h2(spread02(t0)), m2, a2);
-  const half2_t p1 = __builtin_elementwise_fma(as_h2(spread13(t0)), m2, a2);
-  const half2_t p2 = __builtin_elementwise_fma(as_h2(spread02(t1)), m2, a2);
-  const half2_t p3 = __builtin_elementwise_fma(as_h2(spread13(t1)), m2, a2);
-  half8_t v;
-  v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
-  v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
-  return v;
-}
-
-// lo = fp16(x - hi) for the two halves of `hi2` (fp16 hi parts of x0, x1):
-// v_fma_mix evaluates x - hi exactly in fp32 and rounds once to fp16.
-__device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1) {
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi2), "v"(x0));
-  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-      : "+v"(r) : "v"(hi2), "v"(x1));
-  return r;
-}
 
 __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     const float *X, const uint8_t *w, float *__restrict__ Y, int M, int nb,
@@ -188,7 +143,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
       half2_t h02, h13;
       h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
       h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
-      const uint32_t hw02 = as_u32(h02), hw13 = as_u32(h13);
+      const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
       const int tok = 2 * i + tok_lo;
       *reinterpret_cast<uint2 *>(&xh[xb][tok][2 * lane]) = make_uint2(hw02, hw13);
       *reinterpret_cast<uint2 *>(&xl[xb][tok][2 * lane]) =
@@ -256,7 +211,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
             half2_t m2, a2;
             m2.x = m2.y = (_Float16)mulf;
             a2.x = a2.y = (_Float16)addf;
-            sc_tab[bb][s][hrow] = make_uint2(as_u32(m2), as_u32(a2));
+            sc_tab[bb][s][hrow] = make_uint2(as_u32h(m2), as_u32h(a2));
           }
         }
       }

@@ -36,9 +36,6 @@ namespace q4k {
 
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
 constexpr int kBlockBytes = 144;
 constexpr int kTileRows = 16;
 constexpr int kTileBytes = 2304;
@@ -71,18 +68,6 @@ __global__ __launch_bounds__(256) void q4k_relayout_tiled_kernel(
     if (row < N) v = *reinterpret_cast<const uint4 *>(w + (row * nb + b) * kBlockBytes);
   }
   *reinterpret_cast<uint4 *>(out + c * 16) = v;
-}
-
-__device__ __forceinline__ uint32_t as_u32h(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
-
-// lo = fp16(x - hi) for the two halves of `hi2` (fp16 hi parts of x0, x1):
-// v_fma_mix evaluates x - hi exactly in fp32 and rounds once to fp16.
-__device__ __forceinline__ uint32_t lo_pair_t(uint32_t hi2, float x0, float x1) {
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi2), "v"(x0));
-  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-      : "+v"(r) : "v"(hi2), "v"(x1));
-  return r;
 }
 
 // Workgroup: W waves, `rg_per_wg` consecutive row groups (their tiles are
@@ -154,7 +139,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_kernel(
     const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
     *reinterpret_cast<uint2 *>(&xh[2 * f]) = make_uint2(hw02, hw13);
     *reinterpret_cast<uint2 *>(&xl[2 * f]) =
-        make_uint2(lo_pair_t(hw02, v.x, v.z), lo_pair_t(hw13, v.y, v.w));
+        make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
     const float sum = group_sum<8>(sum4(v0));
     if ((lane & 7) == 0) {
       const int sb = f >> 3;
@@ -378,7 +363,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
       const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
       *reinterpret_cast<uint2 *>(&xh[wave][t][2 * lane]) = make_uint2(hw02, hw13);
       *reinterpret_cast<uint2 *>(&xl[wave][t][2 * lane]) =
-          make_uint2(lo_pair_t(hw02, v.x, v.z), lo_pair_t(hw13, v.y, v.w));
+          make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
       xs[wave][t][lane >> 3] = group_sum<8>(sum4(v0));  // 8 lanes write one value
       xe[wave][t] = e;                                  // every lane, one value
     }
@@ -488,35 +473,6 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
 // ahead (its A operand bytes are its own 16-byte slots) and decodes its
 // rows' headers in registers; only the activations go through LDS.
 
-__device__ __forceinline__ half2_t as_h2t(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
-
-// Bytes (0, 2) or (1, 3) of `t` as the low bytes of two fp16 halves whose
-// high byte is 0x64: a byte value v becomes the fp16 number 1024 + v.
-__device__ __forceinline__ uint32_t spread02_t(uint32_t t) {
-  return __builtin_amdgcn_perm(0x64646464u, t, 0x04020400u);
-}
-__device__ __forceinline__ uint32_t spread13_t(uint32_t t) {
-  return __builtin_amdgcn_perm(0x64646464u, t, 0x04030401u);
-}
-
-// One MFMA A operand (8 codes of one sub-block) from two qs dwords: their
-// low nibbles, or their high nibbles kept in place (16 v); (mul, add) turn
-// 1024 + v (or 1024 + 16 v) into sc * v, exact in fp16.
-__device__ __forceinline__ half8_t dequant8_t(uint32_t w0, uint32_t w1, bool hi_nib,
-                                              uint32_t mul, uint32_t add) {
-  const uint32_t mask = hi_nib ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
-  const uint32_t t0 = w0 & mask, t1 = w1 & mask;
-  const half2_t m2 = as_h2t(mul), a2 = as_h2t(add);
-  const half2_t p0 = __builtin_elementwise_fma(as_h2t(spread02_t(t0)), m2, a2);
-  const half2_t p1 = __builtin_elementwise_fma(as_h2t(spread13_t(t0)), m2, a2);
-  const half2_t p2 = __builtin_elementwise_fma(as_h2t(spread02_t(t1)), m2, a2);
-  const half2_t p3 = __builtin_elementwise_fma(as_h2t(spread13_t(t1)), m2, a2);
-  half8_t v;
-  v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
-  v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
-  return v;
-}
-
 constexpr int TP_TOK = 16;    // tokens per workgroup (one MFMA token tile)
 constexpr int TP_BLKS = 4;    // super-blocks per stage
 constexpr int TP_WAVES = 8;
@@ -581,7 +537,7 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
       const int tok = 2 * i + tok_lo;
       *reinterpret_cast<uint2 *>(&xh[xb][tok][2 * l]) = make_uint2(hw02, hw13);
       *reinterpret_cast<uint2 *>(&xl[xb][tok][2 * l]) =
-          make_uint2(lo_pair_t(hw02, v.x, v.z), lo_pair_t(hw13, v.y, v.w));
+          make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
     }
   };
 
@@ -642,7 +598,7 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
         half8_t A[2];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
-          A[a] = dequant8_t(qb[a].x, qb[a].y, hh != 0, mul[a][sb], add[a][sb]);
+          A[a] = dequant8(qb[a].x, qb[a].y, hh != 0, mul[a][sb], add[a][sb]);
         floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
         for (int a = 0; a < 2; ++a)

@@ -38,9 +38,6 @@ namespace q4k {
 
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
 constexpr int TR_ROWS = 64;            // rows per workgroup (4 row tiles)
 constexpr int TR_TOK = 16;             // tokens per workgroup
 constexpr int TR_WAVES = 8;
@@ -54,18 +51,6 @@ constexpr int CROW = TR_CB / 4 + 2;
 constexpr int C_PER_THREAD = TR_ROWS * TR_CB / 16 / TR_THREADS;  // 2
 constexpr int X_PER_THREAD = TR_TOK / 2;                          // 8
 static_assert(C_PER_THREAD * 16 * TR_THREADS == TR_ROWS * TR_CB, "code chunks must divide evenly");
-
-__device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
-
-// lo = fp16(x - hi) for the two halves of `hi2` (fp16 hi parts of x0, x1):
-// v_fma_mix evaluates x - hi exactly in fp32 and rounds once to fp16.
-__device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1) {
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi2), "v"(x0));
-  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-      : "+v"(r) : "v"(hi2), "v"(x1));
-  return r;
-}
 
 // The A operand from 16 bits of codes (8 fields): fields (0,2), (1,3) of the
 // low byte, then (4,6), (5,7) of the high byte, as the fp16 codes u - 1.
@@ -154,7 +139,7 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
       half2_t h02, h13;
       h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
       h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
-      const uint32_t hw02 = as_u32(h02), hw13 = as_u32(h13);
+      const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
       const int tok = 2 * i + tok_lo;
       if (lane == 0) xe[xb][tok] = e;
       *reinterpret_cast<uint2 *>(&xh[xb][tok][2 * lane]) = make_uint2(hw02, hw13);
