@@ -91,10 +91,11 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
  *   input_dim, output_dim as for q4k_gemv
  *   Y          fp32 [n_tokens, output_dim]
  * Same error behaviour and tolerance as q4k_gemv.  Three kernels serve it:
- * M == 1 is q4k_gemv; a few tokens (M <= 2 at any output_dim, M <= 4 with
- * output_dim <= 8192, M <= 8 with output_dim <= 4096) run on a batched
- * matrix-core GEMV that reads each weight once for all of them; larger
- * batches run on the prefill tiles (64 rows x 16 tokens).  The batched and
+ * M == 1 is q4k_gemv; a few tokens (M <= 2 at any shape, M <= 4 with
+ * output_dim <= 4096, M <= 8 with output_dim <= 4096 and input_dim > 8192)
+ * run on a batched matrix-core GEMV that reads each weight once for all of
+ * them; larger batches run on the prefill tiles (64 rows x 16 tokens,
+ * narrowed to 32 or 16 rows when 64-row tiles would leave CUs idle).  The batched and
  * prefill kernels pass the activations through fp16 (split into a high and
  * a low half, both exact MFMA operands); the batched one first scales each
  * token's super-block by a power of two (any |x| < 2^96), the prefill one
@@ -324,7 +325,7 @@ int q4k_gemv_tiled(const float *x, const uint8_t *w_tiled, int64_t input_dim,
  *   n_tokens   M > 0 (M == 1 runs q4k_gemv_tiled)
  *   input_dim, output_dim, Y as for q4k_matmul
  * The kernels mirror q4k_matmul's: a few tokens (M <= 4, or M <= 8 with
- * output_dim <= 8192 and input_dim >= 4096) on the batched matrix-core GEMV
+ * output_dim <= 4096 and input_dim >= 4096) on the batched matrix-core GEMV
  * (any |X| < 2^96), more on the 64-row x 16-token prefill tiles
  * (|X| < 65504); every tile is loaded straight into registers.  Errors and
  * tolerance as for q4k_matmul.
@@ -343,6 +344,28 @@ int q4k_matmul_tiled(const float *X, const uint8_t *w_tiled, int64_t n_tokens,
 int q4k_gemv_tiled_shaped(const float *x, const uint8_t *w_tiled, int64_t input_dim,
                           int64_t output_dim, float *y, void *stream, int waves,
                           int row_groups, int depth);
+
+/*
+ * q4k_matmul_shaped -- q4k_matmul with its kernel forced, for sweeps and
+ * tests: form 1 runs the few-token matrix-core GEMV (n_tokens <= 8, any
+ * |X| < 2^96); form 16, 32 or 64 runs the prefill tiles with that many
+ * weight rows per workgroup (x 16 tokens, |X| < 65504) at any token count;
+ * 0 is q4k_matmul itself.  Any other value (or form 1 with more than 8
+ * tokens) gives Q4K_EINVAL_DIM.  Results are within the q4k_matmul
+ * tolerance for every form.
+ */
+int q4k_matmul_shaped(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
+                      int64_t input_dim, int64_t output_dim, float *Y, void *stream,
+                      int form);
+
+/*
+ * q4k_matmul_tiled_shaped -- q4k_matmul_tiled with its kernel forced: form
+ * as for q4k_matmul_shaped (1 = the few-token GEMV, 16 / 32 / 64 = the
+ * prefill tiles, 0 = q4k_matmul_tiled itself).
+ */
+int q4k_matmul_tiled_shaped(const float *X, const uint8_t *w_tiled, int64_t n_tokens,
+                            int64_t input_dim, int64_t output_dim, float *Y, void *stream,
+                            int form);
 
 /* Static description of a return code; for Q4K_EHIP it includes the HIP
  * error text of the failing call on this host thread. */

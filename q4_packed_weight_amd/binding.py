@@ -23,7 +23,7 @@ EXPORTED = (
     "q4k_gemv", "q4k_matmul", "ternary_gemv_codes", "ternary_gemv", "ternary_matmul",
     "q4k_gemv_shaped", "q4_0_gemv", "q4_0_gemv_shaped", "q6k_gemv", "q6k_gemv_shaped",
     "q4k_tiled_size", "q4k_relayout_tiled", "q4k_gemv_tiled", "q4k_gemv_tiled_shaped",
-    "q4k_matmul_tiled",
+    "q4k_matmul_tiled", "q4k_matmul_shaped", "q4k_matmul_tiled_shaped",
     "q4k_strerror",
     "q4k_bench_empty", "q4k_bench_stream_read", "q4k_bench_copy",
 )
@@ -65,6 +65,8 @@ def lib():
         "q4k_gemv_tiled": [P, P, I64, I64, P, P],
         "q4k_gemv_tiled_shaped": [P, P, I64, I64, P, P, I, I, I],
         "q4k_matmul_tiled": [P, P, I64, I64, I64, P, P],
+        "q4k_matmul_shaped": [P, P, I64, I64, I64, P, P, I],
+        "q4k_matmul_tiled_shaped": [P, P, I64, I64, I64, P, P, I],
         "q4k_bench_empty": [P],
         "q4k_bench_stream_read": [P, I64, P, I64, P],
         "q4k_bench_copy": [P, P, I64, P],
@@ -211,6 +213,16 @@ def q4k_gemv_tiled(x, w_tiled, input_dim, output_dim, y, stream=None):
     return y
 
 
+def q4k_matmul_shaped(X, w_blocks, n_tokens, input_dim, output_dim, Y, form=0, stream=None):
+    M, K, N = int(n_tokens), int(input_dim), int(output_dim)
+    _expect(X, torch.float32, "X", M * K if _pos(M, K, N) else 0)
+    _expect(w_blocks, torch.uint8, "w_blocks", _q4k_need(K, N))
+    _expect(Y, torch.float32, "Y", M * N if _pos(M, K, N) else 0)
+    _check(lib().q4k_matmul_shaped(_ptr(X), _ptr(w_blocks), M, K, N, _ptr(Y), _stream(stream),
+                                   int(form)), "q4k_matmul_shaped")
+    return Y
+
+
 def q4k_matmul_tiled(X, w_tiled, n_tokens, input_dim, output_dim, Y, stream=None):
     M, K, N = int(n_tokens), int(input_dim), int(output_dim)
     _expect(X, torch.float32, "X", M * K if _pos(M, K, N) else 0)
@@ -218,6 +230,18 @@ def q4k_matmul_tiled(X, w_tiled, n_tokens, input_dim, output_dim, Y, stream=None
     _expect(Y, torch.float32, "Y", M * N if _pos(M, K, N) else 0)
     _check(lib().q4k_matmul_tiled(_ptr(X), _ptr(w_tiled), M, K, N, _ptr(Y), _stream(stream)),
            "q4k_matmul_tiled")
+    return Y
+
+
+def q4k_matmul_tiled_shaped(X, w_tiled, n_tokens, input_dim, output_dim, Y, form=0,
+                            stream=None):
+    M, K, N = int(n_tokens), int(input_dim), int(output_dim)
+    _expect(X, torch.float32, "X", M * K if _pos(M, K, N) else 0)
+    _expect(w_tiled, torch.uint8, "w_tiled", _tiled_need(K, N))
+    _expect(Y, torch.float32, "Y", M * N if _pos(M, K, N) else 0)
+    _check(lib().q4k_matmul_tiled_shaped(_ptr(X), _ptr(w_tiled), M, K, N, _ptr(Y),
+                                         _stream(stream), int(form)),
+           "q4k_matmul_tiled_shaped")
     return Y
 
 

@@ -145,11 +145,35 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
 }
 
 // Few tokens run on the batched matrix-core GEMV, one launch of up to 8
-// tokens, where it beats the 16-token prefill tiles: measured (graph-replayed
-// calls over rotating weights, input_dim 2048 to 14336) for every N with 2
-// tokens, N <= 8192 with up to 4 and N <= 4096 with up to 8.
-static bool use_gemv_batch(int64_t M, int64_t N) {
-  return M <= 2 || (M <= 4 && N <= 8192) || (M <= 8 && N <= 4096);
+// tokens, where it beats the prefill tiles (at the height prefill_rows
+// picks).  Measured on MI355X (graph-replayed calls over rotating weights,
+// batched / prefill us/call): 4096x4096 with 4 tokens 7.8 / 9.5 and with 5
+// to 8 tokens 10.0-10.2 / 9.5; 14336->4096 with 8 tokens 26.6 / 27.1;
+// 4096->8192 with 3 tokens 13.8 / 12.2; 2 tokens win everywhere (4096 ->
+// 14336: 14.6 / 16.8).
+static bool use_gemv_batch(int64_t M, int64_t K, int64_t N) {
+  return M <= 2 || (M <= 4 && N <= 4096) || (M <= 8 && N <= 4096 && K > 8192);
+}
+
+// Valid explicit forms of the batched products: 1 = the few-token GEMV
+// (at most 8 tokens), 16 / 32 / 64 = the prefill tiles with that many
+// weight rows per workgroup.
+static bool valid_matmul_form(int form, int64_t n_tokens) {
+  return (form == 1 && n_tokens <= 8) || form == 16 || form == 32 || form == 64;
+}
+
+int q4k_matmul_shaped(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
+                      int64_t input_dim, int64_t output_dim, float *Y, void *stream, int form) {
+  int rc = check_q4k(X, w_blocks, Y, n_tokens, input_dim, output_dim);
+  if (rc) return rc;
+  if (form == 0) return q4k_matmul(X, w_blocks, n_tokens, input_dim, output_dim, Y, stream);
+  if (!valid_matmul_form(form, n_tokens)) return Q4K_EINVAL_DIM;
+  hipError_t e = form == 1
+      ? q4k::gemv_batch_launch(X, w_blocks, Y, n_tokens, input_dim / 256, output_dim,
+                               (hipStream_t)stream)
+      : q4k::prefill_launch(X, w_blocks, n_tokens, input_dim, output_dim, Y,
+                            (hipStream_t)stream, form);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_matmul launch");
 }
 
 int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
@@ -157,7 +181,7 @@ int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
   int rc = check_q4k(X, w_blocks, Y, n_tokens, input_dim, output_dim);
   if (rc) return rc;
   if (n_tokens == 1) return q4k_gemv(X, w_blocks, input_dim, output_dim, Y, stream);
-  if (use_gemv_batch(n_tokens, output_dim)) {
+  if (use_gemv_batch(n_tokens, input_dim, output_dim)) {
     hipError_t e = q4k::gemv_batch_launch(X, w_blocks, Y, n_tokens, input_dim / 256, output_dim,
                                           (hipStream_t)stream);
     return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_matmul launch");
@@ -255,13 +279,29 @@ int q4k_gemv_tiled(const float *x, const uint8_t *w_tiled, int64_t input_dim,
 }
 
 // On tiled weights the batched kernel streams its tiles without LDS staging
-// and wins over the prefill tiles further out than on canonical weights:
-// measured (graph-replayed calls over rotating tiled copies, batched /
-// prefill us/call) 4096->14336 with 3 tokens 15.2 / 16.1, 4 tokens 15.8 /
-// 16.0, 5 tokens 21.4 / 16.1; 4096->8192 with 5 to 8 tokens 12.8-13.2 /
-// 15.3-15.4; 2048->8192 with 5 tokens 9.1 / 8.3; 14336->4096 equal up to 8.
+// and wins over the prefill tiles further out than on canonical weights.
+// Measured (graph-replayed calls over rotating tiled copies, batched /
+// prefill at the height prefill_rows picks, us/call): 4096x4096 with 8
+// tokens 8.6 / 9.9; 14336->4096 with 8 tokens 22.1 / 30.3; 4096->14336
+// with 4 tokens 15.6 / 16.0 and with 5 tokens 16.1 / 16.0; 4096->8192 with
+// 4 tokens 9.2 / 12.1 and with 5 to 8 tokens 12.6-12.8 / 12.0.
 static bool use_tiled_batch(int64_t M, int64_t K, int64_t N) {
-  return M <= 4 || (M <= 8 && N <= 8192 && K >= 4096);
+  return M <= 4 || (M <= 8 && N <= 4096 && K >= 4096);
+}
+
+int q4k_matmul_tiled_shaped(const float *X, const uint8_t *w_tiled, int64_t n_tokens,
+                            int64_t input_dim, int64_t output_dim, float *Y, void *stream,
+                            int form) {
+  int rc = check_q4k(X, w_tiled, Y, n_tokens, input_dim, output_dim);
+  if (rc) return rc;
+  if (form == 0) return q4k_matmul_tiled(X, w_tiled, n_tokens, input_dim, output_dim, Y, stream);
+  if (!valid_matmul_form(form, n_tokens)) return Q4K_EINVAL_DIM;
+  hipError_t e = form == 1
+      ? q4k::gemv_tiled_batch_launch(X, w_tiled, Y, n_tokens, input_dim / 256, output_dim,
+                                     (hipStream_t)stream)
+      : q4k::prefill_tiled_launch(X, w_tiled, n_tokens, input_dim / 256, output_dim, Y,
+                                  (hipStream_t)stream, form);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_matmul_tiled launch");
 }
 
 // One token is q4k_gemv_tiled, a few tokens the batched kernel, more the

@@ -57,7 +57,7 @@ hipError_t gemv_tiled_launch(const float *x, const uint8_t *wt, float *y, int64_
 hipError_t gemv_tiled_batch_launch(const float *X, const uint8_t *wt, float *Y, int64_t M,
                                    int64_t nb, int64_t N, hipStream_t stream);
 hipError_t prefill_tiled_launch(const float *X, const uint8_t *wt, int64_t M, int64_t nb,
-                                int64_t N, float *Y, hipStream_t stream);
+                                int64_t N, float *Y, hipStream_t stream, int rows = 0);
 
 hipError_t ternary_launch(const float *x, const uint8_t *codes, float scale,
                           bool apply_scale, int64_t K, int64_t N, float *y,
@@ -68,8 +68,10 @@ hipError_t ternary_launch(const float *x, const uint8_t *codes, float scale,
 hipError_t ternary_matmul_launch(const float *X, const uint8_t *codes, float scale, int64_t M,
                                  int64_t K, int64_t N, float *Y, hipStream_t stream);
 
+// rows: weight rows per workgroup (64, 32 or 16); 0 = prefill_rows(M, N).
 hipError_t prefill_launch(const float *X, const uint8_t *w, int64_t M,
-                          int64_t K, int64_t N, float *Y, hipStream_t stream);
+                          int64_t K, int64_t N, float *Y, hipStream_t stream, int rows = 0);
+int prefill_rows(int64_t M, int64_t N);
 
 // 1 <= M <= 8 tokens on the matrix cores (q4k_gemv_batch.hip); X is
 // [M][nb*256], Y is [M][N].

@@ -15,7 +15,9 @@
 // atomics, and the result does not depend on scheduling.  For 256
 // workgroups the 64x16 tile keeps the bytes a CU pulls from L2 near their
 // minimum (64 rows of weights and 16 rows of activations per unit of
-// input_dim).  The token groups of a row tile are gridDim.x workgroup ids
+// input_dim).  With few token tiles 64-row workgroups leave CUs idle (16
+// tokens x 4096 rows is 64 workgroups), so the launch narrows them to 32
+// or 16 rows until the grid reaches one workgroup per CU.  The token groups of a row tile are gridDim.x workgroup ids
 // apart, which puts them on the same XCD (and its L2) whenever the number
 // of row tiles is a multiple of 8.
 //
@@ -51,30 +53,38 @@ namespace q4k {
 namespace {
 
 constexpr int kBlockBytes = 144;
-constexpr int PF_ROWS = 64;           // weight rows per workgroup (4 row tiles)
 constexpr int PF_TOK = 16;            // tokens per workgroup (one token tile)
 constexpr int PF_BLKS = 4;            // super-blocks per stage
-constexpr int PF_WAVES = 8;           // two waves per block: row tiles {0,1} and {2,3}
+constexpr int PF_WAVES = 8;           // two waves per block of a stage
 constexpr int PF_THREADS = 64 * PF_WAVES;
-constexpr int PF_RPAD = PF_ROWS + 4;  // padded row dimension of the header tables
 // LDS row pitches in dwords: an activation row (256 fp16 positions) + 16 B,
-// a staged weight block (144 B) + 8 B, and one super-block of all 64 rows
-// + 32 B; the pads spread consecutive rows over the banks.
+// a staged weight block (144 B) + 8 B; the pads spread consecutive rows over
+// the banks.
 constexpr int XROW = 128 + 4;
 constexpr int WROW = 36 + 2;
-constexpr int WBLK = PF_ROWS * WROW + 8;
-// Loads of a stage: waves 0-3 (256 threads) bring the weights, 16-byte
-// chunk q = t + 256 m of the 64 rows' 576-byte stage pieces; all 8 waves
-// bring the activations, float4 i of thread tid = token 2i + (tid >= 256),
-// positions 4t .. 4t+3 of the stage (t = tid % 256).
-constexpr int W_CHUNKS = PF_ROWS * PF_BLKS * 9;           // 2304
-constexpr int W_PER_THREAD = W_CHUNKS / 256;              // 9
 constexpr int X_PER_THREAD = PF_TOK / 2;                  // 8
-static_assert(W_CHUNKS % 256 == 0, "weight chunks must divide evenly");
+constexpr int W_PER_THREAD = 9;  // 16-byte weight chunks per loader thread per stage
 
+// ROWS weight rows (RT = ROWS / 16 MFMA row tiles) per workgroup.  The
+// waves of a stage are (block bb, half): with 4 row tiles half h computes
+// row tiles 2h, 2h+1 over all eight sub-blocks; with 2, row tile h; with 1,
+// the one row tile over sub-blocks 4h .. 4h+3.  Loads: the first RT waves
+// (4 ROWS threads) bring the weights, 16-byte chunk q = t + 4 ROWS m of the
+// rows' 576-byte stage pieces; all 8 waves bring the activations, float4 i
+// of thread tid = token 2i + (tid >= 256), positions 4t .. 4t+3 of the
+// stage (t = tid % 256).
+template <int ROWS>
 __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     const float *X, const uint8_t *w, float *__restrict__ Y, int M, int nb,
     int N) {
+  constexpr int RT = ROWS / 16;
+  constexpr int TPW = RT == 4 ? 2 : 1;    // row tiles per wave
+  constexpr int NJ = RT == 1 ? 2 : 4;     // sub-block pairs per wave
+  constexpr int NS = RT == 1 ? 2 : 1;     // waves sharing a block's rows
+  constexpr int RPAD = ROWS + 4;          // padded row dimension of the header tables
+  constexpr int WBLK = ROWS * WROW + 8;   // one super-block of all rows + 32 B
+  constexpr int LOADERS = 4 * ROWS;       // threads that load the weights
+  static_assert(ROWS * PF_BLKS * 9 == LOADERS * W_PER_THREAD, "weight chunks must divide evenly");
   // xh/xl: fp16 hi and lo activations [block of stage][token][position
   // pairs in operand order]; wt: raw weight blocks [block of stage][row];
   // header tables of the stage's blocks: fp16 scale pairs (mul, add) per
@@ -82,9 +92,9 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   __shared__ __align__(16) uint32_t xh[PF_BLKS][PF_TOK][XROW];
   __shared__ __align__(16) uint32_t xl[PF_BLKS][PF_TOK][XROW];
   __shared__ __align__(16) uint32_t wt[PF_BLKS * WBLK];
-  __shared__ uint2 sc_tab[PF_BLKS][8][PF_RPAD];
-  __shared__ float c_tab[PF_BLKS][8][PF_RPAD];
-  __shared__ __align__(16) float d_tab[PF_BLKS][PF_ROWS];
+  __shared__ uint2 sc_tab[PF_BLKS][8][RPAD];
+  __shared__ float c_tab[PF_BLKS][8][RPAD];
+  __shared__ __align__(16) float d_tab[PF_BLKS][ROWS];
 
   // The host validates nb >= 1; saying so lets the compiler fetch every
   // kernel argument in one round trip.
@@ -92,13 +102,15 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const bool w_loader = wave < 4;
-  const int t = tid & 255;  // thread index within its loader half
+  const bool w_loader = wave < RT;  // waves 0 .. RT-1: threads tid < LOADERS
+  const int t = tid & 255;  // thread index within its activation-loader half
   const int bb = wave & 3;  // block of the stage this wave computes
-  const int half = wave >> 2;  // row tiles 2*half and 2*half + 1
+  const int half = wave >> 2;
+  const int rt0 = RT == 4 ? 2 * half : (RT == 2 ? half : 0);  // first row tile of this wave
+  const int j0 = RT == 1 ? 2 * half : 0;                      // first sub-block pair
   const int r = lane & 15;  // A: row within a row tile; B and D: token
   const int g = lane >> 4;  // lane group
-  const int row0 = blockIdx.x * PF_ROWS;
+  const int row0 = blockIdx.x * ROWS;
   const int tok0 = blockIdx.y * PF_TOK;
   const int K = nb * 256;
   const int row_bytes = nb * kBlockBytes;
@@ -118,7 +130,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   int woff[W_PER_THREAD];
 #pragma unroll
   for (int m = 0; m < W_PER_THREAD; ++m) {
-    const int q = t + 256 * m;
+    const int q = tid + LOADERS * m;
     const int row = q / 36;
     woff[m] = row * row_bytes + 16 * (q - 36 * row);
   }
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     if (w_loader) {
 #pragma unroll
       for (int m = 0; m < W_PER_THREAD; ++m) {
-        const int q = t + 256 * m;
+        const int q = tid + LOADERS * m;
         const int row = q / 36;
         const int cc = q - 36 * row;
         const int b = cc / 9;
@@ -163,14 +175,16 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     }
   };
 
-  floatx4 y_acc[2], m_acc[2];
+  floatx4 y_acc[TPW], m_acc[TPW];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) y_acc[a] = m_acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < TPW; ++a) y_acc[a] = m_acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
   half8_t ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
   const uint32_t *wblk = &wt[bb * WBLK];
-  const int hrow = 32 * half + (lane & 31);  // header row decoded by this lane
+  // header row decoded by this lane: the rows of the wave's row tiles (lanes
+  // past them repeat rows and write the same values)
+  const int hrow = 16 * rt0 + (lane & (16 * TPW - 1));
 
   // The token groups of a row tile start at different stages (and wrap
   // around), so that together they read whole weight rows at any moment
@@ -184,8 +198,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     if (it + 1 < n_stages) load_stage(st + 1 < n_stages ? st + 1 : 0);  // in flight during the MFMAs
 
     if (st * PF_BLKS + bb < nb) {
-      // ---- headers of this wave's 32 rows of block bb (lanes 32-63 repeat
-      //      lanes 0-31 and write the same values)
+      // ---- headers of this wave's rows of block bb
       {
         const uint2 h01 = *reinterpret_cast<const uint2 *>(&wblk[hrow * WROW]);
         const uint2 h23 = *reinterpret_cast<const uint2 *>(&wblk[hrow * WROW + 2]);
@@ -199,6 +212,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
         const uint32_t scw[2] = {sc03, sc47}, mnw[2] = {mn03, mn47};
 #pragma unroll
         for (int hw = 0; hw < 2; ++hw) {
+          if (RT == 1 && hw != half) continue;  // wave-uniform: only its own sub-blocks
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int s = 4 * hw + e;
@@ -216,20 +230,21 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
         }
       }
 
-      // ---- MFMAs for row tiles 2*half + a.  The two accumulator chains are
+      // ---- MFMAs for the wave's row tiles.  The accumulator chains are
       //      interleaved with the sub-block-sum chain.
-      floatx4 acc[2];
+      floatx4 acc[TPW];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int a = 0; a < TPW; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
       // xsb[c]: the B operand of the fp32 MFMA, the sum of x over
       // sub-block 4c + g for token r (lane group g picks its sub-block)
       float xsb[2] = {0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint2 qb[2], tl[2], th[2];
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int j = j0 + jj;
+        uint2 qb[TPW], tl[TPW], th[TPW];
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int row = 16 * (2 * half + a) + r;
+        for (int a = 0; a < TPW; ++a) {
+          const int row = 16 * (rt0 + a) + r;
           qb[a] = *reinterpret_cast<const uint2 *>(&wblk[row * WROW + 4 + 8 * j + 2 * g]);
           tl[a] = sc_tab[bb][2 * j][row];
           th[a] = sc_tab[bb][2 * j + 1][row];
@@ -239,26 +254,26 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
           const int s = 2 * j + h;
           const half8_t Bh = *reinterpret_cast<const half8_t *>(&xh[bb][r][16 * s + 4 * g]);
           const half8_t Bl = *reinterpret_cast<const half8_t *>(&xl[bb][r][16 * s + 4 * g]);
-          half8_t A[2];
+          half8_t A[TPW];
 #pragma unroll
-          for (int a = 0; a < 2; ++a)
+          for (int a = 0; a < TPW; ++a)
             A[a] = h ? dequant8(qb[a].x, qb[a].y, true, th[a].x, th[a].y)
                      : dequant8(qb[a].x, qb[a].y, false, tl[a].x, tl[a].y);
           floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-          for (int a = 0; a < 2; ++a)
+          for (int a = 0; a < TPW; ++a)
             acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[a], Bh, acc[a], 0, 0, 0);
           sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bl, sx, 0, 0, 0);
 #pragma unroll
-          for (int a = 0; a < 2; ++a)
+          for (int a = 0; a < TPW; ++a)
             acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[a], Bl, acc[a], 0, 0, 0);
           // sum of x over sub-block s for token r (every row of the tile)
           if ((s & 3) == g) xsb[s >> 2] = sx[0];
         }
       }
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int rt = 2 * half + a;
+      for (int a = 0; a < TPW; ++a) {
+        const int rt = rt0 + a;
         // d of rows 16 rt + 4g + e (the rows of this lane's D elements)
         const float4 dv = *reinterpret_cast<const float4 *>(&d_tab[bb][16 * rt + 4 * g]);
         y_acc[a][0] = __builtin_fmaf(dv.x, acc[a][0], y_acc[a][0]);
@@ -267,50 +282,92 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
         y_acc[a][3] = __builtin_fmaf(dv.w, acc[a][3], y_acc[a][3]);
         // lazy-dmin term: A[row][kk] = dmin*m of sub-block 4c + kk, B = sums
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c) {
+          if (RT == 1 && c != half) continue;  // wave-uniform: its own sub-blocks
           m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(c_tab[bb][4 * c + g][16 * rt + r], xsb[c],
                                                           m_acc[a], 0, 0, 0);
+        }
       }
     }
     __syncthreads();  // the next stage overwrites the LDS tiles
   }
 
-  // ---- add the four blocks' partial tiles (through the activation tiles,
-  //      no longer needed) and store.  Lane (token r, group g) holds rows
-  //      16 rt + 4g + e of its token.
-  float4 *red = reinterpret_cast<float4 *>(&xh[0][0][0]);  // [block][token][17]
+  // ---- add the waves' partial tiles (through the activation tiles, no
+  //      longer needed) and store.  Lane (token r, group g) holds rows
+  //      16 rt + 4g + e of its token; partial slot (bb, s) of the rows.
+  constexpr int RROW = ROWS + 4;
+  float *red = reinterpret_cast<float *>(&xh[0][0][0]);  // [block][share][token][RROW]
+  static_assert(PF_BLKS * NS * PF_TOK * RROW <= PF_BLKS * PF_TOK * XROW,
+                "the partial tiles must fit in the activation tile");
+  const int sh = RT == 1 ? half : 0;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-    red[(bb * PF_TOK + r) * 17 + 4 * (2 * half + a) + g] =
+  for (int a = 0; a < TPW; ++a)
+    *reinterpret_cast<float4 *>(&red[((bb * NS + sh) * PF_TOK + r) * RROW + 16 * (rt0 + a) + 4 * g]) =
         make_float4(y_acc[a][0] - m_acc[a][0], y_acc[a][1] - m_acc[a][1],
                     y_acc[a][2] - m_acc[a][2], y_acc[a][3] - m_acc[a][3]);
   __syncthreads();
-  const float *redf = reinterpret_cast<const float *>(red);
-  for (int o = tid; o < PF_TOK * PF_ROWS; o += PF_THREADS) {
-    const int tok = o / PF_ROWS, rr = o % PF_ROWS;
+  for (int o = tid; o < PF_TOK * ROWS; o += PF_THREADS) {
+    const int tok = o / ROWS, rr = o % ROWS;
     float v = 0.f;
 #pragma unroll
-    for (int b = 0; b < PF_BLKS; ++b) v += redf[(b * PF_TOK + tok) * 68 + rr];
+    for (int b = 0; b < PF_BLKS; ++b)
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) v += red[((b * NS + s2) * PF_TOK + tok) * RROW + rr];
     if (tok0 + tok < M && row0 + rr < N) Y[(int64_t)(tok0 + tok) * N + row0 + rr] = v;
   }
 }
 
-}  // namespace
-
-hipError_t prefill_launch(const float *X, const uint8_t *w, int64_t M,
-                          int64_t K, int64_t N, float *Y, hipStream_t stream) {
+template <int ROWS>
+hipError_t prefill_launch_rows(const float *X, const uint8_t *w, int64_t M, int64_t K, int64_t N,
+                               float *Y, hipStream_t stream) {
   const int64_t nb = K / 256;
-  // Offsets formed in the kernel (a row tile of 64 rows plus one stage past
-  // its end, 16 rows of X plus one stage) must stay below 2^31 bytes.
-  if ((int64_t)PF_ROWS * nb * kBlockBytes + 4096 >= ((int64_t)1 << 31) ||
+  // Offsets formed in the kernel (a row tile of ROWS rows plus one stage
+  // past its end, 16 rows of X plus one stage) must stay below 2^31 bytes.
+  if ((int64_t)ROWS * nb * kBlockBytes + 4096 >= ((int64_t)1 << 31) ||
       ((int64_t)PF_TOK * K + 2048) * 4 >= ((int64_t)1 << 31) || N > 0x7FFFFFFF ||
       M > 0x7FFFFFFF)
     return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((N + PF_ROWS - 1) / PF_ROWS), (unsigned)((M + PF_TOK - 1) / PF_TOK));
+  const dim3 grid((unsigned)((N + ROWS - 1) / ROWS), (unsigned)((M + PF_TOK - 1) / PF_TOK));
   if (grid.y > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(q4k_prefill_kernel, grid, dim3(PF_THREADS), 0, stream, X, w, Y, (int)M,
-                     (int)nb, (int)N);
+  hipLaunchKernelGGL(q4k_prefill_kernel<ROWS>, grid, dim3(PF_THREADS), 0, stream, X, w, Y,
+                     (int)M, (int)nb, (int)N);
   return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_rows(int64_t M, int64_t N) {
+  // One workgroup per CU at a time (the LDS tiles allow no second), so a
+  // height costs rounds of 256 workgroups x its per-workgroup time.  The
+  // per-workgroup times measured on MI355X (graph-replayed calls, input_dim
+  // 4096, 256 workgroups each): 64 rows 14.3 us, 32 rows 11.0, 16 rows 8.5,
+  // i.e. 100 : 77 : 60.  Measured us/call, 64-row tiles vs the chosen
+  // height: 16 tokens x 4096 rows 15.7 vs 9.9 (16 rows), 32 x 4096 15.5 vs
+  // 12.4 (32 rows), 16 tokens 14336 -> 4096 48.9 vs 29.2 (16 rows); 48 x 4096
+  // and 16 x 14336 stay at 64 rows (doubling the grid past one round cost
+  // 22.2 vs 15.6 and 24.0 vs 17.4).
+  const int64_t tok_groups = (M + PF_TOK - 1) / PF_TOK;
+  const int rows[3] = {64, 32, 16};
+  const int64_t cost[3] = {100, 77, 60};
+  int best = 64;
+  int64_t best_cost = INT64_MAX;
+  for (int i = 0; i < 3; ++i) {
+    const int64_t grid = (N + rows[i] - 1) / rows[i] * tok_groups;
+    const int64_t c = (grid + 255) / 256 * cost[i];
+    if (c < best_cost) { best_cost = c; best = rows[i]; }
+  }
+  return best;
+}
+
+hipError_t prefill_launch(const float *X, const uint8_t *w, int64_t M,
+                          int64_t K, int64_t N, float *Y, hipStream_t stream, int rows) {
+  if (rows == 0) rows = prefill_rows(M, N);
+  switch (rows) {
+    case 64: return prefill_launch_rows<64>(X, w, M, K, N, Y, stream);
+    case 32: return prefill_launch_rows<32>(X, w, M, K, N, Y, stream);
+    case 16: return prefill_launch_rows<16>(X, w, M, K, N, Y, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace q4k

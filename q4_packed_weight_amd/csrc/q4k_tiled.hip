@@ -464,62 +464,77 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
   }
 }
 
-// Prefill on tiled weights: the 64-row x 16-token tiles of q4k_prefill.hip
-// (same arithmetic: A = sc*q exact in fp16, activations split into fp16 hi
-// + lo, d applied per block, the lazy-dmin term on the fp32 MFMA), with the
+// Prefill on tiled weights: the prefill tiles of q4k_prefill.hip (ROWS =
+// 64, 32 or 16 weight rows, i.e. RT row groups, x 16 tokens; the same
+// arithmetic: A = sc*q exact in fp16, activations split into fp16 hi + lo,
+// d applied per block, the lazy-dmin term on the fp32 MFMA), with the
 // weights no longer staged through LDS.  Wave (bb, half) computes
-// super-block bb of each 4-super-block stage for row groups 2 half and
-// 2 half + 1: it loads those two tiles straight into registers one stage
-// ahead (its A operand bytes are its own 16-byte slots) and decodes its
-// rows' headers in registers; only the activations go through LDS.
+// super-block bb of each 4-super-block stage: with 4 row groups for row
+// groups 2 half and 2 half + 1, with 2 for row group half, with 1 for
+// sub-blocks 4 half .. 4 half + 3 of the one row group (then it loads only
+// the qs half it uses).  It loads its tiles straight into registers one
+// stage ahead (its A operand bytes are its own 16-byte slots) and decodes
+// its rows' headers in registers; only the activations go through LDS.
 
 constexpr int TP_TOK = 16;    // tokens per workgroup (one MFMA token tile)
 constexpr int TP_BLKS = 4;    // super-blocks per stage
 constexpr int TP_WAVES = 8;
 constexpr int TP_XROW = 128 + 4;  // LDS dwords per staged activation row (+ 16 B)
 
+template <int ROWS>
 __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     const float *X, const uint8_t *wt, float *__restrict__ Y, int M, int nb, int N) {
+  constexpr int RT = ROWS / 16;            // row groups per workgroup
+  constexpr int TPW = RT == 4 ? 2 : 1;     // row groups per wave
+  constexpr int NJ = RT == 1 ? 2 : 4;      // sub-block pairs per wave
+  constexpr int NH = RT == 1 ? 1 : 2;      // qs halves per tile the wave loads
+  constexpr int NS = RT == 1 ? 2 : 1;      // waves sharing a block's rows
   __shared__ __align__(16) uint32_t xh[TP_BLKS][TP_TOK][TP_XROW];
   __shared__ __align__(16) uint32_t xl[TP_BLKS][TP_TOK][TP_XROW];
-  __shared__ __align__(16) float dtab[TP_WAVES][2][16];
+  __shared__ __align__(16) float dtab[TP_WAVES][TPW][16];
 
   __builtin_assume(nb >= 1);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bb = wave & 3;     // super-block of the stage this wave computes
-  const int half = wave >> 2;  // row groups 2 half and 2 half + 1 of the workgroup
+  const int half = wave >> 2;
+  const int rt0 = RT == 4 ? 2 * half : (RT == 2 ? half : 0);  // first row group of this wave
+  const int j0 = RT == 1 ? 2 * half : 0;                      // first sub-block pair
   const int r = lane & 15;     // A: row within a row group; B and D: token
   const int g = lane >> 4;
   const int t = tid & 255;
   const int NG = (N + kTileRows - 1) / kTileRows;
-  const int rg0 = blockIdx.x * 4;
+  const int rg0 = blockIdx.x * RT;
   const int tok0 = blockIdx.y * TP_TOK;
   const int K = nb * 256;
   const int n_stages = (nb + TP_BLKS - 1) / TP_BLKS;
 
-  // the workgroup's (up to) four row groups, one contiguous tile stream
+  // the workgroup's (up to) RT row groups, one contiguous tile stream
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(
-      wt + (int64_t)rg0 * nb * kTileBytes, (int64_t)min(4, NG - rg0) * nb * kTileBytes);
+      wt + (int64_t)rg0 * nb * kTileBytes, (int64_t)min(RT, NG - rg0) * nb * kTileBytes);
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(X + (int64_t)tok0 * K, (int64_t)(M - tok0) * K * 4);
   constexpr int kPastEnd = 0x7FFFF000;
 
-  const int vq0 = 16 * lane, vq1 = 1024 + 16 * lane, vhd = 2048 + 16 * r;
-  uint4 q0[2][2], q1[2][2], hd[2][2];  // [buffer][row group a]
+  // qs half hs of a tile at 1024 hs + 16 lane (with one row group per
+  // workgroup a wave loads only its own half), the header at 2048 + 16 r
+  const int vq[2] = {16 * lane + (RT == 1 ? 1024 * half : 0), 1024 + 16 * lane};
+  const int vhd = 2048 + 16 * r;
+  uint4 qs[2][TPW][NH], hd[2][TPW];  // [buffer][row group a][qs half]
   float4 xv[8];
   const int tok_lo = tid >> 8;  // float4 i of this thread: token 2i + tok_lo
-  auto load_stage = [&](int st, int buf) {
+  auto load_stage = [&](int st, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       xv[i] = load_buf_f4(xr, 16 * t + 4 * K * (2 * i + tok_lo), 4096 * st);
     const int b = st * TP_BLKS + bb;
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int off = b < nb ? ((2 * half + a) * nb + b) * kTileBytes : kPastEnd;
-      q0[buf][a] = load_buf_stream16(wr, vq0, off);
-      q1[buf][a] = load_buf_stream16(wr, vq1, off);
+    for (int a = 0; a < TPW; ++a) {
+      const int off = b < nb ? ((rt0 + a) * nb + b) * kTileBytes : kPastEnd;
+#pragma unroll
+      for (int hs = 0; hs < NH; ++hs) qs[buf][a][hs] = load_buf_stream16(wr, vq[hs], off);
       hd[buf][a] = load_buf_stream16(wr, vhd, off);
     }
   };
@@ -541,21 +556,22 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     }
   };
 
-  floatx4 y_acc[2], m_acc[2];
+  floatx4 y_acc[TPW], m_acc[TPW];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) y_acc[a] = m_acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < TPW; ++a) y_acc[a] = m_acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
   half8_t ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
 
-  auto compute = [&](int buf) {
-    // headers of row r of this wave's two row groups: the fp16 (mul, add)
-    // pairs per sub-block, dmin*m of sub-blocks g and 4 + g (the lazy-dmin
+  auto compute = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    // headers of row r of this wave's row groups: the fp16 (mul, add) pairs
+    // of its sub-blocks, dmin*m of sub-blocks g and 4 + g (the lazy-dmin
     // MFMA's A operand), and d into the wave's table for the D rows
-    uint32_t mul[2][8], add[2][8];
-    float cm[2][2];
+    uint32_t mul[TPW][2 * NJ], add[TPW][2 * NJ];  // by the wave's own sub-block index
+    float cm[TPW][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < TPW; ++a) {
       const uint4 h = hd[buf][a];
       const float d = half_lo(h.x), dmin = half_hi(h.x);
       const uint32_t sc03 = h.y & 0x3F3F3F3Fu;
@@ -563,49 +579,51 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
       const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
       const uint32_t mn47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
 #pragma unroll
-      for (int sb = 0; sb < 8; ++sb) {
-        const float scf = (float)(((sb < 4 ? sc03 : sc47) >> (8 * (sb & 3))) & 255u);
+      for (int ls = 0; ls < 2 * NJ; ++ls) {  // sub-block 4 half + ls (one row group), else ls
+        const uint32_t scw = RT == 1 ? (half ? sc47 : sc03) : (ls < 4 ? sc03 : sc47);
+        const float scf = (float)((scw >> (8 * (ls & 3))) & 255u);
         // even sub-blocks are low nibbles, odd ones high nibbles (16 v)
-        const float mulf = (sb & 1) ? scf * 0.0625f : scf;
-        const float addf = (sb & 1) ? scf * -64.0f : scf * -1024.0f;
+        const float mulf = (ls & 1) ? scf * 0.0625f : scf;
+        const float addf = (ls & 1) ? scf * -64.0f : scf * -1024.0f;
         half2_t m2, a2;
         m2.x = m2.y = (_Float16)mulf;
         a2.x = a2.y = (_Float16)addf;
-        mul[a][sb] = as_u32h(m2);
-        add[a][sb] = as_u32h(a2);
+        mul[a][ls] = as_u32h(m2);
+        add[a][ls] = as_u32h(a2);
       }
       cm[a][0] = dmin * (float)((mn03 >> (8 * g)) & 255u);  // sub-block g
       cm[a][1] = dmin * (float)((mn47 >> (8 * g)) & 255u);  // sub-block 4 + g
       dtab[wave][a][r] = d;  // the four lane groups write the same value
     }
-    floatx4 acc[2];
+    floatx4 acc[TPW];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < TPW; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
     float xsb[2] = {0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint2 qb[2];
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int j = j0 + jj;
+      uint2 qb[TPW];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const uint4 v = j < 2 ? q0[buf][a] : q1[buf][a];
-        qb[a] = (j & 1) ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
+      for (int a = 0; a < TPW; ++a) {
+        const uint4 v = qs[buf][a][NH == 1 ? 0 : jj >> 1];
+        qb[a] = (jj & 1) ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int sb = 2 * j + hh;
         const half8_t Bh = *reinterpret_cast<const half8_t *>(&xh[bb][r][16 * sb + 4 * g]);
         const half8_t Bl = *reinterpret_cast<const half8_t *>(&xl[bb][r][16 * sb + 4 * g]);
-        half8_t A[2];
+        half8_t A[TPW];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-          A[a] = dequant8(qb[a].x, qb[a].y, hh != 0, mul[a][sb], add[a][sb]);
+        for (int a = 0; a < TPW; ++a)
+          A[a] = dequant8(qb[a].x, qb[a].y, hh != 0, mul[a][2 * jj + hh], add[a][2 * jj + hh]);
         floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < TPW; ++a)
           acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[a], Bh, acc[a], 0, 0, 0);
         sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bl, sx, 0, 0, 0);
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < TPW; ++a)
           acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[a], Bl, acc[a], 0, 0, 0);
         // sum of x over sub-block sb for token r (every row of the tile)
         if ((sb & 3) == g) xsb[sb >> 2] = sx[0];
@@ -616,7 +634,7 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < TPW; ++a) {
       const float4 dv = *reinterpret_cast<const float4 *>(&dtab[wave][a][4 * g]);
       y_acc[a][0] = __builtin_fmaf(dv.x, acc[a][0], y_acc[a][0]);
       y_acc[a][1] = __builtin_fmaf(dv.y, acc[a][1], y_acc[a][1]);
@@ -624,8 +642,10 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
       y_acc[a][3] = __builtin_fmaf(dv.w, acc[a][3], y_acc[a][3]);
       // lazy-dmin term: A[row][kk] = dmin*m of sub-block 4c + kk, B = sums
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 2; ++c) {
+        if (RT == 1 && c != half) continue;  // wave-uniform: its own sub-blocks
         m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(cm[a][c], xsb[c], m_acc[a], 0, 0, 0);
+      }
     }
     // the next block's d values overwrite the table only after these reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -642,36 +662,54 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     const int st = st0 + it < n_stages ? st0 + it : st0 + it - n_stages;
     stage_x();
     __syncthreads();
-    if (it + 1 < n_stages) load_stage(st + 1 < n_stages ? st + 1 : 0, buf ^ 1);
-    if (st * TP_BLKS + bb < nb) compute(buf);  // wave-uniform
+    if (it + 1 < n_stages)
+      load_stage(st + 1 < n_stages ? st + 1 : 0, std::integral_constant<int, buf ^ 1>());
+    if (st * TP_BLKS + bb < nb) compute(bufc);  // wave-uniform
     __syncthreads();  // the next stage overwrites the activation tiles
   };
-  load_stage(st0, 0);
+  load_stage(st0, std::integral_constant<int, 0>());
   for (int it = 0; it < n_stages; it += 2) {
     step(it, std::integral_constant<int, 0>());
     if (it + 1 >= n_stages) break;
     step(it + 1, std::integral_constant<int, 1>());
   }
 
-  // Add the four blocks' partial tiles (through the activation tiles, no
-  // longer needed) and store.  Lane (token r, group g) holds rows
-  // 16 (2 half + a) + 4g + e of its token.
-  float4 *red = reinterpret_cast<float4 *>(&xh[0][0][0]);  // [block][token][17]
+  // Add the waves' partial tiles (through the activation tiles, no longer
+  // needed) and store.  Lane (token r, group g) holds rows 16 (rt0 + a) +
+  // 4g + e of its token; partial slot (bb, share) of the rows.
+  constexpr int RROW = ROWS + 4;
+  float *red = reinterpret_cast<float *>(&xh[0][0][0]);  // [block][share][token][RROW]
+  static_assert(TP_BLKS * NS * TP_TOK * RROW <= TP_BLKS * TP_TOK * TP_XROW,
+                "the partial tiles must fit in the activation tile");
+  const int shr = RT == 1 ? half : 0;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-    red[(bb * TP_TOK + r) * 17 + 4 * (2 * half + a) + g] =
+  for (int a = 0; a < TPW; ++a)
+    *reinterpret_cast<float4 *>(&red[((bb * NS + shr) * TP_TOK + r) * RROW + 16 * (rt0 + a) + 4 * g]) =
         make_float4(y_acc[a][0] - m_acc[a][0], y_acc[a][1] - m_acc[a][1],
                     y_acc[a][2] - m_acc[a][2], y_acc[a][3] - m_acc[a][3]);
   __syncthreads();
-  const float *redf = reinterpret_cast<const float *>(red);
-  for (int o = tid; o < TP_TOK * 64; o += 64 * TP_WAVES) {
-    const int tok = o / 64, rr = o % 64;
+  for (int o = tid; o < TP_TOK * ROWS; o += 64 * TP_WAVES) {
+    const int tok = o / ROWS, rr = o % ROWS;
     float v = 0.f;
 #pragma unroll
-    for (int b = 0; b < TP_BLKS; ++b) v += redf[(b * TP_TOK + tok) * 68 + rr];
+    for (int b = 0; b < TP_BLKS; ++b)
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) v += red[((b * NS + s2) * TP_TOK + tok) * RROW + rr];
     const int row = rg0 * kTileRows + rr;
     if (tok0 + tok < M && row < N) Y[(int64_t)(tok0 + tok) * N + row] = v;
   }
+}
+
+template <int ROWS>
+hipError_t prefill_tiled_launch_rows(const float *X, const uint8_t *wt, int64_t M, int64_t nb,
+                                     int64_t N, float *Y, hipStream_t stream) {
+  const int64_t NG = (N + kTileRows - 1) / kTileRows;
+  const dim3 grid((unsigned)((NG + ROWS / 16 - 1) / (ROWS / 16)),
+                  (unsigned)((M + TP_TOK - 1) / TP_TOK));
+  if (grid.y > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(q4k_prefill_tiled_kernel<ROWS>, grid, dim3(64 * TP_WAVES), 0, stream, X, wt,
+                     Y, (int)M, (int)nb, (int)N);
+  return hipGetLastError();
 }
 
 template <int W, int D, int CAP>
@@ -770,18 +808,19 @@ hipError_t gemv_tiled_batch_launch(const float *X, const uint8_t *wt, float *Y, 
 }
 
 hipError_t prefill_tiled_launch(const float *X, const uint8_t *wt, int64_t M, int64_t nb,
-                               int64_t N, float *Y, hipStream_t stream) {
+                               int64_t N, float *Y, hipStream_t stream, int rows) {
   // Offsets formed in the kernel: four row groups' tiles, and 16 rows of X
   // plus one stage, stay below the past-the-end offset.
   if (4 * nb * kTileBytes > 0x7FFF0000 || ((int64_t)TP_TOK * nb * 256 + 2048) * 4 > 0x7FFF0000 ||
       N > 0x7FFFFFFF || M > 0x7FFFFFFF)
     return hipErrorInvalidValue;
-  const int64_t NG = (N + kTileRows - 1) / kTileRows;
-  const dim3 grid((unsigned)((NG + 3) / 4), (unsigned)((M + TP_TOK - 1) / TP_TOK));
-  if (grid.y > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(q4k_prefill_tiled_kernel, grid, dim3(64 * TP_WAVES), 0, stream, X, wt, Y,
-                     (int)M, (int)nb, (int)N);
-  return hipGetLastError();
+  if (rows == 0) rows = prefill_rows(M, N);
+  switch (rows) {
+    case 64: return prefill_tiled_launch_rows<64>(X, wt, M, nb, N, Y, stream);
+    case 32: return prefill_tiled_launch_rows<32>(X, wt, M, nb, N, Y, stream);
+    case 16: return prefill_tiled_launch_rows<16>(X, wt, M, nb, N, Y, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace q4k

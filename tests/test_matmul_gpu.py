@@ -97,18 +97,37 @@ def test_matmul_rejects_bad_input_dim():
     assert bool(torch.all(torch.isnan(buf)))
 
 
-# ---- a few tokens: the batched matrix-core GEMV (M <= 8 at output_dim <=
-#      4096; 9 to 16 tokens check the hand-over to the prefill tiles)
+# ---- a few tokens: the batched matrix-core GEMV (forced with form 1; the
+#      automatic choice is checked by the token-count tests)
 
-@pytest.mark.parametrize("M", [2, 3, 4, 5, 7, 8, 9, 12, 15, 16])
+def run_batch(X, w, M, K, N):
+    buf, Y = out_with_canary(N, rows=M)
+    binding.q4k_matmul_shaped(dev(X), dev(w), M, K, N, Y, 1)
+    out = host(Y)
+    assert canary_intact(buf, M * N)
+    return out
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8])
 def test_batch_token_counts(oracle_lib, M):
     """Every token count of the batched form (2, 4 and 8-token kernels with
-    tokens past M zero), and the counts just above it."""
+    tokens past M zero)."""
     K, N = 4096, 300
     w = synth.q4k_weights(N, K, config=36, copy=M)
     X = synth.activations(K, n_tokens=M, config=36, copy=M)
-    Y = run(X, w, M, K, N)
+    Y = run_batch(X, w, M, K, N)
     assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"M={M}")
+
+
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 7, 8, 9, 12, 15, 16])
+def test_automatic_choice_token_counts(oracle_lib, M):
+    """The automatic choice around the hand-over between the batched form
+    and the prefill tiles."""
+    for K, N in ((4096, 300), (14336, 64)):
+        w = synth.q4k_weights(N, K, config=53, copy=M)
+        X = synth.activations(K, n_tokens=M, config=53, copy=M)
+        Y = run(X, w, M, K, N)
+        assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"{M}x{K}x{N}")
 
 
 @pytest.mark.parametrize("M,K,N", [(8, 256, 1), (4, 512, 17), (6, 1280, 129), (8, 14336, 64),
@@ -119,7 +138,7 @@ def test_batch_shapes(oracle_lib, M, K, N):
     per wave, ragged row tiles, long rows."""
     w = synth.q4k_weights(N, K, config=37, copy=K + N)
     X = synth.activations(K, n_tokens=M, config=37, copy=K + N)
-    Y = run(X, w, M, K, N)
+    Y = run_batch(X, w, M, K, N)
     assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"{M}x{K}x{N}")
 
 
@@ -128,18 +147,18 @@ def test_batch_full_size(oracle_lib):
     M, K, N = 8, 4096, 4096
     w = synth.q4k_weights(N, K, config=synth.C2_Q4K_4K)
     X = synth.activations(K, n_tokens=M, config=synth.C2_Q4K_4K)
-    Y = run(X, w, M, K, N)
+    Y = run_batch(X, w, M, K, N)
     assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what="8x4096x4096")
 
 
-@pytest.mark.parametrize("M", [2, 8, 13])
+@pytest.mark.parametrize("M", [2, 5, 8])
 def test_batch_integer_bit_exact(oracle_lib, M):
     """d = dmin = 1, x in {-1, 0, 1}: every partial sum is an exact integer,
     so the batched form equals the oracle bit for bit."""
     K, N = 4096, 256
     w = synth.q4k_integer_weights(N, K, config=38)
     X = synth.integer_activations(K, n_tokens=M, config=38)
-    Y = run(X, w, M, K, N)
+    Y = run_batch(X, w, M, K, N)
     assert np.array_equal(Y.astype(np.float64), oracle_lib.q4k_matmul(X, w, M, K, N))
 
 
@@ -155,7 +174,52 @@ def test_batch_wide_range_tokens(oracle_lib):
     tok = np.exp2(np.array([-30, 0, 10, 30, 50, 60, -10, 0], np.float64)).astype(np.float32)
     X = (X.reshape(M, -1, 32) * sub[:, :, None] * tok[:, None, None]).reshape(M, K)
     X[6] = 0.0
-    Y = run(X, w, M, K, N)
+    Y = run_batch(X, w, M, K, N)
     ref = oracle_lib.q4k_matmul(X, w, M, K, N)
     assert np.all(Y[6] == 0.0)
     assert_parity(Y, ref, rowwise=True, what="wide-range tokens")
+
+
+# --- the prefill tiles at every workgroup height (q4k_matmul_shaped) -------
+
+def run_rows(X, w, M, K, N, rows):
+    buf, Y = out_with_canary(N, rows=M)
+    binding.q4k_matmul_shaped(dev(X), dev(w), M, K, N, Y, rows)
+    out = host(Y)
+    assert canary_intact(buf, M * N)
+    return out
+
+
+@pytest.mark.parametrize("rows", [16, 32, 64])
+@pytest.mark.parametrize("M,K,N", [(16, 256, 16), (17, 768, 65), (33, 1280, 130), (2, 1024, 100),
+                                   (64, 4096, 64), (9, 14336, 40), (48, 2304, 129), (16, 512, 4097)])
+def test_prefill_every_workgroup_height(oracle_lib, M, K, N, rows):
+    """Ragged rows (N not a multiple of the height), ragged token tiles and
+    stages; 16 rows splits each block's sub-blocks between two waves."""
+    w = synth.q4k_weights(N, K, config=48, copy=K + N)
+    X = synth.activations(K, n_tokens=M, config=48, copy=K + N)
+    Y = run_rows(X, w, M, K, N, rows)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"{M}x{K}x{N} rows {rows}")
+
+
+@pytest.mark.parametrize("rows", [16, 32, 64])
+def test_prefill_every_height_integer_bit_exact(oracle_lib, rows):
+    M, K, N = 24, 4096, 96
+    w = synth.q4k_integer_weights(N, K, config=49)
+    X = synth.integer_activations(K, n_tokens=M, config=49)
+    Y = run_rows(X, w, M, K, N, rows)
+    assert np.array_equal(Y.astype(np.float64), oracle_lib.q4k_matmul(X, w, M, K, N))
+
+
+@pytest.mark.parametrize("M,N", [(16, 4096), (32, 4096), (16, 14336)])
+def test_prefill_narrow_full_size_sampled(oracle_lib, M, N):
+    """The token counts that narrow the workgroups (automatic choice), at
+    full size: every output of sampled token rows."""
+    K = 4096
+    w = synth.q4k_weights(N, K, config=50, copy=M)
+    X = synth.activations(K, n_tokens=M, config=50, copy=M)
+    Y = run(X, w, M, K, N)
+    for t in (0, M // 2, M - 1):
+        ref = oracle_lib.q4k_matmul_part(X, w, M, K, N, (t, t + 1), (0, N))[t]
+        assert_parity(Y[t], ref, what=f"token {t}")
+

@@ -234,9 +234,17 @@ def matmul_tiled(X, wt, M, K, N):
     return out
 
 
-def matmul_canonical(X, w, M, K, N):
+def matmul_tiled_form(X, wt, M, K, N, form):
     buf, Y = out_with_canary(N, rows=M)
-    binding.q4k_matmul(dev(X), dev(w), M, K, N, Y)
+    binding.q4k_matmul_tiled_shaped(dev(X), wt, M, K, N, Y, form)
+    out = host(Y)
+    assert canary_intact(buf, M * N), "write past the end of Y"
+    return out
+
+
+def matmul_canonical(X, w, M, K, N, form=0):
+    buf, Y = out_with_canary(N, rows=M)
+    binding.q4k_matmul_shaped(dev(X), dev(w), M, K, N, Y, form)
     return host(Y)
 
 
@@ -270,17 +278,43 @@ def test_matmul_tiled_shapes(oracle_lib, M, K, N):
 
 @pytest.mark.parametrize("M,K,N", [(64, 4096, 512), (17, 768, 65), (33, 1280, 130), (16, 14336, 64)])
 def test_prefill_tiled_equals_canonical_prefill(M, K, N):
-    """The tiled prefill does the canonical prefill's arithmetic in the same
-    order (only where the weight bytes come from differs): bit for bit."""
+    """The tiled prefill does the canonical 64-row prefill's arithmetic in
+    the same order (only where the weight bytes come from differs): bit for
+    bit."""
     w = synth.q4k_weights(N, K, config=43, copy=M)
     X = synth.activations(K, n_tokens=M, config=43, copy=M)
     wt, _ = relayout(w, K, N)
-    a = matmul_tiled(X, wt, M, K, N)
-    b = matmul_canonical(X, w, M, K, N)
+    a = matmul_tiled_form(X, wt, M, K, N, 64)
+    b = matmul_canonical(X, w, M, K, N, form=64)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("M", [2, 3, 4])
+@pytest.mark.parametrize("rows", [16, 32, 64])
+@pytest.mark.parametrize("M,K,N", [(16, 256, 16), (17, 768, 65), (33, 1280, 130), (2, 1024, 100),
+                                   (9, 14336, 40), (16, 512, 4097)])
+def test_prefill_tiled_every_height_equals_canonical(M, K, N, rows):
+    """At every workgroup height the tiled prefill does the canonical
+    prefill's arithmetic in the same order: bit for bit (and both pass the
+    oracle's bar in tests/test_matmul_gpu.py)."""
+    w = synth.q4k_weights(N, K, config=51, copy=K + N)
+    X = synth.activations(K, n_tokens=M, config=51, copy=K + N)
+    wt, _ = relayout(w, K, N)
+    a = matmul_tiled_form(X, wt, M, K, N, rows)
+    b = matmul_canonical(X, w, M, K, N, form=rows)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows", [16, 32])
+def test_prefill_tiled_narrow_parity(oracle_lib, rows):
+    M, K, N = 24, 4096, 300
+    w = synth.q4k_weights(N, K, config=52)
+    X = synth.activations(K, n_tokens=M, config=52)
+    wt, _ = relayout(w, K, N)
+    assert_parity(matmul_tiled_form(X, wt, M, K, N, rows), oracle_lib.q4k_matmul(X, w, M, K, N),
+                  rowwise=True, what=f"rows {rows}")
+
+
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 8])
 def test_batch_tiled_equals_canonical_batch_one_block_per_wave(M):
     """With 8 super-blocks per row each of the 8 waves owns one super-block
     in both batched forms: the tiled one equals the canonical one bit for
@@ -289,8 +323,8 @@ def test_batch_tiled_equals_canonical_batch_one_block_per_wave(M):
     w = synth.q4k_weights(N, K, config=44, copy=M)
     X = synth.activations(K, n_tokens=M, config=44, copy=M)
     wt, _ = relayout(w, K, N)
-    a = matmul_tiled(X, wt, M, K, N)
-    b = matmul_canonical(X, w, M, K, N)
+    a = matmul_tiled_form(X, wt, M, K, N, 1)
+    b = matmul_canonical(X, w, M, K, N, form=1)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
@@ -327,9 +361,9 @@ def test_matmul_tiled_integer_bit_exact(oracle_lib, M):
 
 def test_batch_tiled_wide_range_tokens(oracle_lib):
     """Tokens at 2^-30 .. 2^60 (one all zero), sub-blocks at 2^-20 .. 2^20:
-    each token's super-block is rescaled before its fp16 split (8 tokens
-    with input_dim 4096 take the batched kernel)."""
-    M, K, N = 8, 4096, 200
+    each token's super-block is rescaled before its fp16 split (the
+    batched kernel, forced)."""
+    M, K, N = 8, 2048, 200
     w = synth.q4k_weights(N, K, config=46)
     X = synth.activations(K, n_tokens=M, config=46)
     g = np.random.default_rng(46)
@@ -338,7 +372,7 @@ def test_batch_tiled_wide_range_tokens(oracle_lib):
     X = (X.reshape(M, -1, 32) * sub[:, :, None] * tok[:, None, None]).reshape(M, K)
     X[6] = 0.0
     wt, _ = relayout(w, K, N)
-    Y = matmul_tiled(X, wt, M, K, N)
+    Y = matmul_tiled_form(X, wt, M, K, N, 1)
     assert np.all(Y[6] == 0.0)
     assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what="wide-range tokens")
 
