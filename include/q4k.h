@@ -231,15 +231,28 @@ int ternary_gemv(const float *x, const uint8_t *codes, float scale,
  *   input_dim, output_dim as for ternary_gemv_codes
  *   Y          fp32 [n_tokens, output_dim] (row r at Y + r*output_dim)
  * With input_dim % 64 == 0, 16-byte aligned X and codes, and more than 2
- * tokens (more than 4 when input_dim > 8192) the products run
- * on 16x16x32 f16 MFMA tiles: the codes enter exactly, and X, after each
- * token's 256-position block is scaled by a power of two, as exact fp16 hi
- * and lo halves (any |X| < 2^96); the sum is fp32 (tolerance as q4k_gemv;
+ * tokens (more than 3 when input_dim > 8192) the products run on 16x16x32
+ * f16 MFMA tiles (64, 32 or 16 rows x 16 tokens per workgroup, the height
+ * chosen as for q4k_matmul's prefill tiles): the codes enter exactly, and
+ * X, after each token's 256-position block is scaled by a power of two, as
+ * exact fp16 hi and lo halves (any |X| < 2^96); the sum is fp32 (tolerance as q4k_gemv;
  * exact for integer X with sum_i |X[r,i]| * 3 < 2^22).  Otherwise it runs
  * one ternary_gemv launch per token row.  Y must not alias X or the codes.
  */
 int ternary_matmul(const float *X, const uint8_t *codes, float scale, int64_t n_tokens,
                    int64_t input_dim, int64_t output_dim, float *Y, void *stream);
+
+/*
+ * ternary_matmul_shaped -- ternary_matmul with its kernel forced, for
+ * sweeps and tests: form 1 runs the row loop (one ternary_gemv launch per
+ * token row); form 16, 32 or 64 runs the matrix-core tiles with that many
+ * rows per workgroup (x 16 tokens; input_dim a multiple of 64 else
+ * Q4K_EINVAL_DIM, X and codes 16-byte aligned else Q4K_EALIGN); 0 is
+ * ternary_matmul itself.  Any other value gives Q4K_EINVAL_DIM.
+ */
+int ternary_matmul_shaped(const float *X, const uint8_t *codes, float scale, int64_t n_tokens,
+                          int64_t input_dim, int64_t output_dim, float *Y, void *stream,
+                          int form);
 
 /*
  * q4k_gemv_shaped -- q4k_gemv with an explicit launch shape, for sweeps and

@@ -23,7 +23,7 @@ EXPORTED = (
     "q4k_gemv", "q4k_matmul", "ternary_gemv_codes", "ternary_gemv", "ternary_matmul",
     "q4k_gemv_shaped", "q4_0_gemv", "q4_0_gemv_shaped", "q6k_gemv", "q6k_gemv_shaped",
     "q4k_tiled_size", "q4k_relayout_tiled", "q4k_gemv_tiled", "q4k_gemv_tiled_shaped",
-    "q4k_matmul_tiled", "q4k_matmul_shaped", "q4k_matmul_tiled_shaped",
+    "q4k_matmul_tiled", "q4k_matmul_shaped", "q4k_matmul_tiled_shaped", "ternary_matmul_shaped",
     "q4k_strerror",
     "q4k_bench_empty", "q4k_bench_stream_read", "q4k_bench_copy",
 )
@@ -56,6 +56,7 @@ def lib():
         "ternary_gemv_codes": [P, P, I64, I64, P, P],
         "ternary_gemv": [P, P, F, I64, I64, P, P],
         "ternary_matmul": [P, P, F, I64, I64, I64, P, P],
+        "ternary_matmul_shaped": [P, P, F, I64, I64, I64, P, P, I],
         "q4k_gemv_shaped": [P, P, I64, I64, P, P, I, I, I],
         "q4_0_gemv": [P, P, I64, I64, P, P],
         "q4_0_gemv_shaped": [P, P, I64, I64, P, P, I, I, I],
@@ -316,6 +317,18 @@ def ternary_matmul(X, codes, scale, n_tokens, input_dim, output_dim, Y, stream=N
     _expect(Y, torch.float32, "Y", M * N if ok else 0)
     _check(lib().ternary_matmul(_ptr(X), _ptr(codes), float(scale), M, K, N, _ptr(Y),
                                 _stream(stream)), "ternary_matmul")
+    return Y
+
+
+def ternary_matmul_shaped(X, codes, scale, n_tokens, input_dim, output_dim, Y, form=0,
+                          stream=None):
+    M, K, N = int(n_tokens), int(input_dim), int(output_dim)
+    ok = M > 0 and _ternary_need(K, N) > 0
+    _expect(X, torch.float32, "X", M * K if ok else 0)
+    _expect(codes, torch.uint8, "codes", _ternary_need(K, N))
+    _expect(Y, torch.float32, "Y", M * N if ok else 0)
+    _check(lib().ternary_matmul_shaped(_ptr(X), _ptr(codes), float(scale), M, K, N, _ptr(Y),
+                                       _stream(stream), int(form)), "ternary_matmul_shaped")
     return Y
 
 

@@ -215,10 +215,40 @@ int ternary_gemv(const float *x, const uint8_t *codes, float scale,
 // code byte read once per 16 tokens); anything else is the ternary page's
 // row loop, one ternary_gemv launch per token row.  The row loop also wins
 // for very few tokens (measured on MI355X, graph-replayed calls over
-// rotating codes, 4096x4096: 2 tokens 8.1 us looped vs 15.3 tiled, 4
-// tokens 15.9 vs 15.4; 14336->4096: 4 tokens 40.4 vs 48.7).
+// rotating codes, loop / tiles at the height prefill_rows picks: 4096x4096
+// with 2 tokens 8.1 / 10.9 and with 3 tokens 12.1 / 10.9; 14336->4096 with
+// 3 tokens 31.1 / 33.7 and with 4 tokens 41.0 / 33.7).
 static bool ternary_row_loop_wins(int64_t M, int64_t K) {
-  return M <= 2 || (M <= 4 && K > 8192);
+  return M <= 2 || (M <= 3 && K > 8192);
+}
+
+static int ternary_row_loop(const float *X, const uint8_t *codes, float scale, int64_t n_tokens,
+                            int64_t input_dim, int64_t output_dim, float *Y, void *stream) {
+  for (int64_t r = 0; r < n_tokens; ++r) {
+    hipError_t e = q4k::ternary_launch(X + r * input_dim, codes, scale, true, input_dim,
+                                       output_dim, Y + r * output_dim, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "ternary_matmul launch");
+  }
+  return Q4K_OK;
+}
+
+// form 1 = the row loop of ternary_gemv launches; 16 / 32 / 64 = the matrix-
+// core tiles with that many rows per workgroup (input_dim a multiple of 64,
+// X and codes 16-byte aligned); 0 = ternary_matmul's own choice.
+int ternary_matmul_shaped(const float *X, const uint8_t *codes, float scale, int64_t n_tokens,
+                          int64_t input_dim, int64_t output_dim, float *Y, void *stream,
+                          int form) {
+  if (n_tokens <= 0) return Q4K_EINVAL_DIM;
+  int rc = check_ternary(X, codes, Y, input_dim, output_dim);
+  if (rc) return rc;
+  if (form == 0) return ternary_matmul(X, codes, scale, n_tokens, input_dim, output_dim, Y, stream);
+  if (form == 1)
+    return ternary_row_loop(X, codes, scale, n_tokens, input_dim, output_dim, Y, stream);
+  if ((form != 16 && form != 32 && form != 64) || input_dim % 64 != 0) return Q4K_EINVAL_DIM;
+  if (!aligned16(X) || !aligned16(codes)) return Q4K_EALIGN;
+  hipError_t e = q4k::ternary_matmul_launch(X, codes, scale, n_tokens, input_dim, output_dim, Y,
+                                            (hipStream_t)stream, form);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "ternary_matmul launch");
 }
 
 int ternary_matmul(const float *X, const uint8_t *codes, float scale, int64_t n_tokens,
@@ -233,12 +263,7 @@ int ternary_matmul(const float *X, const uint8_t *codes, float scale, int64_t n_
                                               Y, (hipStream_t)stream);
     return e == hipSuccess ? Q4K_OK : hip_fail(e, "ternary_matmul launch");
   }
-  for (int64_t r = 0; r < n_tokens; ++r) {
-    hipError_t e = q4k::ternary_launch(X + r * input_dim, codes, scale, true, input_dim,
-                                       output_dim, Y + r * output_dim, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "ternary_matmul launch");
-  }
-  return Q4K_OK;
+  return ternary_row_loop(X, codes, scale, n_tokens, input_dim, output_dim, Y, stream);
 }
 
 int64_t q4k_tiled_size(int64_t input_dim, int64_t output_dim) {

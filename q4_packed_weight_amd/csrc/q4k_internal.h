@@ -66,7 +66,8 @@ hipError_t ternary_launch(const float *x, const uint8_t *codes, float scale,
 // Batched ternary product on the matrix cores (ternary_matmul.hip); K a
 // multiple of 64, X and codes 16-byte aligned.
 hipError_t ternary_matmul_launch(const float *X, const uint8_t *codes, float scale, int64_t M,
-                                 int64_t K, int64_t N, float *Y, hipStream_t stream);
+                                 int64_t K, int64_t N, float *Y, hipStream_t stream,
+                                 int rows = 0);
 
 // rows: weight rows per workgroup (64, 32 or 16); 0 = prefill_rows(M, N).
 hipError_t prefill_launch(const float *X, const uint8_t *w, int64_t M,

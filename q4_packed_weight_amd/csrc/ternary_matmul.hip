@@ -8,8 +8,9 @@
 // with u the 2-bit field of element i (byte i/4, bits 2*(i%4)).
 //
 // Work decomposition and pipeline follow the Q4_K prefill kernel: a
-// workgroup owns 64 rows (4 MFMA row tiles) and 16 tokens (one token tile)
-// over the whole of input_dim and walks it in stages of 1024 positions.
+// workgroup owns 64 rows (4 MFMA row tiles; 32 or 16 when few token tiles
+// would leave CUs idle) and 16 tokens (one token tile) over the whole of
+// input_dim and walks it in stages of 1024 positions.
 // Every thread loads two 16-byte code chunks and eight activation float4
 // of the next stage while the current one is computed; the activations go
 // to LDS already split into exact fp16 hi + lo halves in MFMA operand order
@@ -17,8 +18,7 @@
 // 256-position block first scaled by the power of two that brings its
 // largest |x| into [2^14, 2^15) (so the halves neither overflow fp16 nor
 // lose bits of lo to its subnormal range, for any |x| below 2^96).  Wave w takes
-// positions 256*(w%4) .. +255 of the stage for row tiles 2*(w/4) and
-// 2*(w/4)+1.
+// positions 256*(w%4) .. +255 of the stage for its row tiles.
 //
 // Operands (16x16x32 f16 MFMA; lane (r, g) = (lane % 16, lane / 16)): the A
 // operand is 8 codes of row 16a + r, positions 8g .. 8g+7 of one 32-position
@@ -38,7 +38,6 @@ namespace q4k {
 
 namespace {
 
-constexpr int TR_ROWS = 64;            // rows per workgroup (4 row tiles)
 constexpr int TR_TOK = 16;             // tokens per workgroup
 constexpr int TR_WAVES = 8;
 constexpr int TR_THREADS = 64 * TR_WAVES;
@@ -48,9 +47,7 @@ constexpr int TR_CB = TR_STAGE / 4;    // code bytes of one row per stage
 // (128 fp16 pairs) + 16 B; a row's codes of one stage (256 B) + 8 B.
 constexpr int XROW = 128 + 4;
 constexpr int CROW = TR_CB / 4 + 2;
-constexpr int C_PER_THREAD = TR_ROWS * TR_CB / 16 / TR_THREADS;  // 2
 constexpr int X_PER_THREAD = TR_TOK / 2;                          // 8
-static_assert(C_PER_THREAD * 16 * TR_THREADS == TR_ROWS * TR_CB, "code chunks must divide evenly");
 
 // The A operand from 16 bits of codes (8 fields): fields (0,2), (1,3) of the
 // low byte, then (4,6), (5,7) of the high byte, as the fp16 codes u - 1.
@@ -67,14 +64,27 @@ __device__ __forceinline__ half8_t code_operand(uint32_t w16) {
   return a - half8_t{off, off, off, off, off, off, off, off};
 }
 
+// ROWS = 64, 32 or 16 rows (RT row tiles) per workgroup.  Wave (bb, half):
+// with 4 row tiles, tiles 2 half and 2 half + 1 over the block's eight
+// 32-position steps; with 2, tile half; with 1, the one tile over steps
+// 4 half .. 4 half + 3.
+template <int ROWS>
 __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
     const float *X, const uint8_t *codes, float *__restrict__ Y, float scale, int M, int K,
     int N) {
+  constexpr int RT = ROWS / 16;
+  constexpr int TPW = RT == 4 ? 2 : 1;       // row tiles per wave
+  constexpr int NSTEP = RT == 1 ? 4 : 8;     // 32-position steps per wave and block
+  constexpr int NS = RT == 1 ? 2 : 1;        // waves sharing a block's rows
+  constexpr int CHUNKS = ROWS * TR_CB / 16;  // 16-byte code chunks per stage
+  constexpr int C_PER_THREAD = CHUNKS > TR_THREADS ? CHUNKS / TR_THREADS : 1;
+  constexpr int C_WAVES = CHUNKS >= TR_THREADS ? TR_WAVES : CHUNKS / 64;  // waves that load codes
+  static_assert(C_PER_THREAD * 64 * C_WAVES == CHUNKS, "code chunks must divide evenly");
   // xh/xl: fp16 hi and lo activations [block of stage][token][pairs in
   // operand order]; ct: the stage's codes [row][dword].
   __shared__ __align__(16) uint32_t xh[4][TR_TOK][XROW];
   __shared__ __align__(16) uint32_t xl[4][TR_TOK][XROW];
-  __shared__ __align__(16) uint32_t ct[TR_ROWS * CROW];
+  __shared__ __align__(16) uint32_t ct[ROWS * CROW];
   __shared__ int xe[4][TR_TOK];  // scaling exponent per (block, token) of the stage
 
   // The host validates K >= 64; saying so lets the compiler fetch every
@@ -85,10 +95,13 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = tid & 255;     // thread index within its half of the workgroup
   const int bb = wave & 3;     // 256-position block of the stage this wave computes
-  const int half = wave >> 2;  // row tiles 2*half and 2*half + 1
+  const int half = wave >> 2;
+  const int rt0 = RT == 4 ? 2 * half : (RT == 2 ? half : 0);  // first row tile of this wave
+  const int s0 = RT == 1 ? 4 * half : 0;                      // first step of this wave
+  const bool c_loader = wave < C_WAVES;
   const int r = lane & 15;     // A: row within a row tile; B and D: token
   const int g = lane >> 4;
-  const int row0 = blockIdx.x * TR_ROWS;
+  const int row0 = blockIdx.x * ROWS;
   const int tok0 = blockIdx.y * TR_TOK;
   const int row_bytes = K / 4;
   const int n_stages = (K + TR_STAGE - 1) / TR_STAGE;
@@ -123,7 +136,7 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
       xv[i] = load_buf_f4(xr, in_k ? 16 * t + 4 * K * (2 * i + tok_lo) : 0x7FFFFFF0, 4096 * st);
 #pragma unroll
     for (int m = 0; m < C_PER_THREAD; ++m)
-      cv[m] = __builtin_bit_cast(uint4, load_buf_f4(cr, coff[m], TR_CB * st));
+      if (c_loader) cv[m] = __builtin_bit_cast(uint4, load_buf_f4(cr, coff[m], TR_CB * st));
   };
   auto stage_to_lds = [&]() {
     // this wave stages block xb of the tokens of parity tok_lo: the block's
@@ -146,18 +159,20 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
       *reinterpret_cast<uint2 *>(&xl[xb][tok][2 * lane]) =
           make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
     }
+    if (c_loader) {
 #pragma unroll
-    for (int m = 0; m < C_PER_THREAD; ++m) {
-      const int q = tid + TR_THREADS * m;
-      uint32_t *dst = &ct[(q >> 4) * CROW + 4 * (q & 15)];
-      *reinterpret_cast<uint2 *>(dst) = make_uint2(cv[m].x, cv[m].y);
-      *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(cv[m].z, cv[m].w);
+      for (int m = 0; m < C_PER_THREAD; ++m) {
+        const int q = tid + TR_THREADS * m;
+        uint32_t *dst = &ct[(q >> 4) * CROW + 4 * (q & 15)];
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(cv[m].x, cv[m].y);
+        *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(cv[m].z, cv[m].w);
+      }
     }
   };
 
-  floatx4 acc[2];
+  floatx4 acc[TPW];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < TPW; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
   // this lane's code bytes for step s of block bb: byte 64*bb + 8*s + 2*g
   // of its row, i.e. half (g & 1) of dword 16*bb + 2*s + g/2
   const uint32_t hsh = 16u * (uint32_t)(g & 1);
@@ -169,16 +184,17 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
     if (st + 1 < n_stages) load_stage(st + 1);  // in flight during the MFMAs
     // per row tile: the block's hi and lo products in separate accumulators
     // (four independent MFMA chains)
-    floatx4 bh[2], bl[2];
+    floatx4 bh[TPW], bl[TPW];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) bh[a] = bl[a] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < TPW; ++a) bh[a] = bl[a] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int ss = 0; ss < NSTEP; ++ss) {
+      const int s = s0 + ss;
       const half8_t Bh = *reinterpret_cast<const half8_t *>(&xh[bb][r][16 * s + 4 * g]);
       const half8_t Bl = *reinterpret_cast<const half8_t *>(&xl[bb][r][16 * s + 4 * g]);
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int row = 16 * (2 * half + a) + r;
+      for (int a = 0; a < TPW; ++a) {
+        const int row = 16 * (rt0 + a) + r;
         const uint32_t w = ct[row * CROW + 16 * bb + 2 * s + (g >> 1)] >> hsh;
         const half8_t A = code_operand(w);
         bh[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, bh[a], 0, 0, 0);
@@ -188,45 +204,64 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
     // undo the scaling of token r's block (the D column of this lane)
     const int e = xe[bb][r];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < TPW; ++a)
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc[a][k] += __builtin_ldexpf(bh[a][k] + bl[a][k], e);
     __syncthreads();  // the next stage overwrites the LDS tiles
   }
 
-  // Add the four blocks' partial tiles (through the activation tiles, no
-  // longer needed); lane (token r, group g) holds rows 16 rt + 4g + e.
-  float4 *red = reinterpret_cast<float4 *>(&xh[0][0][0]);  // [block][token][17]
+  // Add the waves' partial tiles (through the activation tiles, no longer
+  // needed); lane (token r, group g) holds rows 16 rt + 4g + e; partial slot
+  // (block, share) of the rows.
+  constexpr int RROW = ROWS + 4;
+  float *red = reinterpret_cast<float *>(&xh[0][0][0]);  // [block][share][token][RROW]
+  static_assert(4 * NS * TR_TOK * RROW <= 4 * TR_TOK * XROW,
+                "the partial tiles must fit in the activation tile");
+  const int shr = RT == 1 ? half : 0;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-    red[(bb * TR_TOK + r) * 17 + 4 * (2 * half + a) + g] =
+  for (int a = 0; a < TPW; ++a)
+    *reinterpret_cast<float4 *>(&red[((bb * NS + shr) * TR_TOK + r) * RROW + 16 * (rt0 + a) + 4 * g]) =
         make_float4(acc[a][0], acc[a][1], acc[a][2], acc[a][3]);
   __syncthreads();
-  const float *redf = reinterpret_cast<const float *>(red);
-  for (int o = tid; o < TR_TOK * TR_ROWS; o += TR_THREADS) {
-    const int tok = o / TR_ROWS, rr = o % TR_ROWS;
+  for (int o = tid; o < TR_TOK * ROWS; o += TR_THREADS) {
+    const int tok = o / ROWS, rr = o % ROWS;
     float v = 0.f;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) v += redf[(b * TR_TOK + tok) * 68 + rr];
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) v += red[((b * NS + s2) * TR_TOK + tok) * RROW + rr];
     if (tok0 + tok < M && row0 + rr < N) Y[(int64_t)(tok0 + tok) * N + row0 + rr] = scale * v;
   }
+}
+
+template <int ROWS>
+hipError_t ternary_matmul_launch_rows(const float *X, const uint8_t *codes, float scale,
+                                      int64_t M, int64_t K, int64_t N, float *Y,
+                                      hipStream_t stream) {
+  const dim3 grid((unsigned)((N + ROWS - 1) / ROWS), (unsigned)((M + TR_TOK - 1) / TR_TOK));
+  if (grid.y > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(ternary_matmul_kernel<ROWS>, grid, dim3(TR_THREADS), 0, stream, X, codes, Y,
+                     scale, (int)M, (int)K, (int)N);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t ternary_matmul_launch(const float *X, const uint8_t *codes, float scale, int64_t M,
-                                 int64_t K, int64_t N, float *Y, hipStream_t stream) {
+                                 int64_t K, int64_t N, float *Y, hipStream_t stream, int rows) {
   // Offsets formed in the kernel (64 rows of codes, 16 rows of X, plus one
   // stage) must stay below 2^31 bytes; K must be whole 16-byte code chunks.
-  if (K % 64 != 0 || (int64_t)TR_ROWS * (K / 4) + 4096 >= ((int64_t)1 << 31) ||
+  if (K % 64 != 0 || (int64_t)64 * (K / 4) + 4096 >= ((int64_t)1 << 31) ||
       ((int64_t)TR_TOK * K + 4096) * 4 >= ((int64_t)1 << 31) || N > 0x7FFFFFFF ||
       M > 0x7FFFFFFF)
     return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((N + TR_ROWS - 1) / TR_ROWS), (unsigned)((M + TR_TOK - 1) / TR_TOK));
-  if (grid.y > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(ternary_matmul_kernel, grid, dim3(TR_THREADS), 0, stream, X, codes, Y,
-                     scale, (int)M, (int)K, (int)N);
-  return hipGetLastError();
+  if (rows == 0) rows = prefill_rows(M, N);
+  switch (rows) {
+    case 64: return ternary_matmul_launch_rows<64>(X, codes, scale, M, K, N, Y, stream);
+    case 32: return ternary_matmul_launch_rows<32>(X, codes, scale, M, K, N, Y, stream);
+    case 16: return ternary_matmul_launch_rows<16>(X, codes, scale, M, K, N, Y, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace q4k

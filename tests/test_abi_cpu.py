@@ -139,6 +139,15 @@ def test_q6k_rejects_null_misaligned_and_bad_shape(lib):
     assert lib.q6k_gemv_shaped(GOOD, GOOD2, 4096, 8, GOOD3, None, 8, 4, 4) == -1
 
 
+def test_ternary_matmul_shaped_rejects_bad_forms(lib):
+    F = ctypes.c_float
+    for form in (2, 8, 48, 128, -16):
+        assert lib.ternary_matmul_shaped(GOOD, GOOD2, F(1.0), 16, 256, 8, GOOD3, None, form) == -1
+    assert lib.ternary_matmul_shaped(GOOD, GOOD2, F(1.0), 16, 100, 8, GOOD3, None, 16) == -1
+    assert lib.ternary_matmul_shaped(ODD, GOOD2, F(1.0), 16, 256, 8, GOOD3, None, 32) == -3
+    assert lib.ternary_matmul_shaped(GOOD, GOOD2, F(1.0), 0, 256, 8, GOOD3, None, 16) == -1
+
+
 def test_ternary_matmul_rejects_bad_args(lib):
     F = ctypes.c_float
     assert lib.ternary_matmul(GOOD, GOOD2, F(1.0), 0, 64, 8, GOOD3, None) == -1

@@ -115,3 +115,56 @@ def test_ternary_matmul_rejects_bad_dims(M, K):
         binding.ternary_matmul(Xd, cd, 1.0, M, K, 4, Y)
     assert getattr(e.value, "code", binding.Q4K_EINVAL_DIM) == binding.Q4K_EINVAL_DIM
     assert np.all(np.isnan(host(ybuf)))
+
+
+# --- the matrix-core tiles at every workgroup height (ternary_matmul_shaped) --
+
+def run_form(X, codes, scale, M, K, N, form):
+    ybuf, Y = out_with_canary(N, rows=M)
+    binding.ternary_matmul_shaped(dev(X), dev(codes), scale, M, K, N, Y, form)
+    out = host(Y)
+    assert canary_intact(ybuf, M * N), "write past the end of Y"
+    return out
+
+
+@pytest.mark.parametrize("rows", [16, 32, 64])
+@pytest.mark.parametrize("M,K,N", [(3, 64, 5), (16, 4096, 64), (17, 1088, 130), (33, 2048, 100),
+                                   (2, 14336, 40), (9, 256, 4097)])
+def test_ternary_matmul_every_height(oracle_lib, M, K, N, rows):
+    """Ragged rows, token tiles and stages; 16 rows splits each block's
+    steps between two waves."""
+    codes, _ = synth.ternary_codes(N, K, copy=M + K + rows)
+    X = synth.activations(K, n_tokens=M, config=synth.C5_TERNARY, copy=M + K + rows)
+    Y = run_form(X, codes, 0.8, M, K, N, rows)
+    assert_parity(Y, oracle_lib.ternary_matmul(X, codes, 0.8, M, K, N), rowwise=True,
+                  what=f"M={M} K={K} N={N} rows {rows}")
+
+
+@pytest.mark.parametrize("rows", [16, 32, 64])
+def test_ternary_matmul_every_height_integer_bit_exact(oracle_lib, rows):
+    M, K, N = 24, 4096, 96
+    codes, _ = synth.ternary_codes(N, K, copy=15, allow_code3=True)
+    X = synth.integer_activations(K, lo=-8, hi=8, n_tokens=M, config=synth.C5_TERNARY, copy=15)
+    Y = run_form(X, codes, 1.0, M, K, N, rows)
+    assert np.array_equal(Y.astype(np.float64), oracle_lib.ternary_matmul(X, codes, 1.0, M, K, N))
+
+
+def test_ternary_matmul_forced_row_loop(oracle_lib):
+    M, K, N = 20, 1024, 70
+    codes, _ = synth.ternary_codes(N, K, copy=16)
+    X = synth.activations(K, n_tokens=M, config=synth.C5_TERNARY, copy=16)
+    Y = run_form(X, codes, 1.25, M, K, N, 1)
+    assert_parity(Y, oracle_lib.ternary_matmul(X, codes, 1.25, M, K, N), rowwise=True)
+
+
+@pytest.mark.parametrize("rows", [16, 32])
+def test_ternary_matmul_narrow_wide_range(oracle_lib, rows):
+    """Per-(token, block) scaling at the narrow heights (shared exponent
+    table, two waves per block at 16 rows)."""
+    M, K, N = 16, 2048, 300
+    codes, _ = synth.ternary_codes(N, K, copy=17)
+    X = synth.activations(K, n_tokens=M, config=synth.C5_TERNARY, copy=17)
+    X *= np.exp2(np.linspace(-30, 40, M)).astype(np.float32)[:, None]
+    Y = run_form(X, codes, 1.0, M, K, N, rows)
+    assert_parity(Y, oracle_lib.ternary_matmul(X, codes, 1.0, M, K, N), rowwise=True)
+
