@@ -26,6 +26,35 @@ __device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1) {
   return r;
 }
 
+// Two codes of a qs dword as exact *normal* fp16 MFMA operands: with mask
+// 0x000F000F the low nibbles of bytes 0 and 2 as q, with 0x00F000F0 their
+// high nibbles, kept in place, as 16 q (shift the dword right by 8 first for
+// bytes 1 and 3).  (w & mask) | 0x6400 is the fp16 number 1024 + v, and a
+// packed subtraction of 1024 leaves v exactly.  Normal operands matter: with
+// the codes as fp16 subnormals (v * 2^-24, only masked) the 16x16x32 f16
+// MFMA measured a biased loss of up to 4e-6 of a dot whose products span a
+// wide range, against about one fp32 ulp with normal codes.
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t mask) {
+  const half2_t v = as_h2((w & mask) | 0x64006400u);
+  return as_u32h(v - half2_t{(_Float16)1024.0f, (_Float16)1024.0f});
+}
+
+// The code operands of the matrix-core GEMV kernels.  Masked into fp16
+// subnormals (v * 2^-24) a pair costs one AND; its measured bias is about
+// 1.6e-7 of a dot, which stays within fp32-level error up to a few hundred
+// super-blocks per row but reaches ~1e-4 at input_dim 2^24.  Rows longer
+// than kNormalCodesAbove super-blocks therefore use exact normal codes
+// (NC), one packed subtraction more per pair.
+constexpr int kNormalCodesAbove = 256;
+template <bool NC>
+__device__ __forceinline__ uint32_t code_operand_pair(uint32_t w, uint32_t mask) {
+  if constexpr (NC) return code_pair(w, mask);
+  else return w & mask;
+}
+// the power of two the codes carry: a low nibble enters as q * 2^-kCodeShift,
+// a high nibble in place as 16 q * 2^-kCodeShift
+template <bool NC> constexpr int kCodeShift = NC ? 0 : 24;
+
 // Bytes (0, 2) or (1, 3) of `t` as the low bytes of two fp16 halves whose
 // high byte is 0x64: a byte value v becomes the fp16 number 1024 + v.
 __device__ __forceinline__ uint32_t spread02(uint32_t t) {

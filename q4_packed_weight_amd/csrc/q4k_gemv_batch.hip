@@ -12,8 +12,9 @@
 // Layout: a workgroup owns 16 weight rows (the MFMA's column tile); its 8
 // waves split the row's super-blocks and walk them one at a time, loading
 // the next one ahead (coalesced 16-byte loads into a wave-private LDS tile).
-// The nibbles enter the MFMA's B operand masked into exact fp16 subnormals
-// (q * 2^-24 low, 16q * 2^-24 high).  The A operand's 16 rows carry the
+// The nibbles enter the MFMA's B operand masked into fp16 subnormals (q *
+// 2^-24 low, 16q * 2^-24 high), or as exact normal codes for very long rows
+// (code_operand_pair).  The A operand's 16 rows carry the
 // tokens: row 2t the fp16 hi part of token t's activations, row 2t + 1 the
 // lo part (hi = fp16(x), lo = fp16(x - hi), both exact), so one 16x16x32
 // MFMA serves up to 8 tokens and every product is exact.  Before the split
@@ -39,7 +40,9 @@ constexpr int MB_WCH = MB_ROWS * 9;              // 16-byte weight pieces per su
 constexpr int MB_WPL = (MB_WCH + 63) / 64;       // weight loads per lane
 constexpr int MB_WROW = 36 + 2;                  // LDS dwords per staged row (+ 8 B)
 
-template <int T>  // tokens of the launch: 2, 4 or 8 (rows of X past M read as zeros)
+// T: tokens of the launch, 2, 4 or 8 (rows of X past M read as zeros); NC:
+// exact normal code operands (rows of more than 256 super-blocks)
+template <int T, bool NC>
 __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
     const float *X, const uint8_t *w, float *__restrict__ Y, int M, int nb, int N) {
   // Per wave: the staged weight rows of its super-block, each token's fp16 hi
@@ -150,17 +153,17 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
     for (int j = 0; j < 4; ++j) {
       const uint32_t s0 = qb[j].x >> 8, s1 = qb[j].y >> 8;
       uint4 blo, bhi;
-      blo.x = qb[j].x & 0x000F000Fu; blo.y = s0 & 0x000F000Fu;
-      blo.z = qb[j].y & 0x000F000Fu; blo.w = s1 & 0x000F000Fu;
-      bhi.x = qb[j].x & 0x00F000F0u; bhi.y = s0 & 0x00F000F0u;
-      bhi.z = qb[j].y & 0x00F000F0u; bhi.w = s1 & 0x00F000F0u;
+      blo.x = code_operand_pair<NC>(qb[j].x, 0x000F000Fu); blo.y = code_operand_pair<NC>(s0, 0x000F000Fu);
+      blo.z = code_operand_pair<NC>(qb[j].y, 0x000F000Fu); blo.w = code_operand_pair<NC>(s1, 0x000F000Fu);
+      bhi.x = code_operand_pair<NC>(qb[j].x, 0x00F000F0u); bhi.y = code_operand_pair<NC>(s0, 0x00F000F0u);
+      bhi.z = code_operand_pair<NC>(qb[j].y, 0x00F000F0u); bhi.w = code_operand_pair<NC>(s1, 0x00F000F0u);
       dlo[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           alo[j], __builtin_bit_cast(half8_t, blo), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       dhi[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           ahi[j], __builtin_bit_cast(half8_t, bhi), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     }
     // Scaled code dots of this super-block: sub-block 2j (low nibbles, q *
-    // 2^-24) weighs sc, sub-block 2j+1 (high nibbles, 16q * 2^-24) sc / 16.
+    // 2^-c) weighs sc, sub-block 2j+1 (high nibbles, 16q * 2^-c) sc / 16.
     float c0 = 0.f, c1 = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -183,9 +186,9 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
                      m4 * sa1.x + m5 * sa1.y + m6 * sa1.z + m7 * sa1.w;
     const float z1 = m0 * sb0.x + m1 * sb0.y + m2 * sb0.z + m3 * sb0.w +
                      m4 * sb1.x + m5 * sb1.y + m6 * sb1.z + m7 * sb1.w;
-    // the activations entered as x * 2^-e, the codes as q * 2^-24
-    y0 += __builtin_ldexpf(d * c0, xe[wave][t0] + 24) - dmin * z0;
-    y1 += __builtin_ldexpf(d * c1, xe[wave][t1] + 24) - dmin * z1;
+    // the activations entered as x * 2^-e, the codes as q * 2^-c
+    y0 += __builtin_ldexpf(d * c0, xe[wave][t0] + kCodeShift<NC>) - dmin * z0;
+    y1 += __builtin_ldexpf(d * c1, xe[wave][t1] + kCodeShift<NC>) - dmin * z1;
   };
 
   if (n_chunks > 0) {  // wave-uniform
@@ -232,12 +235,22 @@ hipError_t gemv_batch_launch(const float *X, const uint8_t *w, float *Y, int64_t
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + MB_ROWS - 1) / MB_ROWS));
   const dim3 block(64 * MB_WAVES);
-  if (M <= 2)
-    hipLaunchKernelGGL(q4k_gemv_batch_kernel<2>, grid, block, 0, stream, X, w, Y, (int)M, (int)nb, (int)N);
-  else if (M <= 4)
-    hipLaunchKernelGGL(q4k_gemv_batch_kernel<4>, grid, block, 0, stream, X, w, Y, (int)M, (int)nb, (int)N);
-  else
-    hipLaunchKernelGGL(q4k_gemv_batch_kernel<8>, grid, block, 0, stream, X, w, Y, (int)M, (int)nb, (int)N);
+  const bool nc = nb > kNormalCodesAbove;
+#define Q4K_BATCH_CASE(T_)                                                                 \
+  if (nc)                                                                                  \
+    hipLaunchKernelGGL((q4k_gemv_batch_kernel<T_, true>), grid, block, 0, stream, X, w, Y,  \
+                       (int)M, (int)nb, (int)N);                                           \
+  else                                                                                     \
+    hipLaunchKernelGGL((q4k_gemv_batch_kernel<T_, false>), grid, block, 0, stream, X, w, Y, \
+                       (int)M, (int)nb, (int)N);
+  if (M <= 2) {
+    Q4K_BATCH_CASE(2)
+  } else if (M <= 4) {
+    Q4K_BATCH_CASE(4)
+  } else {
+    Q4K_BATCH_CASE(8)
+  }
+#undef Q4K_BATCH_CASE
   return hipGetLastError();
 }
 

@@ -8,9 +8,10 @@
 //
 // Why MFMA for a batch of one: on the vector path every weight costs a
 // mask and an fma_mix; here the nibbles are only masked into fp16
-// subnormals (q * 2^-24, exact) and one 16x16x32 f16 MFMA takes 512 of
-// them.  The MFMA's B operand is 16 weight rows x 32 positions of one
-// sub-block; its A operand carries the activations: rows 0, 2, 4, ... hold
+// subnormals (q * 2^-24, high nibbles in place as 16q * 2^-24; exact normal
+// codes for very long rows, see code_operand_pair) and one 16x16x32 f16
+// MFMA takes 512 of them.  The MFMA's B
+// operand is 16 weight rows x 32 positions of one sub-block; its A operand carries the activations: rows 0, 2, 4, ... hold
 // the fp16 hi part of x and rows 1, 3, 5, ... the lo part (hi = fp16(x),
 // lo = fp16(x - hi), both exact as MFMA inputs), so D rows 4g and 4g + 1
 // of every lane hold the hi and lo halves of the same dot product and one
@@ -49,6 +50,7 @@ constexpr int MV_XPL = MV_CB * 256 / 4 / 64;            // activation float4 per
 constexpr int MV_WROW = MV_CB * 36 + 2;                 // LDS dwords per staged row (+ 8 B)
 static_assert(MV_XPL * 64 * 4 == MV_CB * 256, "activation chunk must split evenly");
 
+template <bool NC>  // exact normal code operands (rows of more than 256 super-blocks)
 __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
     const float *x, const uint8_t *w, float *__restrict__ y, int nb, int N) {
   // Per wave: staged weight rows, fp16 hi and lo activations of the chunk
@@ -162,12 +164,12 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
       const uint32_t mp = (m_src & mask_lo) | ((p2 >> 2) & mask_hi);
       const float d = half_lo(h01.x), dmin = half_hi(h01.x);
       const float4 xsp = *reinterpret_cast<const float4 *>(&xse[wave][4 * (4 * bb + j_mine)]);
-      // codes enter as q * 2^-24 (low nibbles) and 16q * 2^-24 (high), the
-      // activations as x * 2^-e
+      // codes enter as q * 2^-c (low nibbles) and 16q * 2^-c (high), c =
+      // kCodeShift<NC>; the activations as x * 2^-e
       const float s_lo = __builtin_ldexpf(d * (float)(scp & 0xFFu),
-                                          __builtin_bit_cast(int, xsp.z) + 24);
+                                          __builtin_bit_cast(int, xsp.z) + kCodeShift<NC>);
       const float s_hi = __builtin_ldexpf(d * (float)((scp >> 8) & 0xFFu),
-                                          __builtin_bit_cast(int, xsp.w) + 20);
+                                          __builtin_bit_cast(int, xsp.w) + kCodeShift<NC> - 4);
       yacc = __builtin_fmaf(-dmin, __builtin_fmaf((float)(mp & 0xFFu), xsp.x,
                                                   (float)((mp >> 8) & 0xFFu) * xsp.y), yacc);
       // All operands of the block first, then eight independent MFMAs, then
@@ -186,10 +188,10 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
       for (int j = 0; j < 4; ++j) {
         const uint32_t s0 = qb[j].x >> 8, s1 = qb[j].y >> 8;
         uint4 blo, bhi;
-        blo.x = qb[j].x & 0x000F000Fu; blo.y = s0 & 0x000F000Fu;
-        blo.z = qb[j].y & 0x000F000Fu; blo.w = s1 & 0x000F000Fu;
-        bhi.x = qb[j].x & 0x00F000F0u; bhi.y = s0 & 0x00F000F0u;
-        bhi.z = qb[j].y & 0x00F000F0u; bhi.w = s1 & 0x00F000F0u;
+        blo.x = code_operand_pair<NC>(qb[j].x, 0x000F000Fu); blo.y = code_operand_pair<NC>(s0, 0x000F000Fu);
+        blo.z = code_operand_pair<NC>(qb[j].y, 0x000F000Fu); blo.w = code_operand_pair<NC>(s1, 0x000F000Fu);
+        bhi.x = code_operand_pair<NC>(qb[j].x, 0x00F000F0u); bhi.y = code_operand_pair<NC>(s0, 0x00F000F0u);
+        bhi.z = code_operand_pair<NC>(qb[j].y, 0x00F000F0u); bhi.w = code_operand_pair<NC>(s1, 0x00F000F0u);
         dlo[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
             alo[j], __builtin_bit_cast(half8_t, blo), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         dhi[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -259,8 +261,12 @@ hipError_t gemv_mfma_launch(const float *x, const uint8_t *w, float *y, int64_t 
   if (grid > 0x7FFFFFFF || N > 0x7FFFFFFF ||
       (int64_t)MV_ROWS * nb * kBlockBytes >= ((int64_t)1 << 31))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(q4k_gemv_mfma_kernel, dim3((unsigned)grid), dim3(64 * MV_WAVES), 0, stream,
-                     x, w, y, (int)nb, (int)N);
+  if (nb > kNormalCodesAbove)
+    hipLaunchKernelGGL(q4k_gemv_mfma_kernel<true>, dim3((unsigned)grid), dim3(64 * MV_WAVES), 0,
+                       stream, x, w, y, (int)nb, (int)N);
+  else
+    hipLaunchKernelGGL(q4k_gemv_mfma_kernel<false>, dim3((unsigned)grid), dim3(64 * MV_WAVES), 0,
+                       stream, x, w, y, (int)nb, (int)N);
   return hipGetLastError();
 }
 

@@ -22,7 +22,8 @@
 // The arithmetic is the canonical matrix-core GEMV's (Q4_K page: SKaiNET PR
 // #562, "feat(kernel): SIMD-fused Q4_K matmul kernel + Q4KMatmulKernel SPI",
 // sections "Summary" and "Pipeline", in the lazy-dmin form): nibbles masked
-// into exact fp16 subnormals, activations split into exact fp16 hi + lo
+// into fp16 subnormals (exact normal codes for very long rows,
+// code_operand_pair), activations split into exact fp16 hi + lo
 // parts (A rows of alternating parity), every 32-activation sub-block scaled
 // by a power of two first, scales applied per sub-block in fp32 after the
 // MFMAs.
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256) void q4k_relayout_tiled_kernel(
 // A wave's partial sums go to LDS whenever its row group changes; the
 // waves' partials are summed in a fixed order at the end (one writer per
 // output, deterministic).
-template <int W, int D, int CAP, bool PRIV>
+template <int W, int D, int CAP, bool PRIV, bool NC>
 __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_kernel(
     const float *x, const uint8_t *wt, float *__restrict__ y, int nb, int N, int rg_per_wg) {
   constexpr int XPL = CAP * 64 / (64 * W);  // activation float4 per thread per chunk
@@ -213,12 +214,12 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_kernel(
       const uint32_t mp = (m_src & mask_lo) | ((p2 >> 2) & mask_hi);
       const float d = half_lo(hd.x), dmin = half_hi(hd.x);
       const float4 xsp = *reinterpret_cast<const float4 *>(&xse[4 * (4 * bl + g)]);
-      // codes enter as q * 2^-24 (low nibbles) and 16q * 2^-24 (high), the
-      // activations as x * 2^-e
+      // codes enter as q * 2^-c (low nibbles) and 16q * 2^-c (high), c =
+      // kCodeShift<NC>; the activations as x * 2^-e
       const float s_lo = __builtin_ldexpf(d * (float)(scp & 0xFFu),
-                                          __builtin_bit_cast(int, xsp.z) + 24);
+                                          __builtin_bit_cast(int, xsp.z) + kCodeShift<NC>);
       const float s_hi = __builtin_ldexpf(d * (float)((scp >> 8) & 0xFFu),
-                                          __builtin_bit_cast(int, xsp.w) + 20);
+                                          __builtin_bit_cast(int, xsp.w) + kCodeShift<NC> - 4);
       acc = __builtin_fmaf(-dmin, __builtin_fmaf((float)(mp & 0xFFu), xsp.x,
                                                  (float)((mp >> 8) & 0xFFu) * xsp.y), acc);
       uint2 qb[4];
@@ -238,10 +239,10 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_kernel(
       for (int j = 0; j < 4; ++j) {
         const uint32_t s0 = qb[j].x >> 8, s1 = qb[j].y >> 8;
         uint4 blo, bhi;
-        blo.x = qb[j].x & 0x000F000Fu; blo.y = s0 & 0x000F000Fu;
-        blo.z = qb[j].y & 0x000F000Fu; blo.w = s1 & 0x000F000Fu;
-        bhi.x = qb[j].x & 0x00F000F0u; bhi.y = s0 & 0x00F000F0u;
-        bhi.z = qb[j].y & 0x00F000F0u; bhi.w = s1 & 0x00F000F0u;
+        blo.x = code_operand_pair<NC>(qb[j].x, 0x000F000Fu); blo.y = code_operand_pair<NC>(s0, 0x000F000Fu);
+        blo.z = code_operand_pair<NC>(qb[j].y, 0x000F000Fu); blo.w = code_operand_pair<NC>(s1, 0x000F000Fu);
+        bhi.x = code_operand_pair<NC>(qb[j].x, 0x00F000F0u); bhi.y = code_operand_pair<NC>(s0, 0x00F000F0u);
+        bhi.z = code_operand_pair<NC>(qb[j].y, 0x00F000F0u); bhi.w = code_operand_pair<NC>(s1, 0x00F000F0u);
         dlo[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
             alo[j], __builtin_bit_cast(half8_t, blo), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         dhi[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_kernel(
 // T tokens' activations of each super-block riding in the same ring and
 // staged in a wave-private LDS slot just before use (every super-block's
 // activations are staged once per workgroup, as in the canonical form).
-template <int T, int W, int D>
+template <int T, int W, int D, bool NC>
 __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
     const float *X, const uint8_t *wt, float *__restrict__ Y, int M, int nb, int N) {
   __shared__ __align__(16) uint32_t xh[W][T][128];
@@ -396,16 +397,16 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
     for (int j = 0; j < 4; ++j) {
       const uint32_t s0 = qb[j].x >> 8, s1 = qb[j].y >> 8;
       uint4 blo, bhi;
-      blo.x = qb[j].x & 0x000F000Fu; blo.y = s0 & 0x000F000Fu;
-      blo.z = qb[j].y & 0x000F000Fu; blo.w = s1 & 0x000F000Fu;
-      bhi.x = qb[j].x & 0x00F000F0u; bhi.y = s0 & 0x00F000F0u;
-      bhi.z = qb[j].y & 0x00F000F0u; bhi.w = s1 & 0x00F000F0u;
+      blo.x = code_operand_pair<NC>(qb[j].x, 0x000F000Fu); blo.y = code_operand_pair<NC>(s0, 0x000F000Fu);
+      blo.z = code_operand_pair<NC>(qb[j].y, 0x000F000Fu); blo.w = code_operand_pair<NC>(s1, 0x000F000Fu);
+      bhi.x = code_operand_pair<NC>(qb[j].x, 0x00F000F0u); bhi.y = code_operand_pair<NC>(s0, 0x00F000F0u);
+      bhi.z = code_operand_pair<NC>(qb[j].y, 0x00F000F0u); bhi.w = code_operand_pair<NC>(s1, 0x00F000F0u);
       dlo[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           alo[j], __builtin_bit_cast(half8_t, blo), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       dhi[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
           ahi[j], __builtin_bit_cast(half8_t, bhi), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     }
-    // sub-block 2j (low nibbles, q * 2^-24) weighs sc, 2j+1 (16q * 2^-24) sc/16
+    // sub-block 2j (low nibbles, q * 2^-c) weighs sc, 2j+1 (16q * 2^-c) sc/16
     float c0 = 0.f, c1 = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -428,9 +429,9 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
                      m4 * sa1.x + m5 * sa1.y + m6 * sa1.z + m7 * sa1.w;
     const float z1 = m0 * sb0.x + m1 * sb0.y + m2 * sb0.z + m3 * sb0.w +
                      m4 * sb1.x + m5 * sb1.y + m6 * sb1.z + m7 * sb1.w;
-    // the activations entered as x * 2^-e, the codes as q * 2^-24
-    y0 += __builtin_ldexpf(d * c0, xe[wave][t0] + 24) - dmin * z0;
-    y1 += __builtin_ldexpf(d * c1, xe[wave][t1] + 24) - dmin * z1;
+    // the activations entered as x * 2^-e, the codes as q * 2^-c
+    y0 += __builtin_ldexpf(d * c0, xe[wave][t0] + kCodeShift<NC>) - dmin * z0;
+    y1 += __builtin_ldexpf(d * c1, xe[wave][t1] + kCodeShift<NC>) - dmin * z1;
     // the next staging overwrites this slot's activations only after these reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -721,10 +722,13 @@ hipError_t launch_tiled(const float *x, const uint8_t *wt, float *y, int64_t nb,
   // 8.67 vs 9.02 us/call); with 16 super-blocks per row the cooperative
   // staging, which overlaps the first tiles' loads, wins by 0.1 - 0.35 us.
   if (CAP > 16 && nb > 16 && nb % W == 0 && nb <= CAP)
-    hipLaunchKernelGGL((q4k_gemv_tiled_kernel<W, D, CAP, CAP != 16>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((q4k_gemv_tiled_kernel<W, D, CAP, CAP != 16, false>), dim3((unsigned)grid),
+                       dim3(64 * W), 0, stream, x, wt, y, (int)nb, (int)N, rg);
+  else if (CAP > 16 && nb > kNormalCodesAbove)
+    hipLaunchKernelGGL((q4k_gemv_tiled_kernel<W, D, CAP, false, CAP != 16>), dim3((unsigned)grid),
                        dim3(64 * W), 0, stream, x, wt, y, (int)nb, (int)N, rg);
   else
-    hipLaunchKernelGGL((q4k_gemv_tiled_kernel<W, D, CAP, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((q4k_gemv_tiled_kernel<W, D, CAP, false, false>), dim3((unsigned)grid),
                        dim3(64 * W), 0, stream, x, wt, y, (int)nb, (int)N, rg);
   return hipGetLastError();
 }
@@ -795,15 +799,22 @@ hipError_t gemv_tiled_batch_launch(const float *X, const uint8_t *wt, float *Y, 
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + kTileRows - 1) / kTileRows));
   constexpr int W = 8, D = 2;
-  if (M <= 2)
-    hipLaunchKernelGGL((q4k_gemv_tiled_batch_kernel<2, W, D>), grid, dim3(64 * W), 0, stream, X,
-                       wt, Y, (int)M, (int)nb, (int)N);
-  else if (M <= 4)
-    hipLaunchKernelGGL((q4k_gemv_tiled_batch_kernel<4, W, D>), grid, dim3(64 * W), 0, stream, X,
-                       wt, Y, (int)M, (int)nb, (int)N);
-  else
-    hipLaunchKernelGGL((q4k_gemv_tiled_batch_kernel<8, W, D>), grid, dim3(64 * W), 0, stream, X,
-                       wt, Y, (int)M, (int)nb, (int)N);
+  const bool nc = nb > kNormalCodesAbove;
+#define Q4K_TBATCH_CASE(T_)                                                                 \
+  if (nc)                                                                                   \
+    hipLaunchKernelGGL((q4k_gemv_tiled_batch_kernel<T_, W, D, true>), grid, dim3(64 * W), 0,  \
+                       stream, X, wt, Y, (int)M, (int)nb, (int)N);                          \
+  else                                                                                      \
+    hipLaunchKernelGGL((q4k_gemv_tiled_batch_kernel<T_, W, D, false>), grid, dim3(64 * W), 0, \
+                       stream, X, wt, Y, (int)M, (int)nb, (int)N);
+  if (M <= 2) {
+    Q4K_TBATCH_CASE(2)
+  } else if (M <= 4) {
+    Q4K_TBATCH_CASE(4)
+  } else {
+    Q4K_TBATCH_CASE(8)
+  }
+#undef Q4K_TBATCH_CASE
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ def run(X, codes, scale, M, K, N, x_offset=0):
 
 
 # token tiles (3..100, ragged), stages (input_dim 64 .. 14336, ragged last
-# stage when input_dim % 1024 != 0), row tiles (ragged N); 2 tokens (and 3-4
+# stage when input_dim % 1024 != 0), row tiles (ragged N); 2 tokens (and 3
 # with input_dim > 8192) take the row loop
 SHAPES = [(2, 64, 1), (3, 64, 5), (3, 1024, 64), (16, 4096, 64), (17, 1088, 130),
           (5, 11008, 300), (4, 11008, 40), (33, 2048, 1000), (64, 4096, 4096),
