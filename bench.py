@@ -94,7 +94,7 @@ def make_workload(name, torch, binding, synth):
         wl.bytes = wbytes + 4 * K + 4 * N
         wl.flops = 2 * K * N
         # 4096 x 4096 runs the matrix-core form (256 workgroups of 16 rows)
-        wl.kernel = "q4k_gemv_mfma_kernel" if name == "c2" else "q4k_gemv_kernel"
+        wl.kernel = "q4k_gemv_mfma_kernel<false>" if name == "c2" else "q4k_gemv_kernel"
         wl.src_files = GEMV_SRC
         wl.config = {"workload": f"q4k_gemv {K}x{N} batch 1", "input_dim": K,
                      "output_dim": N, "batch": 1, "rotating_copies": copies,
