@@ -67,8 +67,8 @@ constexpr int W_PER_THREAD = 9;  // 16-byte weight chunks per loader thread per 
 
 // ROWS weight rows (RT = ROWS / 16 MFMA row tiles) per workgroup.  The
 // waves of a stage are (block bb, half): with 4 row tiles half h computes
-// row tiles 2h, 2h+1 over all eight sub-blocks; with 2, row tile h; with 1,
-// the one row tile over sub-blocks 4h .. 4h+3.  Loads: the first RT waves
+// row tiles 2h, 2h+1 over all eight sub-blocks; with 2 or 1, all row tiles
+// over sub-blocks 4h .. 4h+3.  Loads: the first RT waves
 // (4 ROWS threads) bring the weights, 16-byte chunk q = t + 4 ROWS m of the
 // rows' 576-byte stage pieces; all 8 waves bring the activations, float4 i
 // of thread tid = token 2i + (tid >= 256), positions 4t .. 4t+3 of the
@@ -78,9 +78,16 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     const float *X, const uint8_t *w, float *__restrict__ Y, int M, int nb,
     int N) {
   constexpr int RT = ROWS / 16;
-  constexpr int TPW = RT == 4 ? 2 : 1;    // row tiles per wave
-  constexpr int NJ = RT == 1 ? 2 : 4;     // sub-block pairs per wave
-  constexpr int NS = RT == 1 ? 2 : 1;     // waves sharing a block's rows
+  // Up to 2 row tiles the block's two waves split its sub-blocks (each wave:
+  // all row tiles, half the sub-blocks), so each activation operand and sub-
+  // block sum is produced once per workgroup; measured at 32 rows, 16 and 32
+  // tokens, 4096 and 14336 inputs: 6-7% faster than one row tile per wave.
+  // At 4 row tiles splitting the sub-blocks measured no faster (and needs
+  // more registers), so each wave takes two row tiles over all sub-blocks.
+  constexpr bool SPLIT = RT <= 2;
+  constexpr int TPW = SPLIT ? RT : (RT == 4 ? 2 : 1);  // row tiles per wave
+  constexpr int NJ = SPLIT ? 2 : 4;                    // sub-block pairs per wave
+  constexpr int NS = SPLIT ? 2 : 1;                    // waves sharing a block's rows
   constexpr int RPAD = ROWS + 4;          // padded row dimension of the header tables
   constexpr int WBLK = ROWS * WROW + 8;   // one super-block of all rows + 32 B
   constexpr int LOADERS = 4 * ROWS;       // threads that load the weights
@@ -106,8 +113,8 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   const int t = tid & 255;  // thread index within its activation-loader half
   const int bb = wave & 3;  // block of the stage this wave computes
   const int half = wave >> 2;
-  const int rt0 = RT == 4 ? 2 * half : (RT == 2 ? half : 0);  // first row tile of this wave
-  const int j0 = RT == 1 ? 2 * half : 0;                      // first sub-block pair
+  const int rt0 = SPLIT ? 0 : (RT == 4 ? 2 * half : half);  // first row tile of this wave
+  const int j0 = SPLIT ? 2 * half : 0;                      // first sub-block pair
   const int r = lane & 15;  // A: row within a row tile; B and D: token
   const int g = lane >> 4;  // lane group
   const int row0 = blockIdx.x * ROWS;
@@ -212,7 +219,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
         const uint32_t scw[2] = {sc03, sc47}, mnw[2] = {mn03, mn47};
 #pragma unroll
         for (int hw = 0; hw < 2; ++hw) {
-          if (RT == 1 && hw != half) continue;  // wave-uniform: only its own sub-blocks
+          if (SPLIT && hw != half) continue;  // wave-uniform: only its own sub-blocks
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int s = 4 * hw + e;
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
         // lazy-dmin term: A[row][kk] = dmin*m of sub-block 4c + kk, B = sums
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          if (RT == 1 && c != half) continue;  // wave-uniform: its own sub-blocks
+          if (SPLIT && c != half) continue;  // wave-uniform: its own sub-blocks
           m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(c_tab[bb][4 * c + g][16 * rt + r], xsb[c],
                                                           m_acc[a], 0, 0, 0);
         }
@@ -296,13 +303,15 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   //      longer needed) and store.  Lane (token r, group g) holds rows
   //      16 rt + 4g + e of its token; partial slot (bb, s) of the rows.
   constexpr int RROW = ROWS + 4;
-  float *red = reinterpret_cast<float *>(&xh[0][0][0]);  // [block][share][token][RROW]
-  static_assert(PF_BLKS * NS * PF_TOK * RROW <= PF_BLKS * PF_TOK * XROW,
-                "the partial tiles must fit in the activation tile");
-  const int sh = RT == 1 ? half : 0;
+  // [block][token][RROW] per share: the first share in xh, the second in xl
+  float *red0 = reinterpret_cast<float *>(&xh[0][0][0]);
+  float *red1 = reinterpret_cast<float *>(&xl[0][0][0]);
+  static_assert(PF_BLKS * PF_TOK * RROW <= PF_BLKS * PF_TOK * XROW,
+                "the partial tiles must fit in the activation tiles");
+  float *red = NS == 2 && half ? red1 : red0;
 #pragma unroll
   for (int a = 0; a < TPW; ++a)
-    *reinterpret_cast<float4 *>(&red[((bb * NS + sh) * PF_TOK + r) * RROW + 16 * (rt0 + a) + 4 * g]) =
+    *reinterpret_cast<float4 *>(&red[(bb * PF_TOK + r) * RROW + 16 * (rt0 + a) + 4 * g]) =
         make_float4(y_acc[a][0] - m_acc[a][0], y_acc[a][1] - m_acc[a][1],
                     y_acc[a][2] - m_acc[a][2], y_acc[a][3] - m_acc[a][3]);
   __syncthreads();
@@ -310,9 +319,10 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     const int tok = o / ROWS, rr = o % ROWS;
     float v = 0.f;
 #pragma unroll
-    for (int b = 0; b < PF_BLKS; ++b)
-#pragma unroll
-      for (int s2 = 0; s2 < NS; ++s2) v += red[((b * NS + s2) * PF_TOK + tok) * RROW + rr];
+    for (int b = 0; b < PF_BLKS; ++b) {
+      v += red0[(b * PF_TOK + tok) * RROW + rr];
+      if (NS == 2) v += red1[(b * PF_TOK + tok) * RROW + rr];
+    }
     if (tok0 + tok < M && row0 + rr < N) Y[(int64_t)(tok0 + tok) * N + row0 + rr] = v;
   }
 }
@@ -340,15 +350,15 @@ int prefill_rows(int64_t M, int64_t N) {
   // One workgroup per CU at a time (the LDS tiles allow no second), so a
   // height costs rounds of 256 workgroups x its per-workgroup time.  The
   // per-workgroup times measured on MI355X (graph-replayed calls, input_dim
-  // 4096, 256 workgroups each): 64 rows 14.3 us, 32 rows 11.0, 16 rows 8.5,
-  // i.e. 100 : 77 : 60.  Measured us/call, 64-row tiles vs the chosen
-  // height: 16 tokens x 4096 rows 15.7 vs 9.9 (16 rows), 32 x 4096 15.5 vs
-  // 12.4 (32 rows), 16 tokens 14336 -> 4096 48.9 vs 29.2 (16 rows); 48 x 4096
-  // and 16 x 14336 stay at 64 rows (doubling the grid past one round cost
-  // 22.2 vs 15.6 and 24.0 vs 17.4).
+  // 4096, 256 workgroups each, less the 1.4 us between graph nodes): 64 rows
+  // 14.3 us, 32 rows 10.1, 16 rows 8.1, i.e. 100 : 71 : 57.  Measured
+  // us/call, 64-row tiles vs the chosen height: 16 tokens x 4096 rows 15.7
+  // vs 9.5 (16 rows), 32 x 4096 15.5 vs 11.5 (32 rows), 16 tokens 14336 ->
+  // 4096 48.9 vs 27.7 (16 rows); 48 x 4096 and 16 x 14336 stay at 64 rows
+  // (doubling the grid past one round cost 22.2 vs 15.6 and 24.0 vs 17.4).
   const int64_t tok_groups = (M + PF_TOK - 1) / PF_TOK;
   const int rows[3] = {64, 32, 16};
-  const int64_t cost[3] = {100, 77, 60};
+  const int64_t cost[3] = {100, 71, 57};
   int best = 64;
   int64_t best_cost = INT64_MAX;
   for (int i = 0; i < 3; ++i) {

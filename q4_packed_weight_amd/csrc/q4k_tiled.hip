@@ -470,10 +470,10 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
 // arithmetic: A = sc*q exact in fp16, activations split into fp16 hi + lo,
 // d applied per block, the lazy-dmin term on the fp32 MFMA), with the
 // weights no longer staged through LDS.  Wave (bb, half) computes
-// super-block bb of each 4-super-block stage: with 4 row groups for row
-// groups 2 half and 2 half + 1, with 2 for row group half, with 1 for
-// sub-blocks 4 half .. 4 half + 3 of the one row group (then it loads only
-// the qs half it uses).  It loads its tiles straight into registers one
+// super-block bb of each 4-super-block stage, as in q4k_prefill.hip: with 4
+// row groups for row groups 2 half and 2 half + 1, with 2 or 1 for all row
+// groups over sub-blocks 4 half .. 4 half + 3 (then it loads only the qs
+// half it uses).  It loads its tiles straight into registers one
 // stage ahead (its A operand bytes are its own 16-byte slots) and decodes
 // its rows' headers in registers; only the activations go through LDS.
 
@@ -486,10 +486,11 @@ template <int ROWS>
 __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     const float *X, const uint8_t *wt, float *__restrict__ Y, int M, int nb, int N) {
   constexpr int RT = ROWS / 16;            // row groups per workgroup
-  constexpr int TPW = RT == 4 ? 2 : 1;     // row groups per wave
-  constexpr int NJ = RT == 1 ? 2 : 4;      // sub-block pairs per wave
-  constexpr int NH = RT == 1 ? 1 : 2;      // qs halves per tile the wave loads
-  constexpr int NS = RT == 1 ? 2 : 1;      // waves sharing a block's rows
+  constexpr bool SPLIT = RT <= 2;          // the block's two waves split its sub-blocks
+  constexpr int TPW = SPLIT ? RT : 2;      // row groups per wave
+  constexpr int NJ = SPLIT ? 2 : 4;        // sub-block pairs per wave
+  constexpr int NH = SPLIT ? 1 : 2;        // qs halves per tile the wave loads
+  constexpr int NS = SPLIT ? 2 : 1;        // waves sharing a block's rows
   __shared__ __align__(16) uint32_t xh[TP_BLKS][TP_TOK][TP_XROW];
   __shared__ __align__(16) uint32_t xl[TP_BLKS][TP_TOK][TP_XROW];
   __shared__ __align__(16) float dtab[TP_WAVES][TPW][16];
@@ -500,8 +501,8 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bb = wave & 3;     // super-block of the stage this wave computes
   const int half = wave >> 2;
-  const int rt0 = RT == 4 ? 2 * half : (RT == 2 ? half : 0);  // first row group of this wave
-  const int j0 = RT == 1 ? 2 * half : 0;                      // first sub-block pair
+  const int rt0 = SPLIT ? 0 : 2 * half;  // first row group of this wave
+  const int j0 = SPLIT ? 2 * half : 0;   // first sub-block pair
   const int r = lane & 15;     // A: row within a row group; B and D: token
   const int g = lane >> 4;
   const int t = tid & 255;
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
 
   // qs half hs of a tile at 1024 hs + 16 lane (with one row group per
   // workgroup a wave loads only its own half), the header at 2048 + 16 r
-  const int vq[2] = {16 * lane + (RT == 1 ? 1024 * half : 0), 1024 + 16 * lane};
+  const int vq[2] = {16 * lane + (SPLIT ? 1024 * half : 0), 1024 + 16 * lane};
   const int vhd = 2048 + 16 * r;
   uint4 qs[2][TPW][NH], hd[2][TPW];  // [buffer][row group a][qs half]
   float4 xv[8];
@@ -580,8 +581,8 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
       const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
       const uint32_t mn47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
 #pragma unroll
-      for (int ls = 0; ls < 2 * NJ; ++ls) {  // sub-block 4 half + ls (one row group), else ls
-        const uint32_t scw = RT == 1 ? (half ? sc47 : sc03) : (ls < 4 ? sc03 : sc47);
+      for (int ls = 0; ls < 2 * NJ; ++ls) {  // sub-block 4 half + ls (SPLIT), else ls
+        const uint32_t scw = SPLIT ? (half ? sc47 : sc03) : (ls < 4 ? sc03 : sc47);
         const float scf = (float)((scw >> (8 * (ls & 3))) & 255u);
         // even sub-blocks are low nibbles, odd ones high nibbles (16 v)
         const float mulf = (ls & 1) ? scf * 0.0625f : scf;
@@ -644,7 +645,7 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
       // lazy-dmin term: A[row][kk] = dmin*m of sub-block 4c + kk, B = sums
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        if (RT == 1 && c != half) continue;  // wave-uniform: its own sub-blocks
+        if (SPLIT && c != half) continue;  // wave-uniform: its own sub-blocks
         m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(cm[a][c], xsb[c], m_acc[a], 0, 0, 0);
       }
     }
@@ -679,13 +680,15 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
   // needed) and store.  Lane (token r, group g) holds rows 16 (rt0 + a) +
   // 4g + e of its token; partial slot (bb, share) of the rows.
   constexpr int RROW = ROWS + 4;
-  float *red = reinterpret_cast<float *>(&xh[0][0][0]);  // [block][share][token][RROW]
-  static_assert(TP_BLKS * NS * TP_TOK * RROW <= TP_BLKS * TP_TOK * TP_XROW,
-                "the partial tiles must fit in the activation tile");
-  const int shr = RT == 1 ? half : 0;
+  // [block][token][RROW] per share: the first share in xh, the second in xl
+  float *red0 = reinterpret_cast<float *>(&xh[0][0][0]);
+  float *red1 = reinterpret_cast<float *>(&xl[0][0][0]);
+  static_assert(TP_BLKS * TP_TOK * RROW <= TP_BLKS * TP_TOK * TP_XROW,
+                "the partial tiles must fit in the activation tiles");
+  float *red = NS == 2 && half ? red1 : red0;
 #pragma unroll
   for (int a = 0; a < TPW; ++a)
-    *reinterpret_cast<float4 *>(&red[((bb * NS + shr) * TP_TOK + r) * RROW + 16 * (rt0 + a) + 4 * g]) =
+    *reinterpret_cast<float4 *>(&red[(bb * TP_TOK + r) * RROW + 16 * (rt0 + a) + 4 * g]) =
         make_float4(y_acc[a][0] - m_acc[a][0], y_acc[a][1] - m_acc[a][1],
                     y_acc[a][2] - m_acc[a][2], y_acc[a][3] - m_acc[a][3]);
   __syncthreads();
@@ -693,9 +696,10 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     const int tok = o / ROWS, rr = o % ROWS;
     float v = 0.f;
 #pragma unroll
-    for (int b = 0; b < TP_BLKS; ++b)
-#pragma unroll
-      for (int s2 = 0; s2 < NS; ++s2) v += red[((b * NS + s2) * TP_TOK + tok) * RROW + rr];
+    for (int b = 0; b < TP_BLKS; ++b) {
+      v += red0[(b * TP_TOK + tok) * RROW + rr];
+      if (NS == 2) v += red1[(b * TP_TOK + tok) * RROW + rr];
+    }
     const int row = rg0 * kTileRows + rr;
     if (tok0 + tok < M && row < N) Y[(int64_t)(tok0 + tok) * N + row] = v;
   }
