@@ -55,31 +55,44 @@ __device__ __forceinline__ uint32_t code_operand_pair(uint32_t w, uint32_t mask)
 // a high nibble in place as 16 q * 2^-kCodeShift
 template <bool NC> constexpr int kCodeShift = NC ? 0 : 24;
 
-// Bytes (0, 2) or (1, 3) of `t` as the low bytes of two fp16 halves whose
-// high byte is 0x64: a byte value v becomes the fp16 number 1024 + v.
-__device__ __forceinline__ uint32_t spread02(uint32_t t) {
-  return __builtin_amdgcn_perm(0x64646464u, t, 0x04020400u);
+// The packed fp16 pair (mul, add) of a sub-block with 6-bit scale sc:
+// (sc, -1024 sc) for its low nibbles, (sc/16, -64 sc) for high nibbles kept
+// in place.  Every value is exact in fp16 (|1024 sc| <= 64512).
+__device__ __forceinline__ uint32_t scale_pair(uint32_t sc, bool odd) {
+  const _Float16 f = (_Float16)(uint16_t)sc;
+  const half2_t k = odd ? half2_t{(_Float16)0.0625f, (_Float16)-64.0f}
+                        : half2_t{(_Float16)1.0f, (_Float16)-1024.0f};
+  return as_u32h(half2_t{f, f} * k);
 }
-__device__ __forceinline__ uint32_t spread13(uint32_t t) {
-  return __builtin_amdgcn_perm(0x64646464u, t, 0x04030401u);
+
+// A three-operand AND-OR takes at most one scalar operand and no literal on
+// this target, so the 0x64 bytes come from a register the caller holds
+// (`hi64` = 0x64006400, made by vgpr_const).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  uint32_t v = c;
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // One MFMA A operand (8 codes of one sub-block) from two qs dwords: their
 // low nibbles (hi_nib false) or their high nibbles kept in place, i.e. as
-// 16 v (true).  mul/add are per-sub-block fp16 pairs that turn 1024 + v (or
-// 1024 + 16 v) into sc*v: (sc, -1024 sc) for low nibbles and (sc/16, -64 sc)
-// for high ones.  The fused multiply-add rounds once, and sc*v is exact in
+// 16 v (true).  Each pair of codes is masked straight under the 0x64 high
+// byte of two fp16 halves (bytes 0 and 2 of a dword in place, bytes 1 and 3
+// after a shift right by 8 that a dword's low and high nibbles share), the
+// fp16 number 1024 + v or 1024 + 16 v; one AND-OR per pair.  `ma` packs the
+// sub-block's fp16 pair (mul, add) (scale_pair), and the fused multiply-add,
+// reading each half for both lanes, turns 1024 + v into sc*v, exact in
 // fp16.  Codes come out in operand order: positions (0,2), (1,3), (4,6),
 // (5,7) of the 8.
-__device__ __forceinline__ half8_t dequant8(uint32_t w0, uint32_t w1, bool hi_nib,
-                                            uint32_t mul, uint32_t add) {
-  const uint32_t mask = hi_nib ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
-  const uint32_t t0 = w0 & mask, t1 = w1 & mask;
-  const half2_t m2 = as_h2(mul), a2 = as_h2(add);
-  const half2_t p0 = __builtin_elementwise_fma(as_h2(spread02(t0)), m2, a2);
-  const half2_t p1 = __builtin_elementwise_fma(as_h2(spread13(t0)), m2, a2);
-  const half2_t p2 = __builtin_elementwise_fma(as_h2(spread02(t1)), m2, a2);
-  const half2_t p3 = __builtin_elementwise_fma(as_h2(spread13(t1)), m2, a2);
+__device__ __forceinline__ half8_t dequant8_ma(uint32_t w0, uint32_t w1, bool hi_nib,
+                                               uint32_t ma, uint32_t hi64) {
+  const uint32_t mask = hi_nib ? 0x00F000F0u : 0x000F000Fu;
+  const half2_t pr = as_h2(ma);
+  const half2_t m2 = {pr.x, pr.x}, a2 = {pr.y, pr.y};
+  const half2_t p0 = __builtin_elementwise_fma(as_h2((w0 & mask) | hi64), m2, a2);
+  const half2_t p1 = __builtin_elementwise_fma(as_h2(((w0 >> 8) & mask) | hi64), m2, a2);
+  const half2_t p2 = __builtin_elementwise_fma(as_h2((w1 & mask) | hi64), m2, a2);
+  const half2_t p3 = __builtin_elementwise_fma(as_h2(((w1 >> 8) & mask) | hi64), m2, a2);
   half8_t v;
   v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
   v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;

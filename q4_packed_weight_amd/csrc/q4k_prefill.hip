@@ -63,14 +63,13 @@ constexpr int PF_THREADS = 64 * PF_WAVES;
 constexpr int XROW = 128 + 4;
 constexpr int WROW = 36 + 2;
 constexpr int X_PER_THREAD = PF_TOK / 2;                  // 8
-constexpr int W_PER_THREAD = 9;  // 16-byte weight chunks per loader thread per stage
 
 // ROWS weight rows (RT = ROWS / 16 MFMA row tiles) per workgroup.  The
 // waves of a stage are (block bb, half): with 4 row tiles half h computes
 // row tiles 2h, 2h+1 over all eight sub-blocks; with 2 or 1, all row tiles
-// over sub-blocks 4h .. 4h+3.  Loads: the first RT waves
-// (4 ROWS threads) bring the weights, 16-byte chunk q = t + 4 ROWS m of the
-// rows' 576-byte stage pieces; all 8 waves bring the activations, float4 i
+// over sub-blocks 4h .. 4h+3.  Loads: 16-byte chunk q of the rows' 576-byte
+// stage pieces is brought by thread q % W_STRIDE (all 8 waves at 64 rows,
+// the first RT waves otherwise); all 8 waves bring the activations, float4 i
 // of thread tid = token 2i + (tid >= 256), positions 4t .. 4t+3 of the
 // stage (t = tid % 256).
 template <int ROWS>
@@ -90,16 +89,28 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   constexpr int NS = SPLIT ? 2 : 1;                    // waves sharing a block's rows
   constexpr int RPAD = ROWS + 4;          // padded row dimension of the header tables
   constexpr int WBLK = ROWS * WROW + 8;   // one super-block of all rows + 32 B
-  constexpr int LOADERS = 4 * ROWS;       // threads that load the weights
-  static_assert(ROWS * PF_BLKS * 9 == LOADERS * W_PER_THREAD, "weight chunks must divide evenly");
+  // Two choices measured per height (MI355X, graph-replayed calls at input_
+  // dim 4096 and 14336): at 64 rows every wave loads weight chunks (chunk
+  // q = tid + 512 m; the last round covers the first W_LAST threads, whole
+  // waves) and the next stage's loads leave after the barrier, 3-7% faster
+  // than 4 loader waves; at 32 and 16 rows the 4 ROWS threads of the first
+  // RT waves load 9 chunks each and the next stage's loads leave before the
+  // barrier, 3-8% faster.  Each choice slowed the other height.
+  constexpr bool SPREAD = ROWS == 64;
+  constexpr bool EARLY = !SPREAD;
+  constexpr int W_CHUNKS = ROWS * 36;  // 16-byte weight chunks of a stage
+  constexpr int W_STRIDE = SPREAD ? PF_THREADS : 4 * ROWS;
+  constexpr int W_ITERS = (W_CHUNKS + W_STRIDE - 1) / W_STRIDE;
+  constexpr int W_LAST = W_CHUNKS - W_STRIDE * (W_ITERS - 1);
+  static_assert(W_CHUNKS % 64 == 0 && W_LAST % 64 == 0, "weight rounds must cover whole waves");
   // xh/xl: fp16 hi and lo activations [block of stage][token][position
   // pairs in operand order]; wt: raw weight blocks [block of stage][row];
-  // header tables of the stage's blocks: fp16 scale pairs (mul, add) per
-  // sub-block and row, dmin*m, d.
+  // header tables of the stage's blocks: the fp16 scale pair (mul, add) of
+  // each sub-block and row packed in a dword, dmin*m, d.
   __shared__ __align__(16) uint32_t xh[PF_BLKS][PF_TOK][XROW];
   __shared__ __align__(16) uint32_t xl[PF_BLKS][PF_TOK][XROW];
   __shared__ __align__(16) uint32_t wt[PF_BLKS * WBLK];
-  __shared__ uint2 sc_tab[PF_BLKS][8][RPAD];
+  __shared__ uint2 sc_tab[PF_BLKS][4][RPAD];  // (even, odd) sub-block of a pair
   __shared__ float c_tab[PF_BLKS][8][RPAD];
   __shared__ __align__(16) float d_tab[PF_BLKS][ROWS];
 
@@ -109,7 +120,8 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const bool w_loader = wave < RT;  // waves 0 .. RT-1: threads tid < LOADERS
+  // wave-uniform: takes part in the weight loads of round m
+  auto w_round = [&](int m) { return wave < (m + 1 < W_ITERS ? W_STRIDE : W_LAST) / 64; };
   const int t = tid & 255;  // thread index within its activation-loader half
   const int bb = wave & 3;  // block of the stage this wave computes
   const int half = wave >> 2;
@@ -132,12 +144,12 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   // Prefetch registers.  The per-thread part of every load offset is fixed;
   // the stage part is wave-uniform and goes into the loads' scalar offset.
   // Chunks past a row's last block (ragged last stage) are never consumed.
-  uint4 wv[W_PER_THREAD];
+  uint4 wv[W_ITERS];
   float4 xv[X_PER_THREAD];
-  int woff[W_PER_THREAD];
+  int woff[W_ITERS];
 #pragma unroll
-  for (int m = 0; m < W_PER_THREAD; ++m) {
-    const int q = tid + LOADERS * m;
+  for (int m = 0; m < W_ITERS; ++m) {
+    const int q = tid + W_STRIDE * m;
     const int row = q / 36;
     woff[m] = row * row_bytes + 16 * (q - 36 * row);
   }
@@ -146,11 +158,10 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
 #pragma unroll
     for (int i = 0; i < X_PER_THREAD; ++i)
       xv[i] = load_buf_f4(xr, 16 * t + 4 * K * (2 * i + tok_lo), 4096 * st);
-    if (w_loader) {
 #pragma unroll
-      for (int m = 0; m < W_PER_THREAD; ++m)
+    for (int m = 0; m < W_ITERS; ++m)
+      if (w_round(m))
         wv[m] = __builtin_bit_cast(uint4, load_buf_f4(wr, woff[m], st * (4 * kBlockBytes)));
-    }
   };
   auto stage_to_lds = [&]() {
     // float4 i: token 2i + tok_lo, block (t / 64), positions 4*lane ..
@@ -168,10 +179,10 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
       *reinterpret_cast<uint2 *>(&xl[xb][tok][2 * lane]) =
           make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
     }
-    if (w_loader) {
 #pragma unroll
-      for (int m = 0; m < W_PER_THREAD; ++m) {
-        const int q = tid + LOADERS * m;
+    for (int m = 0; m < W_ITERS; ++m) {
+      if (w_round(m)) {
+        const int q = tid + W_STRIDE * m;
         const int row = q / 36;
         const int cc = q - 36 * row;
         const int b = cc / 9;
@@ -189,9 +200,15 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
   const uint32_t *wblk = &wt[bb * WBLK];
-  // header row decoded by this lane: the rows of the wave's row tiles (lanes
-  // past them repeat rows and write the same values)
-  const int hrow = 16 * rt0 + (lane & (16 * TPW - 1));
+  const uint32_t hi64 = vgpr_const(0x64006400u);
+  // Header decoding: the wave's HROWS rows x NSUB sub-blocks, SPL sub-
+  // blocks per lane (4, 2 or 1), each (row, sub-block) once.
+  constexpr int HROWS = 16 * TPW;
+  constexpr int NSUB = SPLIT ? 4 : 8;
+  constexpr int SPL = HROWS * NSUB / 64;
+  static_assert(SPL >= 1 && HROWS * NSUB == 64 * SPL, "header work must split evenly");
+  const int hrow = 16 * rt0 + lane % HROWS;
+  const int s_first = (SPLIT ? 4 * half : 0) + SPL * (lane / HROWS);  // lane's first sub-block
 
   // The token groups of a row tile start at different stages (and wrap
   // around), so that together they read whole weight rows at any moment
@@ -201,8 +218,11 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   for (int it = 0; it < n_stages; ++it) {
     const int st = st0 + it < n_stages ? st0 + it : st0 + it - n_stages;
     stage_to_lds();
+    // the registers are free again; the next stage's loads stay in flight
+    // during the MFMAs
+    if (EARLY && it + 1 < n_stages) load_stage(st + 1 < n_stages ? st + 1 : 0);
     __syncthreads();
-    if (it + 1 < n_stages) load_stage(st + 1 < n_stages ? st + 1 : 0);  // in flight during the MFMAs
+    if (!EARLY && it + 1 < n_stages) load_stage(st + 1 < n_stages ? st + 1 : 0);
 
     if (st * PF_BLKS + bb < nb) {
       // ---- headers of this wave's rows of block bb
@@ -210,30 +230,30 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
         const uint2 h01 = *reinterpret_cast<const uint2 *>(&wblk[hrow * WROW]);
         const uint2 h23 = *reinterpret_cast<const uint2 *>(&wblk[hrow * WROW + 2]);
         const float d = half_lo(h01.x), dmin = half_hi(h01.x);
-        // 6-bit scales and mins, four per dword (one per byte)
-        const uint32_t sc03 = h01.y & 0x3F3F3F3Fu;
-        const uint32_t mn03 = h23.x & 0x3F3F3F3Fu;
-        const uint32_t sc47 = (h23.y & 0x0F0F0F0Fu) | ((h01.y >> 2) & 0x30303030u);
-        const uint32_t mn47 = ((h23.y >> 4) & 0x0F0F0F0Fu) | ((h23.x >> 2) & 0x30303030u);
-        d_tab[bb][hrow] = d;
-        const uint32_t scw[2] = {sc03, sc47}, mnw[2] = {mn03, mn47};
+        // 6-bit scales and mins of sub-blocks 4hw .. 4hw+3, one per byte
+        const bool hw = s_first >= 4;
+        const uint32_t scw = hw ? (h23.y & 0x0F0F0F0Fu) | ((h01.y >> 2) & 0x30303030u)
+                                : h01.y & 0x3F3F3F3Fu;
+        const uint32_t mnw = hw ? ((h23.y >> 4) & 0x0F0F0F0Fu) | ((h23.x >> 2) & 0x30303030u)
+                                : h23.x & 0x3F3F3F3Fu;
+        const int sh = 8 * (s_first & 3);
+        if (s_first == (SPLIT ? 4 * half : 0)) d_tab[bb][hrow] = d;
+        uint32_t pk[SPL];
 #pragma unroll
-        for (int hw = 0; hw < 2; ++hw) {
-          if (SPLIT && hw != half) continue;  // wave-uniform: only its own sub-blocks
+        for (int e = 0; e < SPL; ++e) {
+          const int s = s_first + e;
+          const float mnf = (float)((mnw >> (sh + 8 * e)) & 255u);
+          c_tab[bb][s][hrow] = dmin * mnf;
+          // even sub-blocks are low nibbles, odd ones high nibbles (16 v)
+          pk[e] = scale_pair((scw >> (sh + 8 * e)) & 255u, SPL > 1 ? (e & 1) : (s & 1));
+        }
+        uint32_t *tab = reinterpret_cast<uint32_t *>(&sc_tab[bb][s_first >> 1][hrow]);
+        if constexpr (SPL == 1) {
+          tab[s_first & 1] = pk[0];
+        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int s = 4 * hw + e;
-            const float scf = (float)((scw[hw] >> (8 * e)) & 255u);
-            const float mnf = (float)((mnw[hw] >> (8 * e)) & 255u);
-            c_tab[bb][s][hrow] = dmin * mnf;
-            // even sub-blocks are low nibbles, odd ones high nibbles (16 v)
-            const float mulf = (s & 1) ? scf * 0.0625f : scf;
-            const float addf = (s & 1) ? scf * -64.0f : scf * -1024.0f;
-            half2_t m2, a2;
-            m2.x = m2.y = (_Float16)mulf;
-            a2.x = a2.y = (_Float16)addf;
-            sc_tab[bb][s][hrow] = make_uint2(as_u32h(m2), as_u32h(a2));
-          }
+          for (int e = 0; e < SPL; e += 2)
+            *reinterpret_cast<uint2 *>(tab + 2 * RPAD * (e >> 1)) = make_uint2(pk[e], pk[e + 1]);
         }
       }
 
@@ -248,13 +268,12 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
 #pragma unroll
       for (int jj = 0; jj < NJ; ++jj) {
         const int j = j0 + jj;
-        uint2 qb[TPW], tl[TPW], th[TPW];
+        uint2 qb[TPW], sp[TPW];
 #pragma unroll
         for (int a = 0; a < TPW; ++a) {
           const int row = 16 * (rt0 + a) + r;
           qb[a] = *reinterpret_cast<const uint2 *>(&wblk[row * WROW + 4 + 8 * j + 2 * g]);
-          tl[a] = sc_tab[bb][2 * j][row];
-          th[a] = sc_tab[bb][2 * j + 1][row];
+          sp[a] = sc_tab[bb][j][row];
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -264,8 +283,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
           half8_t A[TPW];
 #pragma unroll
           for (int a = 0; a < TPW; ++a)
-            A[a] = h ? dequant8(qb[a].x, qb[a].y, true, th[a].x, th[a].y)
-                     : dequant8(qb[a].x, qb[a].y, false, tl[a].x, tl[a].y);
+            A[a] = dequant8_ma(qb[a].x, qb[a].y, h != 0, h ? sp[a].y : sp[a].x, hi64);
           floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
           for (int a = 0; a < TPW; ++a)

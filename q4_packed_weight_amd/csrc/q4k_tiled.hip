@@ -564,13 +564,14 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
   half8_t ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
+  const uint32_t hi64 = vgpr_const(0x64006400u);
 
   auto compute = [&](auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    // headers of row r of this wave's row groups: the fp16 (mul, add) pairs
-    // of its sub-blocks, dmin*m of sub-blocks g and 4 + g (the lazy-dmin
-    // MFMA's A operand), and d into the wave's table for the D rows
-    uint32_t mul[TPW][2 * NJ], add[TPW][2 * NJ];  // by the wave's own sub-block index
+    // headers of row r of this wave's row groups: the packed fp16 (mul, add)
+    // pairs of its sub-blocks, dmin*m of sub-blocks g and 4 + g (the lazy-
+    // dmin MFMA's A operand), and d into the wave's table for the D rows
+    uint32_t ma[TPW][2 * NJ];  // by the wave's own sub-block index
     float cm[TPW][2];
 #pragma unroll
     for (int a = 0; a < TPW; ++a) {
@@ -583,15 +584,8 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
 #pragma unroll
       for (int ls = 0; ls < 2 * NJ; ++ls) {  // sub-block 4 half + ls (SPLIT), else ls
         const uint32_t scw = SPLIT ? (half ? sc47 : sc03) : (ls < 4 ? sc03 : sc47);
-        const float scf = (float)((scw >> (8 * (ls & 3))) & 255u);
         // even sub-blocks are low nibbles, odd ones high nibbles (16 v)
-        const float mulf = (ls & 1) ? scf * 0.0625f : scf;
-        const float addf = (ls & 1) ? scf * -64.0f : scf * -1024.0f;
-        half2_t m2, a2;
-        m2.x = m2.y = (_Float16)mulf;
-        a2.x = a2.y = (_Float16)addf;
-        mul[a][ls] = as_u32h(m2);
-        add[a][ls] = as_u32h(a2);
+        ma[a][ls] = scale_pair((scw >> (8 * (ls & 3))) & 255u, ls & 1);
       }
       cm[a][0] = dmin * (float)((mn03 >> (8 * g)) & 255u);  // sub-block g
       cm[a][1] = dmin * (float)((mn47 >> (8 * g)) & 255u);  // sub-block 4 + g
@@ -618,7 +612,7 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
         half8_t A[TPW];
 #pragma unroll
         for (int a = 0; a < TPW; ++a)
-          A[a] = dequant8(qb[a].x, qb[a].y, hh != 0, mul[a][2 * jj + hh], add[a][2 * jj + hh]);
+          A[a] = dequant8_ma(qb[a].x, qb[a].y, hh != 0, ma[a][2 * jj + hh], hi64);
         floatx4 sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, Bh, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
         for (int a = 0; a < TPW; ++a)
@@ -663,9 +657,10 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     constexpr int buf = decltype(bufc)::value;
     const int st = st0 + it < n_stages ? st0 + it : st0 + it - n_stages;
     stage_x();
-    __syncthreads();
+    // the next stage's loads go out before the barrier (xv is free again)
     if (it + 1 < n_stages)
       load_stage(st + 1 < n_stages ? st + 1 : 0, std::integral_constant<int, buf ^ 1>());
+    __syncthreads();
     if (st * TP_BLKS + bb < nb) compute(bufc);  // wave-uniform
     __syncthreads();  // the next stage overwrites the activation tiles
   };
