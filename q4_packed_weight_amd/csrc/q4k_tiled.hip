@@ -657,10 +657,14 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     constexpr int buf = decltype(bufc)::value;
     const int st = st0 + it < n_stages ? st0 + it : st0 + it - n_stages;
     stage_x();
-    // the next stage's loads go out before the barrier (xv is free again)
-    if (it + 1 < n_stages)
+    // Narrow tiles send the next stage's loads before the barrier (xv is
+    // free again), 64-row tiles after it: the faster placement of each, as
+    // measured for the canonical prefill.
+    if (ROWS < 64 && it + 1 < n_stages)
       load_stage(st + 1 < n_stages ? st + 1 : 0, std::integral_constant<int, buf ^ 1>());
     __syncthreads();
+    if (ROWS == 64 && it + 1 < n_stages)
+      load_stage(st + 1 < n_stages ? st + 1 : 0, std::integral_constant<int, buf ^ 1>());
     if (st * TP_BLKS + bb < nb) compute(bufc);  // wave-uniform
     __syncthreads();  // the next stage overwrites the activation tiles
   };
