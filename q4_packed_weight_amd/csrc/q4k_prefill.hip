@@ -369,14 +369,14 @@ int prefill_rows(int64_t M, int64_t N) {
   // height costs rounds of 256 workgroups x its per-workgroup time.  The
   // per-workgroup times measured on MI355X (graph-replayed calls, input_dim
   // 4096, 256 workgroups each, less the 1.4 us between graph nodes): 64 rows
-  // 14.3 us, 32 rows 10.1, 16 rows 8.1, i.e. 100 : 71 : 57.  Measured
-  // us/call, 64-row tiles vs the chosen height: 16 tokens x 4096 rows 15.7
-  // vs 9.5 (16 rows), 32 x 4096 15.5 vs 11.5 (32 rows), 16 tokens 14336 ->
-  // 4096 48.9 vs 27.7 (16 rows); 48 x 4096 and 16 x 14336 stay at 64 rows
-  // (doubling the grid past one round cost 22.2 vs 15.6 and 24.0 vs 17.4).
+  // 13.4 us, 32 rows 9.4, 16 rows 7.4, i.e. 100 : 70 : 55.  Measured
+  // us/call, 64-row tiles vs the chosen height: 16 tokens x 4096 rows 14.6
+  // vs 8.8 (16 rows), 32 x 4096 14.5 vs 10.8 (32 rows), 16 tokens 14336 ->
+  // 4096 44.4 vs 25.5 (16 rows); 48 x 4096 and 16 x 14336 stay at 64 rows
+  // (the 32-row grid, past one round, cost 19.6 vs 14.6 and 20.7 vs 15.8).
   const int64_t tok_groups = (M + PF_TOK - 1) / PF_TOK;
   const int rows[3] = {64, 32, 16};
-  const int64_t cost[3] = {100, 71, 57};
+  const int64_t cost[3] = {100, 70, 55};
   int best = 64;
   int64_t best_cost = INT64_MAX;
   for (int i = 0; i < 3; ++i) {
