@@ -92,8 +92,7 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
  *   Y          fp32 [n_tokens, output_dim]
  * Same error behaviour and tolerance as q4k_gemv.  Three kernels serve it:
  * M == 1 is q4k_gemv; a few tokens (M <= 2 at any shape, M <= 4 with
- * output_dim <= 4096, M <= 8 with output_dim <= 4096 and input_dim > 8192)
- * run on a batched matrix-core GEMV that reads each weight once for all of
+ * output_dim <= 4096) run on a batched matrix-core GEMV that reads each weight once for all of
  * them; larger batches run on the prefill tiles (64 rows x 16 tokens,
  * narrowed to 32 or 16 rows when 64-row tiles would leave CUs idle).  The batched and
  * prefill kernels pass the activations through fp16 (split into a high and
@@ -337,8 +336,9 @@ int q4k_gemv_tiled(const float *x, const uint8_t *w_tiled, int64_t input_dim,
  *   w_tiled    as for q4k_gemv_tiled
  *   n_tokens   M > 0 (M == 1 runs q4k_gemv_tiled)
  *   input_dim, output_dim, Y as for q4k_matmul
- * The kernels mirror q4k_matmul's: a few tokens (M <= 4, or M <= 8 with
- * output_dim <= 4096 and input_dim >= 4096) on the batched matrix-core GEMV
+ * The kernels are q4k_matmul's on this layout, with a hand-over measured
+ * for it: a few tokens (M <= 4, or M <= 8 with output_dim <= 4096 and
+ * input_dim >= 4096) on the batched matrix-core GEMV
  * (any |X| < 2^96), more on the 64-row x 16-token prefill tiles
  * (|X| < 65504); every tile is loaded straight into registers.  Errors and
  * tolerance as for q4k_matmul.
