@@ -5,6 +5,12 @@ import torch
 DEV = "cuda:0"
 CANARY = 64  # extra output elements that must stay untouched
 
+# Every launch shape (rows per lane, k-waves, workgroup waves) the vector-form
+# GEMVs accept; 8 waves with 8 rows per lane is rejected (test_abi_cpu).
+VECTOR_SHAPES = [(rpl, kw, wg) for rpl in (1, 2, 4, 8)
+                 for kw, wg in ((1, 1), (1, 2), (2, 2), (1, 4), (2, 4), (4, 4), (1, 8), (2, 8))
+                 if not (wg == 8 and rpl == 8)]
+
 
 def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)

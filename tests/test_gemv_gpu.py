@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from q4_packed_weight_amd import binding, synth
-from gpu_util import canary_intact, dev, host, out_with_canary
+from gpu_util import VECTOR_SHAPES, canary_intact, dev, host, out_with_canary
 from tolerance import assert_parity
 
 pytestmark = pytest.mark.gpu
@@ -101,12 +101,9 @@ def test_matrix_core_form_rejects_shape_fields():
         binding.q4k_gemv_shaped(xd, wd, 256, 1, y, 4, 0, 16)
 
 
-@pytest.mark.parametrize("rpl", [1, 2, 4, 8])
-@pytest.mark.parametrize("kw,wg", [(1, 1), (1, 2), (2, 2), (1, 4), (2, 4), (4, 4), (1, 8), (2, 8)])
+@pytest.mark.parametrize("rpl,kw,wg", VECTOR_SHAPES)
 @pytest.mark.parametrize("K,N", [(4096, 333), (14336, 67), (1024, 129), (256, 50)])
 def test_every_launch_shape(oracle_lib, K, N, rpl, kw, wg):
-    if wg == 8 and rpl == 8:
-        pytest.skip("8 waves x 8 rows per lane is not a supported shape")
     w = synth.q4k_weights(N, K, config=11, copy=K)
     x = synth.activations(K, config=11, copy=K)
     y = run_gemv(x, w, K, N, shape=(rpl, kw, wg))

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from q4_packed_weight_amd import binding, synth
-from gpu_util import canary_intact, dev, host, out_with_canary
+from gpu_util import VECTOR_SHAPES, canary_intact, dev, host, out_with_canary
 from tolerance import assert_parity
 
 pytestmark = pytest.mark.gpu
@@ -42,12 +42,9 @@ def test_q4_0_parity(oracle_lib, K, N):
     assert_parity(y, oracle_lib.q4_0_gemv(x, w, K, N), what=f"K={K} N={N}")
 
 
-@pytest.mark.parametrize("rpl", [1, 2, 4, 8])
-@pytest.mark.parametrize("kw,wg", [(1, 1), (1, 2), (2, 2), (1, 4), (2, 4), (4, 4), (1, 8), (2, 8)])
+@pytest.mark.parametrize("rpl,kw,wg", VECTOR_SHAPES)
 @pytest.mark.parametrize("K,N", [(4096, 333), (14336, 67), (1024, 129), (256, 50)])
 def test_q4_0_every_launch_shape(oracle_lib, K, N, rpl, kw, wg):
-    if wg == 8 and rpl == 8:
-        pytest.skip("8 waves x 8 rows per lane is not a supported shape")
     w = synth.q4_0_weights(N, K, copy=3 * K)
     x = synth.activations(K, config=synth.Q40_4K, copy=3 * K)
     y = run(x, w, K, N, shape=(rpl, kw, wg))

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from q4_packed_weight_amd import binding, synth
-from gpu_util import canary_intact, dev, host, out_with_canary
+from gpu_util import VECTOR_SHAPES, canary_intact, dev, host, out_with_canary
 from tolerance import assert_parity
 
 pytestmark = pytest.mark.gpu
@@ -44,12 +44,9 @@ def test_q6k_parity(oracle_lib, K, N):
     assert_parity(y, oracle_lib.q6k_gemv(x, w, K, N), what=f"K={K} N={N}")
 
 
-@pytest.mark.parametrize("rpl", [1, 2, 4, 8])
-@pytest.mark.parametrize("kw,wg", [(1, 1), (1, 2), (2, 2), (1, 4), (2, 4), (4, 4), (1, 8), (2, 8)])
+@pytest.mark.parametrize("rpl,kw,wg", VECTOR_SHAPES)
 @pytest.mark.parametrize("K,N", [(4096, 333), (14336, 67), (1024, 129), (768, 50)])
 def test_q6k_every_launch_shape(oracle_lib, K, N, rpl, kw, wg):
-    if wg == 8 and rpl == 8:
-        pytest.skip("8 waves x 8 rows per lane is not a supported shape")
     w = synth.q6k_weights(N, K, copy=5 * K)
     x = synth.activations(K, config=synth.Q6K_4K, copy=5 * K)
     if rpl == 8 and kw == 4 and 4 * (K // 256) > 32:
