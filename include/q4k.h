@@ -339,9 +339,11 @@ int q4k_gemv_tiled(const float *x, const uint8_t *w_tiled, int64_t input_dim,
  * The kernels are q4k_matmul's on this layout, with a hand-over measured
  * for it: a few tokens (M <= 4, or M <= 8 with output_dim <= 4096 and
  * input_dim >= 4096) on the batched matrix-core GEMV
- * (any |X| < 2^96), more on the 64-row x 16-token prefill tiles
- * (|X| < 65504); every tile is loaded straight into registers.  Errors and
- * tolerance as for q4k_matmul.
+ * (any |X| < 2^96), more on the prefill tiles of q4k_matmul (64, 32 or 16
+ * rows x 16 tokens, |X| < 65504), which give q4k_matmul's bits: 64-row tiles
+ * with input_dim below 8192 load each wave's tiles straight into registers,
+ * the rest stage whole tiles through LDS.  Errors and tolerance as for
+ * q4k_matmul.
  */
 int q4k_matmul_tiled(const float *X, const uint8_t *w_tiled, int64_t n_tokens,
                      int64_t input_dim, int64_t output_dim, float *Y, void *stream);

@@ -53,6 +53,9 @@ namespace q4k {
 namespace {
 
 constexpr int kBlockBytes = 144;
+constexpr int kTileRows = 16;                      // tiled block order: rows per group
+constexpr int kTileBytes = 16 * kBlockBytes;       // one tile: a group's super-block
+constexpr int kTileChunks = kTileBytes / 16;
 constexpr int PF_TOK = 16;            // tokens per workgroup (one token tile)
 constexpr int PF_BLKS = 4;            // super-blocks per stage
 constexpr int PF_WAVES = 8;           // two waves per block of a stage
@@ -72,7 +75,13 @@ constexpr int X_PER_THREAD = PF_TOK / 2;                  // 8
 // the first RT waves otherwise); all 8 waves bring the activations, float4 i
 // of thread tid = token 2i + (tid >= 256), positions 4t .. 4t+3 of the
 // stage (t = tid % 256).
-template <int ROWS>
+// TILED: w holds the weights in the tiled block order (16-row groups, one
+// 2304-byte tile per group and super-block: 16-byte chunk c < 128 carries
+// qs bytes 8g .. 8g+7 of pairs 2h and 2h+1 of row n, h = c / 64, n = c % 16,
+// g = (c % 64) / 16; chunks 128 + n the header of row n).  The stage's
+// chunks are then whole tiles, read contiguously, and staging scatters each
+// into the same LDS block layout, so both orders give the same bits.
+template <int ROWS, bool TILED>
 __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     const float *X, const uint8_t *w, float *__restrict__ Y, int M, int nb,
     int N) {
@@ -135,9 +144,13 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   const int row_bytes = nb * kBlockBytes;
   const int n_stages = (nb + PF_BLKS - 1) / PF_BLKS;
 
-  // Range-checked views: rows past N and tokens past M read as zeros.
+  // Range-checked views: rows past N and tokens past M read as zeros (the
+  // tiled order pads its last row group with zero rows).
+  const int ng_left = (N - row0 + kTileRows - 1) / kTileRows;  // row groups from row0 on
   const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(w + (int64_t)row0 * row_bytes, (int64_t)(N - row0) * row_bytes);
+      TILED ? make_rsrc(w + (int64_t)(row0 / kTileRows) * nb * kTileBytes,
+                        (int64_t)min(RT, ng_left) * nb * kTileBytes)
+            : make_rsrc(w + (int64_t)row0 * row_bytes, (int64_t)(N - row0) * row_bytes);
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(X + (int64_t)tok0 * K, (int64_t)(M - tok0) * K * 4);
 
@@ -150,9 +163,16 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
 #pragma unroll
   for (int m = 0; m < W_ITERS; ++m) {
     const int q = tid + W_STRIDE * m;
-    const int row = q / 36;
-    woff[m] = row * row_bytes + 16 * (q - 36 * row);
+    if constexpr (TILED) {
+      // chunk q: tile q / 144 = (row group a, block bb of the stage)
+      const int tile = q / kTileChunks;
+      woff[m] = ((tile >> 2) * nb + (tile & 3)) * kTileBytes + 16 * (q - kTileChunks * tile);
+    } else {
+      const int row = q / 36;
+      woff[m] = row * row_bytes + 16 * (q - 36 * row);
+    }
   }
+  constexpr int W_STAGE_BYTES = PF_BLKS * (TILED ? kTileBytes : kBlockBytes);
   const int tok_lo = tid >> 8;  // tokens 2i + tok_lo
   auto load_stage = [&](int st) {
 #pragma unroll
@@ -161,7 +181,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
 #pragma unroll
     for (int m = 0; m < W_ITERS; ++m)
       if (w_round(m))
-        wv[m] = __builtin_bit_cast(uint4, load_buf_f4(wr, woff[m], st * (4 * kBlockBytes)));
+        wv[m] = __builtin_bit_cast(uint4, load_buf_f4(wr, woff[m], st * W_STAGE_BYTES));
   };
   auto stage_to_lds = [&]() {
     // float4 i: token 2i + tok_lo, block (t / 64), positions 4*lane ..
@@ -183,12 +203,27 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
     for (int m = 0; m < W_ITERS; ++m) {
       if (w_round(m)) {
         const int q = tid + W_STRIDE * m;
-        const int row = q / 36;
-        const int cc = q - 36 * row;
-        const int b = cc / 9;
-        uint32_t *dst = &wt[b * WBLK + row * WROW + 4 * (cc - 9 * b)];
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(wv[m].x, wv[m].y);
-        *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wv[m].z, wv[m].w);
+        uint32_t *d0, *d1;  // LDS homes of the chunk's two 8-byte halves
+        if constexpr (TILED) {
+          const int tile = q / kTileChunks;
+          const int c = q - kTileChunks * tile;
+          uint32_t *blk = &wt[(tile & 3) * WBLK + 16 * (tile >> 2) * WROW];
+          if (c < 128) {  // pair 2h at dword 4 + 16h + 2g of row n, pair 2h+1 8 dwords on
+            d0 = blk + (c & 15) * WROW + 4 + 16 * (c >> 6) + 2 * ((c >> 4) & 3);
+            d1 = d0 + 8;
+          } else {  // header of row c - 128
+            d0 = blk + (c - 128) * WROW;
+            d1 = d0 + 2;
+          }
+        } else {
+          const int row = q / 36;
+          const int cc = q - 36 * row;
+          const int b = cc / 9;
+          d0 = &wt[b * WBLK + row * WROW + 4 * (cc - 9 * b)];
+          d1 = d0 + 2;
+        }
+        *reinterpret_cast<uint2 *>(d0) = make_uint2(wv[m].x, wv[m].y);
+        *reinterpret_cast<uint2 *>(d1) = make_uint2(wv[m].z, wv[m].w);
       }
     }
   };
@@ -345,21 +380,33 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   }
 }
 
-template <int ROWS>
+template <int ROWS, bool TILED>
 hipError_t prefill_launch_rows(const float *X, const uint8_t *w, int64_t M, int64_t K, int64_t N,
                                float *Y, hipStream_t stream) {
   const int64_t nb = K / 256;
   // Offsets formed in the kernel (a row tile of ROWS rows plus one stage
   // past its end, 16 rows of X plus one stage) must stay below 2^31 bytes.
-  if ((int64_t)ROWS * nb * kBlockBytes + 4096 >= ((int64_t)1 << 31) ||
+  if ((int64_t)ROWS * nb * kBlockBytes + 4 * kTileBytes >= ((int64_t)1 << 31) ||
       ((int64_t)PF_TOK * K + 2048) * 4 >= ((int64_t)1 << 31) || N > 0x7FFFFFFF ||
       M > 0x7FFFFFFF)
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + ROWS - 1) / ROWS), (unsigned)((M + PF_TOK - 1) / PF_TOK));
   if (grid.y > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(q4k_prefill_kernel<ROWS>, grid, dim3(PF_THREADS), 0, stream, X, w, Y,
-                     (int)M, (int)nb, (int)N);
+  hipLaunchKernelGGL((q4k_prefill_kernel<ROWS, TILED>), grid, dim3(PF_THREADS), 0, stream, X, w,
+                     Y, (int)M, (int)nb, (int)N);
   return hipGetLastError();
+}
+
+template <bool TILED>
+hipError_t prefill_launch_any(const float *X, const uint8_t *w, int64_t M, int64_t K, int64_t N,
+                              float *Y, hipStream_t stream, int rows) {
+  if (rows == 0) rows = prefill_rows(M, N);
+  switch (rows) {
+    case 64: return prefill_launch_rows<64, TILED>(X, w, M, K, N, Y, stream);
+    case 32: return prefill_launch_rows<32, TILED>(X, w, M, K, N, Y, stream);
+    case 16: return prefill_launch_rows<16, TILED>(X, w, M, K, N, Y, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -389,13 +436,12 @@ int prefill_rows(int64_t M, int64_t N) {
 
 hipError_t prefill_launch(const float *X, const uint8_t *w, int64_t M,
                           int64_t K, int64_t N, float *Y, hipStream_t stream, int rows) {
-  if (rows == 0) rows = prefill_rows(M, N);
-  switch (rows) {
-    case 64: return prefill_launch_rows<64>(X, w, M, K, N, Y, stream);
-    case 32: return prefill_launch_rows<32>(X, w, M, K, N, Y, stream);
-    case 16: return prefill_launch_rows<16>(X, w, M, K, N, Y, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return prefill_launch_any<false>(X, w, M, K, N, Y, stream, rows);
+}
+
+hipError_t prefill_staged_tiled_launch(const float *X, const uint8_t *wt, int64_t M, int64_t K,
+                                       int64_t N, float *Y, hipStream_t stream, int rows) {
+  return prefill_launch_any<true>(X, wt, M, K, N, Y, stream, rows);
 }
 
 }  // namespace q4k

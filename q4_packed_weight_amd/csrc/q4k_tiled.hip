@@ -465,17 +465,18 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
   }
 }
 
-// Prefill on tiled weights: the prefill tiles of q4k_prefill.hip (ROWS =
-// 64, 32 or 16 weight rows, i.e. RT row groups, x 16 tokens; the same
+// Prefill on tiled weights, 64 rows (4 row groups) x 16 tokens per
+// workgroup: the 64-row prefill tiles of q4k_prefill.hip (the same
 // arithmetic: A = sc*q exact in fp16, activations split into fp16 hi + lo,
-// d applied per block, the lazy-dmin term on the fp32 MFMA), with the
+// d applied per block, the lazy-dmin term on the fp32 MFMA) with the
 // weights no longer staged through LDS.  Wave (bb, half) computes
-// super-block bb of each 4-super-block stage, as in q4k_prefill.hip: with 4
-// row groups for row groups 2 half and 2 half + 1, with 2 or 1 for all row
-// groups over sub-blocks 4 half .. 4 half + 3 (then it loads only the qs
-// half it uses).  It loads its tiles straight into registers one
-// stage ahead (its A operand bytes are its own 16-byte slots) and decodes
-// its rows' headers in registers; only the activations go through LDS.
+// super-block bb of each 4-super-block stage for row groups 2 half and
+// 2 half + 1, as in q4k_prefill.hip.  It loads its tiles straight into
+// registers one stage ahead (its A operand bytes are its own 16-byte slots)
+// and decodes its rows' headers in registers; only the activations go
+// through LDS.  (Narrower tiles, and 64-row tiles from input_dim 8192 on,
+// run q4k_prefill.hip's kernel on the tiled order instead: measured faster
+// there.)
 
 // A 16-byte tile load, cached (REUSE) or streaming.
 template <bool REUSE>
@@ -484,6 +485,7 @@ __device__ __forceinline__ uint4 load_tile16(__amdgpu_buffer_rsrc_t r, int off, 
   else return load_buf_stream16(r, off, soff);
 }
 
+constexpr int TP_ROWS = 64;   // weight rows per workgroup
 constexpr int TP_TOK = 16;    // tokens per workgroup (one MFMA token tile)
 constexpr int TP_BLKS = 4;    // super-blocks per stage
 constexpr int TP_WAVES = 8;
@@ -493,15 +495,13 @@ constexpr int TP_XROW = 128 + 4;  // LDS dwords per staged activation row (+ 16 
 // loaded as ordinary cached loads that the later groups find in L2 (64
 // tokens x 4096 -> 4096 measured 15.0 us with streaming loads, 13.7
 // cached); a single token group streams them (10.0 vs 10.3 us at 16 tokens).
-template <int ROWS, bool REUSE>
+template <bool REUSE>
 __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     const float *X, const uint8_t *wt, float *__restrict__ Y, int M, int nb, int N) {
-  constexpr int RT = ROWS / 16;            // row groups per workgroup
-  constexpr bool SPLIT = RT <= 2;          // the block's two waves split its sub-blocks
-  constexpr int TPW = SPLIT ? RT : 2;      // row groups per wave
-  constexpr int NJ = SPLIT ? 2 : 4;        // sub-block pairs per wave
-  constexpr int NH = SPLIT ? 1 : 2;        // qs halves per tile the wave loads
-  constexpr int NS = SPLIT ? 2 : 1;        // waves sharing a block's rows
+  constexpr int ROWS = TP_ROWS;
+  constexpr int RT = ROWS / 16;  // row groups per workgroup
+  constexpr int TPW = 2;         // row groups per wave
+  constexpr int NJ = 4;          // sub-block pairs per wave
   __shared__ __align__(16) uint32_t xh[TP_BLKS][TP_TOK][TP_XROW];
   __shared__ __align__(16) uint32_t xl[TP_BLKS][TP_TOK][TP_XROW];
   __shared__ __align__(16) float dtab[TP_WAVES][TPW][16];
@@ -512,8 +512,7 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bb = wave & 3;     // super-block of the stage this wave computes
   const int half = wave >> 2;
-  const int rt0 = SPLIT ? 0 : 2 * half;  // first row group of this wave
-  const int j0 = SPLIT ? 2 * half : 0;   // first sub-block pair
+  const int rt0 = 2 * half;    // first row group of this wave
   const int r = lane & 15;     // A: row within a row group; B and D: token
   const int g = lane >> 4;
   const int t = tid & 255;
@@ -530,11 +529,10 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
       make_rsrc(X + (int64_t)tok0 * K, (int64_t)(M - tok0) * K * 4);
   constexpr int kPastEnd = 0x7FFFF000;
 
-  // qs half hs of a tile at 1024 hs + 16 lane (with one row group per
-  // workgroup a wave loads only its own half), the header at 2048 + 16 r
-  const int vq[2] = {16 * lane + (SPLIT ? 1024 * half : 0), 1024 + 16 * lane};
+  // qs half hs of a tile at 1024 hs + 16 lane, the header at 2048 + 16 r
+  const int vq[2] = {16 * lane, 1024 + 16 * lane};
   const int vhd = 2048 + 16 * r;
-  uint4 qs[2][TPW][NH], hd[2][TPW];  // [buffer][row group a][qs half]
+  uint4 qs[2][TPW][2], hd[2][TPW];  // [buffer][row group a][qs half]
   float4 xv[8];
   const int tok_lo = tid >> 8;  // float4 i of this thread: token 2i + tok_lo
   auto load_stage = [&](int st, auto bufc) {
@@ -547,7 +545,7 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     for (int a = 0; a < TPW; ++a) {
       const int off = b < nb ? ((rt0 + a) * nb + b) * kTileBytes : kPastEnd;
 #pragma unroll
-      for (int hs = 0; hs < NH; ++hs) qs[buf][a][hs] = load_tile16<REUSE>(wr, vq[hs], off);
+      for (int hs = 0; hs < 2; ++hs) qs[buf][a][hs] = load_tile16<REUSE>(wr, vq[hs], off);
       hd[buf][a] = load_tile16<REUSE>(wr, vhd, off);
     }
   };
@@ -593,8 +591,8 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
       const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
       const uint32_t mn47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
 #pragma unroll
-      for (int ls = 0; ls < 2 * NJ; ++ls) {  // sub-block 4 half + ls (SPLIT), else ls
-        const uint32_t scw = SPLIT ? (half ? sc47 : sc03) : (ls < 4 ? sc03 : sc47);
+      for (int ls = 0; ls < 2 * NJ; ++ls) {  // sub-block ls
+        const uint32_t scw = ls < 4 ? sc03 : sc47;
         // even sub-blocks are low nibbles, odd ones high nibbles (16 v)
         ma[a][ls] = scale_pair((scw >> (8 * (ls & 3))) & 255u, ls & 1);
       }
@@ -608,11 +606,11 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     float xsb[2] = {0.f, 0.f};
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
-      const int j = j0 + jj;
+      const int j = jj;
       uint2 qb[TPW];
 #pragma unroll
       for (int a = 0; a < TPW; ++a) {
-        const uint4 v = qs[buf][a][NH == 1 ? 0 : jj >> 1];
+        const uint4 v = qs[buf][a][jj >> 1];
         qb[a] = (jj & 1) ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
       }
 #pragma unroll
@@ -650,7 +648,6 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
       // lazy-dmin term: A[row][kk] = dmin*m of sub-block 4c + kk, B = sums
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        if (SPLIT && c != half) continue;  // wave-uniform: its own sub-blocks
         m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(cm[a][c], xsb[c], m_acc[a], 0, 0, 0);
       }
     }
@@ -668,13 +665,10 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     constexpr int buf = decltype(bufc)::value;
     const int st = st0 + it < n_stages ? st0 + it : st0 + it - n_stages;
     stage_x();
-    // Narrow tiles send the next stage's loads before the barrier (xv is
-    // free again), 64-row tiles after it: the faster placement of each, as
-    // measured for the canonical prefill.
-    if (ROWS < 64 && it + 1 < n_stages)
-      load_stage(st + 1 < n_stages ? st + 1 : 0, std::integral_constant<int, buf ^ 1>());
     __syncthreads();
-    if (ROWS == 64 && it + 1 < n_stages)
+    // the next stage's loads leave after the barrier (measured faster than
+    // before it for 64-row tiles, as for the canonical prefill)
+    if (it + 1 < n_stages)
       load_stage(st + 1 < n_stages ? st + 1 : 0, std::integral_constant<int, buf ^ 1>());
     if (st * TP_BLKS + bb < nb) compute(bufc);  // wave-uniform
     __syncthreads();  // the next stage overwrites the activation tiles
@@ -688,14 +682,12 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
 
   // Add the waves' partial tiles (through the activation tiles, no longer
   // needed) and store.  Lane (token r, group g) holds rows 16 (rt0 + a) +
-  // 4g + e of its token; partial slot (bb, share) of the rows.
+  // 4g + e of its token; partial slot bb of the rows.
   constexpr int RROW = ROWS + 4;
-  // [block][token][RROW] per share: the first share in xh, the second in xl
-  float *red0 = reinterpret_cast<float *>(&xh[0][0][0]);
-  float *red1 = reinterpret_cast<float *>(&xl[0][0][0]);
+  // [block][token][RROW]
+  float *red = reinterpret_cast<float *>(&xh[0][0][0]);
   static_assert(TP_BLKS * TP_TOK * RROW <= TP_BLKS * TP_TOK * TP_XROW,
                 "the partial tiles must fit in the activation tiles");
-  float *red = NS == 2 && half ? red1 : red0;
 #pragma unroll
   for (int a = 0; a < TPW; ++a)
     *reinterpret_cast<float4 *>(&red[(bb * TP_TOK + r) * RROW + 16 * (rt0 + a) + 4 * g]) =
@@ -706,28 +698,24 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     const int tok = o / ROWS, rr = o % ROWS;
     float v = 0.f;
 #pragma unroll
-    for (int b = 0; b < TP_BLKS; ++b) {
-      v += red0[(b * TP_TOK + tok) * RROW + rr];
-      if (NS == 2) v += red1[(b * TP_TOK + tok) * RROW + rr];
-    }
+    for (int b = 0; b < TP_BLKS; ++b) v += red[(b * TP_TOK + tok) * RROW + rr];
     const int row = rg0 * kTileRows + rr;
     if (tok0 + tok < M && row < N) Y[(int64_t)(tok0 + tok) * N + row] = v;
   }
 }
 
-template <int ROWS>
-hipError_t prefill_tiled_launch_rows(const float *X, const uint8_t *wt, int64_t M, int64_t nb,
-                                     int64_t N, float *Y, hipStream_t stream) {
+hipError_t prefill_tiled_launch_64(const float *X, const uint8_t *wt, int64_t M, int64_t nb,
+                                   int64_t N, float *Y, hipStream_t stream) {
   const int64_t NG = (N + kTileRows - 1) / kTileRows;
-  const dim3 grid((unsigned)((NG + ROWS / 16 - 1) / (ROWS / 16)),
+  const dim3 grid((unsigned)((NG + TP_ROWS / 16 - 1) / (TP_ROWS / 16)),
                   (unsigned)((M + TP_TOK - 1) / TP_TOK));
   if (grid.y > 65535) return hipErrorInvalidConfiguration;
   if (grid.y > 1)
-    hipLaunchKernelGGL((q4k_prefill_tiled_kernel<ROWS, true>), grid, dim3(64 * TP_WAVES), 0, stream,
-                       X, wt, Y, (int)M, (int)nb, (int)N);
+    hipLaunchKernelGGL(q4k_prefill_tiled_kernel<true>, grid, dim3(64 * TP_WAVES), 0, stream, X,
+                       wt, Y, (int)M, (int)nb, (int)N);
   else
-    hipLaunchKernelGGL((q4k_prefill_tiled_kernel<ROWS, false>), grid, dim3(64 * TP_WAVES), 0, stream,
-                       X, wt, Y, (int)M, (int)nb, (int)N);
+    hipLaunchKernelGGL(q4k_prefill_tiled_kernel<false>, grid, dim3(64 * TP_WAVES), 0, stream, X,
+                       wt, Y, (int)M, (int)nb, (int)N);
   return hipGetLastError();
 }
 
@@ -844,12 +832,17 @@ hipError_t prefill_tiled_launch(const float *X, const uint8_t *wt, int64_t M, in
       N > 0x7FFFFFFF || M > 0x7FFFFFFF)
     return hipErrorInvalidValue;
   if (rows == 0) rows = prefill_rows(M, N);
-  switch (rows) {
-    case 64: return prefill_tiled_launch_rows<64>(X, wt, M, nb, N, Y, stream);
-    case 32: return prefill_tiled_launch_rows<32>(X, wt, M, nb, N, Y, stream);
-    case 16: return prefill_tiled_launch_rows<16>(X, wt, M, nb, N, Y, stream);
-    default: return hipErrorInvalidValue;
-  }
+  if (rows != 64 && rows != 32 && rows != 16) return hipErrorInvalidValue;
+  // The canonical prefill kernel staging whole tiles through LDS, or this
+  // file's kernel loading each wave's tiles into registers: measured on
+  // MI355X (graph-replayed calls, register / staged us/call), staging wins
+  // at 32 and 16 rows (16 tokens: 4096x4096 10.0 / 9.1, 14336->4096 30.8 /
+  // 25.7; 32 tokens 14336->4096 36.7 / 32.6) and at 64 rows from input_dim
+  // 8192 on (8192->4096 27.0 / 26.1, 14336->4096 46.4 / 43.9), registers at
+  // 64 rows below it (4096x4096 13.7 / 14.5, 2048->8192 14.7 / 16.0).
+  if (rows < 64 || nb >= 32)
+    return prefill_staged_tiled_launch(X, wt, M, nb * 256, N, Y, stream, rows);
+  return prefill_tiled_launch_64(X, wt, M, nb, N, Y, stream);
 }
 
 }  // namespace q4k

@@ -276,11 +276,13 @@ def test_matmul_tiled_shapes(oracle_lib, M, K, N):
     assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"{M}x{K}x{N}")
 
 
-@pytest.mark.parametrize("M,K,N", [(64, 4096, 512), (17, 768, 65), (33, 1280, 130), (16, 14336, 64)])
+@pytest.mark.parametrize("M,K,N", [(64, 4096, 512), (17, 768, 65), (33, 1280, 130), (16, 14336, 64),
+                                   (40, 8448, 130), (64, 8192, 64)])
 def test_prefill_tiled_equals_canonical_prefill(M, K, N):
     """The tiled prefill does the canonical 64-row prefill's arithmetic in
     the same order (only where the weight bytes come from differs): bit for
-    bit."""
+    bit.  From input_dim 8192 on the 64-row tiles are staged through LDS
+    (33 super-blocks: a ragged last stage), below it loaded into registers."""
     w = synth.q4k_weights(N, K, config=43, copy=M)
     X = synth.activations(K, n_tokens=M, config=43, copy=M)
     wt, _ = relayout(w, K, N)
@@ -302,6 +304,17 @@ def test_prefill_tiled_every_height_equals_canonical(M, K, N, rows):
     a = matmul_tiled_form(X, wt, M, K, N, rows)
     b = matmul_canonical(X, w, M, K, N, form=rows)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,M,K,N", [(64, 20, 8448, 70), (64, 64, 16384, 33)])
+def test_prefill_tiled_staged_64_rows_parity(oracle_lib, rows, M, K, N):
+    """The 64-row tiles staged through LDS (input_dim >= 8192) against the
+    oracle: ragged rows, tokens and stages."""
+    w = synth.q4k_weights(N, K, config=54, copy=M)
+    X = synth.activations(K, n_tokens=M, config=54, copy=M)
+    wt, _ = relayout(w, K, N)
+    assert_parity(matmul_tiled_form(X, wt, M, K, N, rows), oracle_lib.q4k_matmul(X, w, M, K, N),
+                  rowwise=True, what=f"{M}x{K}x{N} rows {rows}")
 
 
 @pytest.mark.parametrize("rows", [16, 32])
