@@ -51,14 +51,16 @@ constexpr int X_PER_THREAD = TR_TOK / 2;                          // 8
 
 // The A operand from 16 bits of codes (8 fields): fields (0,2), (1,3) of the
 // low byte, then (4,6), (5,7) of the high byte, as the fp16 codes u - 1.
-__device__ __forceinline__ half8_t code_operand(uint32_t w16) {
+// hi64 = 0x64006400 held in a vector register (vgpr_const), so that each
+// mask-and-insert is one AND-OR.
+__device__ __forceinline__ half8_t code_operand(uint32_t w16, uint32_t hi64) {
   const uint32_t t0 = (w16 & 0xFFu) * 0x1001u;         // b0 | b0 << 12
   const uint32_t t1 = ((w16 >> 8) & 0xFFu) * 0x1001u;  // b1 | b1 << 12
   uint4 v;
-  v.x = (t0 & 0x00030003u) | 0x64006400u;  // fp16 1024 + u in each half
-  v.y = ((t0 >> 2) & 0x00030003u) | 0x64006400u;
-  v.z = (t1 & 0x00030003u) | 0x64006400u;
-  v.w = ((t1 >> 2) & 0x00030003u) | 0x64006400u;
+  v.x = (t0 & 0x00030003u) | hi64;  // fp16 1024 + u in each half
+  v.y = ((t0 >> 2) & 0x00030003u) | hi64;
+  v.z = (t1 & 0x00030003u) | hi64;
+  v.w = ((t1 >> 2) & 0x00030003u) | hi64;
   half8_t a = __builtin_bit_cast(half8_t, v);
   const _Float16 off = (_Float16)1025.0f;
   return a - half8_t{off, off, off, off, off, off, off, off};
@@ -90,6 +92,7 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
   // The host validates K >= 64; saying so lets the compiler fetch every
   // kernel argument in one round trip.
   __builtin_assume(K >= 64);
+  const uint32_t hi64 = vgpr_const(0x64006400u);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
       for (int a = 0; a < TPW; ++a) {
         const int row = 16 * (rt0 + a) + r;
         const uint32_t w = ct[row * CROW + 16 * bb + 2 * s + (g >> 1)] >> hsh;
-        const half8_t A = code_operand(w);
+        const half8_t A = code_operand(w, hi64);
         bh[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, bh[a], 0, 0, 0);
         bl[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, bl[a], 0, 0, 0);
       }
