@@ -16,19 +16,23 @@
 // workgroups the 64x16 tile keeps the bytes a CU pulls from L2 near their
 // minimum (64 rows of weights and 16 rows of activations per unit of
 // input_dim).  With few token tiles 64-row workgroups leave CUs idle (16
-// tokens x 4096 rows is 64 workgroups), so the launch narrows them to 32
-// or 16 rows until the grid reaches one workgroup per CU.  The token groups of a row tile are gridDim.x workgroup ids
-// apart, which puts them on the same XCD (and its L2) whenever the number
-// of row tiles is a multiple of 8.
+// tokens x 4096 rows is 64 workgroups), so the launch can narrow them to 32
+// or 16 rows (prefill_rows: the height with the fewest rounds of 256
+// workgroups times the measured per-workgroup time).  The token groups of a
+// row tile are gridDim.x workgroup ids apart, which puts them on the same
+// XCD (and its L2) whenever the number of row tiles is a multiple of 8.
 //
-// Pipeline: input_dim is walked in stages of 4 super-blocks.  All 256
+// Pipeline: input_dim is walked in stages of 4 super-blocks.  The 512
 // threads load a stage with coalesced 16-byte loads (every wave instruction
 // reads 1 KB of one activation row, or consecutive 16-byte chunks of the
-// weight rows) into registers one stage ahead, then write it to LDS: the
-// activations already split into fp16 hi + lo in MFMA operand order, the
-// weight blocks raw.  Wave w then computes super-block w of the stage:
-// decodes the 64 block headers (one row per lane), dequantizes A operands
-// from LDS and runs the MFMAs, while the next stage's loads are in flight.
+// weight rows, or of whole tiles in the tiled block order) into registers
+// one stage ahead, then write it to LDS: the activations already split into
+// fp16 hi + lo in MFMA operand order, the weight blocks raw.  Waves w and
+// w + 4 then compute super-block w of the stage (two row tiles each, or at
+// 32 and 16 rows half of its sub-blocks each): they decode their rows'
+// block headers into LDS tables, each (row, sub-block) once, dequantize A
+// operands from LDS and run the MFMAs while the next stage's loads are in
+// flight.
 //
 // MFMA layout (16x16x32 f16): lane (r = lane % 16, g = lane / 16) holds for
 // the A operand row 16a + r of row tile a, positions 8g .. 8g+7 of one

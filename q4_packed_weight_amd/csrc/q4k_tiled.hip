@@ -1,6 +1,8 @@
 // q4k_tiled.hip -- the tiled block order of a Q4_K matrix: the one-time
-// relayout from the canonical layout, and the matrix-vector product that
-// streams the tiled order.
+// relayout from the canonical layout, and the matrix-vector, few-token and
+// 64-row prefill products that stream the tiled order (narrower prefill
+// tiles, and 64-row ones from input_dim 8192 on, run q4k_prefill.hip's
+// kernel on it).
 //
 // SKaiNET docs, "Eager execution: backends and kernels": a packed weight
 // reaches a kernel by declaring its block order, and a canonical weight is
