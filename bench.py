@@ -1,7 +1,7 @@
 #!/usr/bin/env python
 """Benchmark of the fused-dequantize Q4_K GEMV on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2|c1|c3|c4|c5]
+    python bench.py [--steps K] [--warmup W] [--workload c2|c1|c3|c4|n1|c5|...]
 
 Default workload: Q4_K GEMV, input_dim 4096 x output_dim 4096, batch 1,
 fp32 activations, 64 distinct weight copies (604 MB, more than twice the
@@ -20,6 +20,8 @@ Other workloads (measurement of the sibling paths, same JSON shape):
   c3  Q4_K FFN pair: up 4096->14336 then down 14336->4096, batch 1; a step
       is the pair (9 rotating pairs)
   c4  Q4_K prefill 64 tokens x 4096 -> 4096 (64 rotating weight copies)
+  n1  Q4_K few-token product, 4 tokens x 4096 -> 4096 (64 rotating weight
+      copies; the batched matrix-core GEMV, weights read once for all tokens)
   c5  ternary GEMV 4096 x 4096, batch 1 (128 rotating copies)
   q40 Q4_0 GEMV 4096 x 4096, batch 1 (64 rotating copies; the Q4_K page's
       follow-up format, the same 9.4 MB of weights per call as c2)
@@ -63,6 +65,8 @@ PREFILL_SRC = ["q4_packed_weight_amd/csrc/q4k_prefill.hip",
 TERNARY_SRC = ["q4_packed_weight_amd/csrc/ternary_gemv.hip",
                "q4_packed_weight_amd/csrc/device_common.h"]
 TILED_SRC = ["q4_packed_weight_amd/csrc/q4k_tiled.hip",
+             "q4_packed_weight_amd/csrc/device_common.h"]
+BATCH_SRC = ["q4_packed_weight_amd/csrc/q4k_gemv_batch.hip",
              "q4_packed_weight_amd/csrc/device_common.h"]
 TERNARY_MM_SRC = ["q4_packed_weight_amd/csrc/ternary_matmul.hip",
                   "q4_packed_weight_amd/csrc/device_common.h"]
@@ -135,6 +139,31 @@ def make_workload(name, torch, binding, synth):
             xu, xd = wl.xu.cpu().numpy(), wl.xd.cpu().numpy()
             return (lambda: (oracle.q4k_gemv(xu, wu, K1, N1), oracle.q4k_gemv(xd, wd, K2, N2))), \
                 1.0, "oracle q4k_gemv up+down pair, full call"
+        wl.cpu = cpu
+    elif name == "n1":
+        # the few-token regime between the GEMV and the prefill tiles: 4
+        # tokens x 4096 -> 4096 runs the batched matrix-core GEMV, every
+        # weight byte read once for all four
+        M, K, N = 4, 4096, 4096
+        wbytes = N * K // 256 * 144
+        copies = 64
+        wl.W = [to_dev(synth.q4k_weights(N, K, config=synth.C2_Q4K_4K, copy=c)) for c in range(copies)]
+        wl.X = to_dev(synth.activations(K, n_tokens=M, config=synth.C2_Q4K_4K))
+        wl.Y = torch.empty(M, N, dtype=torch.float32, device=dev)
+        wl.call = lambda i: binding.q4k_matmul(wl.X, wl.W[i % copies], M, K, N, wl.Y)
+        wl.copies = copies
+        wl.bytes = wbytes + 4 * M * K + 4 * M * N
+        wl.flops = 2 * M * K * N
+        wl.kernel = "q4k_gemv_batch_kernel<4, false>"
+        wl.src_files = BATCH_SRC
+        wl.config = {"workload": "q4k_matmul 4 tokens x 4096 -> 4096", "tokens": M,
+                     "input_dim": K, "output_dim": N, "rotating_copies": copies}
+        wl.metric = "Q4_K few-token matmul us/call + achieved HBM GB/s (% peak), 4x4096x4096"
+
+        def cpu(oracle):
+            w0, X0 = wl.W[0].cpu().numpy(), wl.X.cpu().numpy()
+            return (lambda: oracle.q4k_matmul_part(X0, w0, M, K, N, (0, 1), (0, N))), M / 1, \
+                "oracle q4k_matmul on 1 of 4 token rows, scaled x4 to a call"
         wl.cpu = cpu
     elif name == "c4":
         M, K, N = 64, 4096, 4096
@@ -437,6 +466,7 @@ def cpu_baseline(wl, seconds):
 TRAFFIC_FILES = {"c2": "q4k_gemv_4096x4096_b1.traffic.json",
                  "c3": "q4k_gemv_ffn_4096x14336_pair.traffic.json",
                  "c4": "q4k_prefill_64x4096x4096.traffic.json",
+                 "n1": "q4k_matmul_4x4096x4096.traffic.json",
                  "c5": "ternary_gemv_4096x4096_b1.traffic.json",
                  "q40": "q4_0_gemv_4096x4096_b1.traffic.json",
                  "q6k": "q6k_gemv_4096x4096_b1.traffic.json",
@@ -465,7 +495,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64000)
     ap.add_argument("--warmup", type=int, default=6400)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "q40", "q6k", "t64", "c2t", "c3t", "copy"])
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "n1", "c5", "q40", "q6k", "t64", "c2t", "c3t", "copy"])
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
