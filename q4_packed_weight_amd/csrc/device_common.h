@@ -26,6 +26,22 @@ __device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1) {
   return r;
 }
 
+// A three-operand AND-OR takes at most one scalar operand and no literal on
+// this target, so the 0x64 bytes come from a register the caller holds
+// (`hi64` = 0x64006400, made by vgpr_const).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  uint32_t v = c;
+  asm volatile("" : "+v"(v));
+  return v;
+}
+// The same without volatile, for helpers called many times: the compiler
+// may then share one register among all the uses of a constant.
+__device__ __forceinline__ uint32_t vgpr_const_shared(uint32_t c) {
+  uint32_t v = c;
+  asm("" : "+v"(v));
+  return v;
+}
+
 // Two codes of a qs dword as exact *normal* fp16 MFMA operands: with mask
 // 0x000F000F the low nibbles of bytes 0 and 2 as q, with 0x00F000F0 their
 // high nibbles, kept in place, as 16 q (shift the dword right by 8 first for
@@ -35,7 +51,7 @@ __device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1) {
 // MFMA measured a biased loss of up to 4e-6 of a dot whose products span a
 // wide range, against about one fp32 ulp with normal codes.
 __device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t mask) {
-  const half2_t v = as_h2((w & mask) | 0x64006400u);
+  const half2_t v = as_h2((w & mask) | vgpr_const_shared(0x64006400u));
   return as_u32h(v - half2_t{(_Float16)1024.0f, (_Float16)1024.0f});
 }
 
@@ -63,15 +79,6 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t sc, bool odd) {
   const half2_t k = odd ? half2_t{(_Float16)0.0625f, (_Float16)-64.0f}
                         : half2_t{(_Float16)1.0f, (_Float16)-1024.0f};
   return as_u32h(half2_t{f, f} * k);
-}
-
-// A three-operand AND-OR takes at most one scalar operand and no literal on
-// this target, so the 0x64 bytes come from a register the caller holds
-// (`hi64` = 0x64006400, made by vgpr_const).
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
-  uint32_t v = c;
-  asm volatile("" : "+v"(v));
-  return v;
 }
 
 // One MFMA A operand (8 codes of one sub-block) from two qs dwords: their
