@@ -153,41 +153,35 @@ __device__ __forceinline__ float4 load_buf_f4(__amdgpu_buffer_rsrc_t r, int off,
 
 __device__ __forceinline__ float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
 
-// Maximum over aligned groups of `width` lanes (width 2, 4 or 8): DPP quad
-// permutes and the half-row mirror; every lane of the group receives it.
-template <int width>
-__device__ __forceinline__ float group_max(float v) {
-  static_assert(width == 2 || width == 4 || width == 8, "group_max covers 2, 4 or 8 lanes");
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-      __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true)));  // quad_perm [1,0,3,2]
-  if constexpr (width >= 4)
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-        __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true)));  // quad_perm [2,3,0,1]
-  if constexpr (width >= 8)
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-        __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)));  // row_half_mirror
-  return v;
+// Maximum of non-negative values (NaN included) over aligned groups of
+// `width` lanes, every lane of the group receiving it: the maximum of the bit
+// patterns as unsigned integers is the float maximum, and an integer
+// maximum takes its DPP operand directly (one v_max_u32_dpp per step, where
+// the float maximum needs a move and two NaN-quieting maxima besides).
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp_step(uint32_t b) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, CTRL, 0xF, 0xF, true);
+  return b > o ? b : o;
 }
-
-// Maximum over the 64 lanes of a wave (every lane receives it).
-__device__ __forceinline__ float wave_max(float v) {
-  v = group_max<8>(v);
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-      __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)));  // row_mirror
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+template <int width>
+__device__ __forceinline__ float group_max_nonneg(float v) {
+  static_assert(width == 2 || width == 4 || width == 8 || width == 16,
+                "group_max_nonneg covers 2, 4, 8 or 16 lanes");
+  uint32_t b = __builtin_bit_cast(uint32_t, v);
+  b = max_dpp_step<0xB1>(b);                             // quad_perm [1,0,3,2]
+  if constexpr (width >= 4) b = max_dpp_step<0x4E>(b);   // quad_perm [2,3,0,1]
+  if constexpr (width >= 8) b = max_dpp_step<0x141>(b);  // row_half_mirror
+  if constexpr (width >= 16) b = max_dpp_step<0x140>(b); // row_mirror
+  return __builtin_bit_cast(float, b);
 }
 
 // Maximum of a non-negative value over the 64 lanes of a wave, as a
 // wave-uniform value: DPP within each row of 16 lanes, then the four row
 // results through scalar registers (for non-negative floats, NaN included,
-// the integer order of the bit patterns is the float order).  No LDS
-// round trip, unlike wave_max.
+// the integer order of the bit patterns is the float order); no LDS round
+// trip.
 __device__ __forceinline__ float wave_max_nonneg(float v) {
-  v = group_max<8>(v);
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-      __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)));  // row_mirror
+  v = group_max_nonneg<16>(v);
   const int b = __builtin_bit_cast(int, v);
   const uint32_t m0 = (uint32_t)__builtin_amdgcn_readlane(b, 0);
   const uint32_t m1 = (uint32_t)__builtin_amdgcn_readlane(b, 16);

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_kernel(
   // |x| * 2^-e < 2^15, split into fp16 hi + lo, store its sum and e.
   auto stage4 = [&](float4 v0, int f) {
     float mx = fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w)));
-    mx = group_max<8>(mx);
+    mx = group_max_nonneg<8>(mx);
     const int e = __builtin_amdgcn_frexp_expf(mx) - 15;
     const float4 v = make_float4(__builtin_ldexpf(v0.x, -e), __builtin_ldexpf(v0.y, -e),
                                  __builtin_ldexpf(v0.z, -e), __builtin_ldexpf(v0.w, -e));
