@@ -92,7 +92,8 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
  *   Y          fp32 [n_tokens, output_dim]
  * Same error behaviour and tolerance as q4k_gemv.  Three kernels serve it:
  * M == 1 is q4k_gemv; a few tokens (M <= 2 at any shape, M <= 4 with
- * output_dim <= 4096) run on a batched matrix-core GEMV that reads each weight once for all of
+ * output_dim <= 4096, M <= 8 with output_dim <= 4096 and input_dim > 12288)
+ * run on a batched matrix-core GEMV that reads each weight once for all of
  * them; larger batches run on the prefill tiles (64 rows x 16 tokens,
  * narrowed to 32 or 16 rows when 64-row tiles would leave CUs idle).  The batched and
  * prefill kernels pass the activations through fp16 (split into a high and

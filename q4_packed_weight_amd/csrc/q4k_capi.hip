@@ -147,13 +147,13 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
 // Few tokens run on the batched matrix-core GEMV, one launch of up to 8
 // tokens, where it beats the prefill tiles (at the height prefill_rows
 // picks).  Measured on MI355X (graph-replayed calls over rotating weights,
-// batched / prefill us/call): 4096x4096 with 4 tokens 7.8 / 8.7 and with 5
-// to 8 tokens 10.0-10.1 / 8.7; 14336->4096 with 4 tokens 18.8 / 24.8 and
-// with 5 to 8 tokens 25.8-26.3 / 24.9 (11008->4096: 21.7-22.2 / 20.0);
-// 4096->8192 with 3 tokens 13.8 / 10.8; 2 tokens win everywhere (4096 ->
-// 14336: 14.6 / 16.8).
+// batched / prefill us/call): 4096x4096 with 4 tokens 7.1 / 8.7 and with 5
+// to 8 tokens 9.1-9.2 / 8.7; 14336->4096 with 4 tokens 17.5 / 24.8 and
+// with 5 to 8 tokens 23.2-23.4 / 24.9, while 11008->4096 ties (19.9-20.1 /
+// 19.9-20.0); 4096->8192 with 3 tokens 12.6 / 10.7; 2 tokens win everywhere
+// (4096 -> 14336: 14.6 / 16.8).
 static bool use_gemv_batch(int64_t M, int64_t K, int64_t N) {
-  return M <= 2 || (M <= 4 && N <= 4096);
+  return M <= 2 || (M <= 4 && N <= 4096) || (M <= 8 && N <= 4096 && K > 12288);
 }
 
 // Valid explicit forms of the batched products: 1 = the few-token GEMV
