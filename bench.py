@@ -76,6 +76,16 @@ class Workload:
     """Inputs resident on the GPU plus a `call(i)` that runs step i."""
 
 
+MFMA_DTYPE = "f32 (x as exact fp16 hi+lo MFMA operands, fp32 accumulation)"
+
+
+def row_slices(n_rows, n_chunks=64):
+    """Contiguous output-row ranges covering [0, n_rows): the CPU oracle's
+    work split for the multi-threaded baseline (rows are independent)."""
+    b = [n_rows * i // n_chunks for i in range(n_chunks + 1)]
+    return [(o0, o1) for o0, o1 in zip(b, b[1:]) if o1 > o0]
+
+
 def make_workload(name, torch, binding, synth):
     import numpy as np
     dev = "cuda:0"
@@ -105,10 +115,14 @@ def make_workload(name, torch, binding, synth):
                      "weight_bytes_per_copy": wbytes}
         wl.metric = f"Q4_K GEMV us/call + achieved HBM GB/s (% peak) at {K}x{N}, batch 1"
 
+        wl.dtype = MFMA_DTYPE if name == "c2" else "f32"
+
         def cpu(oracle):
-            w0 = wl.W[0].cpu().numpy()
+            w0 = wl.W[0].cpu().numpy().reshape(-1)
             x0 = wl.x.cpu().numpy()
-            return (lambda: oracle.q4k_gemv(x0, w0, K, N)), 1.0, f"oracle q4k_gemv {K}x{N}, full call"
+            rb = K // 256 * 144
+            return [lambda a=a, b=b: oracle.q4k_gemv(x0, w0[a * rb:b * rb], K, b - a)
+                    for a, b in row_slices(N)], 1.0, f"oracle q4k_gemv {K}x{N}, full call"
         wl.cpu = cpu
     elif name == "c3":
         K1, N1, K2, N2 = 4096, 14336, 14336, 4096
@@ -135,10 +149,13 @@ def make_workload(name, torch, binding, synth):
         wl.metric = "Q4_K FFN GEMV pair us/pair + achieved HBM GB/s (% peak), batch 1"
 
         def cpu(oracle):
-            wu, wd = wl.Wu[0].cpu().numpy(), wl.Wd[0].cpu().numpy()
+            wu, wd = wl.Wu[0].cpu().numpy().reshape(-1), wl.Wd[0].cpu().numpy().reshape(-1)
             xu, xd = wl.xu.cpu().numpy(), wl.xd.cpu().numpy()
-            return (lambda: (oracle.q4k_gemv(xu, wu, K1, N1), oracle.q4k_gemv(xd, wd, K2, N2))), \
-                1.0, "oracle q4k_gemv up+down pair, full call"
+            ru, rd = K1 // 256 * 144, K2 // 256 * 144
+            return ([lambda a=a, b=b: oracle.q4k_gemv(xu, wu[a * ru:b * ru], K1, b - a)
+                     for a, b in row_slices(N1)] +
+                    [lambda a=a, b=b: oracle.q4k_gemv(xd, wd[a * rd:b * rd], K2, b - a)
+                     for a, b in row_slices(N2)]), 1.0, "oracle q4k_gemv up+down pair, full call"
         wl.cpu = cpu
     elif name == "n1":
         # the few-token regime between the GEMV and the prefill tiles: 4
@@ -160,9 +177,13 @@ def make_workload(name, torch, binding, synth):
                      "input_dim": K, "output_dim": N, "rotating_copies": copies}
         wl.metric = "Q4_K few-token matmul us/call + achieved HBM GB/s (% peak), 4x4096x4096"
 
+        wl.dtype = MFMA_DTYPE
+
         def cpu(oracle):
-            w0, X0 = wl.W[0].cpu().numpy(), wl.X.cpu().numpy()
-            return (lambda: oracle.q4k_matmul_part(X0, w0, M, K, N, (0, 1), (0, N))), M / 1, \
+            w0, X0 = wl.W[0].cpu().numpy().reshape(-1), wl.X.cpu().numpy()
+            rb = K // 256 * 144
+            return [lambda a=a, b=b: oracle.q4k_matmul(X0[:1], w0[a * rb:b * rb], 1, K, b - a)
+                    for a, b in row_slices(N)], M / 1, \
                 "oracle q4k_matmul on 1 of 4 token rows, scaled x4 to a call"
         wl.cpu = cpu
     elif name == "c4":
@@ -172,7 +193,9 @@ def make_workload(name, torch, binding, synth):
         wl.W = [to_dev(synth.q4k_weights(N, K, config=synth.C4_PREFILL, copy=c)) for c in range(copies)]
         wl.X = to_dev(synth.activations(K, n_tokens=M, config=synth.C4_PREFILL))
         wl.Y = torch.empty(M, N, dtype=torch.float32, device=dev)
-        wl.call = lambda i: binding.q4k_matmul(wl.X, wl.W[i % copies], M, K, N, wl.Y)
+        form = PREFILL_FORM
+        wl.call = (lambda i: binding.q4k_matmul(wl.X, wl.W[i % copies], M, K, N, wl.Y)) if form == 0 \
+            else (lambda i: binding.q4k_matmul_shaped(wl.X, wl.W[i % copies], M, K, N, wl.Y, form))
         wl.copies = copies
         wl.bytes = wbytes + 4 * M * K + 4 * M * N
         wl.flops = 2 * M * K * N
@@ -180,11 +203,17 @@ def make_workload(name, torch, binding, synth):
         wl.src_files = PREFILL_SRC
         wl.config = {"workload": "q4k_matmul prefill 64 tokens x 4096 -> 4096",
                      "tokens": M, "input_dim": K, "output_dim": N, "rotating_copies": copies}
+        if form:
+            wl.config["form"] = form
         wl.metric = "Q4_K prefill matmul us/call + achieved TFLOP/s (% fp16 MFMA peak), 64x4096x4096"
 
+        wl.dtype = MFMA_DTYPE
+
         def cpu(oracle):
-            w0, X0 = wl.W[0].cpu().numpy(), wl.X.cpu().numpy()
-            return (lambda: oracle.q4k_matmul_part(X0, w0, M, K, N, (0, 2), (0, N))), M / 2, \
+            w0, X0 = wl.W[0].cpu().numpy().reshape(-1), wl.X.cpu().numpy()
+            rb = K // 256 * 144
+            return [lambda a=a, b=b: oracle.q4k_matmul(X0[:2], w0[a * rb:b * rb], 2, K, b - a)
+                    for a, b in row_slices(N)], M / 2, \
                 "oracle q4k_matmul on 2 of 64 token rows, scaled x32 to a call"
         wl.cpu = cpu
     elif name == "c5":
@@ -207,9 +236,10 @@ def make_workload(name, torch, binding, synth):
         wl.metric = "Ternary GEMV us/call + achieved HBM GB/s (% peak) at 4096x4096, batch 1"
 
         def cpu(oracle):
-            c0, x0 = wl.C[0].cpu().numpy(), wl.x.cpu().numpy()
-            return (lambda: oracle.ternary_gemv(x0, c0, wl.scale, K, N)), 1.0, \
-                "oracle ternary_gemv 4096x4096, full call"
+            c0, x0 = wl.C[0].cpu().numpy().reshape(-1), wl.x.cpu().numpy()
+            rb = K // 4
+            return [lambda a=a, b=b: oracle.ternary_gemv(x0, c0[a * rb:b * rb], wl.scale, K, b - a)
+                    for a, b in row_slices(N)], 1.0, "oracle ternary_gemv 4096x4096, full call"
         wl.cpu = cpu
     elif name == "q40":
         K = N = 4096
@@ -231,9 +261,11 @@ def make_workload(name, torch, binding, synth):
         wl.metric = f"Q4_0 GEMV us/call + achieved HBM GB/s (% peak) at {K}x{N}, batch 1"
 
         def cpu(oracle):
-            w0 = wl.W[0].cpu().numpy()
+            w0 = wl.W[0].cpu().numpy().reshape(-1)
             x0 = wl.x.cpu().numpy()
-            return (lambda: oracle.q4_0_gemv(x0, w0, K, N)), 1.0, f"oracle q4_0_gemv {K}x{N}, full call"
+            rb = K // 32 * 18
+            return [lambda a=a, b=b: oracle.q4_0_gemv(x0, w0[a * rb:b * rb], K, b - a)
+                    for a, b in row_slices(N)], 1.0, f"oracle q4_0_gemv {K}x{N}, full call"
         wl.cpu = cpu
     elif name == "q6k":
         K = N = 4096
@@ -255,9 +287,11 @@ def make_workload(name, torch, binding, synth):
         wl.metric = f"Q6_K GEMV us/call + achieved HBM GB/s (% peak) at {K}x{N}, batch 1"
 
         def cpu(oracle):
-            w0 = wl.W[0].cpu().numpy()
+            w0 = wl.W[0].cpu().numpy().reshape(-1)
             x0 = wl.x.cpu().numpy()
-            return (lambda: oracle.q6k_gemv(x0, w0, K, N)), 1.0, f"oracle q6k_gemv {K}x{N}, full call"
+            rb = K // 256 * 210
+            return [lambda a=a, b=b: oracle.q6k_gemv(x0, w0[a * rb:b * rb], K, b - a)
+                    for a, b in row_slices(N)], 1.0, f"oracle q6k_gemv {K}x{N}, full call"
         wl.cpu = cpu
     elif name == "t64":
         M, K, N = 64, 4096, 4096
@@ -278,9 +312,14 @@ def make_workload(name, torch, binding, synth):
                      "tokens": M, "input_dim": K, "output_dim": N, "rotating_copies": copies}
         wl.metric = "Ternary prefill matmul us/call + achieved TFLOP/s (% fp16 MFMA peak), 64x4096x4096"
 
+        wl.dtype = MFMA_DTYPE
+
         def cpu(oracle):
-            c0, X0 = wl.C[0].cpu().numpy(), wl.X.cpu().numpy()
-            return (lambda: oracle.ternary_matmul(X0[:2], c0, wl.scale, 2, K, N)), M / 2, \
+            c0, X0 = wl.C[0].cpu().numpy().reshape(-1), wl.X.cpu().numpy()
+            rb = K // 4
+            return [lambda a=a, b=b: oracle.ternary_matmul(X0[:2], c0[a * rb:b * rb], wl.scale,
+                                                           2, K, b - a)
+                    for a, b in row_slices(N)], M / 2, \
                 "oracle ternary_matmul on 2 of 64 token rows, scaled x32 to a call"
         wl.cpu = cpu
     elif name in ("c2t", "c3t"):
@@ -334,12 +373,19 @@ def make_workload(name, torch, binding, synth):
             wl.metric = "Q4_K FFN GEMV pair (tiled block order) us/pair + achieved HBM GB/s (% peak), batch 1"
         wl.data = "synthetic (seeded numpy generators; random Q4_K blocks relayouted into the tiled order, N(0,1) activations)"
 
+        wl.dtype = MFMA_DTYPE
+
         def cpu(oracle):
             # the oracle multiplies the canonical matrices (the same weights)
-            ws = [synth.q4k_weights(N, K, config=cfg, copy=0, extra=extra) for K, N, cfg, extra in mats]
+            ws = [synth.q4k_weights(N, K, config=cfg, copy=0, extra=extra).reshape(-1)
+                  for K, N, cfg, extra in mats]
             xs = [x.cpu().numpy() for x in wl.xs]
-            return (lambda: [oracle.q4k_gemv(xs[m], ws[m], K, N) for m, (K, N, _, _) in enumerate(mats)]), \
-                1.0, "oracle q4k_gemv on the canonical matrices, full call"
+            jobs = []
+            for m, (K, N, _, _) in enumerate(mats):
+                rb = K // 256 * 144
+                jobs += [lambda m=m, K=K, rb=rb, a=a, b=b: oracle.q4k_gemv(xs[m], ws[m][a * rb:b * rb], K, b - a)
+                         for a, b in row_slices(N)]
+            return jobs, 1.0, "oracle q4k_gemv on the canonical matrices, full call"
         wl.cpu = cpu
     elif name == "copy":
         nbytes = 64 * 2 ** 20
@@ -376,13 +422,25 @@ def capture(torch, wl, start, count):
     return g
 
 
-def time_steps(torch, wl, steps, launch, graphs):
+DELAY_NS = 1_000_000
+PREFILL_FORM = 0  # c4: 0 = q4k_matmul's own choice, else the q4k_matmul_shaped form
+
+
+def time_steps(torch, binding, wl, steps, launch, graphs):
     """Mean ms per step over exactly `steps` steps, HIP events on the stream
-    the kernels run on."""
+    the kernels run on, and the host's submission time of those steps.
+
+    After the synchronization a 1 ms delay kernel is enqueued ahead of the
+    start event: while it runs, the host submits the timed graph replays, so
+    the events time the device's execution of exactly the `steps` calls and
+    not the host's graph-submission latency (which otherwise counts once per
+    replay and dominates short runs)."""
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    binding.bench_delay(DELAY_NS)
     start.record(stream)
+    t0 = time.perf_counter()
     if launch == "eager":
         for i in range(steps):
             wl.call(i)
@@ -393,9 +451,10 @@ def time_steps(torch, wl, steps, launch, graphs):
             full.replay()
         if rem is not None:
             rem.replay()
+    host_s = time.perf_counter() - t0
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    return start.elapsed_time(end) / steps, host_s
 
 
 def context_measurements(torch, binding, wl, launch_graph_len):
@@ -443,24 +502,73 @@ def context_measurements(torch, binding, wl, launch_graph_len):
         nbytes = bufs[0].numel()
         out["stream_read_same_bytes_us"] = round(us, 3)
         out["stream_read_GBps"] = round(nbytes / us / 1e3, 1)
+        # the runtime's own device-to-device copy of each rotating buffer
+        # (graph memcpy nodes): reads the same bytes and writes them once
+        dst = torch.empty_like(bufs[0])
+        g3 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s), torch.cuda.graph(g3, stream=s):
+            for b in bufs:
+                dst.copy_(b)
+        torch.cuda.current_stream().wait_stream(s)
+        for _ in range(3):
+            g3.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g3.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000 / (reps * len(bufs))
+        out["memcpy_d2d_same_bytes_us"] = round(us, 3)
+        out["memcpy_d2d_GBps_read_plus_write"] = round(2 * nbytes / us / 1e3, 1)
     return out
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, seconds):
+    """The oracle (plain scalar C, untouched) timed on the host: one thread,
+    then all threads of the host's share (at most 16) each taking whole
+    output-row ranges.  The oracle releases the interpreter lock inside its
+    C calls, so the row ranges run in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
-    fn, scale, sample = wl.cpu(oracle)
-    fn()  # warm caches / page in
-    times = []
-    t_end = time.perf_counter() + seconds
-    while time.perf_counter() < t_end or len(times) < 3:
-        t0 = time.perf_counter()
-        fn()
-        times.append(time.perf_counter() - t0)
-    times.sort()
-    med = times[len(times) // 2] * scale
-    return {"value": round(med * 1e6, 1), "unit": "us/call", "cores": 1, "kind": "oracle",
-            "sample": f"{sample}; median of {len(times)} calls, single thread, "
-                      f"{os.cpu_count()} host cpus visible"}
+    jobs, scale, sample = wl.cpu(oracle)
+
+    def timed(fn, budget):
+        fn()  # warm caches / page in
+        times = []
+        t_end = time.perf_counter() + budget
+        while time.perf_counter() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        times.sort()
+        return times[len(times) // 2] * scale, len(times)
+
+    def serial():
+        for j in jobs:
+            j()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(threads) as pool:
+        def parallel():
+            list(pool.map(lambda j: j(), jobs))
+        t1, n1 = timed(serial, seconds / 2)
+        tn, nn = timed(parallel, seconds / 2)
+    return {"value": round(tn * 1e6, 1), "unit": "us/call", "cores": threads, "kind": "oracle",
+            "sample": f"{sample}; output rows split into {len(jobs)} ranges over {threads} "
+                      f"threads, median of {nn} calls (1 thread: median of {n1} calls)",
+            "value_1_thread": round(t1 * 1e6, 1), "cpu_model": cpu_model(),
+            "host_cpus_visible": os.cpu_count()}
 
 
 TRAFFIC_FILES = {"c2": "q4k_gemv_4096x4096_b1.traffic.json",
@@ -490,6 +598,21 @@ def traffic_for(wl):
     return t.get("traffic_bytes_per_launch")
 
 
+def trace_for(wl):
+    """Average kernel-trace duration (us per step, rocprofv3 --kernel-trace)
+    from the committed profile summary, if it was taken on the current
+    kernel source; else None."""
+    name = TRAFFIC_FILES.get(wl.name)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_hash(wl.src_files) or "trace_avg_ns_per_step" not in t:
+        return None
+    return round(t["trace_avg_ns_per_step"] / 1000.0, 3)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -500,7 +623,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
+    ap.add_argument("--prefill-form", type=int, default=0,
+                    help="c4 only: force a q4k_matmul_shaped form (0 = q4k_matmul)")
     args = ap.parse_args()
+    global PREFILL_FORM
+    PREFILL_FORM = args.prefill_form
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -530,7 +657,7 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done, timing {steps} steps", file=sys.stderr, flush=True)
 
-    ms = time_steps(torch, wl, steps, args.launch, graphs)
+    ms, host_s = time_steps(torch, binding, wl, steps, args.launch, graphs)
     us = ms * 1000.0
     torch.cuda.synchronize()
     print(f"[bench] {us:.3f} us/step", file=sys.stderr, flush=True)
@@ -557,7 +684,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": getattr(wl, "dtype", "f32"),
         "data": getattr(wl, "data", "synthetic (seeded numpy generators; random Q4_K blocks, "
                                        "N(0,1) activations)"),
         "config": dict(wl.config, launch="hipGraph replay, one node per call"
@@ -570,7 +697,11 @@ def main():
         "kernel_source_hash": kernel_hash(wl.src_files),
     }
     if not args.no_context:
-        line["context"] = context_measurements(torch, binding, wl, min(wl.copies, 256))
+        ctx = context_measurements(torch, binding, wl, min(wl.copies, 256))
+        ctx["host_submit_ms_of_timed_steps"] = round(host_s * 1000, 3)
+        ctx["delay_before_timed_region_ms"] = DELAY_NS / 1e6
+        ctx["kernel_trace_avg_us_per_step"] = trace_for(wl)
+        line["context"] = ctx
     if not args.no_cpu_baseline and wl.cpu is not None:
         print(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

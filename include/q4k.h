@@ -96,10 +96,10 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
  * run on a batched matrix-core GEMV that reads each weight once for all of
  * them; larger batches run on the prefill tiles (64 rows x 16 tokens,
  * narrowed to 32 or 16 rows when 64-row tiles would leave CUs idle).  The batched and
- * prefill kernels pass the activations through fp16 (split into a high and
- * a low half, both exact MFMA operands); the batched one first scales each
- * token's super-block by a power of two (any |x| < 2^96), the prefill one
- * requires |x| < 65504.  Y must not alias X or the weights.
+ * prefill kernels pass the activations through fp16: each token's 256
+ * activations of a super-block are scaled by a power of two, then split
+ * into a high and a low half, both exact MFMA operands (any |x| < 2^96).
+ * Y must not alias X or the weights.
  */
 int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
                int64_t input_dim, int64_t output_dim, float *Y, void *stream);
@@ -238,6 +238,11 @@ int ternary_gemv(const float *x, const uint8_t *codes, float scale,
  * exact fp16 hi and lo halves (any |X| < 2^96); the sum is fp32 (tolerance as q4k_gemv;
  * exact for integer X with sum_i |X[r,i]| * 3 < 2^22).  Otherwise it runs
  * one ternary_gemv launch per token row.  Y must not alias X or the codes.
+ * Error behaviour as for the other calls, with one exception: on the row
+ * loop every launch has the same dimensions, so anything the library
+ * rejects is rejected before the first row, but a failure that the HIP
+ * runtime reports part-way through the loop (Q4K_EHIP) can leave the
+ * earlier token rows of Y written.
  */
 int ternary_matmul(const float *X, const uint8_t *codes, float scale, int64_t n_tokens,
                    int64_t input_dim, int64_t output_dim, float *Y, void *stream);
@@ -341,7 +346,7 @@ int q4k_gemv_tiled(const float *x, const uint8_t *w_tiled, int64_t input_dim,
  * for it: a few tokens (M <= 4, or M <= 8 with output_dim <= 4096 and
  * input_dim >= 4096) on the batched matrix-core GEMV
  * (any |X| < 2^96), more on the prefill tiles of q4k_matmul (64, 32 or 16
- * rows x 16 tokens, |X| < 65504), which give q4k_matmul's bits: 64-row tiles
+ * rows x 16 tokens, any |X| < 2^96), which give q4k_matmul's bits: 64-row tiles
  * with input_dim below 8192 load each wave's tiles straight into registers,
  * the rest stage whole tiles through LDS.  Errors and tolerance as for
  * q4k_matmul.
@@ -365,7 +370,10 @@ int q4k_gemv_tiled_shaped(const float *x, const uint8_t *w_tiled, int64_t input_
  * q4k_matmul_shaped -- q4k_matmul with its kernel forced, for sweeps and
  * tests: form 1 runs the few-token matrix-core GEMV (n_tokens <= 8, any
  * |X| < 2^96); form 16, 32 or 64 runs the prefill tiles with that many
- * weight rows per workgroup (x 16 tokens, |X| < 65504) at any token count;
+ * weight rows per workgroup (x 16 tokens, any |X| < 2^96) at any token count;
+ * form 65 runs 64-row x 16-token tiles whose waves each own whole
+ * super-blocks of all 64 rows, with the activations loaded straight into
+ * matrix-core operand registers (same arithmetic and range);
  * 0 is q4k_matmul itself.  Any other value (or form 1 with more than 8
  * tokens) gives Q4K_EINVAL_DIM.  Results are within the q4k_matmul
  * tolerance for every form.
@@ -377,7 +385,8 @@ int q4k_matmul_shaped(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
 /*
  * q4k_matmul_tiled_shaped -- q4k_matmul_tiled with its kernel forced: form
  * as for q4k_matmul_shaped (1 = the few-token GEMV, 16 / 32 / 64 = the
- * prefill tiles, 0 = q4k_matmul_tiled itself).
+ * prefill tiles, 0 = q4k_matmul_tiled itself; form 65 is canonical-only and
+ * gives Q4K_EINVAL_DIM here).
  */
 int q4k_matmul_tiled_shaped(const float *X, const uint8_t *w_tiled, int64_t n_tokens,
                             int64_t input_dim, int64_t output_dim, float *Y, void *stream,

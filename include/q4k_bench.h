@@ -17,6 +17,13 @@ extern "C" {
 /* One empty kernel of one wave: the launch/dispatch floor. */
 int q4k_bench_empty(void *stream);
 
+/* One wave that waits about ns nanoseconds (at most 0.1 s) on the GPU's
+ * real-time counter, then ends.  Enqueued just before a timed region, it
+ * keeps the GPU busy while the host submits the timed work, so the region
+ * measures the device's steady rate rather than the host's submission
+ * latency. */
+int q4k_bench_delay(int64_t ns, void *stream);
+
 /* Streaming read of nbytes (a multiple of 16, src 16-byte aligned) with
  * non-temporal 16-byte loads, grid-stride over at most sink_words
  * workgroups; each workgroup writes one uint32 to sink so the reads stay

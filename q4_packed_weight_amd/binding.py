@@ -25,7 +25,7 @@ EXPORTED = (
     "q4k_tiled_size", "q4k_relayout_tiled", "q4k_gemv_tiled", "q4k_gemv_tiled_shaped",
     "q4k_matmul_tiled", "q4k_matmul_shaped", "q4k_matmul_tiled_shaped", "ternary_matmul_shaped",
     "q4k_strerror",
-    "q4k_bench_empty", "q4k_bench_stream_read", "q4k_bench_copy",
+    "q4k_bench_empty", "q4k_bench_delay", "q4k_bench_stream_read", "q4k_bench_copy",
 )
 
 _lib = None
@@ -69,6 +69,7 @@ def lib():
         "q4k_matmul_shaped": [P, P, I64, I64, I64, P, P, I],
         "q4k_matmul_tiled_shaped": [P, P, I64, I64, I64, P, P, I],
         "q4k_bench_empty": [P],
+        "q4k_bench_delay": [I64, P],
         "q4k_bench_stream_read": [P, I64, P, I64, P],
         "q4k_bench_copy": [P, P, I64, P],
     }
@@ -334,6 +335,10 @@ def ternary_matmul_shaped(X, codes, scale, n_tokens, input_dim, output_dim, Y, f
 
 def bench_empty(stream=None):
     _check(lib().q4k_bench_empty(_stream(stream)), "q4k_bench_empty")
+
+
+def bench_delay(ns, stream=None):
+    _check(lib().q4k_bench_delay(int(ns), _stream(stream)), "q4k_bench_delay")
 
 
 def bench_stream_read(src, sink, stream=None):

@@ -13,6 +13,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ void empty_kernel() {}
 
+// One wave that waits until `ticks` periods of the constant-rate real-time
+// counter have passed.  The wait is bounded by an iteration count as well,
+// so the kernel ends even if the counter were not advancing.
+__global__ void delay_kernel(uint64_t ticks) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (uint32_t i = 0; i < (1u << 22); ++i) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 >= ticks) break;
+    __builtin_amdgcn_s_sleep(4);
+  }
+}
+
 // Reads n16 16-byte words with grid-stride non-temporal loads and writes one
 // word per workgroup so the reads cannot be elided.
 __global__ __launch_bounds__(256) void stream_read_kernel(
@@ -47,6 +58,14 @@ extern "C" {
 
 int q4k_bench_empty(void *stream) {
   hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int q4k_bench_delay(int64_t ns, void *stream) {
+  if (ns < 0 || ns > 100000000) return -1;
+  // the real-time counter runs at 100 MHz on this part: 10 ns per tick
+  hipLaunchKernelGGL(delay_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (uint64_t)(ns / 10));
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

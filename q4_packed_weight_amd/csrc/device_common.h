@@ -15,15 +15,40 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));  // one 16x16 MFMA D 
 __device__ __forceinline__ uint32_t as_u32h(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
+// The register holding c, as a value the compiler cannot see through: an
+// fma by it is not folded into a plain add (which would lose the single
+// v_fma_mix rounding below).
+__device__ __forceinline__ float opaque_f32(float c) {
+  float v = c;
+  asm("" : "+v"(v));
+  return v;
+}
+
+// hi = fp16(x * s) and lo = fp16(x * s - hi) for two values, s a power of
+// two: each half is one v_fma_mix that evaluates the product (and the
+// difference) exactly in fp32 and rounds once to fp16, so hi + lo carries
+// x * s to 22 significant bits and both are exact MFMA inputs.  Written in
+// C (no inline assembly) so that the compiler sees these register writes
+// and keeps its matrix-core hazard waits around them.
+__device__ __forceinline__ void split_pair(float x0, float x1, float s, uint32_t &hi,
+                                           uint32_t &lo) {
+  const _Float16 h0 = (_Float16)__builtin_fmaf(x0, s, 0.0f);
+  const _Float16 h1 = (_Float16)__builtin_fmaf(x1, s, 0.0f);
+  const _Float16 l0 = (_Float16)__builtin_fmaf(x0, s, -(float)h0);
+  const _Float16 l1 = (_Float16)__builtin_fmaf(x1, s, -(float)h1);
+  hi = __builtin_bit_cast(uint32_t, half2_t{h0, h1});
+  lo = __builtin_bit_cast(uint32_t, half2_t{l0, l1});
+}
+
 // lo = fp16(x - hi) for the two halves of `hi2` (fp16 hi parts of x0, x1):
-// v_fma_mix evaluates x - hi exactly in fp32 and rounds once to fp16, so
-// hi + lo carries x to 22 significant bits and both are exact MFMA inputs.
+// one v_fma_mix each (x * 1 - hi, exact in fp32, rounded once), so hi + lo
+// carries x to 22 significant bits and both are exact MFMA inputs.
 __device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1) {
-  uint32_t r;
-  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi2), "v"(x0));
-  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-      : "+v"(r) : "v"(hi2), "v"(x1));
-  return r;
+  const half2_t h = as_h2(hi2);
+  const float one = opaque_f32(1.0f);
+  const _Float16 l0 = (_Float16)__builtin_fmaf(x0, one, -(float)h.x);
+  const _Float16 l1 = (_Float16)__builtin_fmaf(x1, one, -(float)h.y);
+  return as_u32h(half2_t{l0, l1});
 }
 
 // A three-operand AND-OR takes at most one scalar operand and no literal on
@@ -189,6 +214,20 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
   const uint32_t m3 = (uint32_t)__builtin_amdgcn_readlane(b, 48);
   const uint32_t m01 = m0 > m1 ? m0 : m1, m23 = m2 > m3 ? m2 : m3;
   return __builtin_bit_cast(float, m01 > m23 ? m01 : m23);
+}
+
+// The same maximum without the scalar round trip: after the 16-lane DPP
+// steps, gfx950's lane-swap instructions exchange the two 32-lane halves
+// (lane i with lane i ^ 32) and then neighbouring 16-lane rows (i with
+// i ^ 16), each followed by an integer maximum; every lane ends with the
+// wave's maximum in a vector register.
+__device__ __forceinline__ float wave_max_nonneg_v(float v) {
+  uint32_t b = __builtin_bit_cast(uint32_t, group_max_nonneg<16>(v));
+  const auto h = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  b = h[0] > h[1] ? h[0] : h[1];
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  b = r[0] > r[1] ? r[0] : r[1];
+  return __builtin_bit_cast(float, b);
 }
 
 // Sum over aligned groups of `width` lanes (width a power of two <= 64);

@@ -41,13 +41,7 @@ int check_ternary(const void *x, const uint8_t *c, const void *y, int64_t K,
   return Q4K_OK;
 }
 
-}  // namespace
 
-extern "C" {
-
-}  // extern "C"
-
-namespace {
 
 // Validates an explicit vector-kernel launch shape (see q4k_gemv_shaped).
 bool valid_vector_shape(int rows_per_lane, int k_waves, int workgroup_waves) {
@@ -160,7 +154,7 @@ static bool use_gemv_batch(int64_t M, int64_t K, int64_t N) {
 // (at most 8 tokens), 16 / 32 / 64 = the prefill tiles with that many
 // weight rows per workgroup.
 static bool valid_matmul_form(int form, int64_t n_tokens) {
-  return (form == 1 && n_tokens <= 8) || form == 16 || form == 32 || form == 64;
+  return (form == 1 && n_tokens <= 8) || form == 16 || form == 32 || form == 64 || form == 65;
 }
 
 int q4k_matmul_shaped(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
@@ -172,6 +166,9 @@ int q4k_matmul_shaped(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
   hipError_t e = form == 1
       ? q4k::gemv_batch_launch(X, w_blocks, Y, n_tokens, input_dim / 256, output_dim,
                                (hipStream_t)stream)
+      : form == 65
+      ? q4k::prefill_direct_launch(X, w_blocks, n_tokens, input_dim, output_dim, Y,
+                                   (hipStream_t)stream)
       : q4k::prefill_launch(X, w_blocks, n_tokens, input_dim, output_dim, Y,
                             (hipStream_t)stream, form);
   return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_matmul launch");
@@ -223,6 +220,10 @@ static bool ternary_row_loop_wins(int64_t M, int64_t K) {
   return M <= 2 || (M <= 3 && K > 8192);
 }
 
+// Every launch of the loop has the same dimensions, so a launch that the
+// library itself rejects is rejected for the first row, before anything is
+// written; only a failure reported by the HIP runtime part-way through can
+// leave earlier token rows written (include/q4k.h, ternary_matmul).
 static int ternary_row_loop(const float *X, const uint8_t *codes, float scale, int64_t n_tokens,
                             int64_t input_dim, int64_t output_dim, float *Y, void *stream) {
   for (int64_t r = 0; r < n_tokens; ++r) {
@@ -321,7 +322,7 @@ int q4k_matmul_tiled_shaped(const float *X, const uint8_t *w_tiled, int64_t n_to
   int rc = check_q4k(X, w_tiled, Y, n_tokens, input_dim, output_dim);
   if (rc) return rc;
   if (form == 0) return q4k_matmul_tiled(X, w_tiled, n_tokens, input_dim, output_dim, Y, stream);
-  if (!valid_matmul_form(form, n_tokens)) return Q4K_EINVAL_DIM;
+  if (!valid_matmul_form(form, n_tokens) || form == 65) return Q4K_EINVAL_DIM;
   hipError_t e = form == 1
       ? q4k::gemv_tiled_batch_launch(X, w_tiled, Y, n_tokens, input_dim / 256, output_dim,
                                      (hipStream_t)stream)

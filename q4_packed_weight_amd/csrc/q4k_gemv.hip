@@ -36,7 +36,6 @@ namespace q4k {
 
 namespace {
 
-constexpr int kBlockBytes = 144;
 
 // Per-lane decoded header values for the lane's two sub-blocks.
 struct SlabScales {

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float4 v0 = xv[t];  // positions 4 lane .. 4 lane + 3
-      const float mx = wave_max_nonneg(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
+      const float mx = wave_max_nonneg_v(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
       const int e = __builtin_amdgcn_frexp_expf(mx) - 15;  // |x| * 2^-e < 2^15
       const float4 v = make_float4(__builtin_ldexpf(v0.x, -e), __builtin_ldexpf(v0.y, -e),
                                    __builtin_ldexpf(v0.z, -e), __builtin_ldexpf(v0.w, -e));

@@ -73,6 +73,11 @@ hipError_t ternary_matmul_launch(const float *X, const uint8_t *codes, float sca
 hipError_t prefill_launch(const float *X, const uint8_t *w, int64_t M,
                           int64_t K, int64_t N, float *Y, hipStream_t stream, int rows = 0);
 int prefill_rows(int64_t M, int64_t N);
+// The 64-row x 16-token prefill with each wave owning whole super-blocks and
+// its activations loaded straight into MFMA operand registers
+// (q4k_prefill_direct.hip).
+hipError_t prefill_direct_launch(const float *X, const uint8_t *w, int64_t M, int64_t K,
+                                 int64_t N, float *Y, hipStream_t stream);
 // The same kernel reading tiled weights (q4k_tiled.hip's order): whole tiles
 // are staged through LDS into the canonical block layout, same bits.
 hipError_t prefill_staged_tiled_launch(const float *X, const uint8_t *wt, int64_t M, int64_t K,

@@ -41,14 +41,18 @@
 // same positions.  The D tile has rows 16a + 4g + e and token r in lane
 // (r, g), element e.
 //
-// Precision: A = sc*q (<= 945) is exact in fp16.  The activations are split
-// into fp16 hi + lo (hi = fp16(x), lo = fp16(x - hi)), two MFMAs per tile,
-// so every product is exact and the MFMA's fp32 accumulation gives
-// fp32-level results (|x| must stay below 65504).  The per-block tile is
-// scaled by d once.  The sums of x over each sub-block come from an MFMA
-// with an all-ones A operand, and the lazy-dmin term sum_s (dmin*m_s) *
-// (sum of x over sub-block s) runs on the fp32 MFMA (16x16x4) with exact
-// fp32 operands.
+// Precision: A = sc*q (<= 945) is exact in fp16.  Each token's 256
+// activations of a super-block are first scaled by the power of two that
+// puts their largest |x| into [2^14, 2^15), then split into fp16 hi + lo
+// (hi = fp16(x), lo = fp16(x - hi)), two MFMAs per tile: the halves can
+// neither overflow fp16 nor, for any element within 2^-17 of the block's
+// largest, lose bits of lo to fp16's subnormal range, so every product is
+// exact and the MFMA's fp32 accumulation gives fp32-level results for any
+// |x| < 2^96.  The per-block tile is scaled by d once and the power of two
+// undone (d * tile, then the exponent).  The sums of x over each sub-block
+// come from an MFMA with an all-ones A operand (scaled back the same way),
+// and the lazy-dmin term sum_s (dmin*m_s) * (sum of x over sub-block s)
+// runs on the fp32 MFMA (16x16x4) with exact fp32 operands.
 #include "device_common.h"
 #include "q4k_internal.h"
 
@@ -126,6 +130,7 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   __shared__ uint2 sc_tab[PF_BLKS][4][RPAD];  // (even, odd) sub-block of a pair
   __shared__ float c_tab[PF_BLKS][8][RPAD];
   __shared__ __align__(16) float d_tab[PF_BLKS][ROWS];
+  __shared__ int xe[PF_BLKS][PF_TOK];  // scaling exponent per (block, token) of the stage
 
   // The host validates nb >= 1; saying so lets the compiler fetch every
   // kernel argument in one round trip.
@@ -189,16 +194,23 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
   };
   auto stage_to_lds = [&]() {
     // float4 i: token 2i + tok_lo, block (t / 64), positions 4*lane ..
-    // 4*lane+3; stored as pairs (0,2) and (1,3): operand order
+    // 4*lane+3; stored as pairs (0,2) and (1,3): operand order.  The wave's
+    // 64 lanes hold the whole block of one token, so the block's largest
+    // |x| is a maximum over the wave.
     const int xb = t >> 6;
 #pragma unroll
     for (int i = 0; i < X_PER_THREAD; ++i) {
-      const float4 v = xv[i];
+      const float4 v0 = xv[i];
+      const float mx = wave_max_nonneg_v(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
+      const int e = __builtin_amdgcn_frexp_expf(mx) - 15;  // |x| * 2^-e < 2^15
+      const float4 v = make_float4(__builtin_ldexpf(v0.x, -e), __builtin_ldexpf(v0.y, -e),
+                                   __builtin_ldexpf(v0.z, -e), __builtin_ldexpf(v0.w, -e));
       half2_t h02, h13;
       h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
       h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
       const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
       const int tok = 2 * i + tok_lo;
+      if (lane == 0) xe[xb][tok] = e;
       *reinterpret_cast<uint2 *>(&xh[xb][tok][2 * lane]) = make_uint2(hw02, hw13);
       *reinterpret_cast<uint2 *>(&xl[xb][tok][2 * lane]) =
           make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
@@ -335,21 +347,24 @@ __global__ __launch_bounds__(PF_THREADS) void q4k_prefill_kernel(
           if ((s & 3) == g) xsb[s >> 2] = sx[0];
         }
       }
+      // token r (this lane's D column) entered block bb as x * 2^-e
+      const int er = xe[bb][r];
+      const float xs0 = __builtin_ldexpf(xsb[0], er), xs1 = __builtin_ldexpf(xsb[1], er);
 #pragma unroll
       for (int a = 0; a < TPW; ++a) {
         const int rt = rt0 + a;
         // d of rows 16 rt + 4g + e (the rows of this lane's D elements)
         const float4 dv = *reinterpret_cast<const float4 *>(&d_tab[bb][16 * rt + 4 * g]);
-        y_acc[a][0] = __builtin_fmaf(dv.x, acc[a][0], y_acc[a][0]);
-        y_acc[a][1] = __builtin_fmaf(dv.y, acc[a][1], y_acc[a][1]);
-        y_acc[a][2] = __builtin_fmaf(dv.z, acc[a][2], y_acc[a][2]);
-        y_acc[a][3] = __builtin_fmaf(dv.w, acc[a][3], y_acc[a][3]);
+        y_acc[a][0] += __builtin_ldexpf(dv.x * acc[a][0], er);
+        y_acc[a][1] += __builtin_ldexpf(dv.y * acc[a][1], er);
+        y_acc[a][2] += __builtin_ldexpf(dv.z * acc[a][2], er);
+        y_acc[a][3] += __builtin_ldexpf(dv.w * acc[a][3], er);
         // lazy-dmin term: A[row][kk] = dmin*m of sub-block 4c + kk, B = sums
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           if (SPLIT && c != half) continue;  // wave-uniform: its own sub-blocks
-          m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(c_tab[bb][4 * c + g][16 * rt + r], xsb[c],
-                                                          m_acc[a], 0, 0, 0);
+          m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(c_tab[bb][4 * c + g][16 * rt + r],
+                                                          c ? xs1 : xs0, m_acc[a], 0, 0, 0);
         }
       }
     }

@@ -355,7 +355,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float4 v0 = xq[s][t];
-      const float mx = wave_max_nonneg(
+      const float mx = wave_max_nonneg_v(
           fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
       const int e = __builtin_amdgcn_frexp_expf(mx) - 15;  // |x| * 2^-e < 2^15
       const float4 v = make_float4(__builtin_ldexpf(v0.x, -e), __builtin_ldexpf(v0.y, -e),
@@ -507,6 +507,7 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
   __shared__ __align__(16) uint32_t xh[TP_BLKS][TP_TOK][TP_XROW];
   __shared__ __align__(16) uint32_t xl[TP_BLKS][TP_TOK][TP_XROW];
   __shared__ __align__(16) float dtab[TP_WAVES][TPW][16];
+  __shared__ int xe[TP_BLKS][TP_TOK];  // scaling exponent per (block, token) of the stage
 
   __builtin_assume(nb >= 1);
   const int tid = threadIdx.x;
@@ -553,16 +554,23 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
   };
   auto stage_x = [&]() {
     // float4 i: token 2i + tok_lo, block t / 64, positions 4 (t % 64) ..;
-    // stored as pairs (0,2) and (1,3): operand order
+    // stored as pairs (0,2) and (1,3): operand order.  As in the canonical
+    // prefill, each token's block is first scaled by the power of two that
+    // puts its largest |x| (a maximum over the wave) into [2^14, 2^15).
     const int xb = t >> 6, l = t & 63;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float4 v = xv[i];
+      const float4 v0 = xv[i];
+      const float mx = wave_max_nonneg_v(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
+      const int e = __builtin_amdgcn_frexp_expf(mx) - 15;  // |x| * 2^-e < 2^15
+      const float4 v = make_float4(__builtin_ldexpf(v0.x, -e), __builtin_ldexpf(v0.y, -e),
+                                   __builtin_ldexpf(v0.z, -e), __builtin_ldexpf(v0.w, -e));
       half2_t h02, h13;
       h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
       h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
       const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
       const int tok = 2 * i + tok_lo;
+      if (l == 0) xe[xb][tok] = e;
       *reinterpret_cast<uint2 *>(&xh[xb][tok][2 * l]) = make_uint2(hw02, hw13);
       *reinterpret_cast<uint2 *>(&xl[xb][tok][2 * l]) =
           make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
@@ -640,17 +648,20 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // token r (this lane's D column) entered block bb as x * 2^-e
+    const int er = xe[bb][r];
+    const float xs0 = __builtin_ldexpf(xsb[0], er), xs1 = __builtin_ldexpf(xsb[1], er);
 #pragma unroll
     for (int a = 0; a < TPW; ++a) {
       const float4 dv = *reinterpret_cast<const float4 *>(&dtab[wave][a][4 * g]);
-      y_acc[a][0] = __builtin_fmaf(dv.x, acc[a][0], y_acc[a][0]);
-      y_acc[a][1] = __builtin_fmaf(dv.y, acc[a][1], y_acc[a][1]);
-      y_acc[a][2] = __builtin_fmaf(dv.z, acc[a][2], y_acc[a][2]);
-      y_acc[a][3] = __builtin_fmaf(dv.w, acc[a][3], y_acc[a][3]);
+      y_acc[a][0] += __builtin_ldexpf(dv.x * acc[a][0], er);
+      y_acc[a][1] += __builtin_ldexpf(dv.y * acc[a][1], er);
+      y_acc[a][2] += __builtin_ldexpf(dv.z * acc[a][2], er);
+      y_acc[a][3] += __builtin_ldexpf(dv.w * acc[a][3], er);
       // lazy-dmin term: A[row][kk] = dmin*m of sub-block 4c + kk, B = sums
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(cm[a][c], xsb[c], m_acc[a], 0, 0, 0);
+        m_acc[a] = __builtin_amdgcn_mfma_f32_16x16x4f32(cm[a][c], c ? xs1 : xs0, m_acc[a], 0, 0, 0);
       }
     }
     // the next block's d values overwrite the table only after these reads

@@ -167,7 +167,7 @@ def test_matmul_shaped_rejects_bad_forms(lib):
     assert lib.q4k_matmul_shaped(GOOD, GOOD2, 16, 255, 64, GOOD3, None, 16) == -1
     assert lib.q4k_matmul_shaped(None, GOOD2, 16, 256, 64, GOOD3, None, 16) == -2
     assert lib.q4k_matmul_shaped(ODD, GOOD2, 16, 256, 64, GOOD3, None, 16) == -3
-    for form in (2, 8, 48, 128, -16):
+    for form in (2, 8, 48, 65, 128, -16):
         assert lib.q4k_matmul_tiled_shaped(GOOD, GOOD2, 16, 256, 64, GOOD3, None, form) == -1
     assert lib.q4k_matmul_tiled_shaped(GOOD, ODD, 16, 256, 64, GOOD3, None, 32) == -3
 
@@ -243,3 +243,5 @@ def test_bench_helpers_validate(lib):
     assert lib.q4k_bench_stream_read(GOOD, 100, GOOD2, 4, None) == -1
     assert lib.q4k_bench_stream_read(ODD, 160, GOOD2, 4, None) == -3
     assert lib.q4k_bench_copy(GOOD, None, 160, None) == -2
+    assert lib.q4k_bench_delay(-1, None) == -1
+    assert lib.q4k_bench_delay(200000000, None) == -1

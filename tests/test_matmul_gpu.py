@@ -36,15 +36,14 @@ def test_matmul_parity_shapes(oracle_lib, M, K, N):
     assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"{M}x{K}x{N}")
 
 
-def test_matmul_full_config_sampled_tokens(oracle_lib):
-    """64 x 4096 x 4096: every output of 8 sampled token rows."""
+def test_matmul_full_config_all_tokens(oracle_lib):
+    """64 x 4096 x 4096 (the prefill workload): every output of every token
+    row."""
     M, K, N = 64, 4096, 4096
     w = synth.q4k_weights(N, K, config=synth.C4_PREFILL)
     X = synth.activations(K, n_tokens=M, config=synth.C4_PREFILL)
     Y = run(X, w, M, K, N)
-    for t in (0, 7, 21, 33, 40, 52, 62, 63):
-        ref = oracle_lib.q4k_matmul_part(X, w, M, K, N, (t, t + 1), (0, N))[t]
-        assert_parity(Y[t], ref, what=f"token {t}")
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what="64x4096x4096")
 
 
 def test_matmul_rows_match_gemv_on_integer_inputs(oracle_lib):
@@ -190,7 +189,12 @@ def run_rows(X, w, M, K, N, rows):
     return out
 
 
-@pytest.mark.parametrize("rows", [16, 32, 64])
+# 65: the 64-row tiles whose waves own whole super-blocks (activations
+# loaded straight into MFMA operand registers)
+PREFILL_FORMS = [16, 32, 64, 65]
+
+
+@pytest.mark.parametrize("rows", PREFILL_FORMS)
 @pytest.mark.parametrize("M,K,N", [(16, 256, 16), (17, 768, 65), (33, 1280, 130), (2, 1024, 100),
                                    (64, 4096, 64), (9, 14336, 40), (48, 2304, 129), (16, 512, 4097)])
 def test_prefill_every_workgroup_height(oracle_lib, M, K, N, rows):
@@ -202,7 +206,7 @@ def test_prefill_every_workgroup_height(oracle_lib, M, K, N, rows):
     assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"{M}x{K}x{N} rows {rows}")
 
 
-@pytest.mark.parametrize("rows", [16, 32, 64])
+@pytest.mark.parametrize("rows", PREFILL_FORMS)
 def test_prefill_every_height_integer_bit_exact(oracle_lib, rows):
     M, K, N = 24, 4096, 96
     w = synth.q4k_integer_weights(N, K, config=49)
@@ -223,3 +227,72 @@ def test_prefill_narrow_full_size_sampled(oracle_lib, M, N):
         ref = oracle_lib.q4k_matmul_part(X, w, M, K, N, (t, t + 1), (0, N))[t]
         assert_parity(Y[t], ref, what=f"token {t}")
 
+
+
+def wide_range_subblocks(M, K, config):
+    """N(0,1) activations with every 32-element sub-block scaled by its own
+    power of two in 2^-40 .. 2^40 and about one in ten sub-blocks zero."""
+    X = synth.activations(K, n_tokens=M, config=config)
+    g = np.random.default_rng(config)
+    sub = np.exp2(g.integers(-40, 41, (M, K // 32))).astype(np.float32)
+    sub[g.random((M, K // 32)) < 0.1] = 0.0
+    return (X.reshape(M, -1, 32) * sub[:, :, None]).reshape(M, K)
+
+
+def wide_range_tokens(M, K, config):
+    """Whole token rows at very different magnitudes: 1e-5, 3e5 (above the
+    fp16 range), 2^-60, 2^60, one all-zero row, the rest N(0,1)."""
+    X = synth.activations(K, n_tokens=M, config=config)
+    scale = np.ones(M, np.float32)
+    scale[0:M // 5] = 1e-5
+    scale[M // 5:2 * M // 5] = 3e5
+    scale[2 * M // 5:3 * M // 5] = 2.0 ** -60
+    scale[3 * M // 5:4 * M // 5] = 2.0 ** 60
+    scale[M - 1] = 0.0
+    return X * scale[:, None]
+
+
+@pytest.mark.parametrize("rows", PREFILL_FORMS)
+@pytest.mark.parametrize("M,K,N", [(24, 2048, 200), (40, 4096, 130)])
+def test_prefill_wide_range_subblocks_every_height(oracle_lib, M, K, N, rows):
+    """Sub-blocks from 2^-40 to 2^40 and zero sub-blocks: each token's
+    super-block is scaled by a power of two before its fp16 split, so the
+    prefill tiles stay within the bar at every height."""
+    w = synth.q4k_weights(N, K, config=54, copy=rows)
+    X = wide_range_subblocks(M, K, 54 + rows)
+    Y = run_rows(X, w, M, K, N, rows)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True,
+                  what=f"{M}x{K}x{N} rows {rows}")
+
+
+@pytest.mark.parametrize("rows", PREFILL_FORMS)
+def test_prefill_wide_range_tokens_every_height(oracle_lib, rows):
+    """Token rows at 1e-5, 3e5 (|x| above 65504), 2^-60 and 2^60, and a zero
+    row, at every workgroup height."""
+    M, K, N = 40, 2048, 200
+    w = synth.q4k_weights(N, K, config=55, copy=rows)
+    X = wide_range_tokens(M, K, 55 + rows)
+    Y = run_rows(X, w, M, K, N, rows)
+    ref = oracle_lib.q4k_matmul(X, w, M, K, N)
+    assert np.all(Y[M - 1] == 0.0)
+    assert_parity(Y[:M - 1], ref[:M - 1], rowwise=True, what=f"rows {rows}")
+
+
+def test_matmul_wide_range_full_config(oracle_lib):
+    """The automatic choice at the prefill workload's shape with wide-range
+    sub-blocks: every output of every token row."""
+    M, K, N = 64, 4096, 4096
+    w = synth.q4k_weights(N, K, config=synth.C4_PREFILL)
+    X = wide_range_subblocks(M, K, 56)
+    Y = run(X, w, M, K, N)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what="64x4096x4096")
+
+
+@pytest.mark.parametrize("rows", [64, 65])
+def test_prefill_full_config_every_form(oracle_lib, rows):
+    """64 x 4096 x 4096 on each 64-row prefill kernel, every output."""
+    M, K, N = 64, 4096, 4096
+    w = synth.q4k_weights(N, K, config=synth.C4_PREFILL)
+    X = synth.activations(K, n_tokens=M, config=synth.C4_PREFILL)
+    Y = run_rows(X, w, M, K, N, rows)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"form {rows}")

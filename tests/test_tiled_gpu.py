@@ -402,3 +402,25 @@ def test_matmul_tiled_deterministic_and_rejects():
         with pytest.raises(ValueError):
             binding.q4k_matmul_tiled(dev(X), wt, M, bad_k, N, Y)
     assert bool(torch.all(torch.isnan(buf)))
+
+
+@pytest.mark.parametrize("rows,K", [(16, 2048), (32, 2048), (64, 2048), (64, 8448)])
+def test_prefill_tiled_wide_range(oracle_lib, rows, K):
+    """The prefill tiles on tiled weights (64 rows below input_dim 8192 load
+    tiles into registers, the rest stage them through LDS) with sub-blocks
+    from 2^-40 to 2^40, zero sub-blocks, and whole token rows at 1e-5, 3e5,
+    2^-60 and 2^60: each token's super-block is scaled by a power of two
+    before its fp16 split."""
+    M, N = 40, 130
+    w = synth.q4k_weights(N, K, config=57, copy=rows)
+    X = synth.activations(K, n_tokens=M, config=57, copy=rows)
+    g = np.random.default_rng(57 + rows)
+    sub = np.exp2(g.integers(-40, 41, (M, K // 32))).astype(np.float32)
+    sub[g.random((M, K // 32)) < 0.1] = 0.0
+    X = (X.reshape(M, -1, 32) * sub[:, :, None]).reshape(M, K)
+    X[:8] = synth.activations(K, n_tokens=8, config=58) * np.float32(
+        [1e-5, 1e-5, 3e5, 3e5, 2.0 ** -60, 2.0 ** -60, 2.0 ** 60, 2.0 ** 60])[:, None]
+    wt, _ = relayout(w, K, N)
+    Y = matmul_tiled_form(X, wt, M, K, N, rows)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True,
+                  what=f"{M}x{K}x{N} rows {rows}")
