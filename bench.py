@@ -7,9 +7,11 @@ Default workload: Q4_K GEMV, input_dim 4096 x output_dim 4096, batch 1,
 fp32 activations, 64 distinct weight copies (604 MB, more than twice the
 256 MB Infinity Cache) used in rotation so that every call streams its
 weights from HBM.  A step is one q4k_gemv call on the next copy.  Inputs
-are generated (seeded, synthetic) and copied to HBM before timing.  Calls
-are issued as replays of a captured HIP graph (one graph node per call),
-so the timed region holds kernel work, not Python launch overhead.
+are generated (seeded, synthetic) and copied to HBM before timing.  The
+timed region holds device work only: a delay kernel keeps the GPU busy
+while the host submits the timed calls (one launch per call for up to 512
+steps, replays of a captured HIP graph with one node per call above), and
+HIP events on the launch stream bracket exactly the timed steps.
 
 Prints one JSON line: mean us/call (value), achieved GB/s of algorithmic
 bytes against the 8 TB/s HBM peak (roofline), and the CPU oracle timed on
@@ -61,6 +63,7 @@ GEMV_SRC = ["q4_packed_weight_amd/csrc/q4k_gemv.hip",
             "q4_packed_weight_amd/csrc/q4k_gemv_mfma.hip",
             "q4_packed_weight_amd/csrc/device_common.h"]
 PREFILL_SRC = ["q4_packed_weight_amd/csrc/q4k_prefill.hip",
+               "q4_packed_weight_amd/csrc/q4k_prefill_direct.hip",
                "q4_packed_weight_amd/csrc/device_common.h"]
 TERNARY_SRC = ["q4_packed_weight_amd/csrc/ternary_gemv.hip",
                "q4_packed_weight_amd/csrc/device_common.h"]
@@ -199,7 +202,7 @@ def make_workload(name, torch, binding, synth):
         wl.copies = copies
         wl.bytes = wbytes + 4 * M * K + 4 * M * N
         wl.flops = 2 * M * K * N
-        wl.kernel = "q4k_prefill"
+        wl.kernel = "q4k_prefill_direct_kernel<true>"
         wl.src_files = PREFILL_SRC
         wl.config = {"workload": "q4k_matmul prefill 64 tokens x 4096 -> 4096",
                      "tokens": M, "input_dim": K, "output_dim": N, "rotating_copies": copies}
@@ -423,26 +426,29 @@ def capture(torch, wl, start, count):
 
 
 DELAY_NS = 1_000_000
+EAGER_DELAY_NS_PER_STEP = 20_000  # host time to enqueue one call, with margin
 PREFILL_FORM = 0  # c4: 0 = q4k_matmul's own choice, else the q4k_matmul_shaped form
 
 
-def time_steps(torch, binding, wl, steps, launch, graphs):
+def time_steps(torch, binding, wl, steps, launch, graphs, first=0):
     """Mean ms per step over exactly `steps` steps, HIP events on the stream
     the kernels run on, and the host's submission time of those steps.
 
-    After the synchronization a 1 ms delay kernel is enqueued ahead of the
-    start event: while it runs, the host submits the timed graph replays, so
-    the events time the device's execution of exactly the `steps` calls and
-    not the host's graph-submission latency (which otherwise counts once per
-    replay and dominates short runs)."""
+    After the synchronization a delay kernel (1 ms, or 20 us per step for
+    individual launches) is enqueued ahead of the start event: while it
+    runs, the host submits the timed calls, so the events time the device's
+    execution of exactly the `steps` calls and not the host's submission."""
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    binding.bench_delay(DELAY_NS)
+    delay = DELAY_NS if launch != "eager" else max(DELAY_NS, EAGER_DELAY_NS_PER_STEP * steps)
+    binding.bench_delay(min(delay, 100_000_000))
     start.record(stream)
     t0 = time.perf_counter()
     if launch == "eager":
-        for i in range(steps):
+        # continue the rotation after the warmup calls, so that no timed call
+        # finds its weights left in the Infinity Cache by a recent one
+        for i in range(first, first + steps):
             wl.call(i)
     else:
         full, rem = graphs
@@ -619,7 +625,9 @@ def main():
     ap.add_argument("--steps", type=int, default=64000)
     ap.add_argument("--warmup", type=int, default=6400)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "n1", "c5", "q40", "q6k", "t64", "c2t", "c3t", "copy"])
-    ap.add_argument("--launch", default="graph", choices=["graph", "eager"])
+    ap.add_argument("--launch", default="auto", choices=["auto", "graph", "eager"],
+                    help="auto: individual launches for up to 512 steps (queued while a "
+                         "delay kernel keeps the GPU busy), graph replays above")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
@@ -644,6 +652,13 @@ def main():
     steps, warmup = args.steps, args.warmup
     print(f"[bench] workload {wl.name}: {wl.config}", file=sys.stderr, flush=True)
 
+    # A replay of a captured graph costs the device a few microseconds of its
+    # own on top of its nodes, which a short run cannot amortize; up to 512
+    # steps the calls are therefore launched one by one behind the delay
+    # kernel (the host enqueues them while it runs), above that as graph
+    # replays.
+    if args.launch == "auto":
+        args.launch = "eager" if steps <= 512 else "graph"
     graphs = None
     if args.launch == "graph":
         full = capture(torch, wl, 0, wl.copies)
@@ -657,7 +672,7 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done, timing {steps} steps", file=sys.stderr, flush=True)
 
-    ms, host_s = time_steps(torch, binding, wl, steps, args.launch, graphs)
+    ms, host_s = time_steps(torch, binding, wl, steps, args.launch, graphs, first=warmup)
     us = ms * 1000.0
     torch.cuda.synchronize()
     print(f"[bench] {us:.3f} us/step", file=sys.stderr, flush=True)
@@ -688,7 +703,8 @@ def main():
         "data": getattr(wl, "data", "synthetic (seeded numpy generators; random Q4_K blocks, "
                                        "N(0,1) activations)"),
         "config": dict(wl.config, launch="hipGraph replay, one node per call"
-                       if args.launch == "graph" else "eager, one ctypes call per step"),
+                       if args.launch == "graph" else
+                       "one launch per call, enqueued while a delay kernel runs"),
         "achieved_GBps": round(gbps, 1),
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "gflops": round(wl.flops / us / 1e3, 1) if wl.flops else None,
@@ -699,7 +715,9 @@ def main():
     if not args.no_context:
         ctx = context_measurements(torch, binding, wl, min(wl.copies, 256))
         ctx["host_submit_ms_of_timed_steps"] = round(host_s * 1000, 3)
-        ctx["delay_before_timed_region_ms"] = DELAY_NS / 1e6
+        ctx["delay_before_timed_region_ms"] = (DELAY_NS if args.launch != "eager" else
+                                               min(max(DELAY_NS, EAGER_DELAY_NS_PER_STEP * steps),
+                                                   100_000_000)) / 1e6
         ctx["kernel_trace_avg_us_per_step"] = trace_for(wl)
         line["context"] = ctx
     if not args.no_cpu_baseline and wl.cpu is not None:

@@ -41,14 +41,20 @@ __device__ __forceinline__ void split_pair(float x0, float x1, float s, uint32_t
 }
 
 // lo = fp16(x - hi) for the two halves of `hi2` (fp16 hi parts of x0, x1):
-// one v_fma_mix each (x * 1 - hi, exact in fp32, rounded once), so hi + lo
-// carries x to 22 significant bits and both are exact MFMA inputs.
+// v_fma_mix evaluates x - hi exactly in fp32 and rounds once to fp16, so
+// hi + lo carries x to 22 significant bits and both are exact MFMA inputs.
+// Two instructions reading hi2's halves through op_sel (the compiler's own
+// selection of the same arithmetic re-converts each half first).  Inline
+// assembly gets no matrix-core hazard waits from the compiler, so this is
+// for staging code that runs while no MFMA is in flight (every earlier
+// MFMA result already read by ordinary code); split_pair is the form for
+// code interleaved with MFMAs.
 __device__ __forceinline__ uint32_t lo_pair(uint32_t hi2, float x0, float x1) {
-  const half2_t h = as_h2(hi2);
-  const float one = opaque_f32(1.0f);
-  const _Float16 l0 = (_Float16)__builtin_fmaf(x0, one, -(float)h.x);
-  const _Float16 l1 = (_Float16)__builtin_fmaf(x1, one, -(float)h.y);
-  return as_u32h(half2_t{l0, l1});
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hi2), "v"(x0));
+  asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(r) : "v"(hi2), "v"(x1));
+  return r;
 }
 
 // A three-operand AND-OR takes at most one scalar operand and no literal on

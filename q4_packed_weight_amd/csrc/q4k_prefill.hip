@@ -455,6 +455,17 @@ int prefill_rows(int64_t M, int64_t N) {
 
 hipError_t prefill_launch(const float *X, const uint8_t *w, int64_t M,
                           int64_t K, int64_t N, float *Y, hipStream_t stream, int rows) {
+  // The library's own choice of 64-row tiles runs the kernel whose waves own
+  // whole super-blocks (q4k_prefill_direct.hip): measured on MI355X
+  // (graph-replayed calls over rotating weights, this file's kernel / that
+  // one, us/call): 64x4096x4096 18.9 / 16.9, 48 tokens 18.2 / 16.9,
+  // 64x14336->4096 60.0 / 42.9, 64x11008->4096 47.2 / 35.0, 64x4096->14336
+  // 68.3 / 61.2, 128x4096x4096 34.4 / 31.0.  Here the per-(token,
+  // super-block) maximum for the activations' scaling spans a whole wave,
+  // there it is a maximum within each lane.  rows == 64 still forces this
+  // file's kernel.
+  if (rows == 0 && prefill_rows(M, N) == 64)
+    return prefill_direct_launch(X, w, M, K, N, Y, stream);
   return prefill_launch_any<false>(X, w, M, K, N, Y, stream, rows);
 }
 
