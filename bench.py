@@ -62,8 +62,7 @@ def kernel_hash(files):
 GEMV_SRC = ["q4_packed_weight_amd/csrc/q4k_gemv.hip",
             "q4_packed_weight_amd/csrc/q4k_gemv_mfma.hip",
             "q4_packed_weight_amd/csrc/device_common.h"]
-PREFILL_SRC = ["q4_packed_weight_amd/csrc/q4k_prefill.hip",
-               "q4_packed_weight_amd/csrc/q4k_prefill_direct.hip",
+PREFILL_SRC = ["q4_packed_weight_amd/csrc/q4k_prefill_splitk.hip",
                "q4_packed_weight_amd/csrc/device_common.h"]
 TERNARY_SRC = ["q4_packed_weight_amd/csrc/ternary_gemv.hip",
                "q4_packed_weight_amd/csrc/device_common.h"]
@@ -202,7 +201,7 @@ def make_workload(name, torch, binding, synth):
         wl.copies = copies
         wl.bytes = wbytes + 4 * M * K + 4 * M * N
         wl.flops = 2 * M * K * N
-        wl.kernel = "q4k_prefill_direct_kernel<true>"
+        wl.kernel = "q4k_prefill_splitk_kernel"
         wl.src_files = PREFILL_SRC
         wl.config = {"workload": "q4k_matmul prefill 64 tokens x 4096 -> 4096",
                      "tokens": M, "input_dim": K, "output_dim": N, "rotating_copies": copies}
@@ -661,6 +660,10 @@ def main():
         args.launch = "eager" if steps <= 512 else "graph"
     graphs = None
     if args.launch == "graph":
+        # one call outside the capture: the library allocates its per-device
+        # workspace on the first call that needs one, never inside a capture
+        wl.call(0)
+        torch.cuda.synchronize()
         full = capture(torch, wl, 0, wl.copies)
         rem = capture(torch, wl, 0, steps % wl.copies) if steps % wl.copies else None
         graphs = (full, rem)

@@ -81,25 +81,41 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
  * q4k_matmul -- Y[r, o] = sum_k W[o,k] * X[r,k] for r < n_tokens: the
  * batched (prefill) form.  Row r of X starts at X + r*input_dim and row r
  * of Y at Y + r*output_dim, the row offsets of the ternary page's prefill
- * row loop (SKaiNET issue #1138, section "Tasks"); the weights are read
- * once per call for all tokens, the lesson of the tiling page (llama.cpp
- * fork PR #37, "ggml-cpu: cache-aware tiling in ggml_compute_forward_mul_mat",
- * section "Summary", fix 1).
+ * row loop (SKaiNET issue #1138, section "Tasks").  Following the tiling
+ * page (llama.cpp fork PR #37, "ggml-cpu: cache-aware tiling in
+ * ggml_compute_forward_mul_mat", section "Summary", fix 1), the weights
+ * are not re-streamed per token: each kernel reads a weight tile once for
+ * a whole tile of tokens, and the workgroups that share a weight tile run
+ * on one XCD, so HBM delivers each weight byte once per call; the
+ * activations (4 bytes each) are fetched into every XCD's L2 that uses
+ * them.
  *   X          fp32 [n_tokens, input_dim], 16-byte aligned
  *   w_blocks   as for q4k_gemv
  *   n_tokens   M > 0 (M == 1 runs q4k_gemv)
  *   input_dim, output_dim as for q4k_gemv
  *   Y          fp32 [n_tokens, output_dim]
- * Same error behaviour and tolerance as q4k_gemv.  Three kernels serve it:
+ * Same error behaviour and tolerance as q4k_gemv.  The kernels serving it:
  * M == 1 is q4k_gemv; a few tokens (M <= 2 at any shape, M <= 4 with
  * output_dim <= 4096, M <= 8 with output_dim <= 4096 and input_dim > 12288)
  * run on a batched matrix-core GEMV that reads each weight once for all of
- * them; larger batches run on the prefill tiles (64 rows x 16 tokens,
- * narrowed to 32 or 16 rows when 64-row tiles would leave CUs idle).  The batched and
- * prefill kernels pass the activations through fp16: each token's 256
- * activations of a super-block are scaled by a power of two, then split
- * into a high and a low half, both exact MFMA operands (any |x| < 2^96).
- * Y must not alias X or the weights.
+ * them; from 33 tokens (from 17 with output_dim > 4096, from 9 with
+ * input_dim >= 8192) 128-row x 32-token tiles whose input_dim is split
+ * across workgroups when the tiles alone would leave CUs idle; otherwise
+ * prefill tiles of 64 rows x 16 tokens (narrowed to 32 or 16 rows when
+ * 64-row tiles would leave CUs idle).  The batched and tiled kernels pass
+ * the activations through fp16: each token's 256 activations of a
+ * super-block are scaled by a power of two, then split into a high and a
+ * low half, both exact MFMA operands (any |x| < 2^96).  The split tiles add
+ * their ranges' partial results in a fixed order, so results do not depend
+ * on timing.  Their partial tiles go to a workspace of 32 MiB + 1 KiB that
+ * the library allocates once per device, on the first call that needs it,
+ * and keeps until the process ends; a call that would allocate it while its
+ * stream is being captured into a graph fails with Q4K_EHIP (make one such
+ * call outside the capture first).  Every call on a device shares that
+ * workspace, so calls that use it (q4k_matmul and q4k_matmul_shaped on the
+ * split tiles, graphs holding such calls) must not run at the same time on
+ * one device: on different streams, order them with events.  Y must not
+ * alias X or the weights.
  */
 int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
                int64_t input_dim, int64_t output_dim, float *Y, void *stream);
@@ -373,8 +389,11 @@ int q4k_gemv_tiled_shaped(const float *x, const uint8_t *w_tiled, int64_t input_
  * weight rows per workgroup (x 16 tokens, any |X| < 2^96) at any token count;
  * form 65 runs 64-row x 16-token tiles whose waves each own whole
  * super-blocks of all 64 rows, with the activations loaded straight into
- * matrix-core operand registers (same arithmetic and range);
- * 0 is q4k_matmul itself.  Any other value (or form 1 with more than 8
+ * matrix-core operand registers (same arithmetic and range); form 128 runs
+ * the 128-row x 32-token tiles with the library's number S of input_dim
+ * ranges, and form 128 + S (S = 1..8) fixes it (clamped to at most
+ * input_dim/512 ranges, and to 1 from 256 tiles on; same arithmetic and
+ * range, workspace as for q4k_matmul); 0 is q4k_matmul itself.  Any other value (or form 1 with more than 8
  * tokens) gives Q4K_EINVAL_DIM.  Results are within the q4k_matmul
  * tolerance for every form.
  */
@@ -385,8 +404,8 @@ int q4k_matmul_shaped(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
 /*
  * q4k_matmul_tiled_shaped -- q4k_matmul_tiled with its kernel forced: form
  * as for q4k_matmul_shaped (1 = the few-token GEMV, 16 / 32 / 64 = the
- * prefill tiles, 0 = q4k_matmul_tiled itself; form 65 is canonical-only and
- * gives Q4K_EINVAL_DIM here).
+ * prefill tiles, 0 = q4k_matmul_tiled itself; forms 65 and 128 .. 136 are
+ * canonical-only and give Q4K_EINVAL_DIM here).
  */
 int q4k_matmul_tiled_shaped(const float *X, const uint8_t *w_tiled, int64_t n_tokens,
                             int64_t input_dim, int64_t output_dim, float *Y, void *stream,

@@ -4,6 +4,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "q4k.h"
 #include "q4k_internal.h"
 
@@ -42,6 +45,63 @@ int check_ternary(const void *x, const uint8_t *c, const void *y, int64_t K,
 }
 
 
+
+// The split-K prefill's workspace, owned by the library: one per device, of
+// the largest size any call needs, allocated by the first call that needs
+// it (outside stream capture) and never freed or moved, so graphs that
+// captured calls keep a valid pointer.  Calls that use it must not overlap
+// in time (include/q4k.h).
+struct DeviceWorkspace {
+  int device;
+  void *ptr;
+};
+std::mutex g_ws_mutex;
+std::vector<DeviceWorkspace> g_ws;
+
+hipError_t device_workspace(hipStream_t stream, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  for (const auto &w : g_ws)
+    if (w.device == dev) {
+      *out = w.ptr;
+      return hipSuccess;
+    }
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &st);
+  if (e != hipSuccess) return e;
+  if (st != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+  void *p = nullptr;
+  e = hipMalloc(&p, q4k::kSplitkWorkspaceBytes);
+  if (e != hipSuccess) return e;
+  // the counters start at zero (every call leaves them zero again); done
+  // before any stream can use the workspace
+  e = hipMemsetAsync(p, 0, q4k::kSplitkCounterBytes, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return e;
+  }
+  g_ws.push_back(DeviceWorkspace{dev, p});
+  *out = p;
+  return hipSuccess;
+}
+
+// The split-K prefill on the library's workspace for this device.
+int matmul_splitk(const float *X, const uint8_t *w, int64_t M, int64_t K, int64_t N, float *Y,
+                  void *stream, int ranges = 0) {
+  if (!q4k::splitk_fits(M, K, N)) return Q4K_EINVAL_DIM;
+  const q4k::SplitkPlan p = q4k::splitk_plan(M, K, N, ranges);
+  void *ws = nullptr;
+  if (p.workspace_bytes > 0) {
+    hipError_t e = device_workspace((hipStream_t)stream, &ws);
+    if (e != hipSuccess) return hip_fail(e, "q4k_matmul workspace");
+  }
+  hipError_t e = q4k::prefill_splitk_launch(X, w, M, K, N, Y, ws, p.workspace_bytes,
+                                            (hipStream_t)stream, ranges);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_matmul launch");
+}
 
 // Validates an explicit vector-kernel launch shape (see q4k_gemv_shaped).
 bool valid_vector_shape(int rows_per_lane, int k_waves, int workgroup_waves) {
@@ -154,7 +214,8 @@ static bool use_gemv_batch(int64_t M, int64_t K, int64_t N) {
 // (at most 8 tokens), 16 / 32 / 64 = the prefill tiles with that many
 // weight rows per workgroup.
 static bool valid_matmul_form(int form, int64_t n_tokens) {
-  return (form == 1 && n_tokens <= 8) || form == 16 || form == 32 || form == 64 || form == 65;
+  return (form == 1 && n_tokens <= 8) || form == 16 || form == 32 || form == 64 || form == 65 ||
+         (form >= 128 && form <= 128 + q4k::kSplitkMaxRanges);
 }
 
 int q4k_matmul_shaped(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
@@ -163,6 +224,8 @@ int q4k_matmul_shaped(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
   if (rc) return rc;
   if (form == 0) return q4k_matmul(X, w_blocks, n_tokens, input_dim, output_dim, Y, stream);
   if (!valid_matmul_form(form, n_tokens)) return Q4K_EINVAL_DIM;
+  if (form >= 128)
+    return matmul_splitk(X, w_blocks, n_tokens, input_dim, output_dim, Y, stream, form - 128);
   hipError_t e = form == 1
       ? q4k::gemv_batch_launch(X, w_blocks, Y, n_tokens, input_dim / 256, output_dim,
                                (hipStream_t)stream)
@@ -174,11 +237,26 @@ int q4k_matmul_shaped(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
   return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_matmul launch");
 }
 
+// The 128-row x 32-token tiles with input_dim split across workgroups win
+// from 33 tokens on, from 17 with output_dim above 4096 and from 9 with
+// input_dim from 8192.  Measured on MI355X (graph-replayed calls over
+// rotating weights, the other kernels' best / these tiles, us/call):
+// 64x4096x4096 17.3 / 16.4, 128x4096x4096 31.3 / 22.1, 512x4096x4096 117.3
+// / 67.9, 64x4096->14336 62.7 / 35.5, 64x14336->4096 46.1 / 35.3,
+// 32x4096->14336 33.7 / 23.8, 32x4096->8192 18.1 / 17.1, 16x14336->4096
+// 36.3 / 23.7, 16x11008->4096 28.6 / 20.5; against 16x4096x4096 12.1 /
+// 14.5, 16x4096->14336 20.0 / 22.7 and 24x4096x4096 14.3 / 14.8.
+static bool use_splitk(int64_t M, int64_t K, int64_t N) {
+  return q4k::splitk_fits(M, K, N) && M >= 9 && (M > 32 || K >= 8192 || (M > 16 && N > 4096));
+}
+
 int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
                int64_t input_dim, int64_t output_dim, float *Y, void *stream) {
   int rc = check_q4k(X, w_blocks, Y, n_tokens, input_dim, output_dim);
   if (rc) return rc;
   if (n_tokens == 1) return q4k_gemv(X, w_blocks, input_dim, output_dim, Y, stream);
+  if (use_splitk(n_tokens, input_dim, output_dim))
+    return matmul_splitk(X, w_blocks, n_tokens, input_dim, output_dim, Y, stream);
   if (use_gemv_batch(n_tokens, input_dim, output_dim)) {
     hipError_t e = q4k::gemv_batch_launch(X, w_blocks, Y, n_tokens, input_dim / 256, output_dim,
                                           (hipStream_t)stream);
@@ -322,7 +400,7 @@ int q4k_matmul_tiled_shaped(const float *X, const uint8_t *w_tiled, int64_t n_to
   int rc = check_q4k(X, w_tiled, Y, n_tokens, input_dim, output_dim);
   if (rc) return rc;
   if (form == 0) return q4k_matmul_tiled(X, w_tiled, n_tokens, input_dim, output_dim, Y, stream);
-  if (!valid_matmul_form(form, n_tokens) || form == 65) return Q4K_EINVAL_DIM;
+  if (!valid_matmul_form(form, n_tokens) || form == 65 || form >= 128) return Q4K_EINVAL_DIM;
   hipError_t e = form == 1
       ? q4k::gemv_tiled_batch_launch(X, w_tiled, Y, n_tokens, input_dim / 256, output_dim,
                                      (hipStream_t)stream)

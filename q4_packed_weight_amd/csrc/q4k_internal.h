@@ -83,6 +83,29 @@ hipError_t prefill_direct_launch(const float *X, const uint8_t *w, int64_t M, in
 hipError_t prefill_staged_tiled_launch(const float *X, const uint8_t *wt, int64_t M, int64_t K,
                                        int64_t N, float *Y, hipStream_t stream, int rows = 0);
 
+// The 128-row x 32-token prefill with input_dim split into S ranges across
+// workgroups (q4k_prefill_splitk.hip).  With S > 1 it needs a workspace of
+// workspace_bytes: kSplitkCounterBytes of counters, zero before the first
+// call (every call leaves them zero again), then one partial tile per
+// (output tile, range).  Calls sharing a workspace must not overlap in time.
+constexpr int kSplitkMaxRanges = 8;
+constexpr int64_t kSplitkCounterBytes = 1024;  // S > 1 only below 256 output tiles
+// below 256 tiles, at most 8 ranges of 16 KiB partial tiles each
+constexpr int64_t kSplitkWorkspaceBytes = kSplitkCounterBytes + 255 * 8 * 16384;
+struct SplitkPlan {
+  int64_t n_rt = 0, n_tt = 0;  // 128-row and 32-token tiles
+  int S = 1;                   // ranges of input_dim
+  int64_t counter_bytes = 0;   // counters at the start of the workspace
+  int64_t workspace_bytes = 0; // 0 when S == 1
+};
+// ranges: S itself (clamped to 1 .. min(8, nb/2), and 1 from 256 tiles on);
+// 0 = the library's choice.
+SplitkPlan splitk_plan(int64_t M, int64_t K, int64_t N, int ranges = 0);
+bool splitk_fits(int64_t M, int64_t K, int64_t N);
+hipError_t prefill_splitk_launch(const float *X, const uint8_t *w, int64_t M, int64_t K,
+                                 int64_t N, float *Y, void *workspace, int64_t workspace_bytes,
+                                 hipStream_t stream, int ranges = 0);
+
 // 1 <= M <= 8 tokens on the matrix cores (q4k_gemv_batch.hip); X is
 // [M][nb*256], Y is [M][N].
 hipError_t gemv_batch_launch(const float *X, const uint8_t *w, float *Y, int64_t M, int64_t nb,

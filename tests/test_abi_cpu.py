@@ -160,14 +160,14 @@ def test_ternary_matmul_rejects_bad_args(lib):
 
 
 def test_matmul_shaped_rejects_bad_forms(lib):
-    for form in (2, 8, 48, 128, -16):
+    for form in (2, 8, 48, 137, -16):
         assert lib.q4k_matmul_shaped(GOOD, GOOD2, 16, 256, 64, GOOD3, None, form) == -1
     assert lib.q4k_matmul_shaped(GOOD, GOOD2, 9, 256, 64, GOOD3, None, 1) == -1  # > 8 tokens
     assert lib.q4k_matmul_tiled_shaped(GOOD, GOOD2, 9, 256, 64, GOOD3, None, 1) == -1
     assert lib.q4k_matmul_shaped(GOOD, GOOD2, 16, 255, 64, GOOD3, None, 16) == -1
     assert lib.q4k_matmul_shaped(None, GOOD2, 16, 256, 64, GOOD3, None, 16) == -2
     assert lib.q4k_matmul_shaped(ODD, GOOD2, 16, 256, 64, GOOD3, None, 16) == -3
-    for form in (2, 8, 48, 65, 128, -16):
+    for form in (2, 8, 48, 65, 128, 131, -16):
         assert lib.q4k_matmul_tiled_shaped(GOOD, GOOD2, 16, 256, 64, GOOD3, None, form) == -1
     assert lib.q4k_matmul_tiled_shaped(GOOD, ODD, 16, 256, 64, GOOD3, None, 32) == -3
 

@@ -84,3 +84,17 @@ def test_matmul_few_tokens_graph_replays(M):
     binding.q4k_matmul(X, w, M, K, N, Y)
     eager = host(Y).copy()
     _replays_match(lambda: binding.q4k_matmul(X, w, M, K, N, Y), Y, eager, exact=True)
+
+
+@pytest.mark.parametrize("form", [128, 136])
+def test_matmul_split_graph_replays(form):
+    """The split tiles (input_dim ranges added through the library's
+    workspace, arrival counters left at zero by every call): replays match
+    the eager result bit for bit."""
+    M, K, N = 48, 4096, 640
+    w = dev(synth.q4k_weights(N, K, config=45))
+    X = dev(synth.activations(K, n_tokens=M, config=45))
+    Y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    binding.q4k_matmul_shaped(X, w, M, K, N, Y, form)
+    eager = host(Y).copy()
+    _replays_match(lambda: binding.q4k_matmul_shaped(X, w, M, K, N, Y, form), Y, eager, exact=True)

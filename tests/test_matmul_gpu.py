@@ -118,11 +118,12 @@ def test_batch_token_counts(oracle_lib, M):
     assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"M={M}")
 
 
-@pytest.mark.parametrize("M", [2, 3, 4, 5, 7, 8, 9, 12, 15, 16])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 7, 8, 9, 12, 15, 16, 17, 24, 32, 33])
 def test_automatic_choice_token_counts(oracle_lib, M):
-    """The automatic choice around the hand-over between the batched form
-    and the prefill tiles."""
-    for K, N in ((4096, 300), (14336, 64)):
+    """The automatic choice around the hand-overs between the batched form,
+    the prefill tiles and the split tiles (output_dim above 4096 and
+    input_dim from 8192 move the last hand-over)."""
+    for K, N in ((4096, 300), (14336, 64), (2048, 4200), (8192, 130)):
         w = synth.q4k_weights(N, K, config=53, copy=M)
         X = synth.activations(K, n_tokens=M, config=53, copy=M)
         Y = run(X, w, M, K, N)
@@ -190,8 +191,10 @@ def run_rows(X, w, M, K, N, rows):
 
 
 # 65: the 64-row tiles whose waves own whole super-blocks (activations
-# loaded straight into MFMA operand registers)
-PREFILL_FORMS = [16, 32, 64, 65]
+# loaded straight into MFMA operand registers); 128: the 128-row x 32-token
+# tiles with input_dim split across workgroups (the shapes below give 1 to 8
+# ranges, odd range lengths, a single super-block and ragged rows and tokens)
+PREFILL_FORMS = [16, 32, 64, 65, 128]
 
 
 @pytest.mark.parametrize("rows", PREFILL_FORMS)
@@ -288,7 +291,7 @@ def test_matmul_wide_range_full_config(oracle_lib):
     assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what="64x4096x4096")
 
 
-@pytest.mark.parametrize("rows", [64, 65])
+@pytest.mark.parametrize("rows", [64, 65, 128])
 def test_prefill_full_config_every_form(oracle_lib, rows):
     """64 x 4096 x 4096 on each 64-row prefill kernel, every output."""
     M, K, N = 64, 4096, 4096
@@ -296,3 +299,35 @@ def test_prefill_full_config_every_form(oracle_lib, rows):
     X = synth.activations(K, n_tokens=M, config=synth.C4_PREFILL)
     Y = run_rows(X, w, M, K, N, rows)
     assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"form {rows}")
+
+
+def test_split_input_dim_same_bits_and_growing_workspace(oracle_lib):
+    """Form 128 adds the ranges' partial tiles in range order whichever
+    workgroup arrives last, so repeated calls give the same bits; shapes
+    that need more workspace than the last one (the library grows it
+    between calls) and smaller ones after them stay correct."""
+    shapes = [(33, 1280, 130), (64, 4096, 4096), (9, 14336, 40), (64, 4096, 64), (48, 2304, 129)]
+    for M, K, N in shapes:
+        w = synth.q4k_weights(N, K, config=57, copy=M)
+        X = synth.activations(K, n_tokens=M, config=57, copy=N)
+        Y1 = run_rows(X, w, M, K, N, 128)
+        Y2 = run_rows(X, w, M, K, N, 128)
+        assert np.array_equal(Y1, Y2), f"{M}x{K}x{N}"
+        if M * K * N <= 64 * 4096 * 64:
+            assert_parity(Y1, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True,
+                          what=f"{M}x{K}x{N}")
+        else:
+            for t in (0, M - 1):
+                ref = oracle_lib.q4k_matmul_part(X, w, M, K, N, (t, t + 1), (0, N))[t]
+                assert_parity(Y1[t], ref, what=f"{M}x{K}x{N} token {t}")
+
+
+@pytest.mark.parametrize("S", range(1, 9))
+def test_split_every_range_count(oracle_lib, S):
+    """Forms 129 .. 136 fix the number of input_dim ranges (16 super-blocks:
+    ranges of 2 to 16, some of odd length)."""
+    M, K, N = 40, 4096, 200
+    w = synth.q4k_weights(N, K, config=58, copy=S)
+    X = synth.activations(K, n_tokens=M, config=58, copy=S)
+    Y = run_rows(X, w, M, K, N, 128 + S)
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"S={S}")
