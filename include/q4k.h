@@ -32,6 +32,7 @@ extern "C" {
 #define Q4K_ENULL (-2)      /* a required pointer is NULL */
 #define Q4K_EALIGN (-3)     /* a pointer is not 16-byte aligned where required */
 #define Q4K_EHIP (-4)       /* the HIP runtime reported an error (see q4k_strerror) */
+#define Q4K_ESCRATCH (-5)   /* q4k_matmul_noalloc: the call needs more than its fixed scratch */
 
 /*
  * Q4_K weight format (block_q4_K, 256 weights in 144 bytes), as the Q4_K
@@ -381,6 +382,25 @@ int q4k_matmul_tiled(const float *X, const uint8_t *w_tiled, int64_t n_tokens,
 int q4k_gemv_tiled_shaped(const float *x, const uint8_t *w_tiled, int64_t input_dim,
                           int64_t output_dim, float *y, void *stream, int waves,
                           int row_groups, int depth);
+
+/*
+ * q4k_matmul_noalloc -- q4k_matmul for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, kernels, results and
+ * error behaviour as q4k_matmul, except that the split tiles' counters and
+ * partial tiles live in a fixed scratch array reserved with the library's
+ * code object (4 MiB + 1 KiB per GPU, held until the process ends) instead
+ * of the library's allocated workspace: the call performs no allocation of
+ * any kind.  A call whose tiles would need more scratch than that returns
+ * Q4K_ESCRATCH and launches nothing (the library's own choice of input_dim
+ * ranges always fits: at most 256 partial tiles of 16 KiB).  Every call on
+ * a GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (different streams, concurrent graphs) race and must be ordered by the
+ * caller.  The counters in it start at zero and every call leaves them at
+ * zero.
+ */
+int q4k_matmul_noalloc(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
+                       int64_t input_dim, int64_t output_dim, float *Y, void *stream);
 
 /*
  * q4k_matmul_shaped -- q4k_matmul with its kernel forced, for sweeps and

@@ -18,12 +18,14 @@ Q4K_EINVAL_DIM = -1
 Q4K_ENULL = -2
 Q4K_EALIGN = -3
 Q4K_EHIP = -4
+Q4K_ESCRATCH = -5
 
 EXPORTED = (
     "q4k_gemv", "q4k_matmul", "ternary_gemv_codes", "ternary_gemv", "ternary_matmul",
     "q4k_gemv_shaped", "q4_0_gemv", "q4_0_gemv_shaped", "q6k_gemv", "q6k_gemv_shaped",
     "q4k_tiled_size", "q4k_relayout_tiled", "q4k_gemv_tiled", "q4k_gemv_tiled_shaped",
     "q4k_matmul_tiled", "q4k_matmul_shaped", "q4k_matmul_tiled_shaped", "ternary_matmul_shaped",
+    "q4k_matmul_noalloc",
     "q4k_strerror",
     "q4k_bench_empty", "q4k_bench_delay", "q4k_bench_stream_read", "q4k_bench_copy",
 )
@@ -53,6 +55,7 @@ def lib():
     sig = {
         "q4k_gemv": [P, P, I64, I64, P, P],
         "q4k_matmul": [P, P, I64, I64, I64, P, P],
+        "q4k_matmul_noalloc": [P, P, I64, I64, I64, P, P],
         "ternary_gemv_codes": [P, P, I64, I64, P, P],
         "ternary_gemv": [P, P, F, I64, I64, P, P],
         "ternary_matmul": [P, P, F, I64, I64, I64, P, P],
@@ -156,6 +159,17 @@ def q4k_matmul(X, w_blocks, n_tokens, input_dim, output_dim, Y, stream=None):
     _expect(Y, torch.float32, "Y", M * N if ok else 0)
     _check(lib().q4k_matmul(_ptr(X), _ptr(w_blocks), int(n_tokens), int(input_dim),
                             int(output_dim), _ptr(Y), _stream(stream)), "q4k_matmul")
+    return Y
+
+
+def q4k_matmul_noalloc(X, w_blocks, n_tokens, input_dim, output_dim, Y, stream=None):
+    M, K, N = int(n_tokens), int(input_dim), int(output_dim)
+    ok = _pos(M, K, N)
+    _expect(X, torch.float32, "X", M * K if ok else 0)
+    _expect(w_blocks, torch.uint8, "w_blocks", _q4k_need(K, N) if ok else 0)
+    _expect(Y, torch.float32, "Y", M * N if ok else 0)
+    _check(lib().q4k_matmul_noalloc(_ptr(X), _ptr(w_blocks), M, K, N, _ptr(Y), _stream(stream)),
+           "q4k_matmul_noalloc")
     return Y
 
 

@@ -88,6 +88,51 @@ hipError_t device_workspace(hipStream_t stream, void **out) {
   return hipSuccess;
 }
 
+// Scratch of q4k_matmul_noalloc (for callers that cannot allocate): the
+// split tiles' counters and up to 256 partial tiles in device memory that
+// comes with the code object, one copy per GPU.  Host code uses the address
+// hipGetSymbolAddress gives on each device, never the array's name.
+constexpr int64_t kNoAllocScratchBytes = q4k::kSplitkCounterBytes + 256 * 16384;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+__global__ void zero_words_kernel(uint32_t *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+struct DeviceScratch {
+  int device;
+  void *ptr;
+};
+std::mutex g_scratch_mutex;
+std::vector<DeviceScratch> g_scratch;
+
+// This device's copy of `scratch`, looked up on the first call on the
+// device; that call also zeroes the counters with a kernel on its stream
+// (capturable, unlike a memset; every later call leaves them zero).
+hipError_t device_scratch(hipStream_t stream, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  for (const auto &s : g_scratch)
+    if (s.device == dev) {
+      *out = s.ptr;
+      return hipSuccess;
+    }
+  void *p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  const int words = (int)(q4k::kSplitkCounterBytes / 4);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                     static_cast<uint32_t *>(p), words);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  g_scratch.push_back(DeviceScratch{dev, p});
+  *out = p;
+  return hipSuccess;
+}
+
 // The split-K prefill on the library's workspace for this device.
 int matmul_splitk(const float *X, const uint8_t *w, int64_t M, int64_t K, int64_t N, float *Y,
                   void *stream, int ranges = 0) {
@@ -267,6 +312,30 @@ int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
   return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_matmul launch");
 }
 
+int q4k_matmul_noalloc(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
+                       int64_t input_dim, int64_t output_dim, float *Y, void *stream) {
+  int rc = check_q4k(X, w_blocks, Y, n_tokens, input_dim, output_dim);
+  if (rc) return rc;
+  // every other kernel q4k_matmul may pick uses no scratch and allocates nothing
+  if (!use_splitk(n_tokens, input_dim, output_dim))
+    return q4k_matmul(X, w_blocks, n_tokens, input_dim, output_dim, Y, stream);
+  const q4k::SplitkPlan p = q4k::splitk_plan(n_tokens, input_dim, output_dim);
+  if (p.workspace_bytes > kNoAllocScratchBytes) {
+    snprintf(g_hip_detail, sizeof g_hip_detail,
+             "q4k_matmul_noalloc: the split tiles need %lld bytes of scratch, more than the "
+             "%lld reserved", (long long)p.workspace_bytes, (long long)kNoAllocScratchBytes);
+    return Q4K_ESCRATCH;
+  }
+  void *ws = nullptr;
+  if (p.workspace_bytes > 0) {
+    hipError_t e = device_scratch((hipStream_t)stream, &ws);
+    if (e != hipSuccess) return hip_fail(e, "q4k_matmul_noalloc scratch");
+  }
+  hipError_t e = q4k::prefill_splitk_launch(X, w_blocks, n_tokens, input_dim, output_dim, Y, ws,
+                                            kNoAllocScratchBytes, (hipStream_t)stream);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_matmul_noalloc launch");
+}
+
 int ternary_gemv_codes(const float *x, const uint8_t *codes, int64_t input_dim,
                        int64_t output_dim, float *y, void *stream) {
   int rc = check_ternary(x, codes, y, input_dim, output_dim);
@@ -436,6 +505,9 @@ const char *q4k_strerror(int code) {
     case Q4K_ENULL: return "a required pointer is NULL";
     case Q4K_EALIGN: return "x and the Q4_K, Q4_0 or Q6_K blocks must be 16-byte aligned";
     case Q4K_EHIP: return g_hip_detail[0] ? g_hip_detail : "HIP runtime error";
+    case Q4K_ESCRATCH:
+      return g_hip_detail[0] ? g_hip_detail
+                             : "q4k_matmul_noalloc: the call needs more than its fixed scratch";
     default: return "unknown error code";
   }
 }

@@ -245,3 +245,12 @@ def test_bench_helpers_validate(lib):
     assert lib.q4k_bench_copy(GOOD, None, 160, None) == -2
     assert lib.q4k_bench_delay(-1, None) == -1
     assert lib.q4k_bench_delay(200000000, None) == -1
+
+
+def test_matmul_noalloc_rejects_bad_arguments_before_launching(lib):
+    """The no-allocation form validates like q4k_matmul, before any HIP call."""
+    assert lib.q4k_matmul_noalloc(GOOD, GOOD2, 16, 255, 64, GOOD3, None) == -1
+    assert lib.q4k_matmul_noalloc(GOOD, GOOD2, 0, 256, 64, GOOD3, None) == -1
+    assert lib.q4k_matmul_noalloc(None, GOOD2, 16, 256, 64, GOOD3, None) == -2
+    assert lib.q4k_matmul_noalloc(ODD, GOOD2, 16, 256, 64, GOOD3, None) == -3
+    assert b"scratch" in lib.q4k_strerror(-5)
