@@ -576,7 +576,8 @@ def cpu_baseline(wl, seconds):
             "host_cpus_visible": os.cpu_count()}
 
 
-TRAFFIC_FILES = {"c2": "q4k_gemv_4096x4096_b1.traffic.json",
+TRAFFIC_FILES = {"c1": "q4k_gemv_1024x1024_b1.traffic.json",
+                 "c2": "q4k_gemv_4096x4096_b1.traffic.json",
                  "c3": "q4k_gemv_ffn_4096x14336_pair.traffic.json",
                  "c4": "q4k_prefill_64x4096x4096.traffic.json",
                  "n1": "q4k_matmul_4x4096x4096.traffic.json",
