@@ -39,8 +39,10 @@
 //   - one 16x16x16 MFMA per (row tile, token tile) gives sum_s m_s * (sum of
 //     x over s) from 32*m and the sums' images;
 //   - 2^e * (d * tile - dmin * min tile) goes into the running result.
-// The images are double-buffered, one barrier per step; the next step's
-// weights and activations are loaded before this step's MFMAs.
+// The images are double-buffered, one barrier per step.  Activations are
+// loaded two steps ahead and weights one step ahead, and the next step's
+// activations are split between this step's MFMAs (sub-block t alongside
+// MFMA t), so that a wave's VALU and matrix-core work overlap.
 //
 // The MFMA contraction order.  A lane (row i, lane group g) holds 32 qs
 // bytes of its row: [16g, 16g+16) and [64+16g, 64+16g+16).  MFMA t = 2dp+n
@@ -51,9 +53,10 @@
 // at those positions, in the operand order of the codes ((0,2), (1,3), ...).
 //
 // End: the halves' results are added (half 0 + half 1), then with S = 1 the
-// tile is stored; with S > 1 it is stored to a workspace slot, and the
-// workgroup that finds itself the S-th arrival at the tile's counter
-// (agent-scope release/acquire) adds the S slots in range order, stores Y
+// tile is stored; with S > 1 it is stored to a workspace slot with the
+// agent-coherent cache policy and, once those stores are complete, counted
+// at the tile's counter; the workgroup that finds itself the S-th arrival
+// reads the S slots back (same policy), adds them in range order, stores Y
 // and resets the counter to zero, so every output has one writer and the
 // same bits whatever the arrival order.
 #include <type_traits>

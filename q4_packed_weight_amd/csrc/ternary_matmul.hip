@@ -49,6 +49,13 @@ constexpr int XROW = 128 + 4;
 constexpr int CROW = TR_CB / 4 + 2;
 constexpr int X_PER_THREAD = TR_TOK / 2;                          // 8
 
+// max(m, |a|, |b|) for m >= 0: one v_maximum3_f32 with absolute-value
+// modifiers (the IEEE maximum needs no NaN quieting of loaded values)
+__device__ __forceinline__ float absmax3(float m, float a, float b) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(a)),
+                                       __builtin_fabsf(b));
+}
+
 // The A operand from 16 bits of codes (8 fields): fields (0,2), (1,3) of the
 // low byte, then (4,6), (5,7) of the high byte, as the fp16 codes u - 1.
 // hi64 = 0x64006400 held in a vector register (vgpr_const), so that each
@@ -118,8 +125,10 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
       make_rsrc(X + (int64_t)tok0 * K, (int64_t)(M - tok0) * K * 4);
 
   // code chunk q = t + 256*m + ...: row q / 16, chunk q % 16 of the row's
-  // 256 stage bytes; activations: float4 i of thread tid is token
-  // 2i + (tid >= 256), positions 4t .. 4t+3 of the stage.
+  // 256 stage bytes; activations: wave w stages block w % 4 of the stage for
+  // the tokens of parity w / 4, lane (token 2 (lane / 8) + w / 4, column
+  // j = lane % 8) taking positions 32c + 4j .. +3 of the block (c = 0..7):
+  // a token's 8 lanes read whole 128-byte lines and hold its whole block.
   uint4 cv[C_PER_THREAD];
   float4 xv[X_PER_THREAD];
   int coff[C_PER_THREAD];
@@ -129,38 +138,45 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
     coff[m] = (q >> 4) * row_bytes + 16 * (q & 15);
   }
   const int tok_lo = tid >> 8;
+  const int xb = t >> 6;                     // block of the stage this wave stages
+  const int xj = lane & 7;
+  const int xtok = 2 * (lane >> 3) + tok_lo;  // this lane's token
+  const int xpos = 256 * xb + 4 * xj;         // + 32c: its positions within the stage
   auto load_stage = [&](int st) {
     // positions past K (a ragged last stage) read as zeros: their offsets
     // are moved past the end of the view, since the bytes there would be
     // the next token's activations
-    const bool in_k = st * TR_STAGE + 4 * t < K;
 #pragma unroll
-    for (int i = 0; i < X_PER_THREAD; ++i)
-      xv[i] = load_buf_f4(xr, in_k ? 16 * t + 4 * K * (2 * i + tok_lo) : 0x7FFFFFF0, 4096 * st);
+    for (int c = 0; c < X_PER_THREAD; ++c) {
+      const bool in_k = st * TR_STAGE + xpos + 32 * c < K;
+      xv[c] = load_buf_f4(xr, in_k ? 4 * K * xtok + 4 * (xpos + 32 * c) : 0x7FFFFFF0, 4096 * st);
+    }
 #pragma unroll
     for (int m = 0; m < C_PER_THREAD; ++m)
       if (c_loader) cv[m] = __builtin_bit_cast(uint4, load_buf_f4(cr, coff[m], TR_CB * st));
   };
   auto stage_to_lds = [&]() {
-    // this wave stages block xb of the tokens of parity tok_lo: the block's
-    // largest |x| is a maximum over the wave
-    const int xb = t >> 6;
+    // the token's block maximum: a chain over the lane's 32 values, then a
+    // maximum over its 8 lanes
+    float mx0 = 0.f, mx1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < X_PER_THREAD; ++i) {
-      const float4 v0 = xv[i];
-      const float mx = wave_max_nonneg_v(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
-      const int e = __builtin_amdgcn_frexp_expf(mx) - 15;  // |x| * 2^-e < 2^15
-      const float4 v = make_float4(__builtin_ldexpf(v0.x, -e), __builtin_ldexpf(v0.y, -e),
-                                   __builtin_ldexpf(v0.z, -e), __builtin_ldexpf(v0.w, -e));
-      half2_t h02, h13;
-      h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
-      h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
-      const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
-      const int tok = 2 * i + tok_lo;
-      if (lane == 0) xe[xb][tok] = e;
-      *reinterpret_cast<uint2 *>(&xh[xb][tok][2 * lane]) = make_uint2(hw02, hw13);
-      *reinterpret_cast<uint2 *>(&xl[xb][tok][2 * lane]) =
-          make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
+    for (int c = 0; c < X_PER_THREAD; c += 2) {
+      mx0 = absmax3(absmax3(mx0, xv[c].x, xv[c].y), xv[c].z, xv[c].w);
+      mx1 = absmax3(absmax3(mx1, xv[c + 1].x, xv[c + 1].y), xv[c + 1].z, xv[c + 1].w);
+    }
+    const float mx = group_max_nonneg<8>(fmaxf(mx0, mx1));
+    // |x| * 2^-e < 2^15; e >= -126 keeps both powers of two normal floats
+    int e = __builtin_amdgcn_frexp_expf(mx) - 15;
+    e = e < -126 ? -126 : e;
+    const float sdown = __builtin_ldexpf(1.0f, -e);
+    if (xj == 0) xe[xb][xtok] = e;
+#pragma unroll
+    for (int c = 0; c < X_PER_THREAD; ++c) {
+      uint2 h, l;
+      split_pair(xv[c].x, xv[c].z, sdown, h.x, l.x);
+      split_pair(xv[c].y, xv[c].w, sdown, h.y, l.y);
+      *reinterpret_cast<uint2 *>(&xh[xb][xtok][2 * (xj + 8 * c)]) = h;
+      *reinterpret_cast<uint2 *>(&xl[xb][xtok][2 * (xj + 8 * c)]) = l;
     }
     if (c_loader) {
 #pragma unroll
