@@ -184,6 +184,13 @@ __device__ __forceinline__ float4 load_buf_f4(__amdgpu_buffer_rsrc_t r, int off,
 
 __device__ __forceinline__ float sum4(float4 v) { return (v.x + v.y) + (v.z + v.w); }
 
+// max(m, |a|, |b|) for m >= 0: one v_maximum3_f32 with absolute-value
+// modifiers (the IEEE maximum needs no NaN quieting of loaded values)
+__device__ __forceinline__ float absmax3(float m, float a, float b) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(a)),
+                                       __builtin_fabsf(b));
+}
+
 // Maximum of non-negative values (NaN included) over aligned groups of
 // `width` lanes, every lane of the group receiving it: the maximum of the bit
 // patterns as unsigned integers is the float maximum, and an integer

@@ -60,13 +60,6 @@ constexpr int PD_TREC = 12;            // header record: 8 scale pairs + 4 dword
 constexpr int PD_RROW = PD_ROWS + 4;   // reduction row pitch (floats)
 static_assert(PD_WCH % 64 == 0, "a super-block of the rows must be whole wave loads");
 
-// max(m, |a|, |b|) for m >= 0: one v_maximum3_f32 with absolute-value
-// modifiers (the IEEE maximum needs no NaN quieting of loaded values)
-__device__ __forceinline__ float absmax3(float m, float a, float b) {
-  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(a)),
-                                       __builtin_fabsf(b));
-}
-
 // 32*m for the two 6-bit mins in bytes 0 and 2 of `v` (bytes 1 and 3 zero),
 // as an fp16 pair: v | 0x6400 in each half is 1024 + m, and
 // 32 * (1024 + m) - 32768 is exact in fp16.

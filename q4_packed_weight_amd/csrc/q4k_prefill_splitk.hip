@@ -100,13 +100,6 @@ static_assert(SK_LDS <= 160 * 1024, "LDS of one workgroup");
 static_assert(SK_WAVES / 2 * 4 * 64 * 16 + SK_TOK * (SK_ROWS + 4) * 4 <= SK_LDS,
               "the reduction tiles must fit in the image buffers");
 
-// max(m, |a|, |b|) for m >= 0: one v_maximum3_f32 with absolute-value
-// modifiers (the IEEE maximum needs no NaN quieting of loaded values)
-__device__ __forceinline__ float absmax3(float m, float a, float b) {
-  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(a)),
-                                       __builtin_fabsf(b));
-}
-
 // 32*m for the two 6-bit mins in bytes 0 and 2 of `v` (bytes 1 and 3 zero),
 // as an fp16 pair: v | 0x6400 in each half is 1024 + m, and
 // 32 * (1024 + m) - 32768 is exact in fp16.

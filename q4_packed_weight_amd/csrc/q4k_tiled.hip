@@ -537,12 +537,19 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
   const int vhd = 2048 + 16 * r;
   uint4 qs[2][TPW][2], hd[2][TPW];  // [buffer][row group a][qs half]
   float4 xv[8];
-  const int tok_lo = tid >> 8;  // float4 i of this thread: token 2i + tok_lo
+  const int tok_lo = tid >> 8;
+  // activations: wave w stages block w % 4 of the stage for the tokens of
+  // parity w / 4, lane (token 2 (lane / 8) + w / 4, column j = lane % 8)
+  // taking positions 32c + 4j .. +3 of the block (c = 0..7): a token's 8
+  // lanes read whole 128-byte lines and hold its whole block
+  const int xb = t >> 6;
+  const int xj = (t & 63) & 7;
+  const int xtok = 2 * ((t & 63) >> 3) + tok_lo;
+  const int xoff = 4 * K * xtok + 1024 * xb + 16 * xj;
   auto load_stage = [&](int st, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      xv[i] = load_buf_f4(xr, 16 * t + 4 * K * (2 * i + tok_lo), 4096 * st);
+    for (int c = 0; c < 8; ++c) xv[c] = load_buf_f4(xr, xoff + 128 * c, 4096 * st);
     const int b = st * TP_BLKS + bb;
 #pragma unroll
     for (int a = 0; a < TPW; ++a) {
@@ -553,27 +560,29 @@ __global__ __launch_bounds__(64 * TP_WAVES) void q4k_prefill_tiled_kernel(
     }
   };
   auto stage_x = [&]() {
-    // float4 i: token 2i + tok_lo, block t / 64, positions 4 (t % 64) ..;
-    // stored as pairs (0,2) and (1,3): operand order.  As in the canonical
-    // prefill, each token's block is first scaled by the power of two that
-    // puts its largest |x| (a maximum over the wave) into [2^14, 2^15).
-    const int xb = t >> 6, l = t & 63;
+    // As in the canonical prefill, each token's block is first scaled by the
+    // power of two that puts its largest |x| (a chain over the lane's 32
+    // values, then a maximum over its 8 lanes) into [2^14, 2^15); halves
+    // stored as pairs (0,2) and (1,3): operand order.
+    float mx0 = 0.f, mx1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 v0 = xv[i];
-      const float mx = wave_max_nonneg_v(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))));
-      const int e = __builtin_amdgcn_frexp_expf(mx) - 15;  // |x| * 2^-e < 2^15
-      const float4 v = make_float4(__builtin_ldexpf(v0.x, -e), __builtin_ldexpf(v0.y, -e),
-                                   __builtin_ldexpf(v0.z, -e), __builtin_ldexpf(v0.w, -e));
-      half2_t h02, h13;
-      h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
-      h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
-      const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
-      const int tok = 2 * i + tok_lo;
-      if (l == 0) xe[xb][tok] = e;
-      *reinterpret_cast<uint2 *>(&xh[xb][tok][2 * l]) = make_uint2(hw02, hw13);
-      *reinterpret_cast<uint2 *>(&xl[xb][tok][2 * l]) =
-          make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
+    for (int c = 0; c < 8; c += 2) {
+      mx0 = absmax3(absmax3(mx0, xv[c].x, xv[c].y), xv[c].z, xv[c].w);
+      mx1 = absmax3(absmax3(mx1, xv[c + 1].x, xv[c + 1].y), xv[c + 1].z, xv[c + 1].w);
+    }
+    const float mx = group_max_nonneg<8>(fmaxf(mx0, mx1));
+    // |x| * 2^-e < 2^15; e >= -126 keeps both powers of two normal floats
+    int e = __builtin_amdgcn_frexp_expf(mx) - 15;
+    e = e < -126 ? -126 : e;
+    const float sdown = __builtin_ldexpf(1.0f, -e);
+    if (xj == 0) xe[xb][xtok] = e;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint2 h, l;
+      split_pair(xv[c].x, xv[c].z, sdown, h.x, l.x);
+      split_pair(xv[c].y, xv[c].w, sdown, h.y, l.y);
+      *reinterpret_cast<uint2 *>(&xh[xb][xtok][2 * (xj + 8 * c)]) = h;
+      *reinterpret_cast<uint2 *>(&xl[xb][xtok][2 * (xj + 8 * c)]) = l;
     }
   };
 

@@ -49,13 +49,6 @@ constexpr int XROW = 128 + 4;
 constexpr int CROW = TR_CB / 4 + 2;
 constexpr int X_PER_THREAD = TR_TOK / 2;                          // 8
 
-// max(m, |a|, |b|) for m >= 0: one v_maximum3_f32 with absolute-value
-// modifiers (the IEEE maximum needs no NaN quieting of loaded values)
-__device__ __forceinline__ float absmax3(float m, float a, float b) {
-  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, __builtin_fabsf(a)),
-                                       __builtin_fabsf(b));
-}
-
 // The A operand from 16 bits of codes (8 fields): fields (0,2), (1,3) of the
 // low byte, then (4,6), (5,7) of the high byte, as the fp16 codes u - 1.
 // hi64 = 0x64006400 held in a vector register (vgpr_const), so that each
