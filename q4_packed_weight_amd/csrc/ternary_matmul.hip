@@ -20,13 +20,15 @@
 // lose bits of lo to its subnormal range, for any |x| below 2^96).  Wave w takes
 // positions 256*(w%4) .. +255 of the stage for its row tiles.
 //
-// Operands (16x16x32 f16 MFMA; lane (r, g) = (lane % 16, lane / 16)): the A
-// operand is 8 codes of row 16a + r, positions 8g .. 8g+7 of one 32-position
-// step: two code bytes, each spread as b | b << 12 so that masking with
-// 0x00030003 leaves fields (0,2) and, after a shift by 2, (1,3) in the two
-// halves, in the activations' operand order.  Each field u becomes the fp16
-// 1024 + u (bits 0x6400 | u), and a packed subtraction of 1025 leaves the
-// code u - 1 in {-1, 0, 1, 2}, exactly.  (Feeding the raw fields as fp16
+// Operands (16x16x32 f16 MFMA; lane (r, g) = (lane % 16, lane / 16)): MFMA
+// step s = 2 s2 + h of a block takes from lane group g the code dword q =
+// 4 s2 + g of row 16a + r (positions 16q .. 16q+15) and from it the fields
+// of bytes h and h + 2: shifted right by 8h + 2p and masked with 0x00030003,
+// the dword leaves positions 16q + 4h + p and 16q + 8 + 4h + p (p = 0..3) in
+// its two halves, one shift and one AND-OR per pair.  The activations are
+// staged in that operand order.  Each field u becomes the fp16 1024 + u
+// (bits 0x6400 | u), and a packed subtraction of 1025 leaves the code u - 1
+// in {-1, 0, 1, 2}, exactly.  (Feeding the raw fields as fp16
 // subnormals u*2^-24 loses products of the lo halves on the matrix cores.)
 // The MFMA products are exact and the accumulation is fp32: one tile per
 // block, scaled back by the token's power of two into the running sum; the
@@ -49,18 +51,18 @@ constexpr int XROW = 128 + 4;
 constexpr int CROW = TR_CB / 4 + 2;
 constexpr int X_PER_THREAD = TR_TOK / 2;                          // 8
 
-// The A operand from 16 bits of codes (8 fields): fields (0,2), (1,3) of the
-// low byte, then (4,6), (5,7) of the high byte, as the fp16 codes u - 1.
-// hi64 = 0x64006400 held in a vector register (vgpr_const), so that each
+// The A operand from a dword of 16 codes (positions 0..15 of its range):
+// for H = 0 the pairs (p, 8 + p), for H = 1 the pairs (4 + p, 12 + p), p =
+// 0..3 (fields p of bytes H and H + 2), as the fp16 codes u - 1.  hi64 =
+// 0x64006400 held in a vector register (vgpr_const), so that each
 // mask-and-insert is one AND-OR.
-__device__ __forceinline__ half8_t code_operand(uint32_t w16, uint32_t hi64) {
-  const uint32_t t0 = (w16 & 0xFFu) * 0x1001u;         // b0 | b0 << 12
-  const uint32_t t1 = ((w16 >> 8) & 0xFFu) * 0x1001u;  // b1 | b1 << 12
-  uint4 v;
-  v.x = (t0 & 0x00030003u) | hi64;  // fp16 1024 + u in each half
-  v.y = ((t0 >> 2) & 0x00030003u) | hi64;
-  v.z = (t1 & 0x00030003u) | hi64;
-  v.w = ((t1 >> 2) & 0x00030003u) | hi64;
+template <int H>
+__device__ __forceinline__ half8_t code_operand(uint32_t w, uint32_t hi64) {
+  uint4 v;  // fp16 1024 + u in each half
+  v.x = ((w >> (8 * H)) & 0x00030003u) | hi64;
+  v.y = ((w >> (8 * H + 2)) & 0x00030003u) | hi64;
+  v.z = ((w >> (8 * H + 4)) & 0x00030003u) | hi64;
+  v.w = ((w >> (8 * H + 6)) & 0x00030003u) | hi64;
   half8_t a = __builtin_bit_cast(half8_t, v);
   const _Float16 off = (_Float16)1025.0f;
   return a - half8_t{off, off, off, off, off, off, off, off};
@@ -119,9 +121,10 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
 
   // code chunk q = t + 256*m + ...: row q / 16, chunk q % 16 of the row's
   // 256 stage bytes; activations: wave w stages block w % 4 of the stage for
-  // the tokens of parity w / 4, lane (token 2 (lane / 8) + w / 4, column
-  // j = lane % 8) taking positions 32c + 4j .. +3 of the block (c = 0..7):
-  // a token's 8 lanes read whole 128-byte lines and hold its whole block.
+  // the tokens of parity w / 4, lane (token 2 (lane / 8) + w / 4, j = lane %
+  // 8) taking positions P .. P+3 and P+8 .. P+11 of the block, P = 64 s2 +
+  // 16 (j / 2) + 4 (j % 2) (s2 = 0..3): the operand pairs of MFMA step 2 s2
+  // + j % 2, lane group j / 2, and a token's 8 lanes hold its whole block.
   uint4 cv[C_PER_THREAD];
   float4 xv[X_PER_THREAD];
   int coff[C_PER_THREAD];
@@ -133,16 +136,18 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
   const int tok_lo = tid >> 8;
   const int xb = t >> 6;                     // block of the stage this wave stages
   const int xj = lane & 7;
+  const int xg = xj >> 1, xh2 = xj & 1;       // the operand lane group and half it feeds
   const int xtok = 2 * (lane >> 3) + tok_lo;  // this lane's token
-  const int xpos = 256 * xb + 4 * xj;         // + 32c: its positions within the stage
+  const int xpos = 256 * xb + 16 * xg + 4 * xh2;  // + 64 s2 (+ 8): its positions in the stage
   auto load_stage = [&](int st) {
-    // positions past K (a ragged last stage) read as zeros: their offsets
-    // are moved past the end of the view, since the bytes there would be
-    // the next token's activations
+    // positions past K (a ragged last stage, K a multiple of 64) read as
+    // zeros: their offsets are moved past the end of the view, since the
+    // bytes there would be the next token's activations
 #pragma unroll
     for (int c = 0; c < X_PER_THREAD; ++c) {
-      const bool in_k = st * TR_STAGE + xpos + 32 * c < K;
-      xv[c] = load_buf_f4(xr, in_k ? 4 * K * xtok + 4 * (xpos + 32 * c) : 0x7FFFFFF0, 4096 * st);
+      const int pos = xpos + 64 * (c >> 1) + 8 * (c & 1);
+      const bool in_k = st * TR_STAGE + pos < K;
+      xv[c] = load_buf_f4(xr, in_k ? 4 * K * xtok + 4 * pos : 0x7FFFFFF0, 4096 * st);
     }
 #pragma unroll
     for (int m = 0; m < C_PER_THREAD; ++m)
@@ -164,12 +169,16 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
     const float sdown = __builtin_ldexpf(1.0f, -e);
     if (xj == 0) xe[xb][xtok] = e;
 #pragma unroll
-    for (int c = 0; c < X_PER_THREAD; ++c) {
-      uint2 h, l;
-      split_pair(xv[c].x, xv[c].z, sdown, h.x, l.x);
-      split_pair(xv[c].y, xv[c].w, sdown, h.y, l.y);
-      *reinterpret_cast<uint2 *>(&xh[xb][xtok][2 * (xj + 8 * c)]) = h;
-      *reinterpret_cast<uint2 *>(&xl[xb][xtok][2 * (xj + 8 * c)]) = l;
+    for (int s2 = 0; s2 < X_PER_THREAD / 2; ++s2) {
+      const float4 a = xv[2 * s2], b = xv[2 * s2 + 1];  // positions P + p, P + 8 + p
+      uint4 h, l;
+      split_pair(a.x, b.x, sdown, h.x, l.x);
+      split_pair(a.y, b.y, sdown, h.y, l.y);
+      split_pair(a.z, b.z, sdown, h.z, l.z);
+      split_pair(a.w, b.w, sdown, h.w, l.w);
+      const int d = 16 * (2 * s2 + xh2) + 4 * xg;  // step 2 s2 + xh2, lane group xg
+      *reinterpret_cast<uint4 *>(&xh[xb][xtok][d]) = h;
+      *reinterpret_cast<uint4 *>(&xl[xb][xtok][d]) = l;
     }
     if (c_loader) {
 #pragma unroll
@@ -185,9 +194,8 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
   floatx4 acc[TPW];
 #pragma unroll
   for (int a = 0; a < TPW; ++a) acc[a] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // this lane's code bytes for step s of block bb: byte 64*bb + 8*s + 2*g
-  // of its row, i.e. half (g & 1) of dword 16*bb + 2*s + g/2
-  const uint32_t hsh = 16u * (uint32_t)(g & 1);
+  // this lane's codes for step s of block bb: dword 16 bb + 4 (s / 2) + g of
+  // its row in the stage
 
   load_stage(0);
   for (int st = 0; st < n_stages; ++st) {
@@ -210,8 +218,8 @@ __global__ __launch_bounds__(TR_THREADS) void ternary_matmul_kernel(
 #pragma unroll
       for (int a = 0; a < TPW; ++a) {
         const int row = 16 * (rt0 + a) + r;
-        const uint32_t w = ct[row * CROW + 16 * bb + 2 * s + (g >> 1)] >> hsh;
-        const half8_t A = code_operand(w, hi64);
+        const uint32_t w = ct[row * CROW + 16 * bb + 4 * (s >> 1) + g];
+        const half8_t A = (ss & 1) ? code_operand<1>(w, hi64) : code_operand<0>(w, hi64);
         bh[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, bh[a], 0, 0, 0);
         bl[a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, bl[a], 0, 0, 0);
       }
