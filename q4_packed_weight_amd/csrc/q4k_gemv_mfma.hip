@@ -103,15 +103,8 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
 
   uint32_t *wtw = wt[wave];
   auto stage_chunk = [&](const uint4 (&wv)[MV_WPL], const float4 (&xv)[MV_XPL]) {
-#pragma unroll
-    for (int m = 0; m < MV_WPL; ++m) {
-      const int q = lane + 64 * m;
-      if (MV_WCH % 64 != 0 && q >= MV_WCH) break;  // only the last load is partial
-      const int row = q / (9 * MV_CB);
-      uint32_t *dst = &wtw[row * MV_WROW + 4 * (q - row * 9 * MV_CB)];
-      *reinterpret_cast<uint2 *>(dst) = make_uint2(wv[m].x, wv[m].y);
-      *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wv[m].z, wv[m].w);
-    }
+    // the activations first: they were loaded first (and come from L2), so
+    // their split runs while the weight bytes are still arriving
 #pragma unroll
     for (int i = 0; i < MV_XPL; ++i) {
       const float4 v0 = xv[i];
@@ -136,6 +129,15 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
         xse[wave][4 * (sb >> 1) + (sb & 1)] = s;
         xse[wave][4 * (sb >> 1) + 2 + (sb & 1)] = __builtin_bit_cast(float, e);
       }
+    }
+#pragma unroll
+    for (int m = 0; m < MV_WPL; ++m) {
+      const int q = lane + 64 * m;
+      if (MV_WCH % 64 != 0 && q >= MV_WCH) break;  // only the last load is partial
+      const int row = q / (9 * MV_CB);
+      uint32_t *dst = &wtw[row * MV_WROW + 4 * (q - row * 9 * MV_CB)];
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(wv[m].x, wv[m].y);
+      *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wv[m].z, wv[m].w);
     }
   };
 
