@@ -92,15 +92,8 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
 
   uint32_t *wtw = wt[wave];
   auto stage_chunk = [&](const uint4 (&wv)[MB_WPL], const float4 (&xv)[T]) {
-#pragma unroll
-    for (int m = 0; m < MB_WPL; ++m) {
-      const int q = lane + 64 * m;
-      if (MB_WCH % 64 != 0 && q >= MB_WCH) break;  // only the last load is partial
-      const int row = q / 9;
-      uint32_t *dst = &wtw[row * MB_WROW + 4 * (q - 9 * row)];
-      *reinterpret_cast<uint2 *>(dst) = make_uint2(wv[m].x, wv[m].y);
-      *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wv[m].z, wv[m].w);
-    }
+    // the activations first: they were loaded first (and come from L2), so
+    // their split runs while the weight bytes are still arriving
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float4 v0 = xv[t];  // positions 4 lane .. 4 lane + 3
@@ -118,6 +111,15 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
       // sub-block lane / 8: 8 aligned lanes, which all hold the same sum
       xs[wave][t][lane >> 3] = group_sum<8>(sum4(v0));
       xe[wave][t] = e;  // every lane, one value
+    }
+#pragma unroll
+    for (int m = 0; m < MB_WPL; ++m) {
+      const int q = lane + 64 * m;
+      if (MB_WCH % 64 != 0 && q >= MB_WCH) break;  // only the last load is partial
+      const int row = q / 9;
+      uint32_t *dst = &wtw[row * MB_WROW + 4 * (q - 9 * row)];
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(wv[m].x, wv[m].y);
+      *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wv[m].z, wv[m].w);
     }
   };
 
