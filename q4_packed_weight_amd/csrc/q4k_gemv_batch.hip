@@ -10,7 +10,7 @@
 // Every weight byte is read once for all tokens of the call.
 //
 // Layout: a workgroup owns 16 weight rows (the MFMA's column tile); its 8
-// waves split the row's super-blocks and walk them one at a time, loading
+// or 16 waves split the row's super-blocks and walk them one at a time, loading
 // the next one ahead (coalesced 16-byte loads into a wave-private LDS tile).
 // The nibbles enter the MFMA's B operand masked into fp16 subnormals (q *
 // 2^-24 low, 16q * 2^-24 high), or as exact normal codes for very long rows
@@ -25,7 +25,7 @@
 // Lane (n = lane % 16, g = lane / 16) holds D rows 4g .. 4g+3 of row n, i.e.
 // the hi and lo dots of tokens 2g and 2g + 1, and applies all eight
 // sub-block scales of row n to them in fp32 with the lazy-dmin term; at the
-// end the 8 waves are summed in a fixed order (one writer per output).
+// end the waves are summed in a fixed order (one writer per output).
 #include "device_common.h"
 #include "q4k_internal.h"
 
@@ -35,14 +35,20 @@ namespace {
 
 constexpr int kBlockBytes = 144;
 constexpr int MB_ROWS = 16;                      // rows per workgroup
-constexpr int MB_WAVES = 8;
+// Waves per workgroup: 8, or 16 for 2 tokens when the grid fills the 256
+// CUs at most once (four waves per SIMD, so that one wave's LDS and MFMA
+// latencies hide under another's work).  Measured (graph-replayed calls over
+// rotating weights, us/call, 8 / 16 waves): 2x4096x4096 6.18 / 4.95,
+// 2x14336->4096 14.95 / 14.1, but 2x4096->14336 (896 workgroups) 14.6 /
+// 15.5; with 16 waves the 4-token kernel spills registers (4x4096x4096
+// 6.73 / 7.25).
 constexpr int MB_WCH = MB_ROWS * 9;              // 16-byte weight pieces per super-block
 constexpr int MB_WPL = (MB_WCH + 63) / 64;       // weight loads per lane
 constexpr int MB_WROW = 36 + 2;                  // LDS dwords per staged row (+ 8 B)
 
 // T: tokens of the launch, 2, 4 or 8 (rows of X past M read as zeros); NC:
 // exact normal code operands (rows of more than 256 super-blocks)
-template <int T, bool NC>
+template <int T, bool NC, int MB_WAVES>
 __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
     const float *X, const uint8_t *w, float *__restrict__ Y, int M, int nb, int N) {
   // Per wave: the staged weight rows of its super-block, each token's fp16 hi
@@ -66,8 +72,8 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
   const int K = nb * 256;
   const int row_bytes = nb * kBlockBytes;
   // this wave's super-blocks [b_lo, b_hi)
-  const int b_lo = (nb * wave) >> 3;
-  const int n_chunks = ((nb * (wave + 1)) >> 3) - b_lo;
+  const int b_lo = (nb * wave) / MB_WAVES;
+  const int n_chunks = (nb * (wave + 1)) / MB_WAVES - b_lo;
 
   const __amdgpu_buffer_rsrc_t wr =
       make_rsrc(w + (int64_t)row0 * row_bytes, (int64_t)min(N - row0, MB_ROWS) * row_bytes);
@@ -236,23 +242,26 @@ hipError_t gemv_batch_launch(const float *X, const uint8_t *w, float *Y, int64_t
       (int64_t)8 * nb * 1024 + 1024 * nb >= ((int64_t)1 << 31))
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + MB_ROWS - 1) / MB_ROWS));
-  const dim3 block(64 * MB_WAVES);
   const bool nc = nb > kNormalCodesAbove;
-#define Q4K_BATCH_CASE(T_)                                                                 \
-  if (nc)                                                                                  \
-    hipLaunchKernelGGL((q4k_gemv_batch_kernel<T_, true>), grid, block, 0, stream, X, w, Y,  \
-                       (int)M, (int)nb, (int)N);                                           \
-  else                                                                                     \
-    hipLaunchKernelGGL((q4k_gemv_batch_kernel<T_, false>), grid, block, 0, stream, X, w, Y, \
-                       (int)M, (int)nb, (int)N);
+#define Q4K_BATCH_LAUNCH(T_, W_)                                                              \
+  if (nc)                                                                                     \
+    hipLaunchKernelGGL((q4k_gemv_batch_kernel<T_, true, W_>), grid, dim3(64 * W_), 0, stream, \
+                       X, w, Y, (int)M, (int)nb, (int)N);                                     \
+  else                                                                                        \
+    hipLaunchKernelGGL((q4k_gemv_batch_kernel<T_, false, W_>), grid, dim3(64 * W_), 0, stream, \
+                       X, w, Y, (int)M, (int)nb, (int)N);
   if (M <= 2) {
-    Q4K_BATCH_CASE(2)
+    if (grid.x <= 256) {
+      Q4K_BATCH_LAUNCH(2, 16)
+    } else {
+      Q4K_BATCH_LAUNCH(2, 8)
+    }
   } else if (M <= 4) {
-    Q4K_BATCH_CASE(4)
+    Q4K_BATCH_LAUNCH(4, 8)
   } else {
-    Q4K_BATCH_CASE(8)
+    Q4K_BATCH_LAUNCH(8, 8)
   }
-#undef Q4K_BATCH_CASE
+#undef Q4K_BATCH_LAUNCH
   return hipGetLastError();
 }
 
