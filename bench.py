@@ -175,7 +175,7 @@ def make_workload(name, torch, binding, synth):
         wl.copies = copies
         wl.bytes = wbytes + 4 * M * K + 4 * M * N
         wl.flops = 2 * M * K * N
-        wl.kernel = "q4k_gemv_batch_kernel<4, false, 8>"
+        wl.kernel = "q4k_gemv_batch_kernel<4, false, 16>"
         wl.src_files = BATCH_SRC
         wl.config = {"workload": "q4k_matmul 4 tokens x 4096 -> 4096", "tokens": M,
                      "input_dim": K, "output_dim": N, "rotating_copies": copies}

@@ -96,10 +96,9 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
  *   input_dim, output_dim as for q4k_gemv
  *   Y          fp32 [n_tokens, output_dim]
  * Same error behaviour and tolerance as q4k_gemv.  The kernels serving it:
- * M == 1 is q4k_gemv; a few tokens (M <= 2 at any shape, M <= 4 with
- * output_dim <= 4096, M <= 8 with output_dim <= 4096 and input_dim > 12288)
- * run on a batched matrix-core GEMV that reads each weight once for all of
- * them; from 33 tokens (from 17 with output_dim > 4096, from 9 with
+ * M == 1 is q4k_gemv; a few tokens (M <= 2 at any shape, M <= 8 with
+ * output_dim <= 4096) run on a batched matrix-core GEMV that reads each
+ * weight once for all of them; from 33 tokens (from 17 with output_dim > 4096, from 9 with
  * input_dim >= 8192) 128-row x 32-token tiles whose input_dim is split
  * across workgroups when the tiles alone would leave CUs idle; otherwise
  * prefill tiles of 64 rows x 16 tokens (narrowed to 32 or 16 rows when

@@ -246,13 +246,17 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
 // Few tokens run on the batched matrix-core GEMV, one launch of up to 8
 // tokens, where it beats the prefill tiles (at the height prefill_rows
 // picks).  Measured on MI355X (graph-replayed calls over rotating weights,
-// batched / prefill us/call): 4096x4096 with 4 tokens 7.1 / 8.7 and with 5
-// to 8 tokens 9.1-9.2 / 8.7; 14336->4096 with 4 tokens 17.5 / 24.8 and
-// with 5 to 8 tokens 23.2-23.4 / 24.9, while 11008->4096 ties (19.9-20.1 /
-// 19.9-20.0); 4096->8192 with 3 tokens 12.6 / 10.7; 2 tokens win everywhere
-// (4096 -> 14336: 14.6 / 16.8).
+// batched / prefill us/call): with output_dim 4096, 16 waves per workgroup
+// up to 4 tokens, 8 above: 4096x4096 with 2 tokens 4.9 / 10.4, 3-4 tokens
+// 5.9 / 10.4, 5-8 tokens 8.7-8.8 / 10.4; 11008->4096 with 8 tokens 19.2 /
+// 23.7; 14336->4096 with 5-8 tokens 21.7-22.6 / 22.0-22.6; 2048->4096 with 6
+// tokens 4.9 / 6.6; 4096->2048 with 8 tokens 8.3 / 10.2.  Wider outputs (8
+// waves per workgroup) keep the prefill from 3 tokens on (4096->8192 with 3
+// tokens 12.6 / 10.7, 4096->14336 with 4 tokens 22.7 / 15.4); 2 tokens win
+// everywhere (4096->14336: 13.6 / 16.8).
 static bool use_gemv_batch(int64_t M, int64_t K, int64_t N) {
-  return M <= 2 || (M <= 4 && N <= 4096) || (M <= 8 && N <= 4096 && K > 12288);
+  (void)K;
+  return M <= 2 || (M <= 8 && N <= 4096);
 }
 
 // Valid explicit forms of the batched products: 1 = the few-token GEMV

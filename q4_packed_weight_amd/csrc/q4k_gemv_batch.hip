@@ -35,13 +35,12 @@ namespace {
 
 constexpr int kBlockBytes = 144;
 constexpr int MB_ROWS = 16;                      // rows per workgroup
-// Waves per workgroup: 8, or 16 for 2 tokens when the grid fills the 256
-// CUs at most once (four waves per SIMD, so that one wave's LDS and MFMA
+// Waves per workgroup: 8, or 16 for up to 4 tokens when the grid fills the
+// 256 CUs at most once (four waves per SIMD, so that one wave's LDS and MFMA
 // latencies hide under another's work).  Measured (graph-replayed calls over
 // rotating weights, us/call, 8 / 16 waves): 2x4096x4096 6.18 / 4.95,
-// 2x14336->4096 14.95 / 14.1, but 2x4096->14336 (896 workgroups) 14.6 /
-// 15.5; with 16 waves the 4-token kernel spills registers (4x4096x4096
-// 6.73 / 7.25).
+// 2x14336->4096 14.95 / 14.1, 4x4096x4096 6.73 / 5.93, but 2x4096->14336
+// (896 workgroups) 14.6 / 15.5.
 constexpr int MB_WCH = MB_ROWS * 9;              // 16-byte weight pieces per super-block
 constexpr int MB_WPL = (MB_WCH + 63) / 64;       // weight loads per lane
 constexpr int MB_WROW = 36 + 2;                  // LDS dwords per staged row (+ 8 B)
@@ -88,10 +87,13 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
   }
   uint4 wa[MB_WPL], wb[MB_WPL];
   float4 xa[T], xb[T];
-  auto load_chunk = [&](int c, uint4 (&wv)[MB_WPL], float4 (&xv)[T]) {
+  auto load_x = [&](int c, float4 (&xv)[T]) {
     const int b0 = __builtin_amdgcn_readfirstlane(b_lo + c);  // wave-uniform
 #pragma unroll
     for (int t = 0; t < T; ++t) xv[t] = load_buf_f4(xr, t * K * 4 + 16 * lane, 1024 * b0);
+  };
+  auto load_w = [&](int c, uint4 (&wv)[MB_WPL]) {
+    const int b0 = __builtin_amdgcn_readfirstlane(b_lo + c);  // wave-uniform
 #pragma unroll
     for (int m = 0; m < MB_WPL; ++m) wv[m] = load_buf_stream16(wr, woff[m], kBlockBytes * b0);
   };
@@ -147,28 +149,23 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
     const uint32_t sc47 = (h23.y & 0x0F0F0F0Fu) | ((h01.y >> 2) & 0x30303030u);
     const uint32_t mn47 = ((h23.y >> 4) & 0x0F0F0F0Fu) | ((h23.x >> 2) & 0x30303030u);
     const float d = half_lo(h01.x), dmin = half_hi(h01.x);
-    // All operands first, then eight independent MFMAs, then the combine.
-    uint2 qb[4];
-    half8_t alo[4], ahi[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      qb[j] = *reinterpret_cast<const uint2 *>(rowp + 4 + 8 * j + 2 * g);
-      alo[j] = *reinterpret_cast<const half8_t *>(&xa_src[(64 * j + 8 * g) / 2]);
-      ahi[j] = *reinterpret_cast<const half8_t *>(&xa_src[(64 * j + 32 + 8 * g) / 2]);
-    }
+    // Eight independent MFMAs (two per sub-block pair j), then the combine.
     floatx4 dlo[4], dhi[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t s0 = qb[j].x >> 8, s1 = qb[j].y >> 8;
+      const uint2 qbj = *reinterpret_cast<const uint2 *>(rowp + 4 + 8 * j + 2 * g);
+      const half8_t alo = *reinterpret_cast<const half8_t *>(&xa_src[(64 * j + 8 * g) / 2]);
+      const half8_t ahi = *reinterpret_cast<const half8_t *>(&xa_src[(64 * j + 32 + 8 * g) / 2]);
+      const uint32_t s0 = qbj.x >> 8, s1 = qbj.y >> 8;
       uint4 blo, bhi;
-      blo.x = code_operand_pair<NC>(qb[j].x, 0x000F000Fu); blo.y = code_operand_pair<NC>(s0, 0x000F000Fu);
-      blo.z = code_operand_pair<NC>(qb[j].y, 0x000F000Fu); blo.w = code_operand_pair<NC>(s1, 0x000F000Fu);
-      bhi.x = code_operand_pair<NC>(qb[j].x, 0x00F000F0u); bhi.y = code_operand_pair<NC>(s0, 0x00F000F0u);
-      bhi.z = code_operand_pair<NC>(qb[j].y, 0x00F000F0u); bhi.w = code_operand_pair<NC>(s1, 0x00F000F0u);
+      blo.x = code_operand_pair<NC>(qbj.x, 0x000F000Fu); blo.y = code_operand_pair<NC>(s0, 0x000F000Fu);
+      blo.z = code_operand_pair<NC>(qbj.y, 0x000F000Fu); blo.w = code_operand_pair<NC>(s1, 0x000F000Fu);
+      bhi.x = code_operand_pair<NC>(qbj.x, 0x00F000F0u); bhi.y = code_operand_pair<NC>(s0, 0x00F000F0u);
+      bhi.z = code_operand_pair<NC>(qbj.y, 0x00F000F0u); bhi.w = code_operand_pair<NC>(s1, 0x00F000F0u);
       dlo[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-          alo[j], __builtin_bit_cast(half8_t, blo), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          alo, __builtin_bit_cast(half8_t, blo), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       dhi[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-          ahi[j], __builtin_bit_cast(half8_t, bhi), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          ahi, __builtin_bit_cast(half8_t, bhi), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
     }
     // Scaled code dots of this super-block: sub-block 2j (low nibbles, q *
     // 2^-c) weighs sc, sub-block 2j+1 (high nibbles, 16q * 2^-c) sc / 16.
@@ -199,18 +196,38 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
     y1 += __builtin_ldexpf(d * c1, xe[wave][t1] + kCodeShift<NC>) - dmin * z1;
   };
 
+  // With 16 waves the next chunk's activations go to the same registers,
+  // loaded once the current ones are staged (they come from L2): a second
+  // buffer would not fit the 128 registers of a 16-wave lane (from 3
+  // tokens on).
+  constexpr bool XSINGLE = MB_WAVES == 16 && T > 2;
   if (n_chunks > 0) {  // wave-uniform
-    load_chunk(0, wa, xa);
+    load_x(0, xa);
+    load_w(0, wa);
     for (int c = 0;;) {
       const bool more = c + 1 < n_chunks;
-      if (more) load_chunk(c + 1, wb, xb);
+      if (more) {
+        if constexpr (!XSINGLE) load_x(c + 1, xb);
+        load_w(c + 1, wb);
+      }
       stage_chunk(wa, xa);
+      if constexpr (XSINGLE) {
+        if (more) load_x(c + 1, xa);
+      }
       compute_chunk();
       if (!more) break;
       ++c;
       const bool more2 = c + 1 < n_chunks;
-      if (more2) load_chunk(c + 1, wa, xa);
-      stage_chunk(wb, xb);
+      if (more2) {
+        if constexpr (!XSINGLE) load_x(c + 1, xa);
+        load_w(c + 1, wa);
+      }
+      if constexpr (XSINGLE) {
+        stage_chunk(wb, xa);
+        if (more2) load_x(c + 1, xa);
+      } else {
+        stage_chunk(wb, xb);
+      }
       compute_chunk();
       if (!more2) break;
       ++c;
@@ -257,7 +274,11 @@ hipError_t gemv_batch_launch(const float *X, const uint8_t *w, float *Y, int64_t
       Q4K_BATCH_LAUNCH(2, 8)
     }
   } else if (M <= 4) {
-    Q4K_BATCH_LAUNCH(4, 8)
+    if (grid.x <= 256) {
+      Q4K_BATCH_LAUNCH(4, 16)
+    } else {
+      Q4K_BATCH_LAUNCH(4, 8)
+    }
   } else {
     Q4K_BATCH_LAUNCH(8, 8)
   }
