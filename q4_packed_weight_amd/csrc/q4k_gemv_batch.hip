@@ -36,11 +36,13 @@ namespace {
 constexpr int kBlockBytes = 144;
 constexpr int MB_ROWS = 16;                      // rows per workgroup
 // Waves per workgroup: 8, or 16 for up to 4 tokens when the grid fills the
-// 256 CUs at most once (four waves per SIMD, so that one wave's LDS and MFMA
-// latencies hide under another's work).  Measured (graph-replayed calls over
-// rotating weights, us/call, 8 / 16 waves): 2x4096x4096 6.18 / 4.95,
-// 2x14336->4096 14.95 / 14.1, 4x4096x4096 6.73 / 5.93, but 2x4096->14336
-// (896 workgroups) 14.6 / 15.5.
+// 256 CUs at most once and rows hold at least 16 super-blocks (four waves per
+// SIMD, so that one wave's LDS and MFMA latencies hide under another's work).
+// Measured (graph-replayed calls over rotating weights, us/call, 8 / 16
+// waves): 2x4096x4096 6.15 / 4.84, 4x4096x4096 6.85 / 5.84, 4x11008->4096
+// 14.2 / 13.0, 4x14336->4096 17.1 / 17.6 (even within noise), but
+// 2x4096->14336 (896 workgroups) 14.6 / 15.5 and 4x2048->4096 (8
+// super-blocks a row, half the waves idle) 4.02 / 5.00.
 constexpr int MB_WCH = MB_ROWS * 9;              // 16-byte weight pieces per super-block
 constexpr int MB_WPL = (MB_WCH + 63) / 64;       // weight loads per lane
 constexpr int MB_WROW = 36 + 2;                  // LDS dwords per staged row (+ 8 B)
@@ -260,6 +262,7 @@ hipError_t gemv_batch_launch(const float *X, const uint8_t *w, float *Y, int64_t
     return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + MB_ROWS - 1) / MB_ROWS));
   const bool nc = nb > kNormalCodesAbove;
+  const bool wide = grid.x <= 256 && nb >= 16;
 #define Q4K_BATCH_LAUNCH(T_, W_)                                                              \
   if (nc)                                                                                     \
     hipLaunchKernelGGL((q4k_gemv_batch_kernel<T_, true, W_>), grid, dim3(64 * W_), 0, stream, \
@@ -268,13 +271,13 @@ hipError_t gemv_batch_launch(const float *X, const uint8_t *w, float *Y, int64_t
     hipLaunchKernelGGL((q4k_gemv_batch_kernel<T_, false, W_>), grid, dim3(64 * W_), 0, stream, \
                        X, w, Y, (int)M, (int)nb, (int)N);
   if (M <= 2) {
-    if (grid.x <= 256) {
+    if (wide) {
       Q4K_BATCH_LAUNCH(2, 16)
     } else {
       Q4K_BATCH_LAUNCH(2, 8)
     }
   } else if (M <= 4) {
-    if (grid.x <= 256) {
+    if (wide) {
       Q4K_BATCH_LAUNCH(4, 16)
     } else {
       Q4K_BATCH_LAUNCH(4, 8)

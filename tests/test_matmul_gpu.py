@@ -132,23 +132,28 @@ def test_automatic_choice_token_counts(oracle_lib, M):
 
 @pytest.mark.parametrize("M,K,N", [(8, 256, 1), (4, 512, 17), (6, 1280, 129), (8, 14336, 64),
                                    (3, 768, 4097), (8, 2304, 1000), (2, 65536, 40), (7, 1792, 16),
-                                   (2, 1024, 14341)])
+                                   (2, 1024, 14341), (4, 4352, 100), (2, 8448, 33),
+                                   (3, 66048, 20)])
 def test_batch_shapes(oracle_lib, M, K, N):
     """One super-block (7 of 8 waves without work), ragged super-block counts
-    per wave, ragged row tiles, long rows."""
+    per wave, ragged row tiles, long rows; 16-wave workgroups (up to 4
+    tokens, at most 256 workgroups, 16+ super-blocks a row) with 17, 33 and
+    258 super-blocks, the last with exact normal code operands."""
     w = synth.q4k_weights(N, K, config=37, copy=K + N)
     X = synth.activations(K, n_tokens=M, config=37, copy=K + N)
     Y = run_batch(X, w, M, K, N)
     assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"{M}x{K}x{N}")
 
 
-def test_batch_full_size(oracle_lib):
-    """8 tokens x 4096 -> 4096, every output."""
-    M, K, N = 8, 4096, 4096
+@pytest.mark.parametrize("M", [2, 4, 8])
+def test_batch_full_size(oracle_lib, M):
+    """M tokens x 4096 -> 4096, every output (16-wave workgroups for 2 and
+    4 tokens, 8 waves for 8)."""
+    K, N = 4096, 4096
     w = synth.q4k_weights(N, K, config=synth.C2_Q4K_4K)
     X = synth.activations(K, n_tokens=M, config=synth.C2_Q4K_4K)
     Y = run_batch(X, w, M, K, N)
-    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what="8x4096x4096")
+    assert_parity(Y, oracle_lib.q4k_matmul(X, w, M, K, N), rowwise=True, what=f"{M}x4096x4096")
 
 
 @pytest.mark.parametrize("M", [2, 5, 8])
