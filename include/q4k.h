@@ -66,14 +66,18 @@ extern "C" {
  * relative (elementwise against 1e-4*|y| + 1e-4*rms(y)).  |x| should stay
  * above ~1e-30 for full precision (the vector form's codes enter the
  * multiply scaled by 2^-24).
- * Two kernels compute it: a vector form (lanes own 32-byte slabs of a row
- * and walk rows) and a matrix-core form (16x16x32 f16 MFMA over 16 rows x
+ * Three kernels compute it: a vector form (lanes own 32-byte slabs of a row
+ * and walk rows), a matrix-core form (16x16x32 f16 MFMA over 16 rows x
  * one sub-block; each 32-activation sub-block is scaled by a power of two
  * and split into exact fp16 hi and lo halves, which holds for |x| < 2^96,
- * about 7.9e28).  The
- * call picks the matrix-core form when ceil(output_dim/16) is 240..256 and
- * input_dim/256 is 8..24 (where it measured faster on MI355X), else the
- * vector form; q4k_gemv_shaped selects either explicitly.
+ * about 7.9e28) and a persistent matrix-core walk (the same arithmetic;
+ * workgroups walk groups of 16 rows x one super-block, the next ones in
+ * flight).  Where each measured fastest on MI355X, the call picks the walk
+ * for large matrices (output_dim >= 4096 with input_dim >= 8192, or
+ * output_dim >= 11008 with input_dim >= 4096), the matrix-core form when
+ * ceil(output_dim/16) is 240..256 and input_dim/256 is 8..24, else the
+ * vector form; q4k_gemv_shaped and q4k_gemv_walk_shaped select one
+ * explicitly.
  */
 int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
              int64_t output_dim, float *y, void *stream);
@@ -290,6 +294,20 @@ int ternary_matmul_shaped(const float *X, const uint8_t *codes, float scale, int
 int q4k_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                     int64_t output_dim, float *y, void *stream,
                     int rows_per_lane, int k_waves, int workgroup_waves);
+
+/*
+ * q4k_gemv_walk_shaped -- q4k_gemv's product on the persistent matrix-core
+ * walk, with its launch shape: waves per workgroup in {4, 8, 16}, row_groups
+ * (consecutive groups of 16 rows per workgroup) in 1..4, depth (units of 16
+ * rows x one super-block each wave loads ahead) in {2, 4}, with 4 waves
+ * only depth 4 and with 16 waves only depth 2; 0 lets the library choose
+ * that value.  Any other value gives Q4K_EINVAL_DIM.  Arguments, layouts,
+ * range of x and results as for q4k_gemv (within its tolerance for every
+ * shape).
+ */
+int q4k_gemv_walk_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+                         int64_t output_dim, float *y, void *stream, int waves,
+                         int row_groups, int depth);
 
 /*
  * Q4_K tiled block order.  SKaiNET docs, "Eager execution: backends and

@@ -22,7 +22,8 @@ Q4K_ESCRATCH = -5
 
 EXPORTED = (
     "q4k_gemv", "q4k_matmul", "ternary_gemv_codes", "ternary_gemv", "ternary_matmul",
-    "q4k_gemv_shaped", "q4_0_gemv", "q4_0_gemv_shaped", "q6k_gemv", "q6k_gemv_shaped",
+    "q4k_gemv_shaped", "q4k_gemv_walk_shaped", "q4_0_gemv", "q4_0_gemv_shaped", "q6k_gemv",
+    "q6k_gemv_shaped",
     "q4k_tiled_size", "q4k_relayout_tiled", "q4k_gemv_tiled", "q4k_gemv_tiled_shaped",
     "q4k_matmul_tiled", "q4k_matmul_shaped", "q4k_matmul_tiled_shaped", "ternary_matmul_shaped",
     "q4k_matmul_noalloc",
@@ -68,6 +69,7 @@ def lib():
         "q4k_relayout_tiled": [P, I64, I64, P, P],
         "q4k_gemv_tiled": [P, P, I64, I64, P, P],
         "q4k_gemv_tiled_shaped": [P, P, I64, I64, P, P, I, I, I],
+        "q4k_gemv_walk_shaped": [P, P, I64, I64, P, P, I, I, I],
         "q4k_matmul_tiled": [P, P, I64, I64, I64, P, P],
         "q4k_matmul_shaped": [P, P, I64, I64, I64, P, P, I],
         "q4k_matmul_tiled_shaped": [P, P, I64, I64, I64, P, P, I],
@@ -259,6 +261,18 @@ def q4k_matmul_tiled_shaped(X, w_tiled, n_tokens, input_dim, output_dim, Y, form
                                          _stream(stream), int(form)),
            "q4k_matmul_tiled_shaped")
     return Y
+
+
+def q4k_gemv_walk_shaped(x, w_blocks, input_dim, output_dim, y, waves=0, row_groups=0,
+                         depth=0, stream=None):
+    K, N = int(input_dim), int(output_dim)
+    _expect(x, torch.float32, "x", K if _pos(K, N) else 0)
+    _expect(w_blocks, torch.uint8, "w_blocks", _q4k_need(K, N))
+    _expect(y, torch.float32, "y", N if _pos(K, N) else 0)
+    _check(lib().q4k_gemv_walk_shaped(_ptr(x), _ptr(w_blocks), K, N, _ptr(y), _stream(stream),
+                                      int(waves), int(row_groups), int(depth)),
+           "q4k_gemv_walk_shaped")
+    return y
 
 
 def q4k_gemv_tiled_shaped(x, w_tiled, input_dim, output_dim, y, waves=0, row_groups=0,

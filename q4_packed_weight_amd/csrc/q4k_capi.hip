@@ -237,8 +237,27 @@ int q6k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                          s.rows_per_lane < 2 ? s.rows_per_lane : 2, 1, 0);
 }
 
+int q4k_gemv_walk_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
+                         int64_t output_dim, float *y, void *stream, int waves,
+                         int row_groups, int depth) {
+  int rc = check_q4k(x, w_blocks, y, 1, input_dim, output_dim);
+  if (rc) return rc;
+  if (!(waves == 0 || waves == 4 || waves == 8 || waves == 16) || row_groups < 0 ||
+      row_groups > 4 || !(depth == 0 || depth == 2 || depth == 4))
+    return Q4K_EINVAL_DIM;
+  const q4k::WalkShape s = q4k::choose_walk_shape(input_dim / 256, output_dim, waves,
+                                                  row_groups, depth);
+  if ((s.waves == 4 && s.depth != 4) || (s.waves == 16 && s.depth != 2)) return Q4K_EINVAL_DIM;
+  hipError_t e = q4k::gemv_walk_launch(x, w_blocks, y, input_dim / 256, output_dim, s,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4k_gemv_walk launch");
+}
+
 int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
              int64_t output_dim, float *y, void *stream) {
+  if (input_dim > 0 && output_dim > 0 && input_dim % 256 == 0 &&
+      q4k::use_gemv_walk(input_dim / 256, output_dim))
+    return q4k_gemv_walk_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0, 0);
   return q4k_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0,
                          q4k::use_gemv_mfma(input_dim / 256, output_dim) ? 16 : 0);
 }

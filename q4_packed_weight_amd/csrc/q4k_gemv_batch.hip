@@ -57,8 +57,10 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
   // (5,7) of every 8), their sums per sub-block and the token's scaling
   // exponent; then the waves' partial outputs.
   __shared__ __align__(16) uint32_t wt[MB_WAVES][MB_ROWS * MB_WROW];
-  __shared__ __align__(16) uint32_t xh[MB_WAVES][T][128];
-  __shared__ __align__(16) uint32_t xl[MB_WAVES][T][128];
+  // [wave][2t] token t's hi part, [wave][2t + 1] its lo part: rows 4 dwords
+  // apart modulo the banks, so the A rows that lanes of one group read
+  // together sit in different banks
+  __shared__ __align__(16) uint32_t xhl[MB_WAVES][2 * T][128 + 4];
   __shared__ __align__(16) float xs[MB_WAVES][T][8];
   __shared__ int xe[MB_WAVES][T];
   __shared__ float part[MB_WAVES][T][MB_ROWS];
@@ -115,8 +117,8 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
       h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
       h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
       const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
-      *reinterpret_cast<uint2 *>(&xh[wave][t][2 * lane]) = make_uint2(hw02, hw13);
-      *reinterpret_cast<uint2 *>(&xl[wave][t][2 * lane]) =
+      *reinterpret_cast<uint2 *>(&xhl[wave][2 * t][2 * lane]) = make_uint2(hw02, hw13);
+      *reinterpret_cast<uint2 *>(&xhl[wave][2 * t + 1][2 * lane]) =
           make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
       // sub-block lane / 8: 8 aligned lanes, which all hold the same sum
       xs[wave][t][lane >> 3] = group_sum<8>(sum4(v0));
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
   // A operand: row n is token n / 2 (rows past 2T repeat token T - 1 and
   // are never read back), hi part in even rows, lo part in odd rows.
   const int ta = min(n >> 1, T - 1);
-  const uint32_t *xa_src = (n & 1) ? xl[wave][ta] : xh[wave][ta];
+  const uint32_t *xa_src = xhl[wave][2 * ta + (n & 1)];
   // this lane's tokens (D rows 4g, 4g+1 and 4g+2, 4g+3)
   const int t0 = min(2 * g, T - 1), t1 = min(2 * g + 1, T - 1);
   float y0 = 0.f, y1 = 0.f;

@@ -33,6 +33,8 @@
 // (n = lane % 16, g = lane / 16) applies the scales of sub-blocks 2g and
 // 2g+1 of row n; the four lane groups and the four waves are summed at the
 // end, so every output has one writer and a fixed summation order.
+#include <algorithm>
+
 #include "device_common.h"
 #include "q4k_internal.h"
 
@@ -57,8 +59,10 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
   // (positions in operand order: pairs (0,2), (1,3), (4,6), (5,7) of every
   // 8), the chunk's sub-block sums; then the cross-wave partials.
   __shared__ __align__(16) uint32_t wt[MV_WAVES][MV_ROWS * MV_WROW];
-  __shared__ __align__(16) uint32_t xh[MV_WAVES][MV_CB * 128];
-  __shared__ __align__(16) uint32_t xl[MV_WAVES][MV_CB * 128];
+  // [wave][0] the hi part, [wave][1] the lo part: rows 4 dwords apart modulo
+  // the banks, so the even (hi) and odd (lo) A rows that lanes of one group
+  // read together sit in different banks
+  __shared__ __align__(16) uint32_t xhl[MV_WAVES][2][MV_CB * 128 + 4];
   // per sub-block pair p (sub-blocks 2p, 2p+1): their x sums, then their
   // scaling exponents (int bits), read by one lane as one 16-byte word
   __shared__ __align__(16) float xse[MV_WAVES][MV_CB * 16];
@@ -119,8 +123,8 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
       h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
       const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
       const int f = lane + 64 * i;  // float4 index: positions 4f .. 4f+3
-      *reinterpret_cast<uint2 *>(&xh[wave][2 * f]) = make_uint2(hw02, hw13);
-      *reinterpret_cast<uint2 *>(&xl[wave][2 * f]) =
+      *reinterpret_cast<uint2 *>(&xhl[wave][0][2 * f]) = make_uint2(hw02, hw13);
+      *reinterpret_cast<uint2 *>(&xhl[wave][1][2 * f]) =
           make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
       // sub-block f / 8: the 8 float4 of a sub-block sit in 8 aligned lanes
       const float s = group_sum<8>(sum4(v0));
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
   };
 
   // A operand rows: even rows the hi part, odd rows the lo part.
-  const uint32_t *xa_src = (n & 1) ? xl[wave] : xh[wave];
+  const uint32_t *xa_src = xhl[wave][n & 1];
   const int j_mine = g;  // sub-blocks 2g, 2g+1 are scaled by this lane
   const uint32_t sh = (uint32_t)(g & 1) * 16u;
   const bool jhi = g >= 2;
@@ -244,6 +248,280 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
   }
 }
 
+// The persistent walk: the same product for matrices that the form above
+// does not fill the chip with, i.e. long rows (one workgroup's 16 waves
+// would each walk several super-blocks with one loaded ahead) or many rows
+// (more 16-wave workgroups than fit at once).  A W-wave workgroup owns
+// rg_per_wg consecutive groups of 16 rows and walks input_dim in chunks of
+// up to CAP super-blocks.  Wave w takes units w, w + W, w + 2W, ... of a
+// chunk's (row group, super-block) units in row-group-major order and keeps
+// D units loaded ahead in registers (a unit is the 16 x 144 weight bytes of
+// one super-block of the group: three coalesced 16-byte loads per lane,
+// rows of 9 chunks); computing a unit first moves its bytes through the
+// wave's LDS tile into operand order.  The chunk's activations are staged
+// in LDS as fp16 hi and lo in operand order with their sub-block sums and
+// scaling exponents:
+//   - cooperatively (PRIV false), by the whole workgroup before the chunk's
+//     units and behind a barrier, their loads issued before the first tiles';
+//   - per wave (PRIV, when input_dim / 256 is above 16 and within one
+//     chunk, and a multiple of W or the workgroup owns one row group): wave
+//     w then only ever uses super-blocks w, w + W, ..., and stages each on
+//     first use (in the first row group), its activations loaded with the
+//     unit.
+// A wave's partial sums go to LDS whenever its row group changes; the
+// lanes' and waves' partials are summed in a fixed order at the end (one
+// writer per output).
+constexpr int WK_MAX_RG = 4;  // row groups per workgroup
+
+template <int W, int D, int CAP, bool PRIV, bool NC>
+__global__ __launch_bounds__(64 * W) void q4k_gemv_walk_kernel(
+    const float *x, const uint8_t *w, float *__restrict__ y, int nb, int N, int rg_per_wg) {
+  constexpr int XPL = CAP / W;  // activation float4 per thread of a chunk
+  static_assert(XPL * 64 * W == CAP * 64, "a chunk's activations must split evenly");
+  // the hi part, then the lo part 4 dwords further modulo the banks, so the
+  // even (hi) and odd (lo) A rows that lanes of one group read together sit
+  // in different banks
+  __shared__ __align__(16) uint32_t xhl[2 * CAP * 128 + 4];
+  uint32_t *const xh = xhl;
+  uint32_t *const xl = xhl + CAP * 128 + 4;
+  // per sub-block pair p: its two x sums, then its two exponents (int bits)
+  __shared__ __align__(16) float xse[CAP * 16];
+  __shared__ __align__(16) uint32_t wt[W][MV_ROWS * MV_WROW];
+  __shared__ float part[W][WK_MAX_RG][64];
+
+  __builtin_assume(nb >= 1);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;  // B / D column: weight row of the group; A row
+  const int g = lane >> 4;  // lane group: positions 8g .. 8g+7 of a sub-block
+  const int NG = (N + MV_ROWS - 1) / MV_ROWS;
+  const int rg0 = blockIdx.x * rg_per_wg;
+  const int rgn = min(rg_per_wg, NG - rg0);
+  const int row_bytes = nb * kBlockBytes;
+  const int rg_bytes = MV_ROWS * row_bytes;
+
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(
+      w + (int64_t)rg0 * rg_bytes, (int64_t)(N - rg0 * MV_ROWS) * row_bytes);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)nb * 1024);
+  constexpr int kPastEnd = 0x7FFFF000;  // a unit or activation offset that reads zeros
+
+#pragma unroll
+  for (int r = 0; r < WK_MAX_RG; ++r) part[wave][r][lane] = 0.f;
+
+  // weight chunk q of a unit (clamped; the duplicates are never stored) is
+  // chunk q % 9 of row q / 9
+  int woff[MV_WPL];
+#pragma unroll
+  for (int m = 0; m < MV_WPL; ++m) {
+    const int q = min(lane + 64 * m, MV_WCH - 1);
+    const int row = q / 9;
+    woff[m] = row * row_bytes + 16 * (q - 9 * row);
+  }
+  uint4 wq[D][MV_WPL];
+  float4 xq[PRIV ? D : 1];
+
+  // A operand rows: even rows the hi part, odd rows the lo part.
+  const uint32_t *xa_src = (n & 1) ? xl : xh;
+  const uint32_t sh = (uint32_t)(g & 1) * 16u;
+  const bool jhi = g >= 2;
+  uint32_t *wtw = wt[wave];
+
+  // Stage float4 f of a chunk (positions 4f .. 4f+3; its sub-block f / 8
+  // sits in 8 aligned lanes): scale the sub-block by 2^-e so that
+  // |x| * 2^-e < 2^15, split into fp16 hi + lo, store its sum and e.
+  auto stage4 = [&](float4 v0, int f) {
+    float mx = fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w)));
+    mx = group_max_nonneg<8>(mx);
+    const int e = __builtin_amdgcn_frexp_expf(mx) - 15;
+    const float4 v = make_float4(__builtin_ldexpf(v0.x, -e), __builtin_ldexpf(v0.y, -e),
+                                 __builtin_ldexpf(v0.z, -e), __builtin_ldexpf(v0.w, -e));
+    half2_t h02, h13;
+    h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
+    h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
+    const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
+    *reinterpret_cast<uint2 *>(&xh[2 * f]) = make_uint2(hw02, hw13);
+    *reinterpret_cast<uint2 *>(&xl[2 * f]) =
+        make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
+    const float sum = group_sum<8>(sum4(v0));
+    if ((lane & 7) == 0) {
+      const int sb = f >> 3;
+      xse[4 * (sb >> 1) + (sb & 1)] = sum;
+      xse[4 * (sb >> 1) + 2 + (sb & 1)] = __builtin_bit_cast(float, e);
+    }
+  };
+  // the wave reads what its own lanes wrote: LDS executes one wave's
+  // instructions in order; keep the compiler from moving them
+  auto wave_lds_order = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  for (int c0 = 0; c0 < nb; c0 += CAP) {
+    const int nbc = min(CAP, nb - c0);
+    const int U = rgn * nbc;
+    const int T = wave < U ? (U - wave + W - 1) / W : 0;
+    // unit (i, bl): row group i, super-block c0 + bl
+    auto advance = [&](int &i, int &bl) {
+      bl += W;
+      while (bl >= nbc) { bl -= nbc; ++i; }
+    };
+    auto load_unit = [&](int s, int i, int bl, bool valid) {
+      const int off = valid ? i * rg_bytes + (c0 + bl) * kBlockBytes : kPastEnd;
+      if constexpr (PRIV)  // activations of super-block bl, needed in the first row group only
+        xq[s] = load_buf_f4(xr, 16 * lane, valid && i == 0 ? 1024 * bl : kPastEnd);
+#pragma unroll
+      for (int m = 0; m < MV_WPL; ++m) wq[s][m] = load_buf_stream16(wr, woff[m], off);
+    };
+
+    // Cooperative staging loads the chunk's activations first, then the
+    // first D units: staging waits only for the activation loads.
+    float4 xv[PRIV ? 1 : XPL];
+    if constexpr (!PRIV) {
+#pragma unroll
+      for (int r = 0; r < XPL; ++r) xv[r] = load_buf_f4(xr, 16 * (tid + 64 * W * r), 1024 * c0);
+    }
+    int li = 0, lbl = wave;
+    while (lbl >= nbc) { lbl -= nbc; ++li; }
+    int ci = li, cbl = lbl;
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      load_unit(s, li, lbl, s < T);
+      advance(li, lbl);
+    }
+    if constexpr (!PRIV) {
+      if (c0 > 0) __syncthreads();  // the previous chunk's operands are no longer read
+#pragma unroll
+      for (int r = 0; r < XPL; ++r) stage4(xv[r], tid + 64 * W * r);
+      __syncthreads();
+    }
+
+    float acc = 0.f;
+    int acc_i = ci;
+    auto compute = [&](int s, int bl) {
+      if constexpr (PRIV) {
+        if (ci == 0) stage4(xq[s], 64 * bl + lane);  // wave-uniform: first use of bl
+      }
+      // the unit's weight bytes into the wave's tile, read back in operand order
+#pragma unroll
+      for (int m = 0; m < MV_WPL; ++m) {
+        const int q = lane + 64 * m;
+        if (MV_WCH % 64 != 0 && q >= MV_WCH) break;  // only the last load is partial
+        const int row = q / 9;
+        uint32_t *dst = &wtw[row * MV_WROW + 4 * (q - 9 * row)];
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(wq[s][m].x, wq[s][m].y);
+        *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wq[s][m].z, wq[s][m].w);
+      }
+      wave_lds_order();
+      const uint32_t *rowp = &wtw[n * MV_WROW];
+      // header of row n: d, dmin and the scale/min of sub-blocks 2g, 2g+1
+      const uint2 h01 = *reinterpret_cast<const uint2 *>(rowp);
+      const uint2 h23 = *reinterpret_cast<const uint2 *>(rowp + 2);
+      const uint32_t p1 = h01.y >> sh, p2 = h23.x >> sh, t3 = h23.y >> sh;
+      const uint32_t sc_src = jhi ? t3 : p1;
+      const uint32_t m_src = jhi ? (t3 >> 4) : p2;
+      const uint32_t mask_lo = jhi ? 0x0F0Fu : 0x3F3Fu;
+      const uint32_t mask_hi = jhi ? 0x3030u : 0u;
+      const uint32_t scp = (sc_src & mask_lo) | ((p1 >> 2) & mask_hi);
+      const uint32_t mp = (m_src & mask_lo) | ((p2 >> 2) & mask_hi);
+      const float d = half_lo(h01.x), dmin = half_hi(h01.x);
+      const float4 xsp = *reinterpret_cast<const float4 *>(&xse[4 * (4 * bl + g)]);
+      // codes enter as q * 2^-c (low nibbles) and 16q * 2^-c (high), c =
+      // kCodeShift<NC>; the activations as x * 2^-e
+      const float s_lo = __builtin_ldexpf(d * (float)(scp & 0xFFu),
+                                          __builtin_bit_cast(int, xsp.z) + kCodeShift<NC>);
+      const float s_hi = __builtin_ldexpf(d * (float)((scp >> 8) & 0xFFu),
+                                          __builtin_bit_cast(int, xsp.w) + kCodeShift<NC> - 4);
+      acc = __builtin_fmaf(-dmin, __builtin_fmaf((float)(mp & 0xFFu), xsp.x,
+                                                 (float)((mp >> 8) & 0xFFu) * xsp.y), acc);
+      uint2 qb[4];
+      half8_t alo[4], ahi[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qb[j] = *reinterpret_cast<const uint2 *>(rowp + 4 + 8 * j + 2 * g);
+        const int pos = 128 * bl + 32 * j + 4 * g;  // dword of sub-block 2j, positions 8g..
+        alo[j] = *reinterpret_cast<const half8_t *>(&xa_src[pos]);
+        ahi[j] = *reinterpret_cast<const half8_t *>(&xa_src[pos + 16]);
+      }
+      floatx4 dlo[4], dhi[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t s0 = qb[j].x >> 8, s1 = qb[j].y >> 8;
+        uint4 blo, bhi;
+        blo.x = code_operand_pair<NC>(qb[j].x, 0x000F000Fu); blo.y = code_operand_pair<NC>(s0, 0x000F000Fu);
+        blo.z = code_operand_pair<NC>(qb[j].y, 0x000F000Fu); blo.w = code_operand_pair<NC>(s1, 0x000F000Fu);
+        bhi.x = code_operand_pair<NC>(qb[j].x, 0x00F000F0u); bhi.y = code_operand_pair<NC>(s0, 0x00F000F0u);
+        bhi.z = code_operand_pair<NC>(qb[j].y, 0x00F000F0u); bhi.w = code_operand_pair<NC>(s1, 0x00F000F0u);
+        dlo[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            alo[j], __builtin_bit_cast(half8_t, blo), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        dhi[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            ahi[j], __builtin_bit_cast(half8_t, bhi), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      }
+      // D rows 4g (hi part) and 4g + 1 (lo part) of row n; this lane keeps
+      // sub-block pair j = g
+      float t_lo = dlo[0][0] + dlo[0][1], t_hi = dhi[0][0] + dhi[0][1];
+#pragma unroll
+      for (int j = 1; j < 4; ++j) {
+        if (j == g) {
+          t_lo = dlo[j][0] + dlo[j][1];
+          t_hi = dhi[j][0] + dhi[j][1];
+        }
+      }
+      acc = __builtin_fmaf(s_lo, t_lo, __builtin_fmaf(s_hi, t_hi, acc));
+      // the next unit's stores into the tile come after these reads
+      wave_lds_order();
+    };
+
+    for (int t0 = 0; t0 < T; t0 += D) {
+#pragma unroll
+      for (int s = 0; s < D; ++s) {
+        if (t0 + s < T) {  // wave-uniform
+          if (ci != acc_i) {
+            part[wave][acc_i][lane] += acc;
+            acc = 0.f;
+            acc_i = ci;
+          }
+          compute(s, cbl);
+          advance(ci, cbl);
+        }
+        // always issued (zeros past the wave's units): the number of loads
+        // in flight is the same on every path
+        load_unit(s, li, lbl, t0 + s + D < T);
+        advance(li, lbl);
+      }
+    }
+    if (T > 0) part[wave][acc_i][lane] += acc;
+  }
+
+  __syncthreads();
+  if (tid < rgn * MV_ROWS) {
+    const int i = tid >> 4, r = tid & 15;
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < W; ++k)
+      v += (part[k][i][r] + part[k][i][r + 16]) + (part[k][i][r + 32] + part[k][i][r + 48]);
+    const int row = (rg0 + i) * MV_ROWS + r;
+    if (row < N) y[row] = v;
+  }
+}
+
+template <int W, int D, int CAP>
+void launch_walk(const float *x, const uint8_t *w, float *y, int64_t nb, int64_t N, int rg,
+                 hipStream_t stream) {
+  const int64_t NG = (N + MV_ROWS - 1) / MV_ROWS;
+  const dim3 grid((unsigned)((NG + rg - 1) / rg));
+  if (CAP > 16 && nb > 16 && (nb % W == 0 || rg == 1) && nb <= CAP)
+    hipLaunchKernelGGL((q4k_gemv_walk_kernel<W, D, CAP, CAP != 16, false>), grid, dim3(64 * W), 0,
+                       stream, x, w, y, (int)nb, (int)N, rg);
+  else if (CAP > 16 && nb > kNormalCodesAbove)
+    hipLaunchKernelGGL((q4k_gemv_walk_kernel<W, D, CAP, false, CAP != 16>), grid, dim3(64 * W), 0,
+                       stream, x, w, y, (int)nb, (int)N, rg);
+  else
+    hipLaunchKernelGGL((q4k_gemv_walk_kernel<W, D, CAP, false, false>), grid, dim3(64 * W), 0,
+                       stream, x, w, y, (int)nb, (int)N, rg);
+}
+
 }  // namespace
 
 bool use_gemv_mfma(int64_t nb, int64_t N) {
@@ -270,6 +548,55 @@ hipError_t gemv_mfma_launch(const float *x, const uint8_t *w, float *y, int64_t 
     hipLaunchKernelGGL(q4k_gemv_mfma_kernel<false>, dim3((unsigned)grid), dim3(64 * MV_WAVES), 0,
                        stream, x, w, y, (int)nb, (int)N);
   return hipGetLastError();
+}
+
+WalkShape choose_walk_shape(int64_t nb, int64_t N, int waves, int row_groups, int depth) {
+  WalkShape s;
+  const int64_t NG = (N + MV_ROWS - 1) / MV_ROWS;
+  s.row_groups = row_groups ? row_groups
+                            : (int)std::min<int64_t>(WK_MAX_RG, std::max<int64_t>(1, (NG + 255) / 256));
+  s.waves = waves ? waves : 8;
+  s.depth = depth ? depth : (s.waves == 4 ? 4 : 2);
+  return s;
+}
+
+bool use_gemv_walk(int64_t nb, int64_t N) {
+  // Measured (graph-replayed calls over rotating weights, input_dim 2048 to
+  // 28672, output_dim 1024 to 28672; current choice / walk with 8 waves and
+  // 2 units ahead, us/call): the walk wins once the matrix is large,
+  // 4096->14336 10.17 / 9.62, 14336->4096 11.37 / 9.89, 8192->4096 7.02 /
+  // 6.75, 11008->11008 28.3 / 17.6, 28672->28672 123.0 / 98.1, and loses on
+  // small grids (4096x4096 4.40 / 5.27, 14336->2048 7.89 / 8.78, 4096->8192
+  // 6.68 / 6.83).  The offsets its launch forms must fit (four row groups).
+  if ((int64_t)WK_MAX_RG * MV_ROWS * nb * kBlockBytes > 0x7FFF0000 || nb * 1024 > 0x7FFF0000)
+    return false;
+  return (N >= 4096 && nb >= 32) || (N >= 11008 && nb >= 16);
+}
+
+hipError_t gemv_walk_launch(const float *x, const uint8_t *w, float *y, int64_t nb, int64_t N,
+                            const WalkShape &s, hipStream_t stream) {
+  const int64_t NG = (N + MV_ROWS - 1) / MV_ROWS;
+  // Offsets formed in the kernel: a workgroup's rows stay below the
+  // past-the-end offset its idle loads use, and the activations below 2^31.
+  if (NG > 0x7FFFFFFF || s.row_groups < 1 || s.row_groups > WK_MAX_RG ||
+      (int64_t)s.row_groups * MV_ROWS * nb * kBlockBytes > 0x7FFF0000 ||
+      nb * 1024 > 0x7FFF0000)
+    return hipErrorInvalidValue;
+  const bool small = nb <= 16;
+#define Q4K_WALK_CASE(W_, D_)                                                             \
+  if (s.waves == W_ && s.depth == D_) {                                                   \
+    if (small)                                                                            \
+      launch_walk<W_, D_, 16>(x, w, y, nb, N, s.row_groups, stream);                      \
+    else                                                                                  \
+      launch_walk<W_, D_, 64>(x, w, y, nb, N, s.row_groups, stream);                      \
+    return hipGetLastError();                                                             \
+  }
+  Q4K_WALK_CASE(4, 4)
+  Q4K_WALK_CASE(8, 2)
+  Q4K_WALK_CASE(8, 4)
+  Q4K_WALK_CASE(16, 2)
+#undef Q4K_WALK_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace q4k

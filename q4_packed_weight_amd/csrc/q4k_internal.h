@@ -36,6 +36,22 @@ hipError_t gemv_mfma_launch(const float *x, const uint8_t *w, float *y, int64_t 
 // MI355X: it wins while every wave owns at most one super-block and all
 // workgroups are resident at once).
 bool use_gemv_mfma(int64_t nb, int64_t N);
+// The persistent matrix-core walk over canonical rows: workgroups of
+// `waves` waves own `row_groups` consecutive groups of 16 rows; each wave
+// keeps `depth` units (16 rows x one super-block) loaded ahead.
+struct WalkShape {
+  int waves = 8;       // 4, 8 or 16
+  int row_groups = 1;  // 1 .. 4
+  int depth = 2;       // 2 or 4 (4 waves: 4; 16 waves: 2)
+};
+// Zero fields of the request are chosen by the library.
+WalkShape choose_walk_shape(int64_t nb, int64_t N, int waves, int row_groups, int depth);
+hipError_t gemv_walk_launch(const float *x, const uint8_t *w, float *y, int64_t nb, int64_t N,
+                            const WalkShape &s, hipStream_t stream);
+// Whether q4k_gemv's automatic choice is the walk (measured on MI355X: large
+// matrices, from output_dim 4096 with input_dim 8192, or output_dim 11008
+// with input_dim 4096).
+bool use_gemv_walk(int64_t nb, int64_t N);
 
 // The tiled block order (q4k_tiled.hip): bytes of an N-row matrix of nb
 // super-blocks per row, the one-time relayout, and the matrix-core GEMV

@@ -94,8 +94,12 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_kernel(
     const float *x, const uint8_t *wt, float *__restrict__ y, int nb, int N, int rg_per_wg) {
   constexpr int XPL = CAP * 64 / (64 * W);  // activation float4 per thread per chunk
   static_assert(XPL * 64 * W == CAP * 64, "a chunk's activations must split evenly");
-  __shared__ __align__(16) uint32_t xh[CAP * 128];
-  __shared__ __align__(16) uint32_t xl[CAP * 128];
+  // the hi part, then the lo part 4 dwords further modulo the banks, so the
+  // even (hi) and odd (lo) A rows that lanes of one group read together sit
+  // in different banks
+  __shared__ __align__(16) uint32_t xhl[2 * CAP * 128 + 4];
+  uint32_t *const xh = xhl;
+  uint32_t *const xl = xhl + CAP * 128 + 4;
   // per sub-block pair p: its two x sums, then its two exponents (int bits)
   __shared__ __align__(16) float xse[CAP * 16];
   __shared__ float part[W][kMaxRowGroups][64];
@@ -308,8 +312,10 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_kernel(
 template <int T, int W, int D, bool NC>
 __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
     const float *X, const uint8_t *wt, float *__restrict__ Y, int M, int nb, int N) {
-  __shared__ __align__(16) uint32_t xh[W][T][128];
-  __shared__ __align__(16) uint32_t xl[W][T][128];
+  // [wave][2t] token t's hi part, [wave][2t + 1] its lo part: rows 4 dwords
+  // apart modulo the banks, so the A rows that lanes of one group read
+  // together sit in different banks
+  __shared__ __align__(16) uint32_t xhl[W][2 * T][128 + 4];
   __shared__ __align__(16) float xs[W][T][8];
   __shared__ int xe[W][T];
   __shared__ float part[W][T][kTileRows];
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
   // A operand: row n is token n / 2 (rows past 2T repeat token T - 1 and are
   // never read back), hi part in even rows, lo part in odd rows.
   const int ta = min(n >> 1, T - 1);
-  const uint32_t *xa_src = (n & 1) ? xl[wave][ta] : xh[wave][ta];
+  const uint32_t *xa_src = xhl[wave][2 * ta + (n & 1)];
   const int t0 = min(2 * g, T - 1), t1 = min(2 * g + 1, T - 1);
   float y0 = 0.f, y1 = 0.f;
 
@@ -364,8 +370,8 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_batch_kernel(
       h02.x = (_Float16)v.x; h02.y = (_Float16)v.z;
       h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
       const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
-      *reinterpret_cast<uint2 *>(&xh[wave][t][2 * lane]) = make_uint2(hw02, hw13);
-      *reinterpret_cast<uint2 *>(&xl[wave][t][2 * lane]) =
+      *reinterpret_cast<uint2 *>(&xhl[wave][2 * t][2 * lane]) = make_uint2(hw02, hw13);
+      *reinterpret_cast<uint2 *>(&xhl[wave][2 * t + 1][2 * lane]) =
           make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
       xs[wave][t][lane >> 3] = group_sum<8>(sum4(v0));  // 8 lanes write one value
       xe[wave][t] = e;                                  // every lane, one value

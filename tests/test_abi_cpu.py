@@ -102,6 +102,19 @@ def test_shaped_rejects_bad_launch_shape(lib, rpl, kw, wg):
     assert lib.q4k_gemv_shaped(GOOD, GOOD2, 256, 8, GOOD3, None, rpl, kw, wg) == -1
 
 
+@pytest.mark.parametrize("waves,rg,depth", [(3, 0, 0), (32, 0, 0), (2, 0, 0), (0, 5, 0),
+                                             (0, -1, 0), (0, 0, 3), (0, 0, 1), (4, 0, 2),
+                                             (16, 0, 4), (4, 1, 2), (-8, 0, 0)])
+def test_walk_shaped_rejects_bad_shape(lib, waves, rg, depth):
+    assert lib.q4k_gemv_walk_shaped(GOOD, GOOD2, 256, 8, GOOD3, None, waves, rg, depth) == -1
+
+
+def test_walk_shaped_validates_like_gemv(lib):
+    assert lib.q4k_gemv_walk_shaped(GOOD, GOOD2, 300, 8, GOOD3, None, 0, 0, 0) == -1
+    assert lib.q4k_gemv_walk_shaped(None, GOOD2, 256, 8, GOOD3, None, 0, 0, 0) == -2
+    assert lib.q4k_gemv_walk_shaped(GOOD, ODD, 256, 8, GOOD3, None, 0, 0, 0) == -3
+
+
 @pytest.mark.parametrize("K", [32, 96, 288, 4000, 0, -256, 1 << 31, (1 << 24) + 256])
 def test_q4_0_rejects_bad_input_dim(lib, K):
     """Multiples of 32 that are not whole 144-byte groups are rejected too."""

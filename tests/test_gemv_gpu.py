@@ -15,10 +15,12 @@ from tolerance import assert_parity
 pytestmark = pytest.mark.gpu
 
 
-def run_gemv(x, w, K, N, shape=None):
+def run_gemv(x, w, K, N, shape=None, walk=None):
     xd, wd = dev(x), dev(w)
     buf, y = out_with_canary(N)
-    if shape is None:
+    if walk is not None:
+        binding.q4k_gemv_walk_shaped(xd, wd, K, N, y, *walk)
+    elif shape is None:
         binding.q4k_gemv(xd, wd, K, N, y)
     else:
         binding.q4k_gemv_shaped(xd, wd, K, N, y, *shape)
@@ -73,9 +75,9 @@ def test_matrix_core_form_integer_bit_exact(oracle_lib, K, N):
     assert np.array_equal(y.astype(np.float64), oracle_lib.q4k_gemv(x, w, K, N))
 
 
-@pytest.mark.parametrize("form", [None, (0, 0, 16)], ids=["auto", "mfma"])
+@pytest.mark.parametrize("form", [None, (0, 0, 16), "walk"], ids=["auto", "mfma", "walk"])
 @pytest.mark.parametrize("K,N,lo,hi", [(4096, 4096, -40, 40), (2560, 300, -40, 40),
-                                       (4096, 256, -60, 92)])
+                                       (4096, 256, -60, 92), (18432, 100, -60, 92)])
 def test_wide_range_activations(oracle_lib, K, N, lo, hi, form):
     """Activations far outside fp16's range, with every 32-element sub-block
     at its own scale 2^lo .. 2^hi (up to just below the documented 2^96
@@ -89,8 +91,70 @@ def test_wide_range_activations(oracle_lib, K, N, lo, hi, form):
     scale[g.choice(K // 32, 3, replace=False)] = 0.0
     x = (x.reshape(-1, 32) * scale[:, None]).reshape(-1)
     assert np.abs(x).max() > 1e9
-    y = run_gemv(x, w, K, N, shape=form)
+    if form == "walk":
+        y = run_gemv(x, w, K, N, walk=(8, 0, 2))
+    else:
+        y = run_gemv(x, w, K, N, shape=form)
     assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=f"wide K={K} N={N}")
+
+
+# The persistent matrix-core walk: (waves, row groups per workgroup, units
+# ahead); 0 lets the library choose.
+WALK_SHAPES = [(8, 0, 2), (8, 0, 4), (4, 0, 4), (16, 0, 2), (8, 1, 2), (8, 2, 2), (8, 3, 4),
+               (4, 4, 4), (16, 4, 2)]
+
+
+@pytest.mark.parametrize("wf", WALK_SHAPES)
+@pytest.mark.parametrize("K,N", [(256, 7), (2048, 333), (4096, 1000), (5120, 64), (14336, 100),
+                                 (18432, 37), (65792, 20)])
+def test_walk_every_shape(oracle_lib, K, N, wf):
+    """Every launch shape of the walk over: one super-block and fewer rows
+    than a group (waves without units), fewer super-blocks than waves,
+    16 super-blocks (activations staged for the whole workgroup), 20 and 56
+    (staged per wave where each wave keeps its super-blocks, by the
+    workgroup otherwise), 72 (two chunks of activations) and 257 (exact
+    normal code operands, five chunks); ragged row groups and row-group
+    counts not a multiple of the workgroup's."""
+    w = synth.q4k_weights(N, K, config=23, copy=K + N)
+    x = synth.activations(K, config=23, copy=K + N)
+    y = run_gemv(x, w, K, N, walk=wf)
+    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=f"walk {wf} K={K} N={N}")
+
+
+@pytest.mark.parametrize("wf", [(8, 0, 2), (4, 0, 4), (16, 0, 2)])
+@pytest.mark.parametrize("K,N", [(14336, 64), (4096, 512), (18432, 48), (65792, 16)])
+def test_walk_integer_bit_exact(oracle_lib, K, N, wf):
+    """Integer weights and activations: the walk is exact (exact fp16
+    operands, integer partial sums below 2^24), including the normal-code
+    instantiation for rows of more than 256 super-blocks."""
+    w = synth.q4k_integer_weights(N, K, config=24)
+    x = synth.integer_activations(K, config=24)
+    y = run_gemv(x, w, K, N, walk=wf)
+    assert np.array_equal(y.astype(np.float64), oracle_lib.q4k_gemv(x, w, K, N))
+
+
+@pytest.mark.parametrize("K,N", [(4096, 14341), (8192, 4096), (11008, 4096)])
+def test_walk_automatic_choice(oracle_lib, K, N):
+    """Shapes q4k_gemv hands to the walk: four row groups per workgroup with
+    a ragged last group and a last workgroup of one group; one row group
+    per workgroup with per-wave staging (32 and 43 super-blocks)."""
+    w = synth.q4k_weights(N, K, config=25, copy=K + N)
+    x = synth.activations(K, config=25, copy=K + N)
+    y = run_gemv(x, w, K, N)
+    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=f"auto walk K={K} N={N}")
+    y2 = run_gemv(x, w, K, N, walk=(0, 0, 0))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+def test_walk_deterministic():
+    """One writer per output and a fixed summation order: repeated calls
+    agree bit for bit."""
+    K, N = 14336, 512
+    w = synth.q4k_weights(N, K, config=26)
+    x = synth.activations(K, config=26)
+    a = run_gemv(x, w, K, N, walk=(8, 0, 2))
+    b = run_gemv(x, w, K, N, walk=(8, 0, 2))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
 def test_matrix_core_form_rejects_shape_fields():

@@ -36,8 +36,9 @@ def _replays_match(fn, out, eager, exact=True):
             assert_parity(got, eager.astype(np.float64), rowwise=got.ndim == 2, what=f"replay {i}")
 
 
-def test_gemv_graph_replays():
-    K, N = 4096, 1000
+@pytest.mark.parametrize("K,N", [(4096, 1000), (14336, 4096), (4096, 14336)],
+                         ids=["vector", "walk-per-wave", "walk-4-groups"])
+def test_gemv_graph_replays(K, N):
     w = dev(synth.q4k_weights(N, K, config=40))
     x = dev(synth.activations(K, config=40))
     y = torch.empty(N, dtype=torch.float32, device=DEV)
