@@ -146,7 +146,7 @@ def make_workload(name, torch, binding, synth):
         wl.copies = copies
         wl.bytes = b1 + b2 + 4 * (K1 + N1 + K2 + N2)
         wl.flops = 2 * (K1 * N1 + K2 * N2)
-        wl.kernel = "q4k_gemv_persist_kernel (up) + q4k_gemv_kernel (down)"
+        wl.kernel = "q4k_gemv_walk_kernel (up: 4 row groups per workgroup; down: 1, staged per wave)"
         wl.src_files = GEMV_SRC
         wl.config = {"workload": "q4k_gemv FFN pair 4096->14336 + 14336->4096 batch 1",
                      "rotating_pairs": copies}

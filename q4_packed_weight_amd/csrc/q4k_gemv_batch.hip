@@ -45,7 +45,11 @@ constexpr int MB_ROWS = 16;                      // rows per workgroup
 // super-blocks a row, half the waves idle) 4.02 / 5.00.
 constexpr int MB_WCH = MB_ROWS * 9;              // 16-byte weight pieces per super-block
 constexpr int MB_WPL = (MB_WCH + 63) / 64;       // weight loads per lane
-constexpr int MB_WROW = 36 + 2;                  // LDS dwords per staged row (+ 8 B)
+// LDS dwords per staged row, unpadded: each lane's 16-byte chunk lands in
+// one contiguous 16-byte store and the operand reads of 16 rows hit
+// distinct banks (no bank conflict cycles, against 4 per chunk store and 2
+// per code read with rows of 38)
+constexpr int MB_WROW = 36;
 
 // T: tokens of the launch, 2, 4 or 8 (rows of X past M read as zeros); NC:
 // exact normal code operands (rows of more than 256 super-blocks)
@@ -57,10 +61,12 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
   // (5,7) of every 8), their sums per sub-block and the token's scaling
   // exponent; then the waves' partial outputs.
   __shared__ __align__(16) uint32_t wt[MB_WAVES][MB_ROWS * MB_WROW];
-  // [wave][2t] token t's hi part, [wave][2t + 1] its lo part: rows 4 dwords
-  // apart modulo the banks, so the A rows that lanes of one group read
-  // together sit in different banks
-  __shared__ __align__(16) uint32_t xhl[MB_WAVES][2 * T][128 + 4];
+  // [wave][2t] token t's hi part, [wave][2t + 1] its lo part, rows of 136
+  // dwords: the A rows of all lane groups, read by one instruction, then
+  // fall in different banks (measured with the bank conflict counter: no
+  // conflict cycles for 2, 4 or 8 tokens, against 4 to 28 per read with
+  // rows of 128 or 132)
+  __shared__ __align__(16) uint32_t xhl[MB_WAVES][2 * T][136];
   __shared__ __align__(16) float xs[MB_WAVES][T][8];
   __shared__ int xe[MB_WAVES][T];
   __shared__ float part[MB_WAVES][T][MB_ROWS];
@@ -130,8 +136,7 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
       if (MB_WCH % 64 != 0 && q >= MB_WCH) break;  // only the last load is partial
       const int row = q / 9;
       uint32_t *dst = &wtw[row * MB_WROW + 4 * (q - 9 * row)];
-      *reinterpret_cast<uint2 *>(dst) = make_uint2(wv[m].x, wv[m].y);
-      *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wv[m].z, wv[m].w);
+      *reinterpret_cast<uint4 *>(dst) = wv[m];
     }
   };
 
@@ -142,6 +147,18 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
   // this lane's tokens (D rows 4g, 4g+1 and 4g+2, 4g+3)
   const int t0 = min(2 * g, T - 1), t1 = min(2 * g + 1, T - 1);
   float y0 = 0.f, y1 = 0.f;
+
+  // Code reads: one 8-byte read per sub-block pair, each from its own base
+  // register (8-byte units).  Sharing one base, the compiler pairs them
+  // into ds_read2_b64 (offsets 32 bytes apart), which measured 8
+  // bank-conflict cycles per pair; single reads of the same bytes none.
+  int qoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    qoff[j] = (n * MB_WROW + 4 + 8 * j + 2 * g) >> 1;
+    asm volatile("" : "+v"(qoff[j]));
+  }
+  const uint2 *const wt2 = reinterpret_cast<const uint2 *>(wtw);
 
   auto compute_chunk = [&]() {
     const uint32_t *rowp = &wtw[n * MB_WROW];
@@ -157,7 +174,7 @@ __global__ __launch_bounds__(64 * MB_WAVES) void q4k_gemv_batch_kernel(
     floatx4 dlo[4], dhi[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint2 qbj = *reinterpret_cast<const uint2 *>(rowp + 4 + 8 * j + 2 * g);
+      const uint2 qbj = wt2[qoff[j]];
       const half8_t alo = *reinterpret_cast<const half8_t *>(&xa_src[(64 * j + 8 * g) / 2]);
       const half8_t ahi = *reinterpret_cast<const half8_t *>(&xa_src[(64 * j + 32 + 8 * g) / 2]);
       const uint32_t s0 = qbj.x >> 8, s1 = qbj.y >> 8;

@@ -49,7 +49,11 @@ constexpr int MV_CB = 1;              // super-blocks per chunk
 constexpr int MV_WCH = MV_ROWS * MV_CB * 9;             // 16-byte weight chunks per chunk
 constexpr int MV_WPL = (MV_WCH + 63) / 64;              // weight loads per lane
 constexpr int MV_XPL = MV_CB * 256 / 4 / 64;            // activation float4 per lane
-constexpr int MV_WROW = MV_CB * 36 + 2;                 // LDS dwords per staged row (+ 8 B)
+// LDS dwords per staged row, unpadded: each lane's 16-byte chunk lands in
+// one contiguous 16-byte store and the operand reads of 16 rows hit
+// distinct banks (measured with the bank conflict counter: no conflict
+// cycles, against 4 per chunk store and 2 per code read with rows of 38)
+constexpr int MV_WROW = MV_CB * 36;
 static_assert(MV_XPL * 64 * 4 == MV_CB * 256, "activation chunk must split evenly");
 
 template <bool NC>  // exact normal code operands (rows of more than 256 super-blocks)
@@ -59,10 +63,12 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
   // (positions in operand order: pairs (0,2), (1,3), (4,6), (5,7) of every
   // 8), the chunk's sub-block sums; then the cross-wave partials.
   __shared__ __align__(16) uint32_t wt[MV_WAVES][MV_ROWS * MV_WROW];
-  // [wave][0] the hi part, [wave][1] the lo part: rows 4 dwords apart modulo
-  // the banks, so the even (hi) and odd (lo) A rows that lanes of one group
-  // read together sit in different banks
-  __shared__ __align__(16) uint32_t xhl[MV_WAVES][2][MV_CB * 128 + 4];
+  // [wave][0] the hi part, [wave][1] the lo part, 16 dwords further modulo
+  // the banks: the hi and lo A rows of the four lane groups, read by one
+  // instruction, then fall in different banks (measured with the bank
+  // conflict counter: 4 conflict cycles per read with the parts a multiple
+  // of the banks or 4 dwords apart, none at 8 to 48)
+  __shared__ __align__(16) uint32_t xhl[MV_WAVES][2][MV_CB * 128 + 16];
   // per sub-block pair p (sub-blocks 2p, 2p+1): their x sums, then their
   // scaling exponents (int bits), read by one lane as one 16-byte word
   __shared__ __align__(16) float xse[MV_WAVES][MV_CB * 16];
@@ -140,8 +146,7 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
       if (MV_WCH % 64 != 0 && q >= MV_WCH) break;  // only the last load is partial
       const int row = q / (9 * MV_CB);
       uint32_t *dst = &wtw[row * MV_WROW + 4 * (q - row * 9 * MV_CB)];
-      *reinterpret_cast<uint2 *>(dst) = make_uint2(wv[m].x, wv[m].y);
-      *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wv[m].z, wv[m].w);
+      *reinterpret_cast<uint4 *>(dst) = wv[m];
     }
   };
 
@@ -150,6 +155,17 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
   const int j_mine = g;  // sub-blocks 2g, 2g+1 are scaled by this lane
   const uint32_t sh = (uint32_t)(g & 1) * 16u;
   const bool jhi = g >= 2;
+  // Code reads: one 8-byte read per sub-block pair, each from its own base
+  // register (8-byte units).  Sharing one base, the compiler pairs them
+  // into ds_read2_b64 (offsets 32 bytes apart), which measured 8
+  // bank-conflict cycles per pair; single reads of the same bytes none.
+  int qoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    qoff[j] = (n * MV_WROW + 4 + 8 * j + 2 * g) >> 1;
+    asm volatile("" : "+v"(qoff[j]));
+  }
+  const uint2 *const wt2 = reinterpret_cast<const uint2 *>(wtw);
   float yacc = 0.f;
 
   auto compute_chunk = [&](int c) {
@@ -184,7 +200,7 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
       half8_t alo[4], ahi[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        qb[j] = *reinterpret_cast<const uint2 *>(rowp + 4 + 8 * j + 2 * g);
+        qb[j] = wt2[qoff[j] + 18 * bb];
         const int pos = 256 * bb + 64 * j + 8 * g;  // sub-block 2j, positions 8g..
         alo[j] = *reinterpret_cast<const half8_t *>(&xa_src[pos / 2]);
         ahi[j] = *reinterpret_cast<const half8_t *>(&xa_src[(pos + 32) / 2]);
@@ -278,12 +294,12 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_walk_kernel(
     const float *x, const uint8_t *w, float *__restrict__ y, int nb, int N, int rg_per_wg) {
   constexpr int XPL = CAP / W;  // activation float4 per thread of a chunk
   static_assert(XPL * 64 * W == CAP * 64, "a chunk's activations must split evenly");
-  // the hi part, then the lo part 4 dwords further modulo the banks, so the
-  // even (hi) and odd (lo) A rows that lanes of one group read together sit
-  // in different banks
-  __shared__ __align__(16) uint32_t xhl[2 * CAP * 128 + 4];
+  // the hi part, then the lo part 16 dwords further modulo the banks: the
+  // hi and lo A rows of the four lane groups, read by one instruction, then
+  // fall in different banks (4 conflict cycles per read otherwise)
+  __shared__ __align__(16) uint32_t xhl[2 * CAP * 128 + 16];
   uint32_t *const xh = xhl;
-  uint32_t *const xl = xhl + CAP * 128 + 4;
+  uint32_t *const xl = xhl + CAP * 128 + 16;
   // per sub-block pair p: its two x sums, then its two exponents (int bits)
   __shared__ __align__(16) float xse[CAP * 16];
   __shared__ __align__(16) uint32_t wt[W][MV_ROWS * MV_WROW];
@@ -326,6 +342,17 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_walk_kernel(
   const uint32_t sh = (uint32_t)(g & 1) * 16u;
   const bool jhi = g >= 2;
   uint32_t *wtw = wt[wave];
+  // Code reads: one 8-byte read per sub-block pair, each from its own base
+  // register (8-byte units).  Sharing one base, the compiler pairs them
+  // into ds_read2_b64 (offsets 32 bytes apart), which measured 8
+  // bank-conflict cycles per pair; single reads of the same bytes none.
+  int qoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    qoff[j] = (n * MV_WROW + 4 + 8 * j + 2 * g) >> 1;
+    asm volatile("" : "+v"(qoff[j]));
+  }
+  const uint2 *const wt2 = reinterpret_cast<const uint2 *>(wtw);
 
   // Stage float4 f of a chunk (positions 4f .. 4f+3; its sub-block f / 8
   // sits in 8 aligned lanes): scale the sub-block by 2^-e so that
@@ -410,8 +437,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_walk_kernel(
         if (MV_WCH % 64 != 0 && q >= MV_WCH) break;  // only the last load is partial
         const int row = q / 9;
         uint32_t *dst = &wtw[row * MV_WROW + 4 * (q - 9 * row)];
-        *reinterpret_cast<uint2 *>(dst) = make_uint2(wq[s][m].x, wq[s][m].y);
-        *reinterpret_cast<uint2 *>(dst + 2) = make_uint2(wq[s][m].z, wq[s][m].w);
+        *reinterpret_cast<uint4 *>(dst) = wq[s][m];
       }
       wave_lds_order();
       const uint32_t *rowp = &wtw[n * MV_WROW];
@@ -439,7 +465,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_walk_kernel(
       half8_t alo[4], ahi[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        qb[j] = *reinterpret_cast<const uint2 *>(rowp + 4 + 8 * j + 2 * g);
+        qb[j] = wt2[qoff[j]];
         const int pos = 128 * bl + 32 * j + 4 * g;  // dword of sub-block 2j, positions 8g..
         alo[j] = *reinterpret_cast<const half8_t *>(&xa_src[pos]);
         ahi[j] = *reinterpret_cast<const half8_t *>(&xa_src[pos + 16]);
