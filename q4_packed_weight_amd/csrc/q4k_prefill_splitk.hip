@@ -80,12 +80,15 @@ constexpr int SK_TILE = SK_ROWS * SK_TOK;  // floats of one workspace slot
 constexpr int kCoherent = 16;
 
 // One half's image buffer (bytes).  Image I = (t*2 + tt)*2 + hl holds MFMA
-// t's B operand for token tile tt (hl: hi or lo halves), lane (token j, group
-// g) at I*SK_IMG + 16 (j + 16 g): every 16-lane quarter reads 256 contiguous
-// bytes; the 16-byte pad between images leaves the splitting lanes' 8-byte
-// writes at most two to a bank.
+// t's B operand for token tile tt (hl: hi or lo halves) at I*SK_IMG +
+// SK_ISHIFT*(I >> 3), lane (token j, group g) 16 (j + 16 g) into it: every
+// 16-lane quarter reads 256 contiguous bytes.  The pad and the shift were
+// picked with the bank-conflict counter: the splitting lanes' 8-byte stores
+// cost 4 conflict cycles each, 12 without the shift (every stride tried that
+// keeps the images 16-byte aligned).
 constexpr int SK_IMG = 1024 + 16;
-constexpr int SK_MIMG = 32 * SK_IMG;            // sums' images: 2 token tiles x 64 lanes x 8 B
+constexpr int SK_ISHIFT = 32;                   // added per 8 images: img_off(I)
+constexpr int SK_MIMG = 32 * SK_IMG + 4 * SK_ISHIFT;  // sums' images: 2 token tiles x 64 lanes x 8 B
 constexpr int SK_ETAB = SK_MIMG + 2 * 512;      // 32 exponents e
 constexpr int SK_HBUF = SK_ETAB + SK_TOK * 4;
 // A wave's header table (dwords): 32 rows x 8 scale pairs, 32 rows x 4
@@ -202,14 +205,16 @@ __global__ __launch_bounds__(SK_THREADS) void q4k_prefill_splitk_kernel(
   // MFMA t's slots of lane group gg (operand order (0,2), (1,3) | (4,6),
   // (5,7): the low or high 8 bytes of the image entry)
   const int x_tt = tl >> 4, x_tok16 = tl & 15;
-  const int x_img = (x_tt * 2 + 8 * ((j >> 1) & 1)) * SK_IMG + 256 * (j >> 2) + 16 * x_tok16 +
+  const int x_img = (x_tt * 2 + 8 * ((j >> 1) & 1)) * SK_IMG + SK_ISHIFT * ((j >> 1) & 1) +
+                    256 * (j >> 2) + 16 * x_tok16 +
                     8 * (j & 1);
   auto split_chunk = [&](uint8_t *hb, const float4 &v, int c, float sdown) {
     uint2 h, l;
     split_pair(v.x, v.z, sdown, h.x, l.x);
     split_pair(v.y, v.w, sdown, h.y, l.y);
     const int t0 = 4 * (c >> 2) + (c & 1);  // t = t0 + 2 ((j >> 1) & 1)
-    const int off = x_img + t0 * 4 * SK_IMG + 512 * ((c >> 1) & 1);  // group 2((c>>1)&1) + (j>>2)
+    // group 2((c>>1)&1) + (j>>2); images 4 t0 + ... sit 2 (c >> 2) shifts on
+    const int off = x_img + t0 * 4 * SK_IMG + 2 * SK_ISHIFT * (c >> 2) + 512 * ((c >> 1) & 1);
     *reinterpret_cast<uint2 *>(hb + off) = h;
     *reinterpret_cast<uint2 *>(hb + off + SK_IMG) = l;
     return sum4(v);
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(SK_THREADS) void q4k_prefill_splitk_kernel(
         half8_t bh[2], bl[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const int off = (t * 2 + tt) * 2 * SK_IMG + 16 * lane;
+          const int off = (t * 2 + tt) * 2 * SK_IMG + SK_ISHIFT * (t >> 1) + 16 * lane;
           bh[tt] = *reinterpret_cast<const half8_t *>(hb + off);
           bl[tt] = *reinterpret_cast<const half8_t *>(hb + off + SK_IMG);
         }
