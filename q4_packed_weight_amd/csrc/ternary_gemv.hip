@@ -191,9 +191,15 @@ hipError_t ternary_launch(const float *x, const uint8_t *codes, float scale,
                           hipStream_t stream) {
   const bool aligned = ((uintptr_t)x % 16 == 0) && ((uintptr_t)codes % 16 == 0);
   if (K % 64 == 0 && aligned) {
-    // At least one wave per SIMD of the 256 CUs where the row count allows.
-    if (N / 4 >= 1024) return launch_fast<4>(x, codes, scale, apply_scale, K, N, y, stream);
-    if (N / 2 >= 1024) return launch_fast<2>(x, codes, scale, apply_scale, K, N, y, stream);
+    // Rows per lane, measured on MI355X (graph-replayed calls over rotating
+    // codes, us/call at R = 4 / 2 / 1): 4096x4096 4.25 / 3.88 / 3.96,
+    // 14336->4096 10.55 / 8.97 / 10.07, 8192->4096 6.35 / 5.54 / 5.85,
+    // 4096->8192 5.44 / 5.15 / 5.81, 14336->8192 13.46 / 13.98 / 17.85,
+    // 4096->14336 7.30 / 7.8 / 8.8, 14336->2048 - / 7.78 / 7.25: two waves
+    // per SIMD beat one until the grid is large.
+    if (N >= 12288 || (N >= 8192 && K >= 12288))
+      return launch_fast<4>(x, codes, scale, apply_scale, K, N, y, stream);
+    if (N >= 4096) return launch_fast<2>(x, codes, scale, apply_scale, K, N, y, stream);
     return launch_fast<1>(x, codes, scale, apply_scale, K, N, y, stream);
   }
   const int64_t grid = (N + 3) / 4;

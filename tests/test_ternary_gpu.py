@@ -28,9 +28,12 @@ def run(x, codes, K, N, scale=None, x_offset=0):
     return out
 
 
-# fast path (K % 64 == 0) and generic path (K % 64 != 0), ragged rows
+# fast path (K % 64 == 0) and generic path (K % 64 != 0), ragged rows; the
+# fast path's 1, 2 and 4 rows per lane (output_dim below 4096, from 4096,
+# from 12288 or from 8192 with input_dim from 12288)
 SHAPES = [(64, 1), (128, 5), (1024, 333), (4096, 4096), (4160, 77), (4100, 7),
-          (4, 3), (12, 65), (14336, 100), (65536, 9)]
+          (4, 3), (12, 65), (14336, 100), (65536, 9), (2048, 4100), (1024, 12300),
+          (12352, 8195), (4096, 2050)]
 
 
 @pytest.mark.parametrize("K,N", SHAPES)
