@@ -54,6 +54,10 @@ constexpr int MV_XPL = MV_CB * 256 / 4 / 64;            // activation float4 per
 // distinct banks (measured with the bank conflict counter: no conflict
 // cycles, against 4 per chunk store and 2 per code read with rows of 38)
 constexpr int MV_WROW = MV_CB * 36;
+constexpr int MV_XLO = MV_CB * 128 + 16;                // lo part of a wave's activations
+constexpr int MV_XZ = 2 * MV_XLO;                       // zeros for even MFMAs j; + 32: odd
+constexpr int MV_XW = MV_XZ + 64;                       // dwords per wave
+static_assert(MV_CB == 1 && MV_XZ % 64 == 32, "zero areas in the bank halves the reads leave free");
 static_assert(MV_XPL * 64 * 4 == MV_CB * 256, "activation chunk must split evenly");
 
 template <bool NC>  // exact normal code operands (rows of more than 256 super-blocks)
@@ -63,12 +67,14 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
   // (positions in operand order: pairs (0,2), (1,3), (4,6), (5,7) of every
   // 8), the chunk's sub-block sums; then the cross-wave partials.
   __shared__ __align__(16) uint32_t wt[MV_WAVES][MV_ROWS * MV_WROW];
-  // [wave][0] the hi part, [wave][1] the lo part, 16 dwords further modulo
-  // the banks: the hi and lo A rows of the four lane groups, read by one
-  // instruction, then fall in different banks (measured with the bank
-  // conflict counter: 4 conflict cycles per read with the parts a multiple
-  // of the banks or 4 dwords apart, none at 8 to 48)
-  __shared__ __align__(16) uint32_t xhl[MV_WAVES][2][MV_CB * 128 + 16];
+  // Per wave: the hi part at 0, the lo part at MV_XLO (16 dwords further
+  // modulo the banks: the hi and lo A rows of the four lane groups, read by
+  // one instruction, then fall in different banks; measured with the bank
+  // conflict counter, 4 conflict cycles per read with the parts a multiple
+  // of the banks or 4 dwords apart, none at 8 to 48), then two zeroed areas
+  // that A rows read in the MFMAs they do not feed (see compute_chunk), in
+  // the bank half the real reads of that MFMA leave free.
+  __shared__ __align__(16) uint32_t xhl[MV_WAVES][MV_XW];
   // per sub-block pair p (sub-blocks 2p, 2p+1): their x sums, then their
   // scaling exponents (int bits), read by one lane as one 16-byte word
   __shared__ __align__(16) float xse[MV_WAVES][MV_CB * 16];
@@ -129,8 +135,8 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
       h13.x = (_Float16)v.y; h13.y = (_Float16)v.w;
       const uint32_t hw02 = as_u32h(h02), hw13 = as_u32h(h13);
       const int f = lane + 64 * i;  // float4 index: positions 4f .. 4f+3
-      *reinterpret_cast<uint2 *>(&xhl[wave][0][2 * f]) = make_uint2(hw02, hw13);
-      *reinterpret_cast<uint2 *>(&xhl[wave][1][2 * f]) =
+      *reinterpret_cast<uint2 *>(&xhl[wave][2 * f]) = make_uint2(hw02, hw13);
+      *reinterpret_cast<uint2 *>(&xhl[wave][MV_XLO + 2 * f]) =
           make_uint2(lo_pair(hw02, v.x, v.z), lo_pair(hw13, v.y, v.w));
       // sub-block f / 8: the 8 float4 of a sub-block sit in 8 aligned lanes
       const float s = group_sum<8>(sum4(v0));
@@ -150,9 +156,19 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
     }
   };
 
-  // A operand rows: even rows the hi part, odd rows the lo part.
-  const uint32_t *xa_src = xhl[wave][n & 1];
+  // A operand: row n carries the hi part (n even) or the lo part (n odd) of
+  // sub-block 2j (MFMA on low nibbles) or 2j+1 (high nibbles) only in the
+  // MFMAs j = n / 4; in the other three it reads zeros.  So D rows 4j ..
+  // 4j+3 hold sub-block pair j alone, one accumulator per nibble half sums
+  // the four MFMAs, and lane (n, g) finds its pair j = g in its own rows 4g
+  // (hi) and 4g+1 (lo): no selection among four results.  aidx: 16-byte
+  // units of the wave's area.
   const int j_mine = g;  // sub-blocks 2g, 2g+1 are scaled by this lane
+  int aidx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    aidx[j] = (n >> 2) == j ? ((n & 1) * MV_XLO + 32 * j + 4 * g) >> 2 : (MV_XZ + 32 * (j & 1)) >> 2;
+  const uint4 *const xa4 = reinterpret_cast<const uint4 *>(xhl[wave]);
   const uint32_t sh = (uint32_t)(g & 1) * 16u;
   const bool jhi = g >= 2;
   // Code reads: one 8-byte read per sub-block pair, each from its own base
@@ -201,11 +217,10 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         qb[j] = wt2[qoff[j] + 18 * bb];
-        const int pos = 256 * bb + 64 * j + 8 * g;  // sub-block 2j, positions 8g..
-        alo[j] = *reinterpret_cast<const half8_t *>(&xa_src[pos / 2]);
-        ahi[j] = *reinterpret_cast<const half8_t *>(&xa_src[(pos + 32) / 2]);
+        alo[j] = __builtin_bit_cast(half8_t, xa4[aidx[j]]);      // positions 8g.. of 2j
+        ahi[j] = __builtin_bit_cast(half8_t, xa4[aidx[j] + 4]);  // of 2j + 1 (32 on)
       }
-      floatx4 dlo[4], dhi[4];
+      floatx4 dlo = {0.f, 0.f, 0.f, 0.f}, dhi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t s0 = qb[j].x >> 8, s1 = qb[j].y >> 8;
@@ -214,25 +229,20 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
         blo.z = code_operand_pair<NC>(qb[j].y, 0x000F000Fu); blo.w = code_operand_pair<NC>(s1, 0x000F000Fu);
         bhi.x = code_operand_pair<NC>(qb[j].x, 0x00F000F0u); bhi.y = code_operand_pair<NC>(s0, 0x00F000F0u);
         bhi.z = code_operand_pair<NC>(qb[j].y, 0x00F000F0u); bhi.w = code_operand_pair<NC>(s1, 0x00F000F0u);
-        dlo[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            alo[j], __builtin_bit_cast(half8_t, blo), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        dhi[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            ahi[j], __builtin_bit_cast(half8_t, bhi), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        dlo = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[j], __builtin_bit_cast(half8_t, blo),
+                                                      dlo, 0, 0, 0);
+        dhi = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[j], __builtin_bit_cast(half8_t, bhi),
+                                                      dhi, 0, 0, 0);
       }
-      // D rows 4g (hi part) and 4g + 1 (lo part) of row n; this lane keeps
-      // sub-block pair j = g
-      float t_lo = dlo[0][0] + dlo[0][1], t_hi = dhi[0][0] + dhi[0][1];
-#pragma unroll
-      for (int j = 1; j < 4; ++j) {
-        if (j == j_mine) {
-          t_lo = dlo[j][0] + dlo[j][1];
-          t_hi = dhi[j][0] + dhi[j][1];
-        }
-      }
+      // D rows 4g (hi part) and 4g + 1 (lo part) of row n: sub-block pair
+      // j = g, the other MFMAs having added exact zeros to them
+      const float t_lo = dlo[0] + dlo[1], t_hi = dhi[0] + dhi[1];
       yacc = __builtin_fmaf(s_lo, t_lo, __builtin_fmaf(s_hi, t_hi, yacc));
     }
   };
 
+  // the zero areas (64 dwords per wave, read after this wave's own stores)
+  xhl[wave][MV_XZ + lane] = 0u;
   if (n_chunks > 0) {  // wave-uniform
     load_chunk(0, wa, xa);
     for (int c = 0;;) {
