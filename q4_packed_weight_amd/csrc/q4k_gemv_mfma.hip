@@ -306,8 +306,11 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_walk_kernel(
   static_assert(XPL * 64 * W == CAP * 64, "a chunk's activations must split evenly");
   // the hi part, then the lo part 16 dwords further modulo the banks: the
   // hi and lo A rows of the four lane groups, read by one instruction, then
-  // fall in different banks (4 conflict cycles per read otherwise)
-  __shared__ __align__(16) uint32_t xhl[2 * CAP * 128 + 16];
+  // fall in different banks (4 conflict cycles per read otherwise); then
+  // the zero areas that A rows read in the MFMAs they do not feed, in the
+  // bank half the real reads of that MFMA leave free (as in the form above)
+  constexpr int XZ = 2 * CAP * 128 + 32;  // even MFMAs j; + 32: odd
+  __shared__ __align__(16) uint32_t xhl[XZ + 64];
   uint32_t *const xh = xhl;
   uint32_t *const xl = xhl + CAP * 128 + 16;
   // per sub-block pair p: its two x sums, then its two exponents (int bits)
@@ -347,11 +350,17 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_walk_kernel(
   uint4 wq[D][MV_WPL];
   float4 xq[PRIV ? D : 1];
 
-  // A operand rows: even rows the hi part, odd rows the lo part.
-  const uint32_t *xa_src = (n & 1) ? xl : xh;
+  // A operand: row n feeds only MFMAs j = n / 4, reading the hi (n even)
+  // or lo (n odd) part there and zeros in the other three, so one
+  // accumulator per nibble half collects sub-block pair j in D rows 4j ..
+  // 4j+3 and lane (n, g) finds its pair g in its rows 4g, 4g+1.  16-byte
+  // units: this lane's part at a_own + 32 * super-block.
+  const int a_own = ((n & 1) * (CAP * 128 + 16) + 32 * (n >> 2) + 4 * g) >> 2;
+  const uint4 *const xa4 = reinterpret_cast<const uint4 *>(xhl);
   const uint32_t sh = (uint32_t)(g & 1) * 16u;
   const bool jhi = g >= 2;
   uint32_t *wtw = wt[wave];
+  xhl[XZ + lane] = 0u;  // each wave before its own reads (same values)
   // Code reads: one 8-byte read per sub-block pair, each from its own base
   // register (8-byte units).  Sharing one base, the compiler pairs them
   // into ds_read2_b64 (offsets 32 bytes apart), which measured 8
@@ -473,14 +482,15 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_walk_kernel(
                                                  (float)((mp >> 8) & 0xFFu) * xsp.y), acc);
       uint2 qb[4];
       half8_t alo[4], ahi[4];
+      const int a_real = a_own + 32 * bl;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         qb[j] = wt2[qoff[j]];
-        const int pos = 128 * bl + 32 * j + 4 * g;  // dword of sub-block 2j, positions 8g..
-        alo[j] = *reinterpret_cast<const half8_t *>(&xa_src[pos]);
-        ahi[j] = *reinterpret_cast<const half8_t *>(&xa_src[pos + 16]);
+        const int ai = (n >> 2) == j ? a_real : (XZ + 32 * (j & 1)) >> 2;
+        alo[j] = __builtin_bit_cast(half8_t, xa4[ai]);      // positions 8g.. of 2j
+        ahi[j] = __builtin_bit_cast(half8_t, xa4[ai + 4]);  // of 2j + 1
       }
-      floatx4 dlo[4], dhi[4];
+      floatx4 dlo = {0.f, 0.f, 0.f, 0.f}, dhi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t s0 = qb[j].x >> 8, s1 = qb[j].y >> 8;
@@ -489,21 +499,13 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_walk_kernel(
         blo.z = code_operand_pair<NC>(qb[j].y, 0x000F000Fu); blo.w = code_operand_pair<NC>(s1, 0x000F000Fu);
         bhi.x = code_operand_pair<NC>(qb[j].x, 0x00F000F0u); bhi.y = code_operand_pair<NC>(s0, 0x00F000F0u);
         bhi.z = code_operand_pair<NC>(qb[j].y, 0x00F000F0u); bhi.w = code_operand_pair<NC>(s1, 0x00F000F0u);
-        dlo[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            alo[j], __builtin_bit_cast(half8_t, blo), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        dhi[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            ahi[j], __builtin_bit_cast(half8_t, bhi), floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        dlo = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[j], __builtin_bit_cast(half8_t, blo),
+                                                      dlo, 0, 0, 0);
+        dhi = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[j], __builtin_bit_cast(half8_t, bhi),
+                                                      dhi, 0, 0, 0);
       }
-      // D rows 4g (hi part) and 4g + 1 (lo part) of row n; this lane keeps
-      // sub-block pair j = g
-      float t_lo = dlo[0][0] + dlo[0][1], t_hi = dhi[0][0] + dhi[0][1];
-#pragma unroll
-      for (int j = 1; j < 4; ++j) {
-        if (j == g) {
-          t_lo = dlo[j][0] + dlo[j][1];
-          t_hi = dhi[j][0] + dhi[j][1];
-        }
-      }
+      // D rows 4g (hi part) and 4g + 1 (lo part) of row n: pair j = g
+      const float t_lo = dlo[0] + dlo[1], t_hi = dhi[0] + dhi[1];
       acc = __builtin_fmaf(s_lo, t_lo, __builtin_fmaf(s_hi, t_hi, acc));
       // the next unit's stores into the tile come after these reads
       wave_lds_order();
