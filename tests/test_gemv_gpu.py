@@ -146,6 +146,19 @@ def test_walk_automatic_choice(oracle_lib, K, N):
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
 
 
+def test_walk_many_rows_sampled(oracle_lib):
+    """2^17 rows of 16 super-blocks (302 MB of weights, 8192 workgroups of
+    four row groups): sampled rows against the oracle run on just those
+    rows, the first and last included."""
+    K, N = 4096, 1 << 17
+    w = synth.q4k_weights(N, K, config=27)
+    x = synth.activations(K, config=27)
+    y = run_gemv(x, w, K, N)
+    rows = np.random.default_rng(27).choice(N, 1500, replace=False)
+    rows = np.concatenate([rows, [0, N - 1]])
+    assert_parity(y[rows], oracle_lib.q4k_gemv(x, w[rows], K, len(rows)), what="sampled rows")
+
+
 def test_walk_deterministic():
     """One writer per output and a fixed summation order: repeated calls
     agree bit for bit."""
