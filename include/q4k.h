@@ -111,7 +111,7 @@ int q4k_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
  * super-block are scaled by a power of two, then split into a high and a
  * low half, both exact MFMA operands (any |x| < 2^96).  The split tiles add
  * their ranges' partial results in a fixed order, so results do not depend
- * on timing.  Their partial tiles go to a workspace of 32 MiB + 1 KiB that
+ * on timing.  Their partial tiles go to a workspace of 32 MiB + 4 KiB that
  * the library allocates once per device, on the first call that needs it,
  * and keeps until the process ends; a call that would allocate it while its
  * stream is being captured into a graph fails with Q4K_EHIP (make one such
@@ -406,7 +406,7 @@ int q4k_gemv_tiled_shaped(const float *x, const uint8_t *w_tiled, int64_t input_
  * harnesses that forbid allocation.  Same arguments, kernels, results and
  * error behaviour as q4k_matmul, except that the split tiles' counters and
  * partial tiles live in a fixed scratch array reserved with the library's
- * code object (4 MiB + 1 KiB per GPU, held until the process ends) instead
+ * code object (4 MiB + 4 KiB per GPU, held until the process ends) instead
  * of the library's allocated workspace: the call performs no allocation of
  * any kind.  A call whose tiles would need more scratch than that returns
  * Q4K_ESCRATCH and launches nothing (the library's own choice of input_dim

@@ -105,7 +105,7 @@ hipError_t prefill_staged_tiled_launch(const float *X, const uint8_t *wt, int64_
 // call (every call leaves them zero again), then one partial tile per
 // (output tile, range).  Calls sharing a workspace must not overlap in time.
 constexpr int kSplitkMaxRanges = 8;
-constexpr int64_t kSplitkCounterBytes = 1024;  // S > 1 only below 256 output tiles
+constexpr int64_t kSplitkCounterBytes = 4096;  // one per (tile, wave); S > 1 only below 256 tiles
 // below 256 tiles, at most 8 ranges of 16 KiB partial tiles each
 constexpr int64_t kSplitkWorkspaceBytes = kSplitkCounterBytes + 255 * 8 * 16384;
 struct SplitkPlan {

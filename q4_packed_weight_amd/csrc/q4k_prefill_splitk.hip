@@ -52,13 +52,15 @@
 // (two sub-blocks per MFMA; A carries each one's scale).  The images hold x
 // at those positions, in the operand order of the codes ((0,2), (1,3), ...).
 //
-// End: the halves' results are added (half 0 + half 1), then with S = 1 the
-// tile is stored; with S > 1 it is stored to a workspace slot with the
-// agent-coherent cache policy and, once those stores are complete, counted
-// at the tile's counter; the workgroup that finds itself the S-th arrival
-// reads the S slots back (same policy), adds them in range order, stores Y
-// and resets the counter to zero, so every output has one writer and the
-// same bits whatever the arrival order.
+// End: the halves' results are added (half 0 + half 1), and each wave of
+// half 0 finishes its 32 rows on its own.  With S = 1 it stores them to Y.
+// With S > 1 it stores them to its range's workspace slot with the
+// agent-coherent cache policy and, once those stores are complete, counts
+// its arrival at the counter of (tile, wave); the wave that finds itself the
+// S-th arrival reads the S slots' rows back (same policy), adds them in range
+// order, stores them to Y and resets the counter to zero, so every output has
+// one writer and the same bits whatever the arrival order.  Y is stored from
+// the MFMA layout directly: 16 bytes (4 rows of one token) per lane.
 #include <type_traits>
 
 #include "device_common.h"
@@ -100,8 +102,7 @@ constexpr int SK_TDD = SK_TMN + 32 * 4;
 constexpr int SK_TAB = SK_TDD + 32;
 constexpr int SK_LDS = 4 * SK_HBUF + SK_WAVES * SK_TAB * 4;
 static_assert(SK_LDS <= 160 * 1024, "LDS of one workgroup");
-static_assert(SK_WAVES / 2 * 4 * 64 * 16 + SK_TOK * (SK_ROWS + 4) * 4 <= SK_LDS,
-              "the reduction tiles must fit in the image buffers");
+static_assert(SK_WAVES / 2 * 4 * 64 * 16 <= SK_LDS, "half 1's sums must fit in the image buffers");
 
 // 32*m for the two 6-bit mins in bytes 0 and 2 of `v` (bytes 1 and 3 zero),
 // as an fp16 pair: v | 0x6400 in each half is 1024 + m, and
@@ -129,7 +130,6 @@ __global__ __launch_bounds__(SK_THREADS) void q4k_prefill_splitk_kernel(
     const float *X, const uint8_t *w, float *__restrict__ Y, float *part, unsigned *cnt,
     int M, int nb, int N, int S, int n_rt, int n_tt) {
   __shared__ __align__(16) uint8_t lds[SK_LDS];
-  __shared__ int sk_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -437,68 +437,65 @@ __global__ __launch_bounds__(SK_THREADS) void q4k_prefill_splitk_kernel(
       yacc[c >> 1][c & 1] += *reinterpret_cast<const floatx4 *>(&red[((wv * 4 + c) * 64 + lane) * 4]);
   }
 
+  if (half == 1) return;  // half 0 holds the workgroup's sums
+
   if (S > 1) {
-    // This range's tile into its workspace slot (lane order), then the
-    // arrival count.  The slots are written and read with the agent-coherent
-    // cache policy (sc1: written through the XCD's L2, read past stale L2
-    // lines), each writer waits for its stores to complete before its
-    // arrival is counted, and the last arrival reads the slots only after
-    // its own count returned; so no L2 write-back or invalidate is needed
-    // (an agent-scope release fence per workgroup costs a whole-L2
-    // write-back, measured at ~20 us per 64x4096x4096 call).
+    // Per wave: this range's 32 rows into its workspace slot (lane order),
+    // then the arrival count of (tile, wave).  The slots are written and
+    // read with the agent-coherent cache policy (sc1: written through the
+    // XCD's L2, read past stale L2 lines), each writer waits for its stores
+    // to complete before its arrival is counted, and the last arrival reads
+    // the slots only after its own count returned; so no L2 write-back or
+    // invalidate is needed (an agent-scope release fence per workgroup costs
+    // a whole-L2 write-back, measured at ~20 us per 64x4096x4096 call).
+    // Every slot is read back, this wave's own included: the same additions
+    // in range order whichever wave comes last.
     const __amdgpu_buffer_rsrc_t pr =
         make_rsrc(part + (int64_t)tile * S * SK_TILE, (int64_t)S * SK_TILE * 4);
-    const int pv = ((wv * 4) * 64 + lane) * 16;  // bytes; + 1024 per (rt, tt) pair
-    if (half == 0) {
+    const int pv = ((wv * 4) * 64 + lane) * 16;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, yacc[c >> 1][c & 1]), pr,
+                                             pv + 1024 * c, s * SK_TILE * 4, kCoherent);
+    __builtin_amdgcn_s_waitcnt(0);
+    unsigned old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(&cnt[tile * 4 + wv], 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    old = (unsigned)__builtin_amdgcn_readfirstlane((int)old);
+    if (old != (unsigned)(S - 1)) return;  // wave-uniform
+    if (lane == 0)
+      __hip_atomic_store(&cnt[tile * 4 + wv], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      yacc[c >> 1][c & 1] = __builtin_bit_cast(
+          floatx4, __builtin_amdgcn_raw_buffer_load_b128(pr, pv + 1024 * c, 0, kCoherent));
+    for (int s2 = 1; s2 < S; ++s2) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, yacc[c >> 1][c & 1]), pr,
-                                               pv + 1024 * c, s * SK_TILE * 4, kCoherent);
-      __builtin_amdgcn_s_waitcnt(0);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned old =
-          __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int last = old == (unsigned)(S - 1);
-      if (last) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sk_last = last;
-    }
-    __syncthreads();
-    if (!sk_last) return;  // workgroup-uniform
-    if (half == 0) {
-      // every slot read back, this workgroup's own included: the same
-      // additions in range order whichever workgroup comes last
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        yacc[c >> 1][c & 1] = __builtin_bit_cast(
-            floatx4, __builtin_amdgcn_raw_buffer_load_b128(pr, pv + 1024 * c, 0, kCoherent));
-      for (int s2 = 1; s2 < S; ++s2) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          yacc[c >> 1][c & 1] += __builtin_bit_cast(
-              floatx4,
-              __builtin_amdgcn_raw_buffer_load_b128(pr, pv + 1024 * c, s2 * SK_TILE * 4, kCoherent));
-      }
+        yacc[c >> 1][c & 1] += __builtin_bit_cast(
+            floatx4,
+            __builtin_amdgcn_raw_buffer_load_b128(pr, pv + 1024 * c, s2 * SK_TILE * 4, kCoherent));
     }
   }
 
-  // ---- store through LDS: lane (token i16, group g) holds rows 4g .. 4g+3
-  constexpr int TY = SK_ROWS + 4;
-  float *ty = reinterpret_cast<float *>(lds) + SK_WAVES / 2 * 4 * 64 * 4;
-  if (half == 0) {
+  // lane (token i16, group g) holds rows 4g .. 4g+3 of each (row tile, token tile)
+  const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-        *reinterpret_cast<floatx4 *>(&ty[(16 * tt + i16) * TY + 32 * wv + 16 * rt + 4 * g]) =
-            yacc[rt][tt];
-  }
-  __syncthreads();
-  for (int o = tid; o < SK_TILE; o += SK_THREADS) {
-    const int tok = o / SK_ROWS, rr = o % SK_ROWS;
-    if (tok0 + tok < M && row0 + rr < N) Y[(int64_t)(tok0 + tok) * N + row0 + rr] = ty[tok * TY + rr];
-  }
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tok = tok0 + 16 * tt + i16, row = row0 + 32 * wv + 16 * rt + 4 * g;
+      if (tok >= M) continue;
+      float *yr = Y + (int64_t)tok * N + row;
+      if (vec && row < N) {
+        *reinterpret_cast<floatx4 *>(yr) = yacc[rt][tt];
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (row + k < N) yr[k] = yacc[rt][tt][k];
+      }
+    }
 }
 
 }  // namespace
@@ -521,13 +518,14 @@ SplitkPlan splitk_plan(int64_t M, int64_t K, int64_t N, int ranges) {
   const int64_t smax = nb / 2 < 1 ? 1 : nb / 2;  // at least one super-block per half
   if (S > smax) S = smax;
   if (S > kSplitkMaxRanges) S = kSplitkMaxRanges;
-  if (tiles >= 256) S = 1;  // the counters' region holds 256
+  if (tiles >= 256) S = 1;  // the counters' region holds 4 per tile for 256 tiles
   p.S = (int)S;
   // S > 1 only below 256 tiles, so the counters fit their fixed region
   p.counter_bytes = S > 1 ? kSplitkCounterBytes : 0;
   p.workspace_bytes = S > 1 ? p.counter_bytes + tiles * S * SK_TILE * 4 : 0;
   static_assert(kSplitkCounterBytes + 255 * kSplitkMaxRanges * SK_TILE * 4 <= kSplitkWorkspaceBytes,
                 "the library's workspace holds every plan");
+  static_assert(255 * (SK_WAVES / 2) * 4 <= kSplitkCounterBytes, "one counter per (tile, wave)");
   return p;
 }
 
