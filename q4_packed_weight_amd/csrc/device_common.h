@@ -243,10 +243,28 @@ __device__ __forceinline__ float wave_max_nonneg_v(float v) {
   return __builtin_bit_cast(float, b);
 }
 
+// v + v of lane i ^ 16 (width 32) or i ^ 32 (width 64), in every lane:
+// gfx950's lane-swap instructions exchange neighbouring 16-lane rows (or
+// the two 32-lane halves) in a vector register, so the partner's value
+// arrives without an LDS round trip; fp32 addition is commutative, so the
+// bits are those of v + partner in either order.  The two results are
+// copied into integers before the float conversion: this compiler turns
+// __builtin_bit_cast(float, h[1]) of the swap's result pair into a second
+// read of h[0] (the sum then comes out as 2 * h[0]).
+template <int width>
+__device__ __forceinline__ float add_partner_row(float v) {
+  static_assert(width == 32 || width == 64, "rows of 16 or halves of 32 lanes");
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto h = width == 32 ? __builtin_amdgcn_permlane16_swap(b, b, false, false)
+                             : __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  const uint32_t own_or_partner0 = h[0], own_or_partner1 = h[1];
+  return __uint_as_float(own_or_partner0) + __uint_as_float(own_or_partner1);
+}
+
 // Sum over aligned groups of `width` lanes (width a power of two <= 64);
 // every lane of the group receives the group sum.  Steps below 16 lanes use
-// DPP quad permutes and row mirrors; the 16- and 32-lane steps use
-// ds_swizzle-free bpermute via __shfl_xor (issued once per output).
+// DPP quad permutes and row mirrors; the 16- and 32-lane steps use the lane
+// swaps (add_partner_row).
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (width >= 2)
@@ -261,8 +279,8 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (width >= 16)
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
         __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)); // row_mirror
-  if constexpr (width >= 32) v += __shfl_xor(v, 16, 64);
-  if constexpr (width >= 64) v += __shfl_xor(v, 32, 64);
+  if constexpr (width >= 32) v = add_partner_row<32>(v);
+  if constexpr (width >= 64) v = add_partner_row<64>(v);
   return v;
 }
 

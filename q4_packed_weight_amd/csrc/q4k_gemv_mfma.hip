@@ -262,8 +262,8 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
   }
 
   // Sum the four lane groups (lanes n, n+16, n+32, n+48), then the waves.
-  yacc += __shfl_xor(yacc, 16, 64);
-  yacc += __shfl_xor(yacc, 32, 64);
+  yacc = add_partner_row<32>(yacc);
+  yacc = add_partner_row<64>(yacc);
   if (lane < MV_ROWS) part[wave][lane] = yacc;
   __syncthreads();
   if (tid < MV_ROWS) {
