@@ -54,8 +54,10 @@ ROTATION_BYTES = 2 * 256 * 2 ** 20
 
 
 def kernel_hash(files):
+    """Hash of a kernel's sources and of the build script that holds the
+    compile flags (a committed profile is valid only for the same code)."""
     h = hashlib.sha256()
-    for f in files:
+    for f in list(files) + ["q4_packed_weight_amd/build.py"]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
