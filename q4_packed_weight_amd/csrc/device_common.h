@@ -168,6 +168,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base,
                                            0x00020000);
 }
 
+// The same view when the caller knows 0 <= bytes < 2^31: no 64-bit clamp,
+// so fewer scalar instructions ahead of a kernel's first load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc32(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // 16-byte loads through a buffer view at a byte offset; the streaming form
 // sets the non-temporal hint (aux bit 1 on gfx94x/gfx950).
 // `soff` is an optional wave-uniform part of the offset (the instruction's

@@ -88,14 +88,16 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
   const int g = lane >> 4;  // lane group: positions 8g .. 8g+7
   const int row0 = blockIdx.x * MV_ROWS;
   const int row_bytes = nb * kBlockBytes;
-  // this wave's super-blocks [b_lo, b_hi)
-  const int b_lo = (int)(((int64_t)nb * wave) / MV_WAVES);
-  const int b_hi = (int)(((int64_t)nb * (wave + 1)) / MV_WAVES);
+  // this wave's super-blocks [b_lo, b_hi) (nb * 16 < 2^31)
+  const int b_lo = (int)((unsigned)(nb * wave) / MV_WAVES);
+  const int b_hi = (int)((unsigned)(nb * (wave + 1)) / MV_WAVES);
   const int n_chunks = (b_hi - b_lo + MV_CB - 1) / MV_CB;
 
+  // A workgroup reads its own 16 rows only; 16 rows and x stay below 2^31
+  // bytes (input_dim <= 2^24, checked by the host).
   const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(w + (int64_t)row0 * row_bytes, (int64_t)(N - row0) * row_bytes);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)nb * 1024);
+      make_rsrc32(w + (int64_t)row0 * row_bytes, (uint32_t)min(N - row0, MV_ROWS) * (uint32_t)row_bytes);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc32(x, (uint32_t)nb * 1024u);
 
   // Load roles: weight chunk q (clamped; the duplicates are never stored)
   // is row q / (9 MV_CB), chunk q % (9 MV_CB) of the row's piece of the chunk;
@@ -116,6 +118,12 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
 #pragma unroll
     for (int m = 0; m < MV_WPL; ++m) wv[m] = load_buf_stream16(wr, woff[m], kBlockBytes * b0);
   };
+
+  // The first chunk's loads leave before the rest of the set-up below (the
+  // operand indices, the zero areas), which then runs while they are in
+  // flight.
+  if (n_chunks > 0) load_chunk(0, wa, xa);
+  __builtin_amdgcn_sched_barrier(0);
 
   uint32_t *wtw = wt[wave];
   auto stage_chunk = [&](const uint4 (&wv)[MV_WPL], const float4 (&xv)[MV_XPL]) {
@@ -244,7 +252,6 @@ __global__ __launch_bounds__(64 * MV_WAVES) void q4k_gemv_mfma_kernel(
   // the zero areas (64 dwords per wave, read after this wave's own stores)
   xhl[wave][MV_XZ + lane] = 0u;
   if (n_chunks > 0) {  // wave-uniform
-    load_chunk(0, wa, xa);
     for (int c = 0;;) {
       const bool more = c + 1 < n_chunks;
       if (more) load_chunk(c + 1, wb, xb);

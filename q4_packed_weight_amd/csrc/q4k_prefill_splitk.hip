@@ -139,16 +139,22 @@ __global__ __launch_bounds__(SK_THREADS) void q4k_prefill_splitk_kernel(
   const int g = lane >> 4;
 
   // ---- work item (consecutive numbers on one XCD)
-  const int G = gridDim.x, L = blockIdx.x;
-  const int xcd = L & 7, q8 = G >> 3, r8 = G & 7;
-  const int work = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + (L >> 3);
-  const int tti = work % n_tt;
-  const int rest = work / n_tt;
-  const int rti = rest % n_rt;
-  const int s = rest / n_rt;
+  // Every quantity here is non-negative and below 2^31 (the launcher
+  // checks the grid; s * nb < 8 * 2^17), so unsigned 32-bit divisions give
+  // the same values as signed or 64-bit ones at a fraction of the
+  // instructions, all of which run before the first load.
+  const unsigned G = gridDim.x, L = blockIdx.x;
+  const unsigned xcd = L & 7, q8 = G >> 3, r8 = G & 7;
+  const unsigned work = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + (L >> 3);
+  const unsigned rest = work / (unsigned)n_tt;
+  const int tti = (int)(work - rest * (unsigned)n_tt);
+  const unsigned sq = rest / (unsigned)n_rt;
+  const int rti = (int)(rest - sq * (unsigned)n_rt);
+  const int s = (int)sq;
   const int tile = rti * n_tt + tti;
   const int row0 = rti * SK_ROWS, tok0 = tti * SK_TOK;
-  const int b0 = (int)((int64_t)s * nb / S), b1 = (int)((int64_t)(s + 1) * nb / S);
+  const int b0 = (int)((unsigned)(s * nb) / (unsigned)S);
+  const int b1 = (int)((unsigned)((s + 1) * nb) / (unsigned)S);
   const int n_steps = (b1 - b0 + 1) >> 1;
   const int K = nb * 256;
   const int row_bytes = nb * kBlockBytes;
