@@ -281,7 +281,11 @@ struct Q6K {
   }
 };
 
-template <class F, int L, int R, int KW, int W>
+// ONE: every wave's part of input_dim fits one iteration (4 nb <= L KW).
+// Its loads then leave before the rest of the set-up, with no loop around
+// them (a load phase peeled off a general loop keeps its registers live
+// through the body and costs occupancy at large grids).
+template <class F, int L, int R, int KW, int W, bool ONE>
 __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
     const float *x, const uint8_t *w, float *__restrict__ y, int nb,
     int64_t N) {
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
   const int64_t row0 = (int64_t)blockIdx.x * (RG * ROWS_W) + (int64_t)rg * ROWS_W;
   const int n_slabs = 4 * nb;
   const int steps = (n_slabs + L - 1) / L;
-  const int iters = (steps + KW - 1) / KW;
+  const int iters = ONE ? 1 : (steps + KW - 1) / KW;
   const int64_t row_bytes = (int64_t)nb * F::kBlockBytes;
   const int j = u & 3;
   const uint32_t sh = (uint32_t)(j & 1) * 16u;
@@ -344,33 +348,32 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
   const int64_t wg_row0 = (int64_t)blockIdx.x * (RG * ROWS_W);
   const int64_t wg_byte0 = wg_row0 * row_bytes;
   const int64_t wg_base = F::kUnaligned ? (wg_byte0 & ~(int64_t)15) : wg_byte0;
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)nb * 1024);
-  const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(w + wg_base, ((N * row_bytes + 3) & ~(int64_t)3) - wg_base);
+  // The view covers this workgroup's rows (fewer at the end of the matrix)
+  // to their last byte rounded up to a dword; the launcher keeps that below
+  // 2^31 bytes, so the size needs no 64-bit clamp ahead of the first load.
+  const int64_t rows_here = N - wg_row0 < RG * ROWS_W ? N - wg_row0 : RG * ROWS_W;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc32(x, (uint32_t)nb * 1024u);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc32(
+      w + wg_base, (uint32_t)(((wg_byte0 + rows_here * row_bytes + 3) & ~(int64_t)3) - wg_base));
   const int wave_off = (int)(wg_byte0 - wg_base + (row0 - wg_row0) * row_bytes);
 
-  float acc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-
-  for (int it = 0; it < iters; ++it) {
-    // 1. Load phase.  Activations for staging first (coalesced, L2-resident,
-    //    they return first), then this wave's weight tile as a coalesced
-    //    stream: chunk q of the tile is row q / CH_ROWP of the wave, chunk
-    //    q % CH_ROWP of this step's piece of that row (from the piece's
-    //    first byte rounded down to 16).  Slabs past the end of x and rows
-    //    past N read as zeros; blocks past the end of a row read the next
-    //    row's bytes and are never consumed.
+  // 1. Load phase of iteration it.  Activations for staging first
+  //    (coalesced, L2-resident, they return first), then this wave's weight
+  //    tile as a coalesced stream: chunk q of the tile is row q / CH_ROWP of
+  //    the wave, chunk q % CH_ROWP of this step's piece of that row (from
+  //    the piece's first byte rounded down to 16).  Slabs past the end of x
+  //    and rows past N read as zeros; blocks past the end of a row read the
+  //    next row's bytes and are never consumed.
+  float4 xv[XQ];
+  uint4 wv[NM];
+  auto load_phase = [&](int it) {
     const int slab_base = it * S;
-    float4 xv[XQ];
 #pragma unroll
     for (int q = 0; q < XQ; ++q) {
       const int f = min(tid + kThreads * q, XF - 1);
       xv[q] = load_buf_f4(xr, 4 * (64 * (slab_base + (f >> 4)) + 4 * (f & 15)));
     }
-    const int t = it * KW + kw;
-    const int b0 = t * BPS;
-    uint4 wv[NM];
+    const int b0 = (it * KW + kw) * BPS;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const int q = 64 * m + lane;
@@ -379,6 +382,20 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_kernel(
       const int start = wave_off + rt * (int)row_bytes + b0 * F::kBlockBytes;
       wv[m] = load_buf_stream16(wr, (start & ~15) + 16 * within);
     }
+  };
+  if constexpr (ONE) {
+    load_phase(0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (!ONE) load_phase(it);
+    const int t = it * KW + kw;
+    const int b0 = t * BPS;
     // Keep the LDS stores below from being hoisted above the load phase.
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -630,6 +647,9 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, int nb,
   constexpr int64_t rows_per_wg = (int64_t)(W / KW) * G * R;
   const int64_t grid = (N + rows_per_wg - 1) / rows_per_wg;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  // a workgroup's rows (its buffer view, plus alignment) stay below 2^31
+  // bytes; every shape the library picks for input_dim <= 2^24 does
+  if (rows_per_wg * nb * F::kBlockBytes + 32 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   if constexpr (KW == 1 && W == 4) {
     // One step per row and more units than resident slots: walk the units
     // with as few workgroups as give every workgroup the same unit count.
@@ -641,8 +661,16 @@ hipError_t launch_gemv(const float *x, const uint8_t *w, float *y, int nb,
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((q4k_gemv_kernel<F, L, R, KW, W>), dim3((unsigned)grid),
-                     dim3(64 * W), 0, stream, x, w, y, nb, N);
+  if (4 * (int64_t)nb <= L * KW) {
+    hipLaunchKernelGGL((q4k_gemv_kernel<F, L, R, KW, W, true>), dim3((unsigned)grid),
+                       dim3(64 * W), 0, stream, x, w, y, nb, N);
+  } else if constexpr (L == 64) {
+    hipLaunchKernelGGL((q4k_gemv_kernel<F, L, R, KW, W, false>), dim3((unsigned)grid),
+                       dim3(64 * W), 0, stream, x, w, y, nb, N);
+  } else {
+    // 16 or 32 lanes are only chosen for rows of one step (4 nb <= L)
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
   }
 }

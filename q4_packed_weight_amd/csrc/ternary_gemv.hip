@@ -33,7 +33,9 @@ __device__ __forceinline__ float comp(float4 v, int f) {
   return f == 0 ? v.x : (f == 1 ? v.y : (f == 2 ? v.z : v.w));
 }
 
-template <int R>
+// ONE: input_dim fits one iteration (n_items <= 64); its loads then leave
+// before the rest of the set-up, with no loop around them.
+template <int R, bool ONE>
 __global__ __launch_bounds__(kThreads) void ternary_gemv_kernel(
     const float *x, const uint8_t *codes, float *__restrict__ y, float scale,
     int apply_scale, int n_items, int64_t N) {
@@ -58,10 +60,37 @@ __global__ __launch_bounds__(kThreads) void ternary_gemv_kernel(
   const int64_t row0 = wg_row0 + (int64_t)wave * R;
   const int row_bytes = n_items * 16;
   // Range-checked views: rows past N and items past the end read as zeros.
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)n_items * 256);
-  const __amdgpu_buffer_rsrc_t cr =
-      make_rsrc(codes + wg_row0 * row_bytes, (N - wg_row0) * (int64_t)row_bytes);
+  // The workgroup reads its own 4R rows only; they and x stay below 2^31
+  // bytes (input_dim <= 2^24, checked by the host), so the sizes need no
+  // 64-bit clamp ahead of the first load.
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc32(x, (uint32_t)n_items * 256u);
+  const int64_t rows_left = N - wg_row0;
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc32(
+      codes + wg_row0 * row_bytes,
+      (uint32_t)(rows_left < (kThreads / 64) * R ? rows_left : (kThreads / 64) * R) *
+          (uint32_t)row_bytes);
   const int wave_off = wave * R * row_bytes;
+
+  // Load phase of iteration it: activations for staging (coalesced), then
+  // the 16 code bytes of this lane's item in each of the R rows (coalesced
+  // rows).
+  float4 xv[XQ];
+  uint4 cw[R];
+  auto load_phase = [&](int it) {
+    const int item_base = it * S;
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+      const int f = tid + kThreads * q;
+      xv[q] = load_buf_f4(xr, 4 * (64 * (item_base + (f >> 4)) + 4 * (f & 15)));
+    }
+    const int i = item_base + lane;
+#pragma unroll
+    for (int r = 0; r < R; ++r) cw[r] = load_buf_stream16(cr, wave_off + r * row_bytes + 16 * i);
+  };
+  if constexpr (ONE) {
+    load_phase(0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   float acc[R][4];
 #pragma unroll
@@ -70,21 +99,10 @@ __global__ __launch_bounds__(kThreads) void ternary_gemv_kernel(
     for (int f = 0; f < 4; ++f) acc[r][f] = 0.f;
   float xsum = 0.f;
 
-  const int iters = (n_items + S - 1) / S;
+  const int iters = ONE ? 1 : (n_items + S - 1) / S;
   for (int it = 0; it < iters; ++it) {
-    // Load phase: activations for staging (coalesced), then the 16 code
-    // bytes of this lane's item in each of the R rows (coalesced rows).
-    const int item_base = it * S;
-    float4 xv[XQ];
-#pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-      const int f = tid + kThreads * q;
-      xv[q] = load_buf_f4(xr, 4 * (64 * (item_base + (f >> 4)) + 4 * (f & 15)));
-    }
-    const int i = item_base + lane;
-    uint4 cw[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) cw[r] = load_buf_stream16(cr, wave_off + r * row_bytes + 16 * i);
+    if constexpr (!ONE) load_phase(it);
+    const int i = it * S + lane;
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
@@ -178,9 +196,14 @@ hipError_t launch_fast(const float *x, const uint8_t *codes, float scale,
   // per-workgroup code offsets must stay below 2^31
   if (rows_per_wg * (K / 4) >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((ternary_gemv_kernel<R>), dim3((unsigned)grid),
-                     dim3(kThreads), 0, s, x, codes, y, scale, apply ? 1 : 0,
-                     (int)(K / 64), N);
+  if (K <= 64 * 64)
+    hipLaunchKernelGGL((ternary_gemv_kernel<R, true>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, s, x, codes, y, scale, apply ? 1 : 0,
+                       (int)(K / 64), N);
+  else
+    hipLaunchKernelGGL((ternary_gemv_kernel<R, false>), dim3((unsigned)grid),
+                       dim3(kThreads), 0, s, x, codes, y, scale, apply ? 1 : 0,
+                       (int)(K / 64), N);
   return hipGetLastError();
 }
 
