@@ -114,13 +114,13 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_kernel(
   const int rg0 = blockIdx.x * rg_per_wg;
   const int rgn = min(rg_per_wg, NG - rg0);
 
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(
-      wt + (int64_t)rg0 * nb * kTileBytes, (int64_t)rgn * nb * kTileBytes);
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (int64_t)nb * 1024);
+  // The workgroup's tiles (at most four row groups) and x stay below 2^31
+  // bytes (input_dim <= 2^24), so the sizes need no 64-bit clamp ahead of
+  // the first load and kPastEnd lies past the view's end.
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc32(
+      wt + (int64_t)rg0 * nb * kTileBytes, (uint32_t)rgn * (uint32_t)nb * (uint32_t)kTileBytes);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc32(x, (uint32_t)nb * 1024u);
   constexpr int kPastEnd = 0x7FFFF000;  // a tile or activation offset that reads zeros
-
-#pragma unroll
-  for (int r = 0; r < kMaxRowGroups; ++r) part[wave][r][lane] = 0.f;
 
   const int vq0 = 16 * lane, vq1 = 1024 + 16 * lane, vhd = 2048 + 16 * n;
   uint4 wq0[D], wq1[D], whd[D];
@@ -187,6 +187,11 @@ __global__ __launch_bounds__(64 * W) void q4k_gemv_tiled_kernel(
     for (int s = 0; s < D; ++s) {
       load_unit(s, li, lbl, s < T);
       advance(li, lbl);
+    }
+    if (c0 == 0) {  // once the first loads have left
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < kMaxRowGroups; ++r) part[wave][r][lane] = 0.f;
     }
 
     if constexpr (!PRIV) {
