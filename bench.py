@@ -608,19 +608,20 @@ def traffic_for(wl):
     return t.get("traffic_bytes_per_launch")
 
 
-def trace_for(wl):
-    """Average kernel-trace duration (us per step, rocprofv3 --kernel-trace)
-    from the committed profile summary, if it was taken on the current
-    kernel source; else None."""
+def trace_for(wl, key="trace_avg_ns_per_step"):
+    """Average (or, with key trace_median_ns_per_step, median) kernel-trace
+    duration (us per step, rocprofv3 --kernel-trace) from the committed
+    profile summary, if it was taken on the current kernel source; else
+    None."""
     name = TRAFFIC_FILES.get(wl.name)
     path = os.path.join(ROOT, "profiles", name) if name else None
     if not path or not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_hash") != kernel_hash(wl.src_files) or "trace_avg_ns_per_step" not in t:
+    if t.get("kernel_hash") != kernel_hash(wl.src_files) or key not in t:
         return None
-    return round(t["trace_avg_ns_per_step"] / 1000.0, 3)
+    return round(t[key] / 1000.0, 3)
 
 
 def main():
@@ -732,6 +733,7 @@ def main():
                                                min(max(DELAY_NS, EAGER_DELAY_NS_PER_STEP * steps),
                                                    100_000_000)) / 1e6
         ctx["kernel_trace_avg_us_per_step"] = trace_for(wl)
+        ctx["kernel_trace_median_us_per_step"] = trace_for(wl, "trace_median_ns_per_step")
         line["context"] = ctx
     if not args.no_cpu_baseline and wl.cpu is not None:
         print(f"[bench] timing the CPU oracle (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
