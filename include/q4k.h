@@ -73,9 +73,9 @@ extern "C" {
  * about 7.9e28) and a persistent matrix-core walk (the same arithmetic;
  * workgroups walk groups of 16 rows x one super-block, the next ones in
  * flight).  Where each measured fastest on MI355X, the call picks the walk
- * for large matrices (output_dim >= 4096 with input_dim >= 8192, or
+ * for large matrices (output_dim >= 3072 with input_dim >= 5120, or
  * output_dim >= 11008 with input_dim >= 4096), the matrix-core form when
- * ceil(output_dim/16) is 240..256 and input_dim/256 is 8..24, else the
+ * ceil(output_dim/16) is 192..256 and input_dim/256 is 12..19, else the
  * vector form; q4k_gemv_shaped and q4k_gemv_walk_shaped select one
  * explicitly.
  */

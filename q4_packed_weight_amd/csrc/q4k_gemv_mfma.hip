@@ -582,12 +582,16 @@ void launch_walk(const float *x, const uint8_t *w, float *y, int64_t nb, int64_t
 }  // namespace
 
 bool use_gemv_mfma(int64_t nb, int64_t N) {
-  // Measured (graph-replayed calls over rotating weights, input_dim 2048 to
-  // 6144, output_dim 2048 to 12288): the matrix-core form wins when its
-  // grid fills the 256 CUs once, one 16-wave workgroup each; with more
-  // workgroups than CUs the vector kernel's several-per-CU occupancy wins.
+  // Measured (graph-replayed calls over rotating weights, input_dim and
+  // output_dim 2048 to 8192; us/call, vector form / this form): the
+  // matrix-core form wins when its grid fills 192 to 256 CUs once, one
+  // 16-wave workgroup each, with 12 to 16 super-blocks a row (3072x3072
+  // 4.06 / 3.56, 4096->3072 4.16 / 3.64, 3072->4096 4.11 / 3.77, 4096x4096
+  // 4.39 / 3.91); with 8 super-blocks (2048->4096 3.12 / 3.46), on 128
+  // workgroups (4096->2048 3.31 / 3.42) or past 256 the vector kernel's
+  // several-per-CU occupancy wins, and from 20 super-blocks the walk does.
   const int64_t grid = (N + MV_ROWS - 1) / MV_ROWS;
-  return grid >= 240 && grid <= 256 && nb >= 8 && nb <= 24;
+  return grid >= 192 && grid <= 256 && nb >= 12 && nb <= 19;
 }
 
 hipError_t gemv_mfma_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
@@ -619,15 +623,19 @@ WalkShape choose_walk_shape(int64_t nb, int64_t N, int waves, int row_groups, in
 
 bool use_gemv_walk(int64_t nb, int64_t N) {
   // Measured (graph-replayed calls over rotating weights, input_dim 2048 to
-  // 28672, output_dim 1024 to 28672; current choice / walk with 8 waves and
-  // 2 units ahead, us/call): the walk wins once the matrix is large,
-  // 4096->14336 10.17 / 9.62, 14336->4096 11.37 / 9.89, 8192->4096 7.02 /
-  // 6.75, 11008->11008 28.3 / 17.6, 28672->28672 123.0 / 98.1, and loses on
-  // small grids (4096x4096 4.40 / 5.27, 14336->2048 7.89 / 8.78, 4096->8192
-  // 6.68 / 6.83).  The offsets its launch forms must fit (four row groups).
+  // 28672, output_dim 1024 to 28672; best other form / walk with 8 waves
+  // and 2 units ahead, us/call): the walk wins once rows hold 20
+  // super-blocks or more and output_dim is 3072 or more, 5120->3072 5.17 /
+  // 4.77, 5120x5120 8.10 / 7.03, 6144->4096 5.95 / 5.67, 6144->8192 10.22 /
+  // 7.71, 8192x8192 10.73 / 9.45, 14336->4096 11.37 / 9.89, 28672->28672
+  // 123.0 / 98.1, and for 16 super-blocks from output_dim 11008 (4096->14336
+  // 10.17 / 9.62); it loses at output_dim 2048 (8192->2048 4.27 / 5.79,
+  // 14336->2048 7.89 / 8.78) and with 16 super-blocks below 11008 rows
+  // (4096x4096 3.91 / 4.71, 4096->8192 5.95 / 6.28).  The offsets its launch
+  // forms must fit (four row groups).
   if ((int64_t)WK_MAX_RG * MV_ROWS * nb * kBlockBytes > 0x7FFF0000 || nb * 1024 > 0x7FFF0000)
     return false;
-  return (N >= 4096 && nb >= 32) || (N >= 11008 && nb >= 16);
+  return (N >= 3072 && nb >= 20) || (N >= 11008 && nb >= 16);
 }
 
 hipError_t gemv_walk_launch(const float *x, const uint8_t *w, float *y, int64_t nb, int64_t N,

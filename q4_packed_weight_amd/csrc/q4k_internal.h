@@ -33,8 +33,9 @@ hipError_t gemv_q6k_launch(const float *x, const uint8_t *w, float *y, int64_t n
 hipError_t gemv_mfma_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
                             int64_t N, hipStream_t stream);
 // Whether q4k_gemv's automatic choice is the matrix-core form (measured on
-// MI355X: it wins while every wave owns at most one super-block and all
-// workgroups are resident at once).
+// MI355X: it wins with 12 to 19 super-blocks a row, so that every wave owns
+// at most one super-block and the row is long enough, and 192 to 256
+// workgroups, all resident at once).
 bool use_gemv_mfma(int64_t nb, int64_t N);
 // The persistent matrix-core walk over canonical rows: workgroups of
 // `waves` waves own `row_groups` consecutive groups of 16 rows; each wave
@@ -49,7 +50,7 @@ WalkShape choose_walk_shape(int64_t nb, int64_t N, int waves, int row_groups, in
 hipError_t gemv_walk_launch(const float *x, const uint8_t *w, float *y, int64_t nb, int64_t N,
                             const WalkShape &s, hipStream_t stream);
 // Whether q4k_gemv's automatic choice is the walk (measured on MI355X: large
-// matrices, from output_dim 4096 with input_dim 8192, or output_dim 11008
+// matrices, from output_dim 3072 with input_dim 5120, or output_dim 11008
 // with input_dim 4096).
 bool use_gemv_walk(int64_t nb, int64_t N);
 

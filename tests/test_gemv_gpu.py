@@ -133,6 +133,29 @@ def test_walk_integer_bit_exact(oracle_lib, K, N, wf):
     assert np.array_equal(y.astype(np.float64), oracle_lib.q4k_gemv(x, w, K, N))
 
 
+# (K, N, form q4k_gemv takes): each side of the measured boundaries between
+# the vector form, the matrix-core form and the walk.
+AUTO_CHOICES = [(2048, 4096, "vector"), (3072, 3072, "mfma"), (3072, 4096, "mfma"),
+                (4096, 2048, "vector"), (4096, 4096, "mfma"), (4096, 8192, "vector"),
+                (4864, 3072, "mfma"), (5120, 3072, "walk"), (6144, 4096, "walk"),
+                (8192, 2048, "vector"), (5120, 5120, "walk")]
+
+
+@pytest.mark.parametrize("K,N,form", AUTO_CHOICES)
+def test_automatic_choice_is_the_measured_form(oracle_lib, K, N, form):
+    """q4k_gemv equals, bit for bit, the form it is documented to take at
+    this shape, and matches the oracle."""
+    w = synth.q4k_weights(N, K, config=26, copy=K + N)
+    x = synth.activations(K, config=26, copy=K + N)
+    y = run_gemv(x, w, K, N)
+    assert_parity(y, oracle_lib.q4k_gemv(x, w, K, N), what=f"auto K={K} N={N}")
+    if form == "walk":
+        y2 = run_gemv(x, w, K, N, walk=(0, 0, 0))
+    else:
+        y2 = run_gemv(x, w, K, N, shape=(0, 0, 16 if form == "mfma" else 0))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), form
+
+
 @pytest.mark.parametrize("K,N", [(4096, 14341), (8192, 4096), (11008, 4096)])
 def test_walk_automatic_choice(oracle_lib, K, N):
     """Shapes q4k_gemv hands to the walk: four row groups per workgroup with
