@@ -66,6 +66,7 @@ def kernel_hash(files):
 GEMV_SRC = ["q4_packed_weight_amd/csrc/q4k_gemv.hip",
             "q4_packed_weight_amd/csrc/q4k_gemv_mfma.hip",
             "q4_packed_weight_amd/csrc/device_common.h"]
+Q40_SRC = GEMV_SRC + ["q4_packed_weight_amd/csrc/q4_0_gemv_mfma.hip"]
 PREFILL_SRC = ["q4_packed_weight_amd/csrc/q4k_prefill_splitk.hip",
                "q4_packed_weight_amd/csrc/device_common.h"]
 TERNARY_SRC = ["q4_packed_weight_amd/csrc/ternary_gemv.hip",
@@ -258,8 +259,8 @@ def make_workload(name, torch, binding, synth):
         wl.copies = copies
         wl.bytes = wbytes + 4 * K + 4 * N
         wl.flops = 2 * K * N
-        wl.kernel = "q4k_gemv_kernel<Q40, 64, 4, 1, 4>"
-        wl.src_files = GEMV_SRC
+        wl.kernel = "q4_0_gemv_mfma_kernel"
+        wl.src_files = Q40_SRC
         wl.data = "synthetic (seeded numpy generators; random Q4_0 blocks, N(0,1) activations)"
         wl.config = {"workload": f"q4_0_gemv {K}x{N} batch 1", "input_dim": K,
                      "output_dim": N, "batch": 1, "rotating_copies": copies,

@@ -149,8 +149,13 @@ int q4k_matmul(const float *X, const uint8_t *w_blocks, int64_t n_tokens,
  *              blocks, which keeps every row 16-byte aligned.
  *   output_dim N > 0
  *   y          fp32 [output_dim]
- * Same error behaviour, determinism and tolerance as q4k_gemv (vector
- * form; |x| should stay above ~1e-30 for full precision).
+ * Same error behaviour, determinism and tolerance as q4k_gemv.  Two kernels
+ * compute it: the vector form (|x| should stay above ~1e-30 for full
+ * precision) and a matrix-core form (16x16x32 f16 MFMA over 16 rows and
+ * eight blocks; each block's activations scaled by a power of two and split
+ * into exact fp16 hi and lo halves, for any |x| < 2^96), taken where it
+ * measured fastest on MI355X: ceil(output_dim/16) 192..256 and
+ * input_dim/256 12..24.
  */
 int q4_0_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
               int64_t output_dim, float *y, void *stream);
@@ -158,8 +163,9 @@ int q4_0_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
 /*
  * q4_0_gemv_shaped -- q4_0_gemv with an explicit launch shape; the values
  * of rows_per_lane, k_waves and workgroup_waves are those of
- * q4k_gemv_shaped except that there is no matrix-core form (16 is
- * Q4K_EINVAL_DIM).
+ * q4k_gemv_shaped, workgroup_waves = 16 selecting the matrix-core form
+ * (rows_per_lane and k_waves then 0), which takes input_dim up to 65536
+ * (256 groups of eight blocks; more is Q4K_EINVAL_DIM) and any |x| < 2^96.
  */
 int q4_0_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                      int64_t output_dim, float *y, void *stream,

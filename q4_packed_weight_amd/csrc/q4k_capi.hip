@@ -191,8 +191,14 @@ int q4_0_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
                      int rows_per_lane, int k_waves, int workgroup_waves) {
   int rc = check_q4k(x, w_blocks, y, 1, input_dim, output_dim);
   if (rc) return rc;
-  if (!valid_vector_shape(rows_per_lane, k_waves, workgroup_waves)) return Q4K_EINVAL_DIM;
   const int64_t ng = input_dim / 256;
+  if (workgroup_waves == 16) {  // the matrix-core form
+    if (rows_per_lane != 0 || k_waves != 0 || ng > q4k::kQ40MfmaMaxGroups) return Q4K_EINVAL_DIM;
+    hipError_t e = q4k::gemv_q4_0_mfma_launch(x, w_blocks, y, ng, output_dim,
+                                              (hipStream_t)stream);
+    return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4_0_gemv launch");
+  }
+  if (!valid_vector_shape(rows_per_lane, k_waves, workgroup_waves)) return Q4K_EINVAL_DIM;
   const q4k::GemvShape s = q4k::choose_gemv_shape(ng, output_dim, rows_per_lane,
                                                   k_waves, workgroup_waves);
   hipError_t e = q4k::gemv_q4_0_launch(x, w_blocks, y, ng, output_dim, s,
@@ -200,9 +206,23 @@ int q4_0_gemv_shaped(const float *x, const uint8_t *w_blocks, int64_t input_dim,
   return e == hipSuccess ? Q4K_OK : hip_fail(e, "q4_0_gemv launch");
 }
 
+// Measured on MI355X (graph-replayed calls over rotating weights, us/call,
+// vector / matrix-core form): the matrix-core form wins on 192 to 256
+// workgroups with 12 to 24 groups of eight blocks a row, 3072x3072 3.93 /
+// 3.56, 4096->3072 4.03 / 3.66, 3072->4096 4.07 / 3.80, 4096x4096 4.32 /
+// 3.93, 4864->4096 6.02 / 4.80, 5120->4096 5.92 / 5.34 (Q4_0 has no walk to
+// take over from 20 groups); it loses with 8 groups (2048->4096 3.07 /
+// 3.43), on 128 workgroups (4096->2048 3.26 / 3.46) and past 256
+// (4096->5120 5.47 / 5.92).
+static bool use_q4_0_mfma(int64_t ng, int64_t N) {
+  const int64_t grid = (N + 15) / 16;
+  return grid >= 192 && grid <= 256 && ng >= 12 && ng <= 24;
+}
+
 int q4_0_gemv(const float *x, const uint8_t *w_blocks, int64_t input_dim,
               int64_t output_dim, float *y, void *stream) {
-  return q4_0_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0, 0);
+  return q4_0_gemv_shaped(x, w_blocks, input_dim, output_dim, y, stream, 0, 0,
+                          use_q4_0_mfma(input_dim / 256, output_dim) ? 16 : 0);
 }
 
 // Q6_K rows of input_dim/256 210-byte blocks (validation as for Q4_K).  The

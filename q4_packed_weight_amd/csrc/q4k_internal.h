@@ -29,6 +29,13 @@ hipError_t gemv_q4_0_launch(const float *x, const uint8_t *w, float *y, int64_t 
 hipError_t gemv_q6k_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
                            int64_t N, const GemvShape &s, hipStream_t stream);
 
+// The Q4_0 products on the matrix cores (q4_0_gemv_mfma.hip): 16 rows per
+// workgroup, rows of at most kQ40MfmaMaxGroups groups of eight blocks (the
+// codes enter as fp16 subnormals, as in the Q4_K form below).
+constexpr int kQ40MfmaMaxGroups = 256;
+hipError_t gemv_q4_0_mfma_launch(const float *x, const uint8_t *w, float *y, int64_t ngroups,
+                                 int64_t N, hipStream_t stream);
+
 // Q4_K GEMV with the multiplies on the matrix cores (16 rows per workgroup).
 hipError_t gemv_mfma_launch(const float *x, const uint8_t *w, float *y, int64_t nb,
                             int64_t N, hipStream_t stream);

@@ -129,8 +129,10 @@ def test_q4_0_rejects_null_misaligned_and_bad_shape(lib):
     assert lib.q4_0_gemv(GOOD, GOOD2, 256, 8, None, None) == -2
     assert lib.q4_0_gemv(ODD, GOOD2, 256, 8, GOOD3, None) == -3
     assert lib.q4_0_gemv(GOOD, ODD, 256, 8, GOOD3, None) == -3
-    for rpl, kw, wg in [(3, 0, 0), (1, 8, 0), (8, 1, 8), (0, 0, 16)]:
+    for rpl, kw, wg in [(3, 0, 0), (1, 8, 0), (8, 1, 8), (1, 0, 16), (0, 1, 16), (0, 0, 32)]:
         assert lib.q4_0_gemv_shaped(GOOD, GOOD2, 256, 8, GOOD3, None, rpl, kw, wg) == -1
+    # the matrix-core form takes rows of at most 256 groups of eight blocks
+    assert lib.q4_0_gemv_shaped(GOOD, GOOD2, 257 * 256, 8, GOOD3, None, 0, 0, 16) == -1
 
 
 @pytest.mark.parametrize("K", [32, 255, 257, 4000, 0, -256, 1 << 31, (1 << 24) + 256])

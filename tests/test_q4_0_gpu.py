@@ -51,6 +51,79 @@ def test_q4_0_every_launch_shape(oracle_lib, K, N, rpl, kw, wg):
     assert_parity(y, oracle_lib.q4_0_gemv(x, w, K, N), what=f"shape {rpl},{kw},{wg}")
 
 
+# the matrix-core form: one group, fewer groups than waves, ragged rows, the
+# shapes the automatic choice gives it, and the longest rows it takes
+MFMA_SHAPES = [(256, 1), (256, 7), (768, 37), (2304, 129), (3072, 3072), (4096, 4096),
+               (4096, 333), (14336, 100), (65536, 20)]
+MFMA = (0, 0, 16)
+
+
+@pytest.mark.parametrize("K,N", MFMA_SHAPES)
+def test_q4_0_matrix_core_form_parity(oracle_lib, K, N):
+    w = synth.q4_0_weights(N, K, copy=K + 2 * N)
+    x = synth.activations(K, config=synth.Q40_4K, copy=K + 2 * N)
+    y = run(x, w, K, N, shape=MFMA)
+    assert_parity(y, oracle_lib.q4_0_gemv(x, w, K, N), what=f"mfma K={K} N={N}")
+
+
+def test_q4_0_matrix_core_form_one_hot_bit_exact(oracle_lib):
+    """x = e_k through the matrix-core form: every position of a group of
+    eight blocks (block order, nibble-to-element mapping, the realigned
+    code bytes of the odd blocks, the lane groups' A rows) gives d*(q-8)
+    exactly, for 17 rows (two row tiles, the second ragged)."""
+    K, N = 256, 17
+    w = synth.q4_0_weights(N, K, copy=11)
+    wd = dev(w)
+    buf, y = out_with_canary(N)
+    X = np.eye(K, dtype=np.float32)
+    for k in range(K):
+        binding.q4_0_gemv_shaped(dev(X[k]), wd, K, N, y, *MFMA)
+        got = host(y)
+        ref = oracle_lib.q4_0_gemv(X[k], w, K, N).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), k
+    assert canary_intact(buf, N)
+
+
+@pytest.mark.parametrize("K,N", [(4096, 512), (3072, 3072), (65536, 16)])
+def test_q4_0_matrix_core_form_integer_bit_exact(oracle_lib, K, N):
+    w = synth.q4_0_integer_weights(N, K, config=74)
+    x = synth.integer_activations(K, config=74)
+    y = run(x, w, K, N, shape=MFMA)
+    assert np.array_equal(y.astype(np.float64), oracle_lib.q4_0_gemv(x, w, K, N))
+
+
+def test_q4_0_matrix_core_form_wide_range_and_subnormal_d(oracle_lib):
+    """Blocks of activations 2^-40 .. 2^40 apart (some zero, some near the
+    largest finite fp32 the split takes) and binary16 subnormal d."""
+    K, N = 4096, 300
+    w = synth.q4_0_weights(N, K, copy=12).reshape(-1, 18).copy()
+    g = np.random.default_rng(75)
+    sub = g.choice(w.shape[0], w.shape[0] // 3, replace=False)
+    w[sub, 0:2] = g.integers(1, 1024, sub.size).astype(np.uint16).view(np.uint8).reshape(-1, 2)
+    w = w.reshape(N, -1)
+    x = synth.activations(K, config=synth.Q40_4K, copy=12)
+    scale = np.exp2(g.integers(-40, 41, K // 32)).astype(np.float32)
+    scale[g.choice(K // 32, 3, replace=False)] = 0.0
+    scale[5] = np.float32(2.0 ** 90)
+    x = (x.reshape(-1, 32) * scale[:, None]).reshape(-1)
+    y = run(x, w, K, N, shape=MFMA)
+    assert_parity(y, oracle_lib.q4_0_gemv(x, w, K, N), what="mfma wide range")
+    a, b = run(x, w, K, N, shape=MFMA), run(x, w, K, N, shape=MFMA)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("K,N,mfma", [(4096, 4096, True), (3072, 3072, True), (6144, 3072, True),
+                                      (2048, 4096, False), (4096, 2048, False),
+                                      (6400, 4096, False), (4096, 8192, False)])
+def test_q4_0_automatic_choice(oracle_lib, K, N, mfma):
+    """q4_0_gemv equals, bit for bit, the form it is documented to take."""
+    w = synth.q4_0_weights(N, K, copy=13)
+    x = synth.activations(K, config=synth.Q40_4K, copy=13)
+    y = run(x, w, K, N)
+    y2 = run(x, w, K, N, shape=MFMA if mfma else (0, 0, 0))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
 def test_q4_0_one_hot_bit_exact_all_positions(oracle_lib):
     """x = e_k: y[o] is the oracle's fp32 weight d*(q-8) exactly, for every
     position of a 256-weight group (eight blocks) -- pins the block order,
