@@ -37,6 +37,9 @@ def test_q4k_gemv_max_input_dim(oracle_lib, x_max):
     ref = oracle_lib.q4k_gemv(x_max, w, KMAX, N)
     assert_parity(gemv(binding.q4k_gemv, x_max, w, N), ref, what="vector form")
     assert_parity(gemv(binding.q4k_gemv_shaped, x_max, w, N, 0, 0, 16), ref, what="matrix-core form")
+    # the walk q4k_gemv takes for such rows from output_dim 3072 on (one
+    # workgroup here, 8192 units per wave)
+    assert_parity(gemv(binding.q4k_gemv_walk_shaped, x_max, w, N, 0, 0, 0), ref, what="walk")
 
 
 def test_q4k_gemv_tiled_max_input_dim(oracle_lib, x_max):
